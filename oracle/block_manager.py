@@ -1,0 +1,183 @@
+"""Plain Python model of the KV block manager.
+
+Pages cited (by title and section):
+  [OS]  "PagedAttention: How vLLM Serves AI Like an Operating System"
+  [VIZ] "vLLM Architecture and PagedAttention - Interactive Visualization"
+
+What it models:
+  * one pool of fixed 16-token blocks; a per-sequence block table maps
+    logical block i to a physical block; the free list holds blocks no
+    sequence uses ([OS] "PagedAttention: Virtual Memory for KV Cache", How It
+    Works and the memory-layout example with its free list);
+  * allocation on demand: a sequence gets a new block only when a token lands
+    at offset 0 of a fresh block, so a sequence of n tokens holds ceil(n/16)
+    blocks and wastes at most 15 slots ([OS] "The Magic: No Pre-allocation");
+  * release on finish: a finished sequence gives its blocks back at once
+    ([VIZ] Page Table Visualization);
+  * sharing with reference counts and copy-on-write: forks for parallel
+    sampling share every block, sequences on a common system prompt share its
+    blocks, and a shared block is copied before a sequence writes into it
+    ([OS] "Copy-on-Write: Sharing KV Cache", Parallel Sampling and Prefix
+    Caching).
+
+Readings where the pages are silent:
+  * the free list is a queue: allocation takes its head, a block whose
+    reference count drops to zero joins its tail; its initial order is an
+    input (ascending when none is given);
+  * a shared prefix is a whole number of blocks;
+  * a write into a block with reference count > 1 first moves the writer onto
+    a fresh copy (the pair (old, new) is reported for the device copy) and
+    drops one reference from the old block;
+  * a freed sequence releases its blocks in logical order;
+  * every update is all-or-nothing: when the pool cannot supply the blocks an
+    operation needs, it raises NoSpace and leaves the state untouched.
+"""
+
+from collections import deque
+
+BLOCK_SIZE = 16
+
+
+class NoSpace(Exception):
+    """The pool has fewer free blocks than the operation needs."""
+
+
+class BadRequest(Exception):
+    """Unknown / duplicate sequence, or arguments outside the contract."""
+
+
+class RefBlockManager:
+    def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE, free_order=None):
+        if block_size != BLOCK_SIZE:
+            raise BadRequest("block_size must be 16")
+        self.num_blocks = int(num_blocks)
+        order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
+        if sorted(order) != list(range(num_blocks)):
+            raise BadRequest("free_order must be a permutation of the pool")
+        self.free = deque(order)
+        self.ref = [0] * num_blocks
+        self.seqs = {}  # seq id -> {"blocks": [...], "n": tokens}
+
+    # -- queries ---------------------------------------------------------
+    def num_free(self) -> int:
+        return len(self.free)
+
+    def refcount(self, block: int) -> int:
+        return self.ref[block]
+
+    def usage(self) -> float:
+        return (self.num_blocks - len(self.free)) / self.num_blocks
+
+    def blocks_of(self, seq):
+        return list(self.seqs[seq]["blocks"])
+
+    def num_tokens(self, seq) -> int:
+        return self.seqs[seq]["n"]
+
+    # -- helpers -----------------------------------------------------------
+    def _take(self) -> int:
+        b = self.free.popleft()
+        self.ref[b] = 1
+        return b
+
+    def _drop(self, b: int) -> None:
+        self.ref[b] -= 1
+        if self.ref[b] == 0:
+            self.free.append(b)
+
+    @staticmethod
+    def _nblocks(n: int) -> int:
+        return -(-n // BLOCK_SIZE)
+
+    # -- updates -----------------------------------------------------------
+    def add_seq(self, seq, num_tokens: int) -> None:
+        if seq in self.seqs or num_tokens < 0:
+            raise BadRequest("duplicate sequence or negative length")
+        need = self._nblocks(num_tokens)
+        if need > len(self.free):
+            raise NoSpace()
+        self.seqs[seq] = {"blocks": [self._take() for _ in range(need)], "n": num_tokens}
+
+    def add_seq_with_prefix(self, seq, prefix_seq, prefix_tokens: int, tail_tokens: int) -> None:
+        if seq in self.seqs or prefix_seq not in self.seqs:
+            raise BadRequest("duplicate sequence or unknown prefix sequence")
+        if prefix_tokens % BLOCK_SIZE or not 0 <= prefix_tokens <= self.seqs[prefix_seq]["n"] or tail_tokens < 0:
+            raise BadRequest("a shared prefix is a whole number of blocks inside the prefix sequence")
+        shared = self.seqs[prefix_seq]["blocks"][: prefix_tokens // BLOCK_SIZE]
+        need = self._nblocks(tail_tokens)
+        if need > len(self.free):
+            raise NoSpace()
+        for b in shared:
+            self.ref[b] += 1
+        own = [self._take() for _ in range(need)]
+        self.seqs[seq] = {"blocks": list(shared) + own, "n": prefix_tokens + tail_tokens}
+
+    def fork(self, parent, child) -> None:
+        if parent not in self.seqs or child in self.seqs:
+            raise BadRequest("unknown parent or duplicate child")
+        blocks = list(self.seqs[parent]["blocks"])
+        for b in blocks:
+            self.ref[b] += 1
+        self.seqs[child] = {"blocks": blocks, "n": self.seqs[parent]["n"]}
+
+    def free_seq(self, seq) -> None:
+        if seq not in self.seqs:
+            raise BadRequest("unknown sequence")
+        for b in self.seqs.pop(seq)["blocks"]:
+            self._drop(b)
+
+    def append_tokens(self, seqs):
+        """Append one token to each listed sequence, in list order.
+
+        Returns (slots, cow_pairs): the slot of every appended token and the
+        (src, dst) block copies the device must perform first.  A sequence may
+        appear several times (it then receives several consecutive tokens).
+        """
+        seqs = [s for s in seqs]
+        for s in seqs:
+            if s not in self.seqs:
+                raise BadRequest("unknown sequence")
+        # all-or-nothing: run the updates on a copy and commit on success
+        saved = (deque(self.free), list(self.ref),
+                 {k: {"blocks": list(v["blocks"]), "n": v["n"]} for k, v in self.seqs.items()})
+        try:
+            slots, cows = [], []
+            for s in seqs:
+                st = self.seqs[s]
+                pos = st["n"]
+                if pos % BLOCK_SIZE == 0:
+                    if not self.free:
+                        raise NoSpace()
+                    st["blocks"].append(self._take())
+                else:
+                    last = st["blocks"][-1]
+                    if self.ref[last] > 1:
+                        if not self.free:
+                            raise NoSpace()
+                        fresh = self._take()
+                        self.ref[last] -= 1
+                        st["blocks"][-1] = fresh
+                        cows.append((last, fresh))
+                slots.append(st["blocks"][pos // BLOCK_SIZE] * BLOCK_SIZE + pos % BLOCK_SIZE)
+                st["n"] = pos + 1
+            return slots, cows
+        except NoSpace:
+            self.free, self.ref, self.seqs = saved
+            raise
+
+    def append_token(self, seq):
+        slots, cows = self.append_tokens([seq])
+        return slots[0], (cows[0] if cows else (-1, -1))
+
+    def block_table(self, seqs, max_blocks: int, pad: int = -1):
+        """Rows of logical -> physical ids (padded with ``pad``) and context lengths."""
+        table, ctx = [], []
+        for s in seqs:
+            if s not in self.seqs:
+                raise BadRequest("unknown sequence")
+            blocks = self.seqs[s]["blocks"]
+            if len(blocks) > max_blocks:
+                raise BadRequest("table too narrow")
+            table.append(list(blocks) + [pad] * (max_blocks - len(blocks)))
+            ctx.append(self.seqs[s]["n"])
+        return table, ctx

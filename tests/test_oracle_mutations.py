@@ -1,0 +1,91 @@
+"""Planted mistakes in the oracle must each break at least one pin.
+
+Each case takes the source of one oracle function, changes one expression
+into a plausible mistake (a dropped term, a wrong index, an off-by-one), runs
+the changed function in place of the real one, and checks that the named pin
+then fails.  Everything here runs on the CPU against the oracle only.
+"""
+import inspect
+import textwrap
+
+import pytest
+
+import oracle.attention
+import oracle.block_manager
+import oracle.layout
+from tests import test_oracle_attention as PA
+from tests import test_oracle_block_manager as PB
+
+MUTATIONS = [
+    # (module, function or Class.method, original text, planted mistake, pin, pin args)
+    (oracle.attention, "decode", "g = h // G", "g = h % Hkv",
+     PA.test_query_heads_read_their_contiguous_kv_group, ()),
+    (oracle.attention, "decode", "z = scale * (K[g] @ qf[s, h])", "z = K[g] @ qf[s, h]",
+     PA.test_decode_matches_brute_force_on_the_tiny_shape, ("f32",)),
+    (oracle.attention, "decode", "out[s, h] = _softmax_weighted_sum(z, V[g])",
+     "out[s, h] = _softmax_weighted_sum(z, K[g])",
+     PA.test_decode_matches_brute_force_on_the_tiny_shape, ("bf16",)),
+    (oracle.attention, "prefill_chunk", "last = n - C + i", "last = n - C + i - 1",
+     PA.test_prefill_matches_brute_force, ()),
+    (oracle.attention, "prefill_chunk", "last = n - C + i", "last = n - 1",
+     PA.test_chunk_of_one_is_decode_and_rows_are_causal, ()),
+    (oracle.attention, "gather_kv", "K = K.transpose(1, 0, 2, 3)", "K = K.transpose(0, 1, 2, 3)",
+     PA.test_decode_matches_brute_force_on_the_tiny_shape, ("f16",)),
+    (oracle.attention, "gather_kv", "phys = np.asarray(table_row[:nb], dtype=np.int64)",
+     "phys = np.arange(nb, dtype=np.int64)",
+     PA.test_decode_matches_brute_force_on_the_tiny_shape, ("f32",)),
+    (oracle.attention, "gather_kv", "V = V.transpose(1, 0, 2, 3).reshape(Hkv, nb * BLOCK_SIZE, D)[:, :ctx]",
+     "V = V.transpose(1, 0, 2, 3).reshape(Hkv, nb * BLOCK_SIZE, D)[:, :nb * BLOCK_SIZE][:, :ctx + 1]",
+     PA.test_unread_table_entries_and_tail_slots_do_not_matter, ()),
+    (oracle.attention, "to_f64", "<< np.uint32(16)", "<< np.uint32(15)",
+     PA.test_bf16_bit_patterns_decode_exactly, ()),
+    (oracle.attention, "reshape_and_cache", "b, o = divmod(slot, BLOCK_SIZE)", "o, b = divmod(slot, BLOCK_SIZE)",
+     PA.test_cache_write_lands_at_the_layout_offsets, ()),
+    (oracle.layout, "k_offset", "((d // 8) * 16 + t) * 8 + d % 8", "(t * 16 + d // 8) * 8 + d % 8",
+     PA.test_tile_layout_matches_hand_derived_offsets, ()),
+    (oracle.layout, "v_offset", "((d // 16) % 2) * 4 + t % 4", "((d // 16) % 2) + (t % 4) * 2",
+     PA.test_tile_layout_matches_hand_derived_offsets, ()),
+    (oracle.block_manager, "RefBlockManager.append_tokens", "if pos % BLOCK_SIZE == 0:",
+     "if pos % BLOCK_SIZE == 1 or pos == 0:",
+     PB.test_on_demand_allocation_schedule, ()),
+    (oracle.block_manager, "RefBlockManager.append_tokens", "self.ref[last] -= 1", "pass",
+     PB.test_copy_on_write_for_a_shared_partial_block, ()),
+    (oracle.block_manager, "RefBlockManager.append_tokens", "if self.ref[last] > 1:", "if False:",
+     PB.test_copy_on_write_for_a_shared_partial_block, ()),
+    (oracle.block_manager, "RefBlockManager._drop", "self.free.append(b)", "self.free.appendleft(b)",
+     PB.test_freed_blocks_join_the_tail_of_the_free_list, ()),
+    (oracle.block_manager, "RefBlockManager.fork", "self.ref[b] += 1", "pass",
+     PB.test_parallel_sampling_example, ()),
+    (oracle.block_manager, "RefBlockManager.add_seq_with_prefix",
+     "shared = self.seqs[prefix_seq][\"blocks\"][: prefix_tokens // BLOCK_SIZE]",
+     "shared = self.seqs[prefix_seq][\"blocks\"][: prefix_tokens // BLOCK_SIZE - 1]",
+     PB.test_prefix_caching_example, ()),
+]
+
+
+def _mutated(module, qualname, old, new):
+    owner = module
+    parts = qualname.split(".")
+    for p in parts[:-1]:
+        owner = getattr(owner, p)
+    fn = getattr(owner, parts[-1])
+    src = textwrap.dedent(inspect.getsource(fn))
+    assert src.count(old) >= 1, f"{qualname}: text to mutate not found"
+    src = src.replace(old, new)
+    ns = dict(vars(module))
+    exec(compile(src, f"<mutant {qualname}>", "exec"), ns)
+    return owner, parts[-1], ns[parts[-1]]
+
+
+@pytest.mark.parametrize("case", range(len(MUTATIONS)),
+                         ids=[f"{m[1]}:{m[3][:30]}" for m in MUTATIONS])
+def test_planted_mistake_breaks_a_pin(case, monkeypatch):
+    module, qualname, old, new, pin, args = MUTATIONS[case]
+    pin(*args)  # the pin holds for the real oracle
+    owner, name, fn = _mutated(module, qualname, old, new)
+    monkeypatch.setattr(owner, name, fn)
+    if module is oracle.layout:
+        # tile_index reads the offset functions from its module namespace
+        monkeypatch.setattr(oracle.layout, name, fn)
+    with pytest.raises(Exception):
+        pin(*args)
