@@ -1,0 +1,255 @@
+/*
+ * pa.h - paged KV-cache attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels and a host-side block manager.
+ * Every argument is a plain pointer or integer; no C++ or framework type
+ * crosses this boundary.
+ *
+ * Pages cited (by title and section):
+ *   [OS]  "PagedAttention: How vLLM Serves AI Like an Operating System"
+ *   [VIZ] "vLLM Architecture and PagedAttention - Interactive Visualization"
+ *
+ * ------------------------------------------------------------------------
+ * Memory model
+ * ------------------------------------------------------------------------
+ * The KV cache is cut into fixed blocks of 16 tokens that can sit anywhere
+ * in one pool; a per-sequence block table maps logical block i to a
+ * physical block ([OS] "PagedAttention: Virtual Memory for KV Cache", How It
+ * Works and the memory-layout example).  block_size must be 16.
+ *
+ * Pools.  k_cache and v_cache are separate device arrays
+ *     [num_blocks][num_kv_heads][16 * head_dim]      (elements of `dtype`)
+ * and one (block, kv head) tile is one contiguous run of 16 * head_dim
+ * elements.  Inside a tile (t = token offset 0..15, d = dim):
+ *     K(t, d) at  ((d / 8) * 16 + t) * 8 + d % 8
+ *                 i.e. [head_dim/8][16 tokens][8 dims]
+ *     V(t, d) at  (((d / 32) * 4 + t / 4) * 16 + d % 16) * 8
+ *                   + ((d / 16) % 2) * 4 + t % 4
+ *                 i.e. [head_dim/32][4 token quads][16 dims][2 halves][4 tokens]
+ * This order lets a 64-lane wave read a tile as whole 1 KiB runs of 16-byte
+ * loads that land directly in matrix-core operand registers.  head_dim must
+ * be a multiple of 32; the kernels support 64 and 128.
+ *
+ * Slots.  Token position p of a sequence lives in logical block p / 16 at
+ * offset p % 16; its slot is  physical_block * 16 + p % 16  (int64).  A
+ * negative slot means "skip this token".
+ *
+ * Block tables.  int32 [num_seqs][max_blocks_per_seq], row-major; only the
+ * first ceil(context_len / 16) entries of a row are read.  context_lens is
+ * int32 [num_seqs] and counts every cached token including the one(s) the
+ * step just wrote.
+ *
+ * Query heads.  q head h reads kv head h / (num_q_heads / num_kv_heads);
+ * num_q_heads must be a multiple of num_kv_heads (1 <= group <= 16).
+ *
+ * ------------------------------------------------------------------------
+ * Conventions
+ * ------------------------------------------------------------------------
+ * Ownership:  every device pointer is allocated and owned by the caller; no
+ *   entry point allocates device memory.  Split-context scratch is a
+ *   caller-provided workspace sized by pa_decode_workspace_bytes().
+ * Streams:    `stream` is a hipStream_t (NULL = the default stream).  Every
+ *   device entry point only enqueues work on it and returns; results are
+ *   valid once the stream reaches that point.  The host never reads device
+ *   memory and never synchronises.
+ * Errors:     every entry point validates its scalar arguments before any
+ *   launch and returns a status; pa_last_error() gives a message (per
+ *   thread).  No C++ exception crosses the ABI.
+ * Device-side guards: a table entry outside [0, num_blocks), a context_len
+ *   above max_context_len or beyond the table width, or a slot beyond the
+ *   pool never causes an out-of-bounds access: the affected output row is
+ *   written as NaN (attention) or the token is skipped (cache write).
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_EINVAL = 1,       /* argument outside the contract                  */
+  PA_EUNSUPPORTED = 2, /* dtype, head_dim, group or block_size not built */
+  PA_EWORKSPACE = 3,   /* workspace missing or smaller than required     */
+  PA_EHIP = 4,         /* the HIP runtime reported an error              */
+  PA_ENOSPC = 5,       /* block manager: not enough free blocks          */
+  PA_ENOENT = 6        /* block manager: unknown sequence                */
+} pa_status_t;
+
+typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype_t;
+
+/* Version string of the library build. */
+const char* pa_version(void);
+
+/* Message describing the last non-OK status returned on this thread. */
+const char* pa_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Cache write.  Stores each new token's K and V rows into its slot, bit for
+ * bit, for every kv head: blocks are filled as tokens arrive ([OS] "The
+ * Magic: No Pre-allocation"; "PagedAttention: Virtual Memory for KV Cache",
+ * How It Works).
+ *   key, value      device [num_tokens][num_kv_heads][head_dim] of dtype
+ *   k_cache,v_cache device pools (layout above), modified in place
+ *   slot_mapping    device int64 [num_tokens]; < 0 skips the token.  Slots in
+ *                   one call must be distinct.
+ * num_tokens == 0 is a no-op.
+ * ---------------------------------------------------------------------- */
+pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                 const int64_t* slot_mapping, int32_t num_tokens,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                 int64_t num_blocks, pa_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Copy whole physical blocks (K and V, all kv heads) src -> dst: the copy a
+ * shared block gets before a sequence writes into it ([OS] "Copy-on-Write:
+ * Sharing KV Cache").
+ *   pairs   device int64 [num_pairs][2] = (src, dst); destinations distinct
+ *           and never a source of the same call.
+ * ---------------------------------------------------------------------- */
+pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t num_pairs,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, pa_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention over the paged cache: for every sequence s and q head h,
+ *     out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s
+ * over the context_lens[s] tokens of s, reading K_s / V_s through the block
+ * table ([OS] "PagedAttention: Virtual Memory for KV Cache"; the result is
+ * that of contiguous attention, [OS] "Throughput Impact: The Numbers").
+ *
+ *   out             device [num_seqs][num_q_heads][head_dim] of out_dtype
+ *                   (PA_F32, or the input dtype)
+ *   q               device [num_seqs][num_q_heads][head_dim] of dtype
+ *   max_context_len host upper bound of context_lens (sizes the grid)
+ *   partition_size  tokens per context partition, a multiple of 16;
+ *                   0 picks the default (512).  Sequences longer than one
+ *                   partition are split; the pieces are merged exactly by a
+ *                   log-sum-exp reduction.
+ *   workspace       device scratch of at least
+ *                   pa_decode_workspace_bytes(...) bytes (may be NULL when
+ *                   that is 0); its contents are private to the call.
+ * A sequence with context_len 0 gets a zero row.  dtype PA_F32 runs on the
+ * vector ALUs; PA_F16 / PA_BF16 use the matrix cores with fp32
+ * accumulation and an fp32 softmax.
+ * ---------------------------------------------------------------------- */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size);
+
+pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* q,
+                      const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                      float scale, int32_t max_context_len, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes,
+                      pa_dtype_t dtype, void* stream);
+
+/* The two launches pa_decode makes, for callers that time or schedule them
+ * separately.  pa_decode_partitions writes finished rows of single-partition
+ * sequences to `out` and partial results of the others to `workspace`;
+ * pa_decode_reduce then merges those partials into `out`.  Same arguments
+ * and contract as pa_decode. */
+pa_status_t pa_decode_partitions(void* out, pa_dtype_t out_dtype, const void* q,
+                                 const void* k_cache, const void* v_cache,
+                                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens,
+                                 int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                 float scale, int32_t max_context_len, int32_t partition_size,
+                                 void* workspace, size_t workspace_bytes,
+                                 pa_dtype_t dtype, void* stream);
+
+pa_status_t pa_decode_reduce(void* out, pa_dtype_t out_dtype, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                             int32_t max_context_len, int32_t partition_size,
+                             const void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Chunked prefill: causal attention of a chunk of chunk_len new queries per
+ * sequence over the paged cache.  The chunk occupies the last chunk_len
+ * positions of the context (its K/V already written by
+ * pa_reshape_and_cache); query i of sequence s sits at position
+ * context_lens[s] - chunk_len + i and attends keys 0 .. that position.
+ *   out  device [num_seqs][chunk_len][num_q_heads][head_dim] of out_dtype
+ *   q    device [num_seqs][chunk_len][num_q_heads][head_dim] of dtype
+ * Requires context_lens[s] >= chunk_len (else that sequence's rows are NaN).
+ * dtype PA_F16 / PA_BF16 only (matrix cores, fp32 accumulation).
+ * ---------------------------------------------------------------------- */
+pa_status_t pa_prefill_chunk(void* out, pa_dtype_t out_dtype, const void* q, int32_t chunk_len,
+                             const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                             float scale, int32_t max_context_len,
+                             pa_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Host block manager.  One pool of num_blocks blocks of 16 tokens; per
+ * sequence a list of physical blocks; a free list; reference counts for
+ * shared blocks.
+ *   - allocation on demand: a token at offset 0 of a fresh block takes a
+ *     new block, so n tokens hold ceil(n/16) blocks and waste at most 15
+ *     slots ([OS] "The Magic: No Pre-allocation");
+ *   - release on finish ([VIZ] "Page Table Visualization");
+ *   - sharing by fork (parallel sampling) and by a common prefix (system
+ *     prompt), with copy-on-write before a write into a shared block
+ *     ([OS] "Copy-on-Write: Sharing KV Cache").
+ * The free list is a queue: allocation takes its head, a block whose count
+ * drops to zero joins its tail.  Its initial order is `free_order` (a
+ * permutation of 0..num_blocks-1), or ascending when NULL.
+ * Every update is all-or-nothing: PA_ENOSPC leaves the state unchanged,
+ * which is the point where a scheduler would preempt.  All pointers here
+ * are host pointers.  A pa_bm_t is not thread-safe.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_bm pa_bm_t;
+
+pa_bm_t* pa_bm_create(int64_t num_blocks, int32_t block_size, const int32_t* free_order);
+void pa_bm_destroy(pa_bm_t* bm);
+
+/* New sequence holding num_tokens (>= 0) tokens in fresh blocks. */
+pa_status_t pa_bm_add_seq(pa_bm_t* bm, int64_t seq, int32_t num_tokens);
+
+/* New sequence sharing the first prefix_tokens (a multiple of 16, within the
+ * prefix sequence) of prefix_seq, plus tail_tokens in fresh blocks. */
+pa_status_t pa_bm_add_seq_with_prefix(pa_bm_t* bm, int64_t seq, int64_t prefix_seq,
+                                      int32_t prefix_tokens, int32_t tail_tokens);
+
+/* child shares every block of parent (reference counts + 1). */
+pa_status_t pa_bm_fork(pa_bm_t* bm, int64_t parent, int64_t child);
+
+/* Drop the sequence; blocks whose count reaches 0 return to the free list
+ * in logical order. */
+pa_status_t pa_bm_free_seq(pa_bm_t* bm, int64_t seq);
+
+/* Append one token to each of seqs[0..n) in order (a sequence may repeat).
+ * slots[i] receives the slot of token i.  When a token lands in a shared
+ * block, the writer first moves to a fresh copy: the pair (old, new) is
+ * appended to cow_pairs ([n][2], may be NULL only if no copy occurs) and
+ * *num_cow counts them; the device copy (pa_copy_blocks) must run before
+ * the cache write. */
+pa_status_t pa_bm_append_tokens(pa_bm_t* bm, const int64_t* seqs, int32_t n, int64_t* slots,
+                                int64_t* cow_pairs, int32_t* num_cow);
+
+/* Fill table [n][max_blocks] (padding with pad_id) and context_lens [n]. */
+pa_status_t pa_bm_block_table(const pa_bm_t* bm, const int64_t* seqs, int32_t n, int32_t max_blocks,
+                              int32_t pad_id, int32_t* table, int32_t* context_lens);
+
+int64_t pa_bm_num_free(const pa_bm_t* bm);
+int32_t pa_bm_refcount(const pa_bm_t* bm, int64_t block);          /* -1: out of range  */
+double pa_bm_usage(const pa_bm_t* bm);                              /* used / num_blocks */
+int32_t pa_bm_num_tokens(const pa_bm_t* bm, int64_t seq);           /* -1: unknown       */
+/* Copy the free list, head first, into out[0..cap); returns its length. */
+int64_t pa_bm_free_list(const pa_bm_t* bm, int32_t* out, int64_t cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,284 @@
+// C ABI of the paged-attention library: argument validation, workspace
+// sizing and kernel dispatch.  Nothing here touches device memory contents or
+// synchronises; every device entry point only enqueues work on `stream`.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "pa_internal.h"
+
+namespace pa {
+
+namespace {
+thread_local std::string g_last_error;
+
+int elem_bytes(pa_dtype_t t) { return t == PA_F32 ? 4 : 2; }
+bool known_dtype(pa_dtype_t t) { return t == PA_F32 || t == PA_F16 || t == PA_BF16; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+constexpr float kLog2e = 1.4426950408889634f;
+
+pa_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PA_OK;
+  return fail(PA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+pa_status_t check_pool(int32_t kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype_t dtype) {
+  if (!known_dtype(dtype)) return fail(PA_EUNSUPPORTED, "unknown dtype %d", int(dtype));
+  if (block_size != 16) return fail(PA_EUNSUPPORTED, "block_size must be 16 (got %d)", block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PA_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (kv_heads <= 0) return fail(PA_EINVAL, "num_kv_heads must be positive (got %d)", kv_heads);
+  if (num_blocks <= 0) return fail(PA_EINVAL, "num_blocks must be positive");
+  return PA_OK;
+}
+
+struct DecodeCheck {
+  int32_t partition;
+  int32_t nparts;
+};
+
+pa_status_t check_decode(const void* out, pa_dtype_t out_dtype, const void* q, const void* k, const void* v,
+                         const int32_t* tables, int32_t max_blocks, const int32_t* ctx, int32_t S, int32_t Hq,
+                         int32_t Hkv, int32_t D, int32_t bs, int64_t NB, float scale, int32_t max_ctx,
+                         int32_t partition, pa_dtype_t dtype, DecodeCheck* dc) {
+  pa_status_t st = check_pool(Hkv, D, bs, NB, dtype);
+  if (st != PA_OK) return st;
+  if (S < 0) return fail(PA_EINVAL, "num_seqs must be >= 0");
+  if (Hq <= 0 || Hq % Hkv != 0) return fail(PA_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(PA_EUNSUPPORTED, "query group %d > 16", Hq / Hkv);
+  if (!(out_dtype == PA_F32 || out_dtype == dtype))
+    return fail(PA_EUNSUPPORTED, "out_dtype must be PA_F32 or the input dtype");
+  if (max_ctx < 0) return fail(PA_EINVAL, "max_context_len must be >= 0");
+  if (max_blocks < 0 || int64_t(max_blocks) * 16 < max_ctx)
+    return fail(PA_EINVAL, "max_blocks_per_seq (%d) cannot hold max_context_len (%d)", max_blocks, max_ctx);
+  if (!isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");
+  if (partition == 0) partition = kDefaultPartition;
+  if (partition < 16 || partition % 16 != 0) return fail(PA_EINVAL, "partition_size must be a positive multiple of 16");
+  if (S > 0 && (!out || !q || !k || !v || !tables || !ctx)) return fail(PA_EINVAL, "null pointer argument");
+  const int64_t nparts = max_ctx == 0 ? 1 : ceil_div(max_ctx, partition);
+  if (nparts > 65535 * 64) return fail(PA_EUNSUPPORTED, "too many partitions");
+  if (S > 65535 || Hq > 65535) return fail(PA_EUNSUPPORTED, "num_seqs and num_q_heads must be <= 65535");
+  dc->partition = partition;
+  dc->nparts = int32_t(nparts);
+  return PA_OK;
+}
+
+size_t ws_size(int64_t S, int64_t Hq, int64_t D, int64_t nparts) {
+  if (nparts <= 1) return 0;
+  const int64_t rows = S * Hq * nparts;
+  // acc [rows][D], then m [rows], then l [rows]; 256-byte aligned pieces
+  auto align = [](int64_t b) { return (b + 255) / 256 * 256; };
+  return size_t(align(rows * D * 4) + 2 * align(rows * 4));
+}
+
+void split_workspace(void* ws, int64_t S, int64_t Hq, int64_t D, int64_t nparts, float** acc, float** m, float** l) {
+  auto align = [](int64_t b) { return (b + 255) / 256 * 256; };
+  const int64_t rows = S * Hq * nparts;
+  char* base = static_cast<char*>(ws);
+  *acc = reinterpret_cast<float*>(base);
+  *m = reinterpret_cast<float*>(base + align(rows * D * 4));
+  *l = reinterpret_cast<float*>(base + align(rows * D * 4) + align(rows * 4));
+}
+
+enum class DecodePhase { kBoth, kPartitions, kReduce };
+
+pa_status_t run_decode(DecodePhase phase, void* out, pa_dtype_t out_dtype, const void* q, const void* k_cache,
+                       const void* v_cache, const int32_t* block_tables, int32_t max_blocks,
+                       const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
+                       int64_t NB, float scale, int32_t max_ctx, int32_t partition, void* workspace,
+                       size_t workspace_bytes_given, pa_dtype_t dtype, void* stream) {
+  DecodeCheck dc{};
+  pa_status_t st = check_decode(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks, context_lens, S, Hq,
+                                Hkv, D, bs, NB, scale, max_ctx, partition, dtype, &dc);
+  if (st != PA_OK) return st;
+  const size_t need = ws_size(S, Hq, D, dc.nparts);
+  if (need > 0 && (workspace == nullptr || workspace_bytes_given < need))
+    return fail(PA_EWORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes_given);
+  if (S == 0) return PA_OK;
+  DecodeArgs a{};
+  a.out = out;
+  a.out_f32 = out_dtype == PA_F32;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks;
+  a.context_lens = context_lens;
+  a.num_seqs = S;
+  a.num_q_heads = Hq;
+  a.num_kv_heads = Hkv;
+  a.head_dim = D;
+  a.num_blocks = NB;
+  a.scale_log2 = scale * kLog2e;
+  a.max_context_len = max_ctx;
+  a.partition = dc.partition;
+  a.num_partitions = dc.nparts;
+  if (need > 0) split_workspace(workspace, S, Hq, D, dc.nparts, &a.ws_acc, &a.ws_m, &a.ws_l);
+  a.dtype = dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  if (phase != DecodePhase::kReduce) {
+    st = hip_status(launch_decode_partitions(a), "decode partition launch");
+    if (st != PA_OK) return st;
+  }
+  if (phase != DecodePhase::kPartitions) st = hip_status(launch_decode_reduce(a), "decode reduce launch");
+  return st;
+}
+
+}  // namespace
+
+pa_status_t fail(pa_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+}  // namespace pa
+
+using namespace pa;
+
+extern "C" {
+
+const char* pa_version(void) { return "pa 0.1 gfx950"; }
+
+const char* pa_last_error(void) { return g_last_error.c_str(); }
+
+pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                 const int64_t* slot_mapping, int32_t num_tokens, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype_t dtype,
+                                 void* stream) {
+  pa_status_t st = check_pool(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0) return fail(PA_EINVAL, "num_tokens must be >= 0");
+  if (num_tokens == 0) return PA_OK;
+  if (!key || !value || !k_cache || !v_cache || !slot_mapping) return fail(PA_EINVAL, "null pointer argument");
+  return hip_status(launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
+                                             head_dim, num_blocks, elem_bytes(dtype), static_cast<hipStream_t>(stream)),
+                    "reshape_and_cache launch");
+}
+
+pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t num_pairs,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           pa_dtype_t dtype, void* stream) {
+  pa_status_t st = check_pool(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_pairs < 0) return fail(PA_EINVAL, "num_pairs must be >= 0");
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !pairs) return fail(PA_EINVAL, "null pointer argument");
+  const int64_t block_bytes = int64_t(num_kv_heads) * 16 * head_dim * elem_bytes(dtype);
+  return hip_status(launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, block_bytes, num_blocks,
+                                       static_cast<hipStream_t>(stream)),
+                    "copy_blocks launch");
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                                 int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  const int32_t p = partition_size == 0 ? kDefaultPartition : partition_size;
+  if (p <= 0) return 0;
+  return ws_size(num_seqs, num_q_heads, head_dim, ceil_div(max_context_len, p));
+}
+
+pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, int64_t num_blocks, float scale, int32_t max_context_len,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype_t dtype,
+                      void* stream) {
+  return run_decode(DecodePhase::kBoth, out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                    context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                    max_context_len, partition_size, workspace, workspace_bytes, dtype, stream);
+}
+
+pa_status_t pa_decode_partitions(void* out, pa_dtype_t out_dtype, const void* q, const void* k_cache,
+                                 const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                                 float scale, int32_t max_context_len, int32_t partition_size, void* workspace,
+                                 size_t workspace_bytes, pa_dtype_t dtype, void* stream) {
+  return run_decode(DecodePhase::kPartitions, out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                    context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                    max_context_len, partition_size, workspace, workspace_bytes, dtype, stream);
+}
+
+pa_status_t pa_decode_reduce(void* out, pa_dtype_t out_dtype, const int32_t* context_lens, int32_t num_seqs,
+                             int32_t num_q_heads, int32_t head_dim, int32_t max_context_len, int32_t partition_size,
+                             const void* workspace, size_t workspace_bytes, void* stream) {
+  if (head_dim != 64 && head_dim != 128) return fail(PA_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
+  if (!(out_dtype == PA_F32 || out_dtype == PA_F16 || out_dtype == PA_BF16))
+    return fail(PA_EUNSUPPORTED, "unknown out_dtype");
+  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return fail(PA_EINVAL, "bad sizes");
+  const int32_t p = partition_size == 0 ? kDefaultPartition : partition_size;
+  if (p < 16 || p % 16 != 0) return fail(PA_EINVAL, "partition_size must be a positive multiple of 16");
+  const int64_t nparts = max_context_len == 0 ? 1 : ceil_div(max_context_len, p);
+  const size_t need = ws_size(num_seqs, num_q_heads, head_dim, nparts);
+  if (need == 0 || num_seqs == 0) return PA_OK;
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(PA_EWORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
+  if (!out || !context_lens) return fail(PA_EINVAL, "null pointer argument");
+  DecodeArgs a{};
+  a.out = out;
+  a.out_f32 = out_dtype == PA_F32;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = 1;
+  a.head_dim = head_dim;
+  a.max_context_len = max_context_len;
+  a.max_blocks = int32_t(ceil_div(max_context_len, 16));
+  a.partition = p;
+  a.num_partitions = int32_t(nparts);
+  split_workspace(const_cast<void*>(workspace), num_seqs, num_q_heads, head_dim, nparts, &a.ws_acc, &a.ws_m, &a.ws_l);
+  a.dtype = out_dtype == PA_F32 ? PA_F16 : out_dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_decode_reduce(a), "decode reduce launch");
+}
+
+pa_status_t pa_prefill_chunk(void* out, pa_dtype_t out_dtype, const void* q, int32_t chunk_len, const void* k_cache,
+                             const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads,
+                             int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                             float scale, int32_t max_context_len, pa_dtype_t dtype, void* stream) {
+  pa_status_t st = check_pool(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (dtype == PA_F32) return fail(PA_EUNSUPPORTED, "prefill runs on the matrix cores: fp16 or bf16 only");
+  if (num_seqs < 0 || chunk_len < 0) return fail(PA_EINVAL, "num_seqs and chunk_len must be >= 0");
+  if (num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", num_q_heads, num_kv_heads);
+  if (num_q_heads / num_kv_heads > 16) return fail(PA_EUNSUPPORTED, "query group %d > 16", num_q_heads / num_kv_heads);
+  if (!(out_dtype == PA_F32 || out_dtype == dtype)) return fail(PA_EUNSUPPORTED, "out_dtype must be PA_F32 or the input dtype");
+  if (max_context_len < chunk_len) return fail(PA_EINVAL, "max_context_len must be >= chunk_len");
+  if (max_blocks_per_seq < 0 || int64_t(max_blocks_per_seq) * 16 < max_context_len)
+    return fail(PA_EINVAL, "max_blocks_per_seq cannot hold max_context_len");
+  if (!isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");
+  if (num_seqs == 0 || chunk_len == 0) return PA_OK;
+  if (num_seqs > 65535 || num_kv_heads > 65535) return fail(PA_EUNSUPPORTED, "grid too large");
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return fail(PA_EINVAL, "null pointer argument");
+  PrefillArgs a{};
+  a.out = out;
+  a.out_f32 = out_dtype == PA_F32;
+  a.q = q;
+  a.chunk = chunk_len;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.block_tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.scale_log2 = scale * kLog2e;
+  a.max_context_len = max_context_len;
+  a.dtype = dtype;
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_prefill_chunk(a), "prefill launch");
+}
+
+}  // extern "C"

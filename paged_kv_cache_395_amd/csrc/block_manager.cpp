@@ -1,0 +1,264 @@
+// Host-side KV block manager: free list, per-sequence block lists, reference
+// counts, copy-on-write.  Pure host code; produces the block tables and slots
+// the device kernels consume.
+//
+// Pages: "PagedAttention: How vLLM Serves AI Like an Operating System" --
+// blocks handed out on demand (section "The Magic: No Pre-allocation"), a
+// logical-to-physical table per request and a free list (section
+// "PagedAttention: Virtual Memory for KV Cache"), shared blocks with
+// copy-on-write for parallel sampling and a common system prompt (section
+// "Copy-on-Write: Sharing KV Cache"); "vLLM Architecture and PagedAttention -
+// Interactive Visualization" (Page Table Visualization): a finished
+// sequence's pages return to the pool at once.
+
+#include <stdint.h>
+
+#include <deque>
+#include <new>
+#include <unordered_map>
+#include <vector>
+
+#include "pa_internal.h"
+
+namespace {
+
+constexpr int32_t kBS = 16;
+
+struct Seq {
+  std::vector<int32_t> blocks;
+  int32_t tokens = 0;
+};
+
+}  // namespace
+
+struct pa_bm {
+  int64_t num_blocks = 0;
+  std::vector<int32_t> ref;
+  std::deque<int32_t> free_q;  // head = next block handed out, tail = most recently released
+  std::unordered_map<int64_t, Seq> seqs;
+
+  int32_t take() {
+    const int32_t b = free_q.front();
+    free_q.pop_front();
+    ref[b] = 1;
+    return b;
+  }
+  void drop(int32_t b) {
+    if (--ref[b] == 0) free_q.push_back(b);
+  }
+};
+
+using pa::fail;
+
+namespace {
+int64_t blocks_for(int64_t tokens) { return (tokens + kBS - 1) / kBS; }
+}  // namespace
+
+extern "C" {
+
+pa_bm_t* pa_bm_create(int64_t num_blocks, int32_t block_size, const int32_t* free_order) {
+  if (num_blocks <= 0 || num_blocks > INT32_MAX || block_size != kBS) {
+    fail(PA_EINVAL, "pa_bm_create: num_blocks must be in [1, 2^31) and block_size 16");
+    return nullptr;
+  }
+  pa_bm* bm = new (std::nothrow) pa_bm;
+  if (!bm) {
+    fail(PA_EINVAL, "pa_bm_create: out of host memory");
+    return nullptr;
+  }
+  bm->num_blocks = num_blocks;
+  bm->ref.assign(size_t(num_blocks), 0);
+  if (free_order) {
+    std::vector<char> seen(size_t(num_blocks), 0);
+    for (int64_t i = 0; i < num_blocks; ++i) {
+      const int32_t b = free_order[i];
+      if (b < 0 || b >= num_blocks || seen[size_t(b)]) {
+        delete bm;
+        fail(PA_EINVAL, "pa_bm_create: free_order is not a permutation of the pool");
+        return nullptr;
+      }
+      seen[size_t(b)] = 1;
+      bm->free_q.push_back(b);
+    }
+  } else {
+    for (int64_t i = 0; i < num_blocks; ++i) bm->free_q.push_back(int32_t(i));
+  }
+  return bm;
+}
+
+void pa_bm_destroy(pa_bm_t* bm) { delete bm; }
+
+pa_status_t pa_bm_add_seq(pa_bm_t* bm, int64_t seq, int32_t num_tokens) {
+  if (!bm) return fail(PA_EINVAL, "null block manager");
+  if (num_tokens < 0) return fail(PA_EINVAL, "negative length");
+  if (bm->seqs.count(seq)) return fail(PA_EINVAL, "sequence %lld already exists", (long long)seq);
+  const int64_t need = blocks_for(num_tokens);
+  if (need > int64_t(bm->free_q.size()))
+    return fail(PA_ENOSPC, "need %lld blocks, %zu free", (long long)need, bm->free_q.size());
+  Seq s;
+  s.tokens = num_tokens;
+  s.blocks.reserve(size_t(need));
+  for (int64_t i = 0; i < need; ++i) s.blocks.push_back(bm->take());
+  bm->seqs.emplace(seq, std::move(s));
+  return PA_OK;
+}
+
+pa_status_t pa_bm_add_seq_with_prefix(pa_bm_t* bm, int64_t seq, int64_t prefix_seq, int32_t prefix_tokens,
+                                      int32_t tail_tokens) {
+  if (!bm) return fail(PA_EINVAL, "null block manager");
+  if (bm->seqs.count(seq)) return fail(PA_EINVAL, "sequence %lld already exists", (long long)seq);
+  auto it = bm->seqs.find(prefix_seq);
+  if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown prefix sequence %lld", (long long)prefix_seq);
+  if (prefix_tokens < 0 || prefix_tokens % kBS != 0 || prefix_tokens > it->second.tokens || tail_tokens < 0)
+    return fail(PA_EINVAL, "a shared prefix is a whole number of blocks inside the prefix sequence");
+  const int64_t need = blocks_for(tail_tokens);
+  if (need > int64_t(bm->free_q.size()))
+    return fail(PA_ENOSPC, "need %lld blocks, %zu free", (long long)need, bm->free_q.size());
+  Seq s;
+  s.tokens = prefix_tokens + tail_tokens;
+  const int32_t shared = prefix_tokens / kBS;
+  s.blocks.assign(it->second.blocks.begin(), it->second.blocks.begin() + shared);
+  for (int32_t b : s.blocks) ++bm->ref[size_t(b)];
+  for (int64_t i = 0; i < need; ++i) s.blocks.push_back(bm->take());
+  bm->seqs.emplace(seq, std::move(s));
+  return PA_OK;
+}
+
+pa_status_t pa_bm_fork(pa_bm_t* bm, int64_t parent, int64_t child) {
+  if (!bm) return fail(PA_EINVAL, "null block manager");
+  auto it = bm->seqs.find(parent);
+  if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown parent %lld", (long long)parent);
+  if (bm->seqs.count(child)) return fail(PA_EINVAL, "sequence %lld already exists", (long long)child);
+  Seq s = it->second;
+  for (int32_t b : s.blocks) ++bm->ref[size_t(b)];
+  bm->seqs.emplace(child, std::move(s));
+  return PA_OK;
+}
+
+pa_status_t pa_bm_free_seq(pa_bm_t* bm, int64_t seq) {
+  if (!bm) return fail(PA_EINVAL, "null block manager");
+  auto it = bm->seqs.find(seq);
+  if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown sequence %lld", (long long)seq);
+  for (int32_t b : it->second.blocks) bm->drop(b);
+  bm->seqs.erase(it);
+  return PA_OK;
+}
+
+pa_status_t pa_bm_append_tokens(pa_bm_t* bm, const int64_t* seqs, int32_t n, int64_t* slots, int64_t* cow_pairs,
+                                int32_t* num_cow) {
+  if (!bm) return fail(PA_EINVAL, "null block manager");
+  if (n < 0 || (n > 0 && (!seqs || !slots))) return fail(PA_EINVAL, "bad arguments");
+  if (num_cow) *num_cow = 0;
+  // Pass 1: decide, without changing anything, how many blocks the batch
+  // takes and whether any copy-on-write happens.  Per sequence track the
+  // token count and whether its last block is already private; per shared
+  // block track its count as earlier writers in the batch leave it.
+  struct SimSeq {
+    int32_t tokens;
+    bool last_private;
+  };
+  std::unordered_map<int64_t, SimSeq> sim;
+  std::unordered_map<int32_t, int32_t> sim_ref;
+  int64_t need = 0, cows = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown sequence %lld", (long long)seqs[i]);
+    auto si = sim.find(seqs[i]);
+    SimSeq st = si == sim.end() ? SimSeq{it->second.tokens, false} : si->second;
+    if (st.tokens == INT32_MAX) return fail(PA_EINVAL, "sequence too long");
+    if (st.tokens % kBS == 0) {
+      ++need;
+      st.last_private = true;
+    } else if (!st.last_private) {
+      const int32_t last = it->second.blocks.back();
+      auto ri = sim_ref.find(last);
+      const int32_t r = ri == sim_ref.end() ? bm->ref[size_t(last)] : ri->second;
+      if (r > 1) {
+        ++need;
+        ++cows;
+        sim_ref[last] = r - 1;
+      }
+      st.last_private = true;
+    }
+    st.tokens += 1;
+    sim[seqs[i]] = st;
+  }
+  if (need > int64_t(bm->free_q.size()))
+    return fail(PA_ENOSPC, "need %lld blocks, %zu free", (long long)need, bm->free_q.size());
+  if (cows > 0 && !cow_pairs) return fail(PA_EINVAL, "copy-on-write needed but cow_pairs is NULL");
+  // Pass 2: apply; cannot fail.
+  int32_t nc = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    Seq& s = bm->seqs.find(seqs[i])->second;
+    const int32_t pos = s.tokens;
+    if (pos % kBS == 0) {
+      s.blocks.push_back(bm->take());
+    } else {
+      const int32_t last = s.blocks.back();
+      if (bm->ref[size_t(last)] > 1) {
+        const int32_t fresh = bm->take();
+        --bm->ref[size_t(last)];
+        s.blocks.back() = fresh;
+        cow_pairs[2 * nc] = last;
+        cow_pairs[2 * nc + 1] = fresh;
+        ++nc;
+      }
+    }
+    slots[i] = int64_t(s.blocks[size_t(pos / kBS)]) * kBS + pos % kBS;
+    s.tokens = pos + 1;
+  }
+  if (num_cow) *num_cow = nc;
+  return PA_OK;
+}
+
+pa_status_t pa_bm_block_table(const pa_bm_t* bm, const int64_t* seqs, int32_t n, int32_t max_blocks, int32_t pad_id,
+                              int32_t* table, int32_t* context_lens) {
+  if (!bm) return fail(PA_EINVAL, "null block manager");
+  if (n < 0 || max_blocks < 0 || (n > 0 && (!seqs || !table || !context_lens))) return fail(PA_EINVAL, "bad arguments");
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown sequence %lld", (long long)seqs[i]);
+    if (int64_t(it->second.blocks.size()) > max_blocks)
+      return fail(PA_EINVAL, "sequence %lld holds %zu blocks > max_blocks %d", (long long)seqs[i],
+                  it->second.blocks.size(), max_blocks);
+  }
+  for (int32_t i = 0; i < n; ++i) {
+    const Seq& s = bm->seqs.find(seqs[i])->second;
+    int32_t* row = table + int64_t(i) * max_blocks;
+    const size_t nb = s.blocks.size();
+    for (size_t j = 0; j < nb; ++j) row[j] = s.blocks[j];
+    for (int64_t j = int64_t(nb); j < max_blocks; ++j) row[j] = pad_id;
+    context_lens[i] = s.tokens;
+  }
+  return PA_OK;
+}
+
+int64_t pa_bm_num_free(const pa_bm_t* bm) { return bm ? int64_t(bm->free_q.size()) : -1; }
+
+int32_t pa_bm_refcount(const pa_bm_t* bm, int64_t block) {
+  if (!bm || block < 0 || block >= bm->num_blocks) return -1;
+  return bm->ref[size_t(block)];
+}
+
+double pa_bm_usage(const pa_bm_t* bm) {
+  if (!bm) return -1.0;
+  return double(bm->num_blocks - int64_t(bm->free_q.size())) / double(bm->num_blocks);
+}
+
+int32_t pa_bm_num_tokens(const pa_bm_t* bm, int64_t seq) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? -1 : it->second.tokens;
+}
+
+int64_t pa_bm_free_list(const pa_bm_t* bm, int32_t* out, int64_t cap) {
+  if (!bm) return -1;
+  int64_t i = 0;
+  for (int32_t b : bm->free_q) {
+    if (i < cap && out) out[i] = b;
+    ++i;
+  }
+  return i;
+}
+
+}  // extern "C"

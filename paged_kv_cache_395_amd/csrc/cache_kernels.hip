@@ -1,0 +1,105 @@
+// Cache write (each new token's K/V rows into its slot) and whole-block copy
+// for copy-on-write.  Both are bit copies; neither interprets the values.
+//
+// Pages: "PagedAttention: How vLLM Serves AI Like an Operating System" --
+// blocks are filled on demand as tokens are stored (section "PagedAttention:
+// Virtual Memory for KV Cache", How It Works; "The Magic: No
+// Pre-allocation"), and a shared block is copied before a sequence may
+// modify it (section "Copy-on-Write: Sharing KV Cache").
+
+#include "device_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+// One thread moves one 8-element run (dims 8j..8j+7 of one kv head) of one
+// token.  K: the run is contiguous in the tile ([D/8][16][8]), one vector
+// store.  V: the 8 dims scatter to 8 positions of the [D/32][4][16][2][4]
+// tile, one element each.
+template <typename E>
+__global__ void __launch_bounds__(256)
+reshape_and_cache_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ kc,
+                         E* __restrict__ vc, const int64_t* __restrict__ slots, int32_t num_tokens,
+                         int32_t kv_heads, int32_t head_dim, int64_t num_blocks) {
+  typedef E vec8 __attribute__((ext_vector_type(8)));
+  const int runs_per_head = head_dim / 8;
+  const int runs_per_token = kv_heads * runs_per_head;
+  const int64_t c = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (c >= int64_t(num_tokens) * runs_per_token) return;
+  const int t = int(c / runs_per_token);
+  const int rem = int(c - int64_t(t) * runs_per_token);
+  const int h = rem / runs_per_head;
+  const int j = rem - h * runs_per_head;
+  const int64_t slot = slots[t];
+  if (slot < 0 || slot >= num_blocks * kBlockTokens) return;  // skipped token, or outside the pool
+  const int64_t blk = slot >> 4;
+  const int o = int(slot & 15);
+  const int64_t src = (int64_t(t) * kv_heads + h) * head_dim + 8 * j;
+  const int64_t tile = (blk * kv_heads + h) * int64_t(kBlockTokens * head_dim);
+
+  const vec8 kv = *reinterpret_cast<const vec8*>(key + src);
+  *reinterpret_cast<vec8*>(kc + tile + (j * kBlockTokens + o) * 8) = kv;
+
+  const vec8 vv = *reinterpret_cast<const vec8*>(value + src);
+  E* vt = vc + tile;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = 8 * j + e;
+    const int off = (((d >> 5) * 4 + (o >> 2)) * 16 + (d & 15)) * 8 + ((d >> 4) & 1) * 4 + (o & 3);
+    vt[off] = vv[e];
+  }
+}
+
+// Grid (chunks of one block, pairs, 2): z = 0 copies K, z = 1 copies V; each
+// thread moves 16 bytes.
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(char* __restrict__ kc, char* __restrict__ vc, const int64_t* __restrict__ pairs,
+                   int64_t block_bytes, int64_t num_blocks) {
+  char* base = blockIdx.z ? vc : kc;
+  const int64_t src = pairs[2 * int64_t(blockIdx.y)];
+  const int64_t dst = pairs[2 * int64_t(blockIdx.y) + 1];
+  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  const int64_t off = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 16;
+  if (off >= block_bytes) return;
+  *reinterpret_cast<u32x4_t*>(base + dst * block_bytes + off) =
+      *reinterpret_cast<const u32x4_t*>(base + src * block_bytes + off);
+}
+
+}  // namespace
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                    const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
+                                    int32_t head_dim, int64_t num_blocks, int elem_bytes, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  const int64_t runs = int64_t(num_tokens) * num_kv_heads * (head_dim / 8);
+  const dim3 grid(unsigned((runs + 255) / 256));
+  if (elem_bytes == 2) {
+    hipLaunchKernelGGL(reshape_and_cache_kernel<uint16_t>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
+                       static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), slots, num_tokens,
+                       num_kv_heads, head_dim, num_blocks);
+  } else {
+    hipLaunchKernelGGL(reshape_and_cache_kernel<uint32_t>, grid, dim3(256), 0, stream,
+                       static_cast<const uint32_t*>(key), static_cast<const uint32_t*>(value),
+                       static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache), slots, num_tokens,
+                       num_kv_heads, head_dim, num_blocks);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t num_pairs,
+                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream) {
+  const unsigned chunks = unsigned((block_bytes / 16 + 255) / 256);
+  for (int32_t first = 0; first < num_pairs; first += 65535) {
+    const int32_t n = num_pairs - first < 65535 ? num_pairs - first : 65535;
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3(chunks, unsigned(n), 2), dim3(256), 0, stream,
+                       static_cast<char*>(k_cache), static_cast<char*>(v_cache), pairs + 2 * int64_t(first),
+                       block_bytes, num_blocks);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace pa

@@ -1,0 +1,514 @@
+// Paged decode attention for gfx950.
+//
+// out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s, where K_s / V_s are the
+// context's K and V rows reached through the sequence's block table: logical
+// block i of a sequence is physical block table[s][i], and blocks sit
+// anywhere in the pool ("PagedAttention: How vLLM Serves AI Like an
+// Operating System", section "PagedAttention: Virtual Memory for KV Cache").
+// Paging moves data, not results ("Throughput Impact: The Numbers"): the
+// output equals contiguous attention up to floating-point order.
+//
+// Work split: one workgroup (4 waves) per (context partition, kv head,
+// sequence).  Each wave walks every 4th 16-token block of the partition,
+// keeps an online softmax (running max in the exp2 domain, running sum,
+// rescaled accumulator), and the 4 waves merge in LDS.  A sequence that fits
+// one partition writes its output row directly; longer ones leave
+// (accumulator, max, sum) partials that the reduce kernel merges by
+// log-sum-exp in a fixed order, so results are deterministic.
+//
+// fp16 / bf16 run on the matrix cores.  All G = Hq / Hkv query heads of a kv
+// head share each K/V tile, so every tile is read from HBM once:
+//   S^T[token][head] = K[token][:] . Q[head][:]     (16x16x32, K tile = A)
+//   O^T[dim][head]  += V^T[dim][token] . P^T[token][head]   (16x16x16)
+// Writing both products transposed puts the 16 (padded) query heads on the
+// accumulator column, so a lane holds one head's scores and one head's
+// output dims: the softmax rescale needs no data movement.  P is split into
+// hi + lo halves of the input type before the PV product so it keeps ~16
+// (bf16) / ~22 (fp16) mantissa bits; K, Q and V products are exact in fp32.
+// fp32 inputs use the vector ALUs (one workgroup per query head).
+
+#include <math.h>
+
+#include "device_common.h"
+#include "pa_internal.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+
+struct KParams {
+  void* out;
+  const uint16_t* q16;
+  const float* q32;
+  const uint16_t* k16;
+  const uint16_t* v16;
+  const float* k32;
+  const float* v32;
+  const int32_t* tables;
+  const int32_t* ctxs;
+  float* ws_acc;
+  float* ws_m;
+  float* ws_l;
+  int64_t num_blocks;
+  float scale_log2;
+  int32_t max_blocks;
+  int32_t hq, hkv, max_ctx, partition, nparts_max;
+};
+
+template <typename T, bool OUT_F32>
+__device__ inline void store_out(void* out, int64_t idx, float v) {
+  if constexpr (OUT_F32) {
+    static_cast<float*>(out)[idx] = v;
+  } else {
+    static_cast<uint16_t*>(out)[idx] = T::from_float(v);
+  }
+}
+
+// A context length the grid / table cannot cover is a caller error: report it
+// as NaN rows instead of reading out of bounds.
+__device__ inline bool context_out_of_contract(int ctx, const KParams& P) {
+  return ctx < 0 || ctx > P.max_ctx || ctx > P.max_blocks * kBlockTokens;
+}
+
+// ------------------------------------------------------------------------
+// Matrix-core partition kernel (fp16 / bf16).  Grid (partitions, Hkv, S).
+// ------------------------------------------------------------------------
+template <typename T, int D, bool OUT_F32>
+__global__ void __launch_bounds__(kThreads)
+decode_mfma_kernel(KParams P) {
+  constexpr int DC = D / 32;  // 16-byte chunks per lane per tile
+  constexpr int NT = D / 16;  // 16-dim output tiles
+  constexpr int64_t kTile = int64_t(kBlockTokens) * D;
+
+  __shared__ float s_m[kWaves][16];
+  __shared__ float s_l[kWaves][16];
+  __shared__ float s_o[kWaves][16][D + 1];
+  __shared__ int s_bad;
+
+  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;     // head column of this lane
+  const int quad = lane >> 4;  // token quad / k-slice of this lane
+  const int G = P.hq / P.hkv;
+  const int ctx = P.ctxs[s];
+  const int64_t row0 = int64_t(s) * P.hq + int64_t(g) * G;  // first q-head row of the group
+
+  if (context_out_of_contract(ctx, P) || ctx == 0) {
+    if (part == 0) {
+      const float v = ctx == 0 ? 0.f : __builtin_nanf("");
+      for (int idx = threadIdx.x; idx < G * D; idx += kThreads) store_out<T, OUT_F32>(P.out, row0 * D + idx, v);
+    }
+    return;
+  }
+  const int tok0 = part * P.partition;
+  if (tok0 >= ctx) return;
+  const int ntok = min(P.partition, ctx - tok0);
+  const int nblk = (ntok + kBlockTokens - 1) / kBlockTokens;
+  const int nparts = (ctx + P.partition - 1) / P.partition;
+  const int32_t* trow = P.tables + int64_t(s) * P.max_blocks + tok0 / kBlockTokens;
+
+  // Q^T as the B operand: lane supplies head n, dims 8 * (4 i + quad) + 0..7.
+  u32x4_t qb[DC];
+#pragma unroll
+  for (int i = 0; i < DC; ++i) {
+    if (n < G) {
+      qb[i] = load16(P.q16 + (row0 + n) * D + 8 * (4 * i + quad));
+    } else {
+      qb[i] = u32x4_t{0u, 0u, 0u, 0u};
+    }
+  }
+
+  const int64_t blk_stride = int64_t(P.hkv) * kTile;
+  const uint16_t* kbase = P.k16 + int64_t(g) * kTile + lane * 8;
+  const uint16_t* vbase = P.v16 + int64_t(g) * kTile + lane * 8;
+
+  float m = -INFINITY;  // running max of head n (exp2 domain), same in every quad
+  float lsum = 0.f;     // this lane's share of the running sum of head n
+  f32x4_t o[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bool bad = false;
+
+  u32x4_t kk[DC], vv[DC];
+  auto load_tile = [&](int j, u32x4_t* kd, u32x4_t* vd) {
+    int phys = trow[j];
+    if (phys < 0 || int64_t(phys) >= P.num_blocks) {
+      bad = true;
+      phys = 0;
+    }
+    const uint16_t* kt = kbase + int64_t(phys) * blk_stride;
+    const uint16_t* vt = vbase + int64_t(phys) * blk_stride;
+#pragma unroll
+    for (int i = 0; i < DC; ++i) kd[i] = load16(kt + i * 512);
+#pragma unroll
+    for (int i = 0; i < DC; ++i) vd[i] = load16(vt + i * 512);
+  };
+
+  int jb = w;
+  if (jb < nblk) load_tile(jb, kk, vv);
+  for (; jb < nblk; jb += kWaves) {
+    // issue the next block's loads before computing on this one
+    u32x4_t kn[DC], vn[DC];
+    const int jn = jb + kWaves;
+    if (jn < nblk) load_tile(jn, kn, vn);
+
+    // scores: lane holds S^T[token 4*quad + r][head n]
+    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < DC; ++i) sc = Mfma<T>::k32(kk[i], qb[i], sc);
+
+    const int valid = min(kBlockTokens, ntok - jb * kBlockTokens);
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sv[r] = (4 * quad + r < valid) ? sc[r] * P.scale_log2 : -INFINITY;
+    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    bm = fmaxf(bm, shfl_xor(bm, 16));
+    bm = fmaxf(bm, shfl_xor(bm, 32));
+    const float mn = fmaxf(m, bm);
+    const float alpha = fast_exp2(m - mn);
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - mn);
+    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+    m = mn;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) o[t] *= alpha;
+
+    // P^T as the B operand, split hi + lo in the input type
+    uint16_t hi[4], lo[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      hi[r] = T::from_float(pr[r]);
+      lo[r] = T::from_float(pr[r] - T::to_float(hi[r]));
+    }
+    const uint32_t bh0 = pack2(hi[0], hi[1]), bh1 = pack2(hi[2], hi[3]);
+    const uint32_t bl0 = pack2(lo[0], lo[1]), bl1 = pack2(lo[2], lo[3]);
+
+    if (valid < kBlockTokens) {
+      // slots past the context may hold anything (NaN included): zero them so
+      // 0 * garbage never reaches the accumulator
+      const int t0 = 4 * quad;
+      const uint32_t m01 = (t0 + 0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
+      const uint32_t m23 = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int i = 0; i < DC; ++i) {
+        vv[i][0] &= m01;
+        vv[i][1] &= m23;
+        vv[i][2] &= m01;
+        vv[i][3] &= m23;
+      }
+    }
+    // V^T as the A operand: tile t = dims 16 t .. 16 t + 15 is half (t % 2)
+    // of chunk t / 2 -- tokens 4 * quad + 0..3 of dim 16 t + n.
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t a0 = vv[t / 2][2 * (t % 2)];
+      const uint32_t a1 = vv[t / 2][2 * (t % 2) + 1];
+      o[t] = Mfma<T>::k16(a0, a1, bh0, bh1, o[t]);
+      o[t] = Mfma<T>::k16(a0, a1, bl0, bl1, o[t]);
+    }
+#pragma unroll
+    for (int i = 0; i < DC; ++i) {
+      kk[i] = kn[i];
+      vv[i] = vn[i];
+    }
+  }
+  lsum += shfl_xor(lsum, 16);
+  lsum += shfl_xor(lsum, 32);
+
+  // ---- merge the 4 waves
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
+  if (bad) s_bad = 1;
+  if (quad == 0) {
+    s_m[w][n] = m;
+    s_l[w][n] = lsum;
+  }
+  if (n < G) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s_o[w][n][16 * t + 4 * quad + r] = o[t][r];
+  }
+  __syncthreads();
+  const bool any_bad = s_bad != 0;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int h = idx / D, d = idx - (idx / D) * D;
+    float M = s_m[0][h];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float f = fast_exp2(s_m[ww][h] - M);
+      L += f * s_l[ww][h];
+      O += f * s_o[ww][h][d];
+    }
+    if (any_bad) O = __builtin_nanf("");
+    if (nparts == 1) {
+      store_out<T, OUT_F32>(P.out, (row0 + h) * D + d, O / L);
+    } else {
+      const int64_t prow = (row0 + h) * P.nparts_max + part;
+      P.ws_acc[prow * D + d] = O;
+      if (d == 0) {
+        P.ws_m[prow] = M;
+        P.ws_l[prow] = L;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Vector-ALU partition kernel (fp32).  Grid (partitions, Hq, S); one
+// workgroup per query head.  Lane (quad, c): K tile token c, V dims
+// 32 i + 16 h + c for tokens 4 quad + 0..3.
+// ------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(kThreads)
+decode_f32_kernel(KParams P) {
+  constexpr int DC = D / 32;
+  constexpr int64_t kTile = int64_t(kBlockTokens) * D;
+  typedef float f32x8_t __attribute__((ext_vector_type(8)));
+
+  __shared__ float s_m[kWaves], s_l[kWaves];
+  __shared__ float s_o[kWaves][D];
+  __shared__ int s_bad;
+
+  const int part = blockIdx.x, h = blockIdx.y, s = blockIdx.z;
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, quad = lane >> 4;
+  const int G = P.hq / P.hkv;
+  const int g = h / G;
+  const int ctx = P.ctxs[s];
+  const int64_t row = int64_t(s) * P.hq + h;
+
+  if (context_out_of_contract(ctx, P) || ctx == 0) {
+    if (part == 0) {
+      const float v = ctx == 0 ? 0.f : __builtin_nanf("");
+      for (int d = threadIdx.x; d < D; d += kThreads) static_cast<float*>(P.out)[row * D + d] = v;
+    }
+    return;
+  }
+  const int tok0 = part * P.partition;
+  if (tok0 >= ctx) return;
+  const int ntok = min(P.partition, ctx - tok0);
+  const int nblk = (ntok + kBlockTokens - 1) / kBlockTokens;
+  const int nparts = (ctx + P.partition - 1) / P.partition;
+  const int32_t* trow = P.tables + int64_t(s) * P.max_blocks + tok0 / kBlockTokens;
+
+  f32x8_t qv[DC];
+#pragma unroll
+  for (int i = 0; i < DC; ++i) qv[i] = *reinterpret_cast<const f32x8_t*>(P.q32 + row * D + 8 * (4 * i + quad));
+
+  const int64_t blk_stride = int64_t(P.hkv) * kTile;
+  float m = -INFINITY, lsum = 0.f;
+  float acc[DC][2];
+#pragma unroll
+  for (int i = 0; i < DC; ++i) acc[i][0] = acc[i][1] = 0.f;
+  bool bad = false;
+
+  for (int jb = w; jb < nblk; jb += kWaves) {
+    int phys = trow[jb];
+    if (phys < 0 || int64_t(phys) >= P.num_blocks) {
+      bad = true;
+      phys = 0;
+    }
+    const float* kt = P.k32 + int64_t(phys) * blk_stride + int64_t(g) * kTile + lane * 8;
+    const float* vt = P.v32 + int64_t(phys) * blk_stride + int64_t(g) * kTile + lane * 8;
+    f32x8_t kk[DC], vv[DC];
+#pragma unroll
+    for (int i = 0; i < DC; ++i) kk[i] = *reinterpret_cast<const f32x8_t*>(kt + i * 512);
+#pragma unroll
+    for (int i = 0; i < DC; ++i) vv[i] = *reinterpret_cast<const f32x8_t*>(vt + i * 512);
+
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < DC; ++i)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) dot = fmaf(qv[i][e], kk[i][e], dot);
+    dot += shfl_xor(dot, 16);
+    dot += shfl_xor(dot, 32);
+    const int valid = min(kBlockTokens, ntok - jb * kBlockTokens);
+    const float sv = c < valid ? dot * P.scale_log2 : -INFINITY;
+    float bm = sv;
+    bm = fmaxf(bm, shfl_xor(bm, 1));
+    bm = fmaxf(bm, shfl_xor(bm, 2));
+    bm = fmaxf(bm, shfl_xor(bm, 4));
+    bm = fmaxf(bm, shfl_xor(bm, 8));
+    const float mn = fmaxf(m, bm);
+    const float alpha = fast_exp2(m - mn);
+    const float pc = fast_exp2(sv - mn);
+    lsum = lsum * alpha + pc;
+    m = mn;
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = shfl(pc, (lane & 48) | (4 * quad + r));
+#pragma unroll
+    for (int i = 0; i < DC; ++i)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        float a = acc[i][hh] * alpha;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float term = pr[r] * vv[i][hh * 4 + r];
+          a += (4 * quad + r < valid) ? term : 0.f;
+        }
+        acc[i][hh] = a;
+      }
+  }
+  // every quad holds the same per-token sums; fold the 16 tokens of a quad
+  lsum += shfl_xor(lsum, 1);
+  lsum += shfl_xor(lsum, 2);
+  lsum += shfl_xor(lsum, 4);
+  lsum += shfl_xor(lsum, 8);
+#pragma unroll
+  for (int i = 0; i < DC; ++i)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      acc[i][hh] += shfl_xor(acc[i][hh], 16);
+      acc[i][hh] += shfl_xor(acc[i][hh], 32);
+    }
+
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
+  if (bad) s_bad = 1;
+  if (lane == 0) {
+    s_m[w] = m;
+    s_l[w] = lsum;
+  }
+  if (quad == 0) {
+#pragma unroll
+    for (int i = 0; i < DC; ++i)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) s_o[w][32 * i + 16 * hh + c] = acc[i][hh];
+  }
+  __syncthreads();
+  const bool any_bad = s_bad != 0;
+  for (int d = threadIdx.x; d < D; d += kThreads) {
+    float M = s_m[0];
+#pragma unroll
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      const float f = fast_exp2(s_m[ww] - M);
+      L += f * s_l[ww];
+      O += f * s_o[ww][d];
+    }
+    if (any_bad) O = __builtin_nanf("");
+    if (nparts == 1) {
+      static_cast<float*>(P.out)[row * D + d] = O / L;
+    } else {
+      const int64_t prow = row * P.nparts_max + part;
+      P.ws_acc[prow * D + d] = O;
+      if (d == 0) {
+        P.ws_m[prow] = M;
+        P.ws_l[prow] = L;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------
+// Log-sum-exp merge of the partition partials.  Grid (Hq, S), one wave:
+//   M = max_j m_j,  w_j = 2^(m_j - M),  out = sum_j w_j acc_j / sum_j w_j l_j
+// summed in partition order.
+// ------------------------------------------------------------------------
+template <typename T, bool OUT_F32>
+__global__ void __launch_bounds__(kWave)
+decode_reduce_kernel(KParams P, int D) {
+  const int h = blockIdx.x, s = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int ctx = P.ctxs[s];
+  if (context_out_of_contract(ctx, P) || ctx <= P.partition) return;  // written by the partition kernel
+  const int nparts = (ctx + P.partition - 1) / P.partition;
+  const int64_t prow0 = (int64_t(s) * P.hq + h) * P.nparts_max;
+
+  float M = -INFINITY;
+  for (int j = lane; j < nparts; j += kWave) M = fmaxf(M, P.ws_m[prow0 + j]);
+#pragma unroll
+  for (int k = 1; k < kWave; k <<= 1) M = fmaxf(M, shfl_xor(M, k));
+  float L = 0.f;
+  for (int j = lane; j < nparts; j += kWave) L += fast_exp2(P.ws_m[prow0 + j] - M) * P.ws_l[prow0 + j];
+#pragma unroll
+  for (int k = 1; k < kWave; k <<= 1) L += shfl_xor(L, k);
+  const float inv = 1.f / L;
+  for (int d = lane; d < D; d += kWave) {
+    float O = 0.f;
+    for (int j = 0; j < nparts; ++j) O += fast_exp2(P.ws_m[prow0 + j] - M) * P.ws_acc[(prow0 + j) * D + d];
+    store_out<T, OUT_F32>(P.out, (int64_t(s) * P.hq + h) * D + d, O * inv);
+  }
+}
+
+KParams make_params(const DecodeArgs& a) {
+  KParams p{};
+  p.out = a.out;
+  p.q16 = static_cast<const uint16_t*>(a.q);
+  p.q32 = static_cast<const float*>(a.q);
+  p.k16 = static_cast<const uint16_t*>(a.k_cache);
+  p.v16 = static_cast<const uint16_t*>(a.v_cache);
+  p.k32 = static_cast<const float*>(a.k_cache);
+  p.v32 = static_cast<const float*>(a.v_cache);
+  p.tables = a.block_tables;
+  p.ctxs = a.context_lens;
+  p.ws_acc = a.ws_acc;
+  p.ws_m = a.ws_m;
+  p.ws_l = a.ws_l;
+  p.num_blocks = a.num_blocks;
+  p.scale_log2 = a.scale_log2;
+  p.max_blocks = a.max_blocks;
+  p.hq = a.num_q_heads;
+  p.hkv = a.num_kv_heads;
+  p.max_ctx = a.max_context_len;
+  p.partition = a.partition;
+  p.nparts_max = a.num_partitions;
+  return p;
+}
+
+template <typename T, int D>
+hipError_t launch_mfma(const DecodeArgs& a, const KParams& p) {
+  const dim3 grid(unsigned(a.num_partitions), unsigned(a.num_kv_heads), unsigned(a.num_seqs));
+  if (a.out_f32) {
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, true>), grid, dim3(kThreads), 0, a.stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_mfma_kernel<T, D, false>), grid, dim3(kThreads), 0, a.stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_partitions(const DecodeArgs& a) {
+  const KParams p = make_params(a);
+  if (a.dtype == PA_F32) {
+    const dim3 grid(unsigned(a.num_partitions), unsigned(a.num_q_heads), unsigned(a.num_seqs));
+    if (a.head_dim == 64) {
+      hipLaunchKernelGGL(decode_f32_kernel<64>, grid, dim3(kThreads), 0, a.stream, p);
+    } else {
+      hipLaunchKernelGGL(decode_f32_kernel<128>, grid, dim3(kThreads), 0, a.stream, p);
+    }
+    return hipGetLastError();
+  }
+  if (a.dtype == PA_BF16) return a.head_dim == 64 ? launch_mfma<Bf16, 64>(a, p) : launch_mfma<Bf16, 128>(a, p);
+  return a.head_dim == 64 ? launch_mfma<F16, 64>(a, p) : launch_mfma<F16, 128>(a, p);
+}
+
+hipError_t launch_decode_reduce(const DecodeArgs& a) {
+  if (a.num_partitions <= 1) return hipSuccess;
+  const KParams p = make_params(a);
+  const dim3 grid(unsigned(a.num_q_heads), unsigned(a.num_seqs));
+  if (a.out_f32) {
+    hipLaunchKernelGGL((decode_reduce_kernel<F16, true>), grid, dim3(kWave), 0, a.stream, p, int(a.head_dim));
+  } else if (a.dtype == PA_BF16) {
+    hipLaunchKernelGGL((decode_reduce_kernel<Bf16, false>), grid, dim3(kWave), 0, a.stream, p, int(a.head_dim));
+  } else {
+    hipLaunchKernelGGL((decode_reduce_kernel<F16, false>), grid, dim3(kWave), 0, a.stream, p, int(a.head_dim));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace pa

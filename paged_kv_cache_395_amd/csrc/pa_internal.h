@@ -1,0 +1,70 @@
+// Host-side declarations shared by the C ABI and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "pa.h"
+
+namespace pa {
+
+// Record a message for pa_last_error() and return `st`.
+pa_status_t fail(pa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// Tokens per context partition when the caller passes 0.
+constexpr int kDefaultPartition = 512;
+
+struct DecodeArgs {
+  void* out;
+  bool out_f32;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int64_t num_blocks;
+  float scale_log2;  // scale * log2(e): scores live in the exp2 domain
+  int32_t max_context_len;
+  int32_t partition;
+  int32_t num_partitions;  // ceil(max_context_len / partition)
+  float* ws_acc;           // [S][Hq][num_partitions][D]
+  float* ws_m;             // [S][Hq][num_partitions]
+  float* ws_l;             // [S][Hq][num_partitions]
+  pa_dtype_t dtype;
+  hipStream_t stream;
+};
+
+hipError_t launch_decode_partitions(const DecodeArgs& a);
+hipError_t launch_decode_reduce(const DecodeArgs& a);
+
+struct PrefillArgs {
+  void* out;
+  bool out_f32;
+  const void* q;
+  int32_t chunk;
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  int32_t max_blocks;
+  const int32_t* context_lens;
+  int32_t num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int64_t num_blocks;
+  float scale_log2;
+  int32_t max_context_len;
+  pa_dtype_t dtype;
+  hipStream_t stream;
+};
+
+hipError_t launch_prefill_chunk(const PrefillArgs& a);
+
+hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
+                                    const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
+                                    int32_t head_dim, int64_t num_blocks, int elem_bytes, hipStream_t stream);
+
+hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t num_pairs,
+                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
+
+}  // namespace pa

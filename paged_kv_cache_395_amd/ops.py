@@ -1,0 +1,146 @@
+"""torch-tensor wrappers over the device entry points of libpa.so.
+
+Argument marshalling only: each function checks shapes / dtypes / devices,
+takes raw device pointers and the current HIP stream, and calls the C ABI.
+All computation happens in the library's gfx950 kernels.
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+
+_DTYPE = {torch.float32: _lib.PA_F32, torch.float16: _lib.PA_F16, torch.bfloat16: _lib.PA_BF16}
+BLOCK_SIZE = 16
+
+
+def _code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPE[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def _dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("all tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _p(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _pool_dims(k_cache: torch.Tensor):
+    if k_cache.dim() != 3 or k_cache.shape[2] % BLOCK_SIZE:
+        raise ValueError("pools are [num_blocks, num_kv_heads, 16 * head_dim]")
+    return k_cache.shape[0], k_cache.shape[1], k_cache.shape[2] // BLOCK_SIZE
+
+
+def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """Write key/value [T, Hkv, D] into their slots (int64 [T]) of the pools."""
+    _dev(key, value, k_cache, v_cache, slot_mapping)
+    NB, Hkv, D = _pool_dims(k_cache)
+    if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (Hkv, D):
+        raise ValueError("key / value must be [T, num_kv_heads, head_dim]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
+        raise ValueError("slot_mapping must be int64 [T]")
+    if not (key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("key, value and the pools must share one dtype")
+    _lib.check(_lib.load().pa_reshape_and_cache(_p(key), _p(value), _p(k_cache), _p(v_cache), _p(slot_mapping),
+                                                key.shape[0], Hkv, D, BLOCK_SIZE, NB, _code(k_cache),
+                                                _stream(stream)))
+
+
+def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
+    """Copy physical blocks src -> dst for each row (src, dst) of int64 ``pairs`` [n, 2]."""
+    _dev(k_cache, v_cache, pairs)
+    NB, Hkv, D = _pool_dims(k_cache)
+    if pairs.dtype != torch.int64 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int64 [n, 2]")
+    _lib.check(_lib.load().pa_copy_blocks(_p(k_cache), _p(v_cache), _p(pairs), pairs.shape[0], Hkv, D, BLOCK_SIZE,
+                                          NB, _code(k_cache), _stream(stream)))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
+                           partition_size: int = 0) -> int:
+    return int(_lib.load().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+                                                     partition_size))
+
+
+def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size,
+                 workspace):
+    _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+    NB, Hkv, D = _pool_dims(k_cache)
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
+    S, Hq = q.shape[0], q.shape[1]
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and the pools must share one dtype")
+    need = decode_workspace_bytes(S, Hq, D, max_context_len, partition_size)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _p(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return (_p(out), _code(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), block_tables.shape[1],
+            _p(context_lens), S, Hq, Hkv, D, BLOCK_SIZE, NB, float(scale), int(max_context_len),
+            int(partition_size), ws_ptr, ws_bytes, _code(q)), workspace
+
+
+def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size=0,
+           workspace=None, stream=None) -> None:
+    """out[s, h] = softmax(scale * q[s, h] . K_s^T) V_s over the paged context of sequence s."""
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                           partition_size, workspace)
+    _lib.check(_lib.load().pa_decode(*args, _stream(stream)))
+
+
+def decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size,
+                      workspace, stream=None) -> None:
+    """First of decode's two launches (see decode_reduce)."""
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                           partition_size, workspace)
+    _lib.check(_lib.load().pa_decode_partitions(*args, _stream(stream)))
+
+
+def decode_reduce(out, context_lens, max_context_len, partition_size, workspace, stream=None) -> None:
+    """Second of decode's launches: merge the partition partials into ``out``."""
+    _dev(out, context_lens)
+    S, Hq, D = out.shape
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _lib.check(_lib.load().pa_decode_reduce(_p(out), _code(out), _p(context_lens), S, Hq, D, int(max_context_len),
+                                            int(partition_size), _p(workspace) if workspace is not None else None,
+                                            ws_bytes, _stream(stream)))
+
+
+def prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, stream=None) -> None:
+    """Causal attention of q [S, C, Hq, D] (the last C positions of each context) over the paged cache."""
+    _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+    NB, Hkv, D = _pool_dims(k_cache)
+    if q.dim() != 4 or q.shape[3] != D:
+        raise ValueError("q must be [num_seqs, chunk_len, num_q_heads, head_dim]")
+    S, C, Hq = q.shape[0], q.shape[1], q.shape[2]
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    _lib.check(_lib.load().pa_prefill_chunk(_p(out), _code(out), _p(q), C, _p(k_cache), _p(v_cache),
+                                            _p(block_tables), block_tables.shape[1], _p(context_lens), S, Hq, Hkv, D,
+                                            BLOCK_SIZE, NB, float(scale), int(max_context_len), _code(q),
+                                            _stream(stream)))

@@ -1,0 +1,115 @@
+"""The C-ABI library loads, exports every symbol include/pa.h declares, and
+rejects arguments outside the contract before any device work (no GPU needed).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_395_amd as pa
+from paged_kv_cache_395_amd import _lib
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "pa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_expected_entry_points():
+    names = declared_functions()
+    for required in ["pa_reshape_and_cache", "pa_decode", "pa_prefill_chunk", "pa_copy_blocks",
+                     "pa_decode_workspace_bytes", "pa_last_error", "pa_bm_create", "pa_bm_append_tokens"]:
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_covers_exactly_the_header():
+    assert sorted(_lib.SIGNATURES) == declared_functions()
+
+
+def test_version_string():
+    assert b"gfx950" in _lib.load().pa_version()
+
+
+L = _lib.load()
+NULL = None
+
+
+def decode_call(**kw):
+    a = dict(out=1, out_dtype=_lib.PA_F32, q=1, k=1, v=1, tables=1, maxb=4, ctx=1, S=1, Hq=4, Hkv=4, D=128, bs=16,
+             NB=10, scale=0.1, max_ctx=64, P=0, ws=None, ws_bytes=0, dtype=_lib.PA_BF16)
+    a.update(kw)
+    return L.pa_decode(a["out"], a["out_dtype"], a["q"], a["k"], a["v"], a["tables"], a["maxb"], a["ctx"], a["S"],
+                       a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["scale"], a["max_ctx"], a["P"], a["ws"],
+                       a["ws_bytes"], a["dtype"], NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), _lib.PA_EUNSUPPORTED),
+    (dict(bs=8), _lib.PA_EUNSUPPORTED),
+    (dict(dtype=7), _lib.PA_EUNSUPPORTED),
+    (dict(Hq=6, Hkv=4), _lib.PA_EINVAL),
+    (dict(Hq=32, Hkv=1), _lib.PA_EUNSUPPORTED),
+    (dict(out_dtype=_lib.PA_F16), _lib.PA_EUNSUPPORTED),
+    (dict(maxb=3), _lib.PA_EINVAL),
+    (dict(P=24), _lib.PA_EINVAL),
+    (dict(out=None), _lib.PA_EINVAL),
+    (dict(max_ctx=600), _lib.PA_EINVAL),  # table of 4 blocks cannot hold 600 tokens
+    (dict(max_ctx=600, maxb=40), _lib.PA_EWORKSPACE),  # two partitions need a workspace
+    (dict(max_ctx=600, maxb=40, ws=1, ws_bytes=10), _lib.PA_EWORKSPACE),
+    (dict(scale=float("inf")), _lib.PA_EINVAL),
+])
+def test_decode_rejects_bad_arguments_before_launch(kw, status):
+    st = decode_call(**kw)
+    assert st == status
+    assert L.pa_last_error()
+
+
+def test_decode_with_no_sequences_is_a_no_op():
+    assert decode_call(S=0, out=None, q=None) == _lib.PA_OK
+
+
+def test_workspace_size_formula():
+    # single partition: no workspace; otherwise acc + m + l, 256-byte aligned
+    assert L.pa_decode_workspace_bytes(8, 32, 128, 512, 512) == 0
+    S, Hq, D, n = 8, 32, 128, 3
+    rows = S * Hq * n
+    align = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert L.pa_decode_workspace_bytes(S, Hq, D, 1100, 512) == align(rows * D * 4) + 2 * align(rows * 4)
+    assert L.pa_decode_workspace_bytes(S, Hq, D, 1100, 0) == L.pa_decode_workspace_bytes(S, Hq, D, 1100, 512)
+
+
+def test_cache_write_and_copy_reject_bad_arguments():
+    assert L.pa_reshape_and_cache(1, 1, 1, 1, 1, 4, 8, 100, 16, 10, _lib.PA_BF16, NULL) == _lib.PA_EUNSUPPORTED
+    assert L.pa_reshape_and_cache(1, 1, 1, 1, 1, -1, 8, 128, 16, 10, _lib.PA_BF16, NULL) == _lib.PA_EINVAL
+    assert L.pa_reshape_and_cache(None, 1, 1, 1, 1, 4, 8, 128, 16, 10, _lib.PA_BF16, NULL) == _lib.PA_EINVAL
+    assert L.pa_reshape_and_cache(None, None, None, None, None, 0, 8, 128, 16, 10, _lib.PA_BF16, NULL) == _lib.PA_OK
+    assert L.pa_copy_blocks(1, 1, 1, 2, 8, 128, 32, 10, _lib.PA_F16, NULL) == _lib.PA_EUNSUPPORTED
+    assert L.pa_copy_blocks(None, None, None, 0, 8, 128, 16, 10, _lib.PA_F16, NULL) == _lib.PA_OK
+
+
+def test_prefill_rejects_bad_arguments():
+    def call(**kw):
+        a = dict(dtype=_lib.PA_BF16, C=16, max_ctx=64, maxb=4, Hq=8, Hkv=2, out_dtype=_lib.PA_F32)
+        a.update(kw)
+        return L.pa_prefill_chunk(1, a["out_dtype"], 1, a["C"], 1, 1, 1, a["maxb"], 1, 2, a["Hq"], a["Hkv"], 128, 16,
+                                  100, 0.1, a["max_ctx"], a["dtype"], NULL)
+    assert call(dtype=_lib.PA_F32) == _lib.PA_EUNSUPPORTED
+    assert call(max_ctx=8) == _lib.PA_EINVAL
+    assert call(maxb=2) == _lib.PA_EINVAL
+    assert call(Hq=7) == _lib.PA_EINVAL
+    assert call(out_dtype=_lib.PA_F16) == _lib.PA_EUNSUPPORTED
+
+
+def test_package_exposes_the_binding():
+    assert pa.BlockManager is not None
+    assert callable(pa.ops.decode)

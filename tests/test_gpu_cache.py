@@ -1,0 +1,106 @@
+"""Cache write, block copy and copy-on-write on the GPU: bit-exact against the
+oracle over the whole pool (which also proves untouched bytes unchanged)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as OA
+from oracle.block_manager import RefBlockManager
+from paged_kv_cache_395_amd import BlockManager, ops
+from tests._gpu import Prepared, say, to_dev, to_host
+from workloads import make_workload, to_storage
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_f32", {}),
+    ("mha7b_f16", dict(num_seqs=8)),
+    ("gqa8b_bf16", {}),
+    ("shared_prefix_bf16", dict(num_users=40, num_prompts=8)),
+    ("longctx_bf16", dict(num_seqs=4, ctx=4096, chunk=512)),
+    ("longctx_bf16", {}),
+], ids=["tiny_f32", "f16", "bf16_full", "shared", "chunk_small", "chunk_full"])
+def test_cache_write_is_bit_exact(name, kw):
+    w = make_workload(name, **kw)
+    say(f"[cache-write] {name} tokens={w.num_seqs * w.append}")
+    p = Prepared(w)
+    d = p.device()
+    p.write_step(d)
+    torch.cuda.synchronize()
+    k_ref, v_ref = p.oracle_pools()
+    assert np.array_equal(to_host(d["k"], w.dtype).view(np.uint8), k_ref.view(np.uint8))
+    assert np.array_equal(to_host(d["v"], w.dtype).view(np.uint8), v_ref.view(np.uint8))
+
+
+def test_cache_write_skips_negative_and_out_of_pool_slots():
+    w = make_workload("tiny_f32")
+    d_k = to_dev(w.k_pool, "f32")
+    d_v = to_dev(w.v_pool, "f32")
+    key = to_dev(w.step_rows("k"), "f32")
+    val = to_dev(w.step_rows("v"), "f32")
+    slots = np.array([-1, 5, w.num_blocks * 16, 16 * 19 + 15], dtype=np.int64)
+    ops.reshape_and_cache(key, val, d_k, d_v, torch.from_numpy(slots).cuda())
+    k_ref, v_ref = w.k_pool.copy(), w.v_pool.copy()
+    ok = np.array([-1, 5, -1, 16 * 19 + 15])  # the out-of-pool slot is skipped like a negative one
+    OA.reshape_and_cache(k_ref, v_ref, w.step_rows("k"), w.step_rows("v"), ok)
+    assert np.array_equal(to_host(d_k, "f32").view(np.uint32), k_ref.view(np.uint32))
+    assert np.array_equal(to_host(d_v, "f32").view(np.uint32), v_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_copy_blocks_is_bit_exact(dtype):
+    rng = np.random.default_rng(21)
+    NB, Hkv, D = 300, 8, 128
+    k = to_storage(rng.standard_normal((NB, Hkv, 16 * D), dtype=np.float32), dtype)
+    v = to_storage(rng.standard_normal((NB, Hkv, 16 * D), dtype=np.float32), dtype)
+    perm = rng.permutation(NB)
+    pairs = np.stack([perm[:70], perm[70:140]], axis=1).astype(np.int64)
+    dk, dv = to_dev(k, dtype), to_dev(v, dtype)
+    ops.copy_blocks(dk, dv, torch.from_numpy(pairs).cuda())
+    OA.copy_blocks(k, v, pairs)
+    assert np.array_equal(to_host(dk, dtype).view(np.uint8), k.view(np.uint8))
+    assert np.array_equal(to_host(dv, dtype).view(np.uint8), v.view(np.uint8))
+
+
+def test_copy_on_write_end_to_end():
+    """A 90-token prompt sampled n=4: the first write of each sample into the
+    shared, partly filled block moves it onto a private copy (block manager ->
+    device copy -> cache write), and decode of every sample matches the oracle."""
+    rng = np.random.default_rng(31)
+    NB, Hkv, Hq, D = 40, 8, 32, 128
+    order = rng.permutation(NB).astype(np.int32)
+    k = to_storage(rng.standard_normal((NB, Hkv, 16 * D), dtype=np.float32), "bf16")
+    v = to_storage(rng.standard_normal((NB, Hkv, 16 * D), dtype=np.float32), "bf16")
+    nat, ref = BlockManager(NB, free_order=order), RefBlockManager(NB, free_order=order)
+    for bm in (nat, ref):
+        bm.add_seq(100, 90)
+        for c in range(4):
+            bm.fork(100, c)
+        bm.free_seq(100)
+    dk, dv = to_dev(k, "bf16"), to_dev(v, "bf16")
+    k_ref, v_ref = k.copy(), v.copy()
+    for step in range(3):
+        batch = [0, 1, 2, 3]
+        slots, cow = nat.append_tokens(batch)
+        r_slots, r_cow = ref.append_tokens(batch)
+        assert slots.tolist() == list(r_slots) and cow.tolist() == [list(p) for p in r_cow]
+        if step == 0:
+            assert len(cow) == 3
+        key = to_storage(rng.standard_normal((4, Hkv, D), dtype=np.float32), "bf16")
+        val = to_storage(rng.standard_normal((4, Hkv, D), dtype=np.float32), "bf16")
+        if len(cow):
+            ops.copy_blocks(dk, dv, torch.from_numpy(np.ascontiguousarray(cow)).cuda())
+            OA.copy_blocks(k_ref, v_ref, np.array(r_cow))
+        ops.reshape_and_cache(to_dev(key, "bf16"), to_dev(val, "bf16"), dk, dv, torch.from_numpy(slots).cuda())
+        OA.reshape_and_cache(k_ref, v_ref, key, val, np.array(r_slots))
+    assert np.array_equal(to_host(dk, "bf16"), k_ref) and np.array_equal(to_host(dv, "bf16"), v_ref)
+    table, ctx = nat.block_table([0, 1, 2, 3], 8, pad=NB + 5)
+    q = to_storage(rng.standard_normal((4, Hq, D), dtype=np.float32), "bf16")
+    out = torch.empty((4, Hq, D), dtype=torch.float32, device="cuda")
+    ops.decode(out, to_dev(q, "bf16"), dk, dv, torch.from_numpy(table).cuda(), torch.from_numpy(ctx).cuda(),
+               D ** -0.5, int(ctx.max()))
+    want = OA.decode(q, k_ref, v_ref, table, ctx, D ** -0.5, "bf16")
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.abs(got - want).max() <= 2e-3
+    assert np.linalg.norm(got - want) / np.linalg.norm(want) <= 1e-3

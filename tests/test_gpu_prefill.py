@@ -1,0 +1,62 @@
+"""Chunked prefill on the GPU against the oracle: reduced sizes in full,
+the 16 x 32768 long-context chunk on sampled rows, the causal edge rows,
+and the agreement of the chunk's last row with decode."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as OA
+from paged_kv_cache_395_amd import ops
+from tests._gpu import Prepared, assert_close, out_f64, say, to_dev
+from workloads import make_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def run_prefill(p, out_f32=True):
+    w = p.w
+    d = p.device()
+    p.write_step(d)
+    q = to_dev(w.q, w.dtype)
+    out = torch.empty(q.shape, dtype=torch.float32 if out_f32 else q.dtype, device="cuda")
+    ops.prefill_chunk(out, q, d["k"], d["v"], d["table"], d["ctx"], w.scale, p.max_ctx)
+    return d, out
+
+
+@pytest.mark.parametrize("kw", [dict(num_seqs=3, ctx=700, chunk=100), dict(num_seqs=2, ctx=300, chunk=37, Hq=16, Hkv=4),
+                                dict(num_seqs=2, ctx=64, chunk=64), dict(num_seqs=1, ctx=515, chunk=3, Hq=8, Hkv=8)],
+                         ids=["c100", "c37_g4", "whole", "g1"])
+def test_prefill_reduced_matches_oracle(kw):
+    p = Prepared(make_workload("longctx_bf16", **kw))
+    say(f"[prefill] {kw}")
+    _, out = run_prefill(p)
+    k, v = p.oracle_pools()
+    ref = OA.prefill_chunk(p.w.q, k, v, p.table, p.ctx, p.w.scale, "bf16")
+    assert_close(out_f64(out), ref, "bf16", str(kw))
+
+
+def test_prefill_full_long_context_on_sampled_rows():
+    p = Prepared(make_workload("longctx_bf16"))
+    say("[prefill] full 16 x 32768, chunk 512")
+    d, out = run_prefill(p)
+    got = out_f64(out)
+    k, v = p.oracle_pools()
+    rng = np.random.default_rng(0)
+    rows = sorted({0, 1, 15, 16, 255, 256, 510, 511} | set(rng.choice(512, 8, replace=False).tolist()))
+    seqs = [0, 9, 15]
+    heads = sorted({0, 7, 8, 63} | set(rng.choice(64, 4, replace=False).tolist()))
+    ref = OA.prefill_chunk(p.w.q, k, v, p.table, p.ctx, p.w.scale, "bf16", seqs=seqs, heads=heads, rows=rows)
+    sel = np.ix_(seqs, rows, heads)
+    assert_close(got[sel], ref[sel], "bf16", "sampled rows")
+    # the chunk's last row is decode over the whole context
+    dec = p.gpu_decode(d, q=to_dev(p.w.decode_q, "bf16"))
+    assert_close(got[:, -1], out_f64(dec), "bf16", "last row vs decode")
+
+
+def test_prefill_output_dtype_and_determinism():
+    p = Prepared(make_workload("longctx_bf16", num_seqs=2, ctx=400, chunk=64))
+    d, out = run_prefill(p)
+    _, out2 = run_prefill(p)
+    assert torch.equal(out, out2)
+    _, outb = run_prefill(p, out_f32=False)
+    assert torch.equal(outb, out.to(torch.bfloat16))
