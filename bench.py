@@ -116,6 +116,8 @@ def main():
     ap.add_argument("--partition", type=int, default=0, help="tokens per context partition (0 = default 512)")
     ap.add_argument("--cold-iters", type=int, default=20, help="decode launches timed after a 1 GiB cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (scales HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -263,6 +265,13 @@ def main():
     del big, scratch
 
     extra_fields = {}
+    if args.copy_probe_mib:
+        src = torch.ones(args.copy_probe_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        extra_fields["copy_probe_bytes"] = {"read": src.numel(), "write": dst.numel()}
+        del src, dst
     if w.append > 1:
         # the chunk workload also times its chunked prefill (matrix-core bound)
         qc = to_dev(w.q)

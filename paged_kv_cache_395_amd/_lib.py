@@ -72,10 +72,21 @@ _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """Load libpa.so once; raise if it has not been built."""
+    """Load libpa.so once; raise if it has not been built.
+
+    A process must hold a single HIP runtime.  torch ships its own
+    libamdhip64 and loads it by path; when libpa.so is loaded first it pulls
+    the system copy through its run path and the two runtimes conflict (the
+    second reports no device).  Importing torch first makes libpa.so bind to
+    the runtime torch already loaded.
+    """
     global _lib
     with _lock:
         if _lib is None:
+            try:
+                import torch  # noqa: F401
+            except ImportError:  # host-only use (block manager) without torch
+                pass
             if not os.path.exists(LIB_PATH):
                 raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_395_amd.build`")
             lib = ctypes.CDLL(LIB_PATH)

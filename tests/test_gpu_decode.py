@@ -67,21 +67,25 @@ def test_output_in_input_dtype_is_the_rounded_result(name, kw):
     dt = p.w.dtype
     got = OA.to_f64(to_host(out, dt), dt)
     want = OA.to_f64(OA.round_f64_to(ref, dt), dt)
-    # at most one unit in the last place from the correctly rounded value
+    # the stored value is the correct rounding of a value within 1e-5 of the
+    # oracle: one unit in the last place for ordinary magnitudes, more only
+    # where the 16-bit spacing is finer than fp32 accumulation error (near 0)
     if dt == "f32":
         assert_close(got, ref, dt)
     else:
-        assert ulp_distance(to_host(out, dt), OA.round_f64_to(ref, dt), dt).max() <= 1
+        g = ordered_bits(to_host(out, dt), dt)
+        lo = ordered_bits(OA.round_f64_to(ref - 1e-5, dt), dt)
+        hi = ordered_bits(OA.round_f64_to(ref + 1e-5, dt), dt)
+        assert np.all((lo <= g) & (g <= hi))
+        assert np.mean(g == ordered_bits(OA.round_f64_to(ref, dt), dt)) > 0.9
     if dt == "f16":
         assert_close(got, ref, dt)
 
 
-def ulp_distance(a_bits: np.ndarray, b_bits: np.ndarray, dt: str) -> np.ndarray:
-    """Distance in representable steps between two arrays of 16-bit patterns."""
-    def ordered(x):
-        x = (x.view(np.uint16) if dt == "f16" else x).astype(np.int64)
-        return np.where(x & 0x8000, -(x & 0x7FFF), x)
-    return np.abs(ordered(a_bits) - ordered(b_bits))
+def ordered_bits(bits: np.ndarray, dt: str) -> np.ndarray:
+    """16-bit float patterns mapped to integers in the order of their values."""
+    x = (bits.view(np.uint16) if dt == "f16" else bits).astype(np.int64)
+    return np.where(x & 0x8000, -(x & 0x7FFF), x)
 
 
 @pytest.mark.parametrize("partition", [16, 64, 512, 2048, 0])
