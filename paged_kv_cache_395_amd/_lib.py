@@ -1,6 +1,6 @@
 """ctypes loader for ``libpa.so`` (the C ABI declared in include/pa.h).
 
-The library must have been built (``paged_kv_cache_395_amd.build``); there is
+The library must have been built (``python paged_kv_cache_395_amd/build.py``); there is
 no fallback of any kind: importing without it raises.
 """
 
@@ -88,7 +88,7 @@ def load() -> ctypes.CDLL:
             except ImportError:  # host-only use (block manager) without torch
                 pass
             if not os.path.exists(LIB_PATH):
-                raise ImportError(f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_395_amd.build`")
+                raise ImportError(f"{LIB_PATH} is missing: build it with `python paged_kv_cache_395_amd/build.py`")
             lib = ctypes.CDLL(LIB_PATH)
             for name, (res, args) in SIGNATURES.items():
                 fn = getattr(lib, name)

@@ -1,9 +1,11 @@
 """Build the C-ABI library ``libpa.so`` for gfx950 with hipcc, in-tree.
 
-    python -m paged_kv_cache_395_amd.build
+    python paged_kv_cache_395_amd/build.py
 
 compiles every source under ``csrc/`` (in parallel) and links
-``paged_kv_cache_395_amd/lib/libpa.so``.  hipcc cross-compiles for gfx950
+``paged_kv_cache_395_amd/lib/libpa.so``.  It is run as a script (or loaded
+by path), never imported through the package, whose import loads the
+library.  hipcc cross-compiles for gfx950
 without a GPU present.
 """
 
