@@ -113,7 +113,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mha7b_f16",
                     choices=["tiny_f32", "mha7b_f16", "gqa8b_bf16", "shared_prefix_bf16", "longctx_bf16"])
-    ap.add_argument("--partition", type=int, default=0, help="tokens per context partition (0 = default 512)")
+    ap.add_argument("--partition", type=int, default=0, help="tokens per context partition (0 = the library's choice)")
     ap.add_argument("--cold-iters", type=int, default=20, help="decode launches timed after a 1 GiB cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -165,8 +165,9 @@ def main():
     d_ctx = dbuf[8 * n_tok: 8 * n_tok + 4 * S].view(torch.int32)
     d_table = dbuf[8 * n_tok + 4 * S:].view(torch.int32).view(S, maxB)
     final_ctx = int(w.lengths["final_ctx"].max()) + extra
-    ws = torch.empty(max(1, ops.decode_workspace_bytes(S, Hq, D, final_ctx, args.partition)), dtype=torch.uint8,
-                     device=dev)
+    first_ctx = int(w.lengths["final_ctx"].max())
+    ws_need = max(ops.decode_workspace_bytes(S, Hq, Hkv, D, c, args.partition) for c in range(first_ctx, final_ctx + 1))
+    ws = torch.empty(max(1, ws_need), dtype=torch.uint8, device=dev)
     seqs = np.ascontiguousarray(w.step_seqs, dtype=np.int64)
     batch = np.ascontiguousarray(w.batch, dtype=np.int64)
     stream = torch.cuda.current_stream()
@@ -213,7 +214,7 @@ def main():
         ops.decode_partitions(out, q, k_pool, v_pool, d_table, d_ctx, w.scale, mx, args.partition, ws)
         if timed:
             e[2].record(stream)
-        ops.decode_reduce(out, d_ctx, mx, args.partition, ws)
+        ops.decode_reduce(out, d_ctx, Hkv, mx, args.partition, ws)
         if timed:
             e[3].record(stream)
             ev_pairs.append(e)
@@ -309,7 +310,7 @@ def main():
         "config": {"workload": f"{w.name}: {w.description}", "num_seqs": S, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": 16,
                    "mean_context": round(float(ctx_now.mean()), 1),
-                   "partition": args.partition or 512},
+                   "partition": ops.decode_partition_size(S, Hkv, int(ctx_now.max()), args.partition)},
         "hbm_frac_whole_step": round(value / HBM_PEAK_GBS, 4),
         "seqs_per_s": round(S * args.steps / elapsed, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",

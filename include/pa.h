@@ -126,10 +126,11 @@ pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, i
  *                   (PA_F32, or the input dtype)
  *   q               device [num_seqs][num_q_heads][head_dim] of dtype
  *   max_context_len host upper bound of context_lens (sizes the grid)
- *   partition_size  tokens per context partition, a multiple of 16;
- *                   0 picks the default (512).  Sequences longer than one
- *                   partition are split; the pieces are merged exactly by a
- *                   log-sum-exp reduction.
+ *   partition_size  tokens per context partition, a multiple of 16, or 0
+ *                   to let the library choose (pa_decode_partition_size
+ *                   reports the choice).  Sequences longer than one
+ *                   partition are split; the pieces are merged exactly by
+ *                   a log-sum-exp reduction.
  *   workspace       device scratch of at least
  *                   pa_decode_workspace_bytes(...) bytes (may be NULL when
  *                   that is 0); its contents are private to the call.
@@ -137,8 +138,15 @@ pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, i
  * vector ALUs; PA_F16 / PA_BF16 use the matrix cores with fp32
  * accumulation and an fp32 softmax.
  * ---------------------------------------------------------------------- */
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_context_len, int32_t partition_size);
+/* Effective partition size for these sizes (partition_size 0 = the
+ * library's choice: 512 to 4096 tokens, the larger the fewer (sequence, kv
+ * head) pairs there are to fill the GPU); -1 for invalid arguments. */
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                 int32_t partition_size);
+
+/* Workspace bytes pa_decode needs for these sizes (0: none). */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_context_len, int32_t partition_size);
 
 pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* q,
                       const void* k_cache, const void* v_cache,
@@ -166,8 +174,8 @@ pa_status_t pa_decode_partitions(void* out, pa_dtype_t out_dtype, const void* q,
                                  pa_dtype_t dtype, void* stream);
 
 pa_status_t pa_decode_reduce(void* out, pa_dtype_t out_dtype, const int32_t* context_lens,
-                             int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
-                             int32_t max_context_len, int32_t partition_size,
+                             int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t max_context_len, int32_t partition_size,
                              const void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

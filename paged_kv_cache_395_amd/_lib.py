@@ -44,12 +44,13 @@ SIGNATURES = {
     "pa_last_error": (ctypes.c_char_p, []),
     "pa_reshape_and_cache": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, ctypes.c_int, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, ctypes.c_int, _vp]),
-    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32]),
+    "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _i64, _f32, _i32, _i32, _vp, _sz, ctypes.c_int, _vp]),
     "pa_decode_partitions": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                             _i32, _i64, _f32, _i32, _i32, _vp, _sz, ctypes.c_int, _vp]),
-    "pa_decode_reduce": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "pa_decode_reduce": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "pa_prefill_chunk": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                         _i32, _i32, _i64, _f32, _i32, ctypes.c_int, _vp]),
     "pa_bm_create": (_vp, [_i64, _i32, _vp]),

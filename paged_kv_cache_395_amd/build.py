@@ -25,7 +25,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # Packed fp32 instructions are switched off for device code: the compiler
 # would otherwise emit v_pk_{add,mul,fma}_f32 from ordinary float code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Matrix-core accumulators are kept in ordinary VGPRs (gfx950 allows either
+# file): the online-softmax rescale multiplies them on the vector ALUs, and
+# in the accumulator file every rescale would copy them out and back.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
           "-Wall", "-Wno-unused-function"] + DEVICE_FLAGS
 

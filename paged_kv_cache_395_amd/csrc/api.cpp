@@ -34,6 +34,33 @@ pa_status_t check_pool(int32_t kv_heads, int32_t head_dim, int32_t block_size, i
   return PA_OK;
 }
 
+// Tokens per context partition when the caller passes 0.  A partition is
+// the work of one workgroup; sequences longer than one partition leave fp32
+// partials (accumulator, max, sum) that a second kernel merges.  Writing
+// those partials costs far more decode time than their share of the bytes
+// (HBM writes interleaved with the read stream), so partitions are made as
+// large as the grid allows: starting from 512 tokens they double, up to
+// 4096, while the grid still holds >= kMinWorkgroups workgroups (4 per CU)
+// and, once the (sequence, kv head) pairs alone fill the GPU, while a
+// partition stays within a quarter of the longest context (larger ones
+// only unbalance ragged batches).
+constexpr int32_t kMinPartition = 512;
+constexpr int32_t kMaxDefaultPartition = 4096;
+constexpr int64_t kMinWorkgroups = 1024;
+
+int32_t choose_partition(int64_t S, int64_t Hkv, int64_t max_ctx, int32_t requested) {
+  if (requested != 0) return requested;
+  const int64_t pairs = S * Hkv;
+  int32_t p = kMinPartition;
+  while (p < kMaxDefaultPartition) {
+    const int64_t next = 2 * int64_t(p);
+    if (pairs * ceil_div(max_ctx, next) < kMinWorkgroups) break;
+    if (pairs >= kMinWorkgroups && next > max_ctx / 4) break;
+    p = int32_t(next);
+  }
+  return p;
+}
+
 struct DecodeCheck {
   int32_t partition;
   int32_t nparts;
@@ -54,8 +81,8 @@ pa_status_t check_decode(const void* out, pa_dtype_t out_dtype, const void* q, c
   if (max_blocks < 0 || int64_t(max_blocks) * 16 < max_ctx)
     return fail(PA_EINVAL, "max_blocks_per_seq (%d) cannot hold max_context_len (%d)", max_blocks, max_ctx);
   if (!isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");
-  if (partition == 0) partition = kDefaultPartition;
-  if (partition < 16 || partition % 16 != 0) return fail(PA_EINVAL, "partition_size must be a positive multiple of 16");
+  if (partition < 0 || partition % 16 != 0) return fail(PA_EINVAL, "partition_size must be 0 or a positive multiple of 16");
+  partition = choose_partition(S, Hkv, max_ctx, partition);
   if (S > 0 && (!out || !q || !k || !v || !tables || !ctx)) return fail(PA_EINVAL, "null pointer argument");
   const int64_t nparts = max_ctx == 0 ? 1 : ceil_div(max_ctx, partition);
   if (nparts > 65535 * 64) return fail(PA_EUNSUPPORTED, "too many partitions");
@@ -176,11 +203,18 @@ pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, i
                     "copy_blocks launch");
 }
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                  int32_t partition_size) {
-  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
-  const int32_t p = partition_size == 0 ? kDefaultPartition : partition_size;
-  if (p <= 0) return 0;
+  if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || partition_size < 0 || partition_size % 16 != 0)
+    return -1;
+  return choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
+  if (partition_size < 0 || partition_size % 16 != 0) return 0;
+  const int32_t p = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
   return ws_size(num_seqs, num_q_heads, head_dim, ceil_div(max_context_len, p));
 }
 
@@ -207,14 +241,18 @@ pa_status_t pa_decode_partitions(void* out, pa_dtype_t out_dtype, const void* q,
 }
 
 pa_status_t pa_decode_reduce(void* out, pa_dtype_t out_dtype, const int32_t* context_lens, int32_t num_seqs,
-                             int32_t num_q_heads, int32_t head_dim, int32_t max_context_len, int32_t partition_size,
-                             const void* workspace, size_t workspace_bytes, void* stream) {
+                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
+                             int32_t partition_size, const void* workspace, size_t workspace_bytes, void* stream) {
   if (head_dim != 64 && head_dim != 128) return fail(PA_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   if (!(out_dtype == PA_F32 || out_dtype == PA_F16 || out_dtype == PA_BF16))
     return fail(PA_EUNSUPPORTED, "unknown out_dtype");
-  if (num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0) return fail(PA_EINVAL, "bad sizes");
-  const int32_t p = partition_size == 0 ? kDefaultPartition : partition_size;
-  if (p < 16 || p % 16 != 0) return fail(PA_EINVAL, "partition_size must be a positive multiple of 16");
+  if (num_seqs < 0 || max_context_len < 0) return fail(PA_EINVAL, "bad sizes");
+  if (num_kv_heads <= 0 || num_q_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(PA_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", num_q_heads,
+                num_kv_heads);
+  if (partition_size < 0 || partition_size % 16 != 0)
+    return fail(PA_EINVAL, "partition_size must be 0 or a positive multiple of 16");
+  const int32_t p = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
   const int64_t nparts = max_context_len == 0 ? 1 : ceil_div(max_context_len, p);
   const size_t need = ws_size(num_seqs, num_q_heads, head_dim, nparts);
   if (need == 0 || num_seqs == 0) return PA_OK;
@@ -227,7 +265,7 @@ pa_status_t pa_decode_reduce(void* out, pa_dtype_t out_dtype, const int32_t* con
   a.context_lens = context_lens;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
-  a.num_kv_heads = 1;
+  a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
   a.max_context_len = max_context_len;
   a.max_blocks = int32_t(ceil_div(max_context_len, 16));

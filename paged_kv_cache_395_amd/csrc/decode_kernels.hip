@@ -8,13 +8,13 @@
 // Paging moves data, not results ("Throughput Impact: The Numbers"): the
 // output equals contiguous attention up to floating-point order.
 //
-// Work split: one workgroup (4 waves) per (context partition, kv head,
-// sequence).  Each wave walks every 4th 16-token block of the partition,
-// keeps an online softmax (running max in the exp2 domain, running sum,
-// rescaled accumulator), and the 4 waves merge in LDS.  A sequence that fits
-// one partition writes its output row directly; longer ones leave
-// (accumulator, max, sum) partials that the reduce kernel merges by
-// log-sum-exp in a fixed order, so results are deterministic.
+// Work split: one workgroup (4 waves) per (kv head, sequence, context
+// partition).  Each wave walks every 4th 16-token block of the partition,
+// keeps an online softmax (reference max in the exp2 domain, running sum,
+// accumulator), and the 4 waves merge in LDS.  A sequence that fits one
+// partition writes its output row directly; longer ones leave (accumulator,
+// max, sum) partials that the reduce kernel merges by log-sum-exp in a fixed
+// order, so results are deterministic.
 //
 // fp16 / bf16 run on the matrix cores.  All G = Hq / Hkv query heads of a kv
 // head share each K/V tile, so every tile is read from HBM once:
@@ -73,21 +73,43 @@ __device__ inline bool context_out_of_contract(int ctx, const KParams& P) {
 }
 
 // ------------------------------------------------------------------------
-// Matrix-core partition kernel (fp16 / bf16).  Grid (partitions, Hkv, S).
+// Matrix-core partition kernel (fp16 / bf16).  Grid (Hkv, S, partitions):
+// the hardware deals workgroups to the 8 XCDs round-robin by linear id, so
+// the kv head runs fastest and every XCD gets an even share of the
+// partitions that hold work (with the partition index fastest, the XCDs
+// serving late partitions, which are empty for short contexts, sat idle).
+//
+// Wave w of the workgroup takes blocks w, w + 4, ... of the partition.  Its
+// physical block ids are read once per window of 64 tiles into one VGPR
+// (lane i = tile i) and picked with readlane.  K and V tiles are fetched
+// with buffer loads through a per-tile resource whose range is the tile:
+// an index past the window gets an empty range, which returns zeros
+// without touching memory, so every loop iteration issues the same loads
+// in the same order and the compiler's wait counts stay exact (a load
+// under a branch makes it wait for all outstanding loads).  The loads are
+// non-temporal: each tile is read exactly once.
 // ------------------------------------------------------------------------
+__device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, kBufferRsrcWord3);
+}
+
+__device__ inline u32x4_t load16_nt(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyNT));
+}
+
 template <typename T, int D, bool OUT_F32>
 __global__ void __launch_bounds__(kThreads)
 decode_mfma_kernel(KParams P) {
   constexpr int DC = D / 32;  // 16-byte chunks per lane per tile
   constexpr int NT = D / 16;  // 16-dim output tiles
-  constexpr int64_t kTile = int64_t(kBlockTokens) * D;
+  constexpr int kTileElems = kBlockTokens * D;
 
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
   __shared__ float s_o[kWaves][16][D + 1];
   __shared__ int s_bad;
 
-  const int part = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  const int g = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;     // head column of this lane
@@ -121,99 +143,116 @@ decode_mfma_kernel(KParams P) {
     }
   }
 
-  const int64_t blk_stride = int64_t(P.hkv) * kTile;
-  const uint16_t* kbase = P.k16 + int64_t(g) * kTile + lane * 8;
-  const uint16_t* vbase = P.v16 + int64_t(g) * kTile + lane * 8;
+  const uint16_t* kg = P.k16 + int64_t(g) * kTileElems;
+  const uint16_t* vg = P.v16 + int64_t(g) * kTileElems;
+  const int64_t blk_stride = int64_t(P.hkv) * kTileElems;
+  const int voff = lane * 16;
 
-  float m = -INFINITY;  // running max of head n (exp2 domain), same in every quad
-  float lsum = 0.f;     // this lane's share of the running sum of head n
+  // Online softmax in the exp2 domain.  The reference max m of head n is
+  // moved only when a score exceeds it by more than 2^8: until then
+  // p = 2^(s - m) <= 256, which fp32 sums and the hi + lo split of P hold
+  // exactly as well as p <= 1, and the accumulator rescale (a multiply of
+  // all of o) is skipped on most tiles.
+  float m = -INFINITY;  // reference max of head n, same in every quad
+  float lsum = 0.f;     // this lane's share of the sum of head n
   f32x4_t o[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   bool bad = false;
 
-  u32x4_t kk[DC], vv[DC];
-  auto load_tile = [&](int j, u32x4_t* kd, u32x4_t* vd) {
-    int phys = trow[j];
-    if (phys < 0 || int64_t(phys) >= P.num_blocks) {
-      bad = true;
-      phys = 0;
-    }
-    const uint16_t* kt = kbase + int64_t(phys) * blk_stride;
-    const uint16_t* vt = vbase + int64_t(phys) * blk_stride;
-#pragma unroll
-    for (int i = 0; i < DC; ++i) kd[i] = load16(kt + i * 512);
-#pragma unroll
-    for (int i = 0; i < DC; ++i) vd[i] = load16(vt + i * 512);
-  };
+  const int ntw_all = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;  // tiles of this wave
+  for (int wb = 0; wb < ntw_all; wb += kWave) {
+    const int ntw = min(kWave, ntw_all - wb);
+    const int tbl = lane < ntw ? trow[kWaves * (wb + lane) + w] : 0;
 
-  int jb = w;
-  if (jb < nblk) load_tile(jb, kk, vv);
-  for (; jb < nblk; jb += kWaves) {
-    // issue the next block's loads before computing on this one
-    u32x4_t kn[DC], vn[DC];
-    const int jn = jb + kWaves;
-    if (jn < nblk) load_tile(jn, kn, vn);
-
-    // scores: lane holds S^T[token 4*quad + r][head n]
-    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    auto rsrc = [&](int i, const uint16_t* base) {
+      const int phys = __builtin_amdgcn_readlane(tbl, i < ntw ? i : 0);
+      const bool ok = i < ntw && phys >= 0 && int64_t(phys) < P.num_blocks;
+      bad |= i < ntw && !ok;  // an entry outside the pool: NaN result, nothing read
+      return tile_rsrc(base + int64_t(ok ? phys : 0) * blk_stride, ok ? kTileElems * 2 : 0);
+    };
+    auto load = [&](int i, u32x4_t* kd, u32x4_t* vd) {
+      const auto rk = rsrc(i, kg);
+      const auto rv = rsrc(i, vg);
+      // fixed issue order of the load groups: the wait counts at the loop
+      // head are exact only when every path issues them in one order
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < DC; ++i) sc = Mfma<T>::k32(kk[i], qb[i], sc);
-
-    const int valid = min(kBlockTokens, ntok - jb * kBlockTokens);
-    float sv[4];
+      for (int c = 0; c < DC; ++c) kd[c] = load16_nt(rk, voff + c * 1024);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = (4 * quad + r < valid) ? sc[r] * P.scale_log2 : -INFINITY;
-    float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bm = fmaxf(bm, shfl_xor(bm, 16));
-    bm = fmaxf(bm, shfl_xor(bm, 32));
-    const float mn = fmaxf(m, bm);
-    const float alpha = fast_exp2(m - mn);
-    float pr[4];
+      for (int c = 0; c < DC; ++c) vd[c] = load16_nt(rv, voff + c * 1024);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    auto step = [&](u32x4_t* kt, u32x4_t* vt, int i) {
+      // scores: lane holds S^T[token 4 * quad + r][head n]
+      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - mn);
-    lsum = lsum * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-    m = mn;
+      for (int c = 0; c < DC; ++c) sc = Mfma<T>::k32(kt[c], qb[c], sc);
+      const int jb = kWaves * (wb + i) + w;
+      const int valid = min(kBlockTokens, ntok - jb * kBlockTokens);
+      float sv[4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) o[t] *= alpha;
-
-    // P^T as the B operand, split hi + lo in the input type
-    uint16_t hi[4], lo[4];
+      for (int r = 0; r < 4; ++r) sv[r] = (4 * quad + r < valid) ? sc[r] * P.scale_log2 : -INFINITY;
+      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+      bm = fmaxf(bm, shfl_xor(bm, 16));
+      bm = fmaxf(bm, shfl_xor(bm, 32));
+      const bool grow = bm > m + 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float mn = grow ? bm : m;
+        const float alpha = fast_exp2(m - mn);
+        lsum *= alpha;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      hi[r] = T::from_float(pr[r]);
-      lo[r] = T::from_float(pr[r] - T::to_float(hi[r]));
-    }
-    const uint32_t bh0 = pack2(hi[0], hi[1]), bh1 = pack2(hi[2], hi[3]);
-    const uint32_t bl0 = pack2(lo[0], lo[1]), bl1 = pack2(lo[2], lo[3]);
-
-    if (valid < kBlockTokens) {
-      // slots past the context may hold anything (NaN included): zero them so
-      // 0 * garbage never reaches the accumulator
-      const int t0 = 4 * quad;
-      const uint32_t m01 = (t0 + 0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
-      const uint32_t m23 = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
-#pragma unroll
-      for (int i = 0; i < DC; ++i) {
-        vv[i][0] &= m01;
-        vv[i][1] &= m23;
-        vv[i][2] &= m01;
-        vv[i][3] &= m23;
+        for (int t = 0; t < NT; ++t) o[t] *= alpha;
+        m = mn;
       }
-    }
-    // V^T as the A operand: tile t = dims 16 t .. 16 t + 15 is half (t % 2)
-    // of chunk t / 2 -- tokens 4 * quad + 0..3 of dim 16 t + n.
+      float pr[4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      const uint32_t a0 = vv[t / 2][2 * (t % 2)];
-      const uint32_t a1 = vv[t / 2][2 * (t % 2) + 1];
-      o[t] = Mfma<T>::k16(a0, a1, bh0, bh1, o[t]);
-      o[t] = Mfma<T>::k16(a0, a1, bl0, bl1, o[t]);
-    }
+      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - m);
+      lsum += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+
+      // P^T as the B operand, split hi + lo in the input type
+      uint16_t hi[4], lo[4];
 #pragma unroll
-    for (int i = 0; i < DC; ++i) {
-      kk[i] = kn[i];
-      vv[i] = vn[i];
+      for (int r = 0; r < 4; ++r) {
+        hi[r] = T::from_float(pr[r]);
+        lo[r] = T::from_float(pr[r] - T::to_float(hi[r]));
+      }
+      const uint32_t bh0 = pack2(hi[0], hi[1]), bh1 = pack2(hi[2], hi[3]);
+      const uint32_t bl0 = pack2(lo[0], lo[1]), bl1 = pack2(lo[2], lo[3]);
+      if (valid < kBlockTokens) {
+        // slots past the context may hold anything (NaN included): zero them
+        // so 0 * garbage never reaches the accumulator
+        const int t0 = 4 * quad;
+        const uint32_t m01 = (t0 + 0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
+        const uint32_t m23 = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+          vt[c][0] &= m01;
+          vt[c][1] &= m23;
+          vt[c][2] &= m01;
+          vt[c][3] &= m23;
+        }
+      }
+      // V^T as the A operand: output tile t = dims 16 t .. 16 t + 15 is half
+      // (t % 2) of chunk t / 2 -- tokens 4 * quad + 0..3 of dim 16 t + n.
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t a0 = vt[t / 2][2 * (t % 2)];
+        const uint32_t a1 = vt[t / 2][2 * (t % 2) + 1];
+        o[t] = Mfma<T>::k16(a0, a1, bh0, bh1, o[t]);
+        o[t] = Mfma<T>::k16(a0, a1, bl0, bl1, o[t]);
+      }
+    };
+
+    // two tiles in flight: while one is computed the other is loading
+    u32x4_t ka[DC], va[DC], kb[DC], vb[DC];
+    load(0, ka, va);
+    load(1, kb, vb);
+    for (int i = 0; i < ntw; i += 2) {
+      step(ka, va, i);
+      load(i + 2, ka, va);
+      if (i + 1 < ntw) step(kb, vb, i + 1);
+      load(i + 3, kb, vb);
     }
   }
   lsum += shfl_xor(lsum, 16);
@@ -414,34 +453,52 @@ decode_f32_kernel(KParams P) {
 }
 
 // ------------------------------------------------------------------------
-// Log-sum-exp merge of the partition partials.  Grid (Hq, S), one wave:
+// Log-sum-exp merge of the partition partials.  Grid (Hq, S), D threads:
 //   M = max_j m_j,  w_j = 2^(m_j - M),  out = sum_j w_j acc_j / sum_j w_j l_j
-// summed in partition order.
+// Thread d owns output dim d; the weights of up to kReduceChunk partitions
+// at a time are computed once into LDS and every partition's row is read
+// with one coalesced load.  Sums run in partition order, so the result is
+// deterministic.
 // ------------------------------------------------------------------------
-template <typename T, bool OUT_F32>
-__global__ void __launch_bounds__(kWave)
-decode_reduce_kernel(KParams P, int D) {
+constexpr int kReduceChunk = 256;
+
+template <typename T, int D, bool OUT_F32>
+__global__ void __launch_bounds__(D)
+decode_reduce_kernel(KParams P) {
+  constexpr int kW = D / kWave;
+  __shared__ float s_w[kReduceChunk];
+  __shared__ float s_red[kW];
   const int h = blockIdx.x, s = blockIdx.y;
-  const int lane = threadIdx.x;
+  const int d = threadIdx.x;
   const int ctx = P.ctxs[s];
   if (context_out_of_contract(ctx, P) || ctx <= P.partition) return;  // written by the partition kernel
   const int nparts = (ctx + P.partition - 1) / P.partition;
   const int64_t prow0 = (int64_t(s) * P.hq + h) * P.nparts_max;
 
   float M = -INFINITY;
-  for (int j = lane; j < nparts; j += kWave) M = fmaxf(M, P.ws_m[prow0 + j]);
+  for (int j = d; j < nparts; j += D) M = fmaxf(M, P.ws_m[prow0 + j]);
 #pragma unroll
   for (int k = 1; k < kWave; k <<= 1) M = fmaxf(M, shfl_xor(M, k));
-  float L = 0.f;
-  for (int j = lane; j < nparts; j += kWave) L += fast_exp2(P.ws_m[prow0 + j] - M) * P.ws_l[prow0 + j];
+  if ((d & (kWave - 1)) == 0) s_red[d / kWave] = M;
+  __syncthreads();
+  M = s_red[0];
 #pragma unroll
-  for (int k = 1; k < kWave; k <<= 1) L += shfl_xor(L, k);
-  const float inv = 1.f / L;
-  for (int d = lane; d < D; d += kWave) {
-    float O = 0.f;
-    for (int j = 0; j < nparts; ++j) O += fast_exp2(P.ws_m[prow0 + j] - M) * P.ws_acc[(prow0 + j) * D + d];
-    store_out<T, OUT_F32>(P.out, (int64_t(s) * P.hq + h) * D + d, O * inv);
+  for (int i = 1; i < kW; ++i) M = fmaxf(M, s_red[i]);
+
+  float L = 0.f, O = 0.f;
+  const float* acc = P.ws_acc + prow0 * D + d;
+  for (int j0 = 0; j0 < nparts; j0 += kReduceChunk) {
+    const int nj = min(kReduceChunk, nparts - j0);
+    __syncthreads();  // s_w and s_red of the previous round are consumed
+    for (int j = d; j < nj; j += D) s_w[j] = fast_exp2(P.ws_m[prow0 + j0 + j] - M);
+    __syncthreads();
+    for (int j = 0; j < nj; ++j) {
+      const float wj = s_w[j];
+      L += wj * P.ws_l[prow0 + j0 + j];
+      O += wj * acc[int64_t(j0 + j) * D];
+    }
   }
+  store_out<T, OUT_F32>(P.out, (int64_t(s) * P.hq + h) * D + d, O / L);
 }
 
 KParams make_params(const DecodeArgs& a) {
@@ -471,11 +528,22 @@ KParams make_params(const DecodeArgs& a) {
 
 template <typename T, int D>
 hipError_t launch_mfma(const DecodeArgs& a, const KParams& p) {
-  const dim3 grid(unsigned(a.num_partitions), unsigned(a.num_kv_heads), unsigned(a.num_seqs));
+  const dim3 grid(unsigned(a.num_kv_heads), unsigned(a.num_seqs), unsigned(a.num_partitions));
   if (a.out_f32) {
     hipLaunchKernelGGL((decode_mfma_kernel<T, D, true>), grid, dim3(kThreads), 0, a.stream, p);
   } else {
     hipLaunchKernelGGL((decode_mfma_kernel<T, D, false>), grid, dim3(kThreads), 0, a.stream, p);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t launch_reduce(const DecodeArgs& a, const KParams& p) {
+  const dim3 grid(unsigned(a.num_q_heads), unsigned(a.num_seqs));
+  if (a.out_f32) {
+    hipLaunchKernelGGL((decode_reduce_kernel<T, D, true>), grid, dim3(D), 0, a.stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_reduce_kernel<T, D, false>), grid, dim3(D), 0, a.stream, p);
   }
   return hipGetLastError();
 }
@@ -500,15 +568,9 @@ hipError_t launch_decode_partitions(const DecodeArgs& a) {
 hipError_t launch_decode_reduce(const DecodeArgs& a) {
   if (a.num_partitions <= 1) return hipSuccess;
   const KParams p = make_params(a);
-  const dim3 grid(unsigned(a.num_q_heads), unsigned(a.num_seqs));
-  if (a.out_f32) {
-    hipLaunchKernelGGL((decode_reduce_kernel<F16, true>), grid, dim3(kWave), 0, a.stream, p, int(a.head_dim));
-  } else if (a.dtype == PA_BF16) {
-    hipLaunchKernelGGL((decode_reduce_kernel<Bf16, false>), grid, dim3(kWave), 0, a.stream, p, int(a.head_dim));
-  } else {
-    hipLaunchKernelGGL((decode_reduce_kernel<F16, false>), grid, dim3(kWave), 0, a.stream, p, int(a.head_dim));
-  }
-  return hipGetLastError();
+  // the output conversion is the only type-dependent step
+  if (a.dtype == PA_BF16) return a.head_dim == 64 ? launch_reduce<Bf16, 64>(a, p) : launch_reduce<Bf16, 128>(a, p);
+  return a.head_dim == 64 ? launch_reduce<F16, 64>(a, p) : launch_reduce<F16, 128>(a, p);
 }
 
 }  // namespace pa

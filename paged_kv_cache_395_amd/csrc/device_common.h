@@ -38,6 +38,14 @@ struct F16 {
 // 16-byte global load of 8 consecutive 16-bit elements as raw bits.
 __device__ inline u32x4_t load16(const uint16_t* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 
+// Buffer resources (base, range) for raw buffer loads.  Word 3 of a CDNA3/4
+// resource: 32-bit data format, no swizzle, no index striding.  A load whose
+// offset falls outside the range returns zeros and issues no memory access.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+// Cache-policy operand of buffer loads: the non-temporal hint (streamed data
+// that is read once).
+constexpr int kCachePolicyNT = 2;
+
 // ---------------------------------------------------------------------------
 // Matrix-core products, 16x16 output tiles, fp32 accumulate.
 //

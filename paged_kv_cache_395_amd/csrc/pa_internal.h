@@ -12,9 +12,6 @@ namespace pa {
 // Record a message for pa_last_error() and return `st`.
 pa_status_t fail(pa_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
-// Tokens per context partition when the caller passes 0.
-constexpr int kDefaultPartition = 512;
-
 struct DecodeArgs {
   void* out;
   bool out_f32;

@@ -70,9 +70,14 @@ def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
                                           NB, _code(k_cache), _stream(stream)))
 
 
-def decode_workspace_bytes(num_seqs: int, num_q_heads: int, head_dim: int, max_context_len: int,
+def decode_partition_size(num_seqs: int, num_kv_heads: int, max_context_len: int, partition_size: int = 0) -> int:
+    """Tokens per context partition decode uses for these sizes (0 = the library's choice)."""
+    return int(_lib.load().pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len, partition_size))
+
+
+def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,
                            partition_size: int = 0) -> int:
-    return int(_lib.load().pa_decode_workspace_bytes(num_seqs, num_q_heads, head_dim, max_context_len,
+    return int(_lib.load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,
                                                      partition_size))
 
 
@@ -91,7 +96,7 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
         raise ValueError("context_lens must be int32 [num_seqs]")
     if not (q.dtype == k_cache.dtype == v_cache.dtype):
         raise TypeError("q and the pools must share one dtype")
-    need = decode_workspace_bytes(S, Hq, D, max_context_len, partition_size)
+    need = decode_workspace_bytes(S, Hq, Hkv, D, max_context_len, partition_size)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _p(workspace) if workspace is not None else None
@@ -117,14 +122,15 @@ def decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scal
     _lib.check(_lib.load().pa_decode_partitions(*args, _stream(stream)))
 
 
-def decode_reduce(out, context_lens, max_context_len, partition_size, workspace, stream=None) -> None:
+def decode_reduce(out, context_lens, num_kv_heads, max_context_len, partition_size, workspace, stream=None) -> None:
     """Second of decode's launches: merge the partition partials into ``out``."""
     _dev(out, context_lens)
     S, Hq, D = out.shape
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _lib.check(_lib.load().pa_decode_reduce(_p(out), _code(out), _p(context_lens), S, Hq, D, int(max_context_len),
-                                            int(partition_size), _p(workspace) if workspace is not None else None,
-                                            ws_bytes, _stream(stream)))
+    _lib.check(_lib.load().pa_decode_reduce(_p(out), _code(out), _p(context_lens), S, Hq, int(num_kv_heads), D,
+                                            int(max_context_len), int(partition_size),
+                                            _p(workspace) if workspace is not None else None, ws_bytes,
+                                            _stream(stream)))
 
 
 def prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, stream=None) -> None:

@@ -66,6 +66,8 @@ def decode_call(**kw):
     (dict(max_ctx=600), _lib.PA_EINVAL),  # table of 4 blocks cannot hold 600 tokens
     (dict(max_ctx=600, maxb=40), _lib.PA_EWORKSPACE),  # two partitions need a workspace
     (dict(max_ctx=600, maxb=40, ws=1, ws_bytes=10), _lib.PA_EWORKSPACE),
+    (dict(max_ctx=600, maxb=40, P=256), _lib.PA_EWORKSPACE),
+    (dict(P=-16), _lib.PA_EINVAL),
     (dict(scale=float("inf")), _lib.PA_EINVAL),
 ])
 def test_decode_rejects_bad_arguments_before_launch(kw, status):
@@ -80,12 +82,31 @@ def test_decode_with_no_sequences_is_a_no_op():
 
 def test_workspace_size_formula():
     # single partition: no workspace; otherwise acc + m + l, 256-byte aligned
-    assert L.pa_decode_workspace_bytes(8, 32, 128, 512, 512) == 0
-    S, Hq, D, n = 8, 32, 128, 3
+    assert L.pa_decode_workspace_bytes(8, 32, 8, 128, 512, 512) == 0
+    S, Hq, Hkv, D, n = 8, 32, 8, 128, 3
     rows = S * Hq * n
     align = lambda b: (b + 255) // 256 * 256  # noqa: E731
-    assert L.pa_decode_workspace_bytes(S, Hq, D, 1100, 512) == align(rows * D * 4) + 2 * align(rows * 4)
-    assert L.pa_decode_workspace_bytes(S, Hq, D, 1100, 0) == L.pa_decode_workspace_bytes(S, Hq, D, 1100, 512)
+    assert L.pa_decode_workspace_bytes(S, Hq, Hkv, D, 1100, 512) == align(rows * D * 4) + 2 * align(rows * 4)
+    # the default partition is reported and sizes the workspace
+    p = L.pa_decode_partition_size(S, Hkv, 1100, 0)
+    n0 = -(-1100 // p)
+    want = 0 if n0 == 1 else align(S * Hq * n0 * D * 4) + 2 * align(S * Hq * n0 * 4)
+    assert L.pa_decode_workspace_bytes(S, Hq, Hkv, D, 1100, 0) == want
+    assert L.pa_decode_partition_size(S, Hkv, 1100, 48) == 48
+    assert L.pa_decode_partition_size(S, Hkv, 1100, 24) == -1
+
+
+@pytest.mark.parametrize("S,Hkv,max_ctx,want", [
+    (4, 4, 57, 512),          # tiny batch: nothing to split
+    (16, 8, 32768, 4096),     # few long sequences: split to fill the GPU, into large pieces
+    (64, 32, 2048, 512),      # many pairs, short contexts: small pieces balance the ragged lengths
+    (256, 8, 8192, 2048),     # many pairs, a long tail of lengths
+    (1024, 8, 1100, 512),
+])
+def test_default_partition_choice(S, Hkv, max_ctx, want):
+    p = L.pa_decode_partition_size(S, Hkv, max_ctx, 0)
+    assert p == want
+    assert 512 <= p <= 4096 and p % 16 == 0
 
 
 def test_cache_write_and_copy_reject_bad_arguments():

@@ -1,7 +1,7 @@
 """Paged decode on the GPU against the oracle.
 
 Every workload at full size with the launch configuration the benchmark
-uses (default 512-token partitions), reduced sizes with ragged tails, the
+uses (the library's default partitions), reduced sizes with ragged tails, the
 output-dtype path, partition-size agreement, and the closed-form / paging
 properties: single-token contexts, dominant keys, zero queries, physical
 relabelling, determinism, NaN poison in unread memory, zero-length
@@ -103,10 +103,16 @@ def test_split_and_unsplit_launches_match_single_call():
     d = p.device()
     p.write_step(d)
     a = p.gpu_decode(d)
-    ws = torch.empty(ops.decode_workspace_bytes(12, 32, 128, p.max_ctx, 0), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(ops.decode_workspace_bytes(12, 32, 8, 128, p.max_ctx, 0), dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     ops.decode_partitions(b, d["q"], d["k"], d["v"], d["table"], d["ctx"], p.w.scale, p.max_ctx, 0, ws)
-    ops.decode_reduce(b, d["ctx"], p.max_ctx, 0, ws)
+    ops.decode_reduce(b, d["ctx"], 8, p.max_ctx, 0, ws)
+    assert torch.equal(a, b)
+    # the same with an explicit split into several partitions
+    a = p.gpu_decode(d, partition=256)
+    ws = torch.empty(ops.decode_workspace_bytes(12, 32, 8, 128, p.max_ctx, 256), dtype=torch.uint8, device="cuda")
+    ops.decode_partitions(b, d["q"], d["k"], d["v"], d["table"], d["ctx"], p.w.scale, p.max_ctx, 256, ws)
+    ops.decode_reduce(b, d["ctx"], 8, p.max_ctx, 256, ws)
     assert torch.equal(a, b)
 
 
