@@ -106,6 +106,88 @@ def cpu_baseline(w, budget_s: float = 15.0):
                       f"{dt:.1f} s; seqs/s {len(done) / dt:.2f}; numpy, BLAS 1 thread"}
 
 
+DECODE_KERNEL = "decode_mfma_kernel"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def _csv_rows(directory: str, suffix: str):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, name: str) -> tuple:
+    vals = [float(r["Counter_Value"]) for r in rows if name in r["Kernel_Name"]]
+    return (sum(vals) / len(vals), len(vals)) if vals else (float("nan"), 0)
+
+
+def summarize(args) -> None:
+    """Turn rocprofv3 output (the kernel trace and the FETCH_SIZE / WRITE_SIZE
+    passes of the commands below) into the summaries kept under profiles/."""
+    wl = args.workload
+    with open(args.bench_json) as f:
+        rec = json.load(f)
+    alg = rec["roofline"]["algorithmic_bytes_per_launch"]
+    prof = os.path.join(ROOT, "profiles")
+    base = "python -u bench.py --workload %s" % wl
+    trace_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_{wl} -o trace -- "
+                 f"{base} --steps 20 --warmup 3 --cold-iters 3 --no-cpu-baseline")
+    pmc_cmd = (f"timeout -s KILL 120 rocprofv3 --pmc {{counter}} --output-format csv -d gpurun_out/pmc_{{tag}}_{wl} "
+               f"-o {{tag}} -- {base} --steps 3 --warmup 1 --cold-iters 0 --no-cpu-baseline --copy-probe-mib 1024")
+    lines = [f"# Kernel trace: {wl}", "", f"{rec['config']['workload']}", "",
+             "Command (from the repository root, one MI355X):", "", "```", trace_cmd, "```", "",
+             "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
+    for r in _csv_rows(args.trace_dir, "kernel_stats.csv"):
+        lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    lines += ["", "Same workload, bench.py without the profiler (HIP events on the launch stream):", "",
+              f"- decode kernel: {rec['kernels_ms']['decode_partitions'] * 1e3:.1f} us per launch, "
+              f"{rec['roofline']['achieved']:.0f} GB/s = {rec['roofline']['frac']:.3f} of 8 TB/s",
+              f"- kernels_ms: {rec['kernels_ms']}", f"- whole step: {rec['value']} GB/s, {rec['ms_per_step']} ms", ""]
+    with open(os.path.join(prof, f"decode_{wl}_kernel_trace.md"), "w") as f:
+        f.write("\n".join(lines))
+
+    fetch = _csv_rows(args.fetch_dir, "counter_collection.csv")
+    write = _csv_rows(args.write_dir, "counter_collection.csv")
+    f_dec, n_dec = _per_dispatch(fetch, DECODE_KERNEL)
+    w_dec, _ = _per_dispatch(write, DECODE_KERNEL)
+    f_cp, _ = _per_dispatch(fetch, COPY_KERNEL)
+    w_cp, _ = _per_dispatch(write, COPY_KERNEL)
+    probe_kib = 1024 * 1024
+    fs, ws = probe_kib / f_cp, probe_kib / w_cp  # each counter against a copy of known size
+    hbm_f, hbm_w = f_dec * 1024 * fs, w_dec * 1024 * ws
+    out = {"workload": wl, "kernel": DECODE_KERNEL, "kernel_source_sha": kernel_source_hash(),
+           "fetch_kib_per_dispatch_raw": f_dec, "write_kib_per_dispatch_raw": w_dec, "dispatches": n_dec,
+           "copy_probe_kib": probe_kib, "copy_fetch_kib_raw": f_cp, "copy_write_kib_raw": w_cp,
+           "fetch_scale": fs, "write_scale": ws, "hbm_fetch_bytes_per_launch": hbm_f,
+           "hbm_write_bytes_per_launch": hbm_w, "hbm_bytes_per_launch": hbm_f + hbm_w,
+           "algorithmic_bytes_per_launch": alg,
+           "commands": [pmc_cmd.format(counter="FETCH_SIZE", tag="fetch"),
+                        pmc_cmd.format(counter="WRITE_SIZE", tag="write")]}
+    with open(os.path.join(prof, f"decode_partitions_{wl}_traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    md = [f"# HBM traffic of `{DECODE_KERNEL}`: {wl}", "",
+          "Two counter passes (one counter each), same command otherwise:", "", "```"] + out["commands"] + [
+          "```", "",
+          f"- FETCH_SIZE per dispatch (raw): {f_dec:.1f} KiB over {n_dec} dispatches",
+          f"- WRITE_SIZE per dispatch (raw): {w_dec:.1f} KiB",
+          f"- calibration: a plain 1 GiB device copy (`{COPY_KERNEL}`) reads FETCH_SIZE {f_cp:.1f} KiB and "
+          f"WRITE_SIZE {w_cp:.1f} KiB for {probe_kib} KiB moved each way: scale x{fs:.4f} (fetch), x{ws:.4f} (write)",
+          f"- HBM bytes per launch (scaled): fetch {hbm_f / 1e9:.4f} GB + write {hbm_w / 1e9:.4f} GB = "
+          f"{(hbm_f + hbm_w) / 1e9:.4f} GB",
+          f"- algorithmic bytes per launch (bench formula): {alg / 1e9:.4f} GB -> traffic / algorithmic = "
+          f"{(hbm_f + hbm_w) / alg:.3f}",
+          f"- kernel source sha256[:16]: {out['kernel_source_sha']} (bench.py reports `traffic` only while this "
+          "matches)", ""]
+    with open(os.path.join(prof, f"decode_{wl}_hbm_traffic.md"), "w") as f:
+        f.write("\n".join(md))
+    print("\n".join(md))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -118,7 +200,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (scales HBM byte counters)")
+    ap.add_argument("--summarize", action="store_true",
+                    help="write profiles/ summaries from rocprofv3 output (--trace-dir, --fetch-dir, --write-dir) "
+                         "and a bench.py JSON line of the same workload (--bench-json); no GPU work")
+    ap.add_argument("--trace-dir")
+    ap.add_argument("--fetch-dir")
+    ap.add_argument("--write-dir")
+    ap.add_argument("--bench-json")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -159,7 +251,6 @@ def main():
     n_tok = S * w.append
     nbytes = 8 * n_tok + 4 * S + 4 * S * maxB
     ring = [torch.empty(nbytes, dtype=torch.uint8, pin_memory=True) for _ in range(4)]
-    ring_ev = [None] * len(ring)
     dbuf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     d_slots = dbuf[: 8 * n_tok].view(torch.int64)
     d_ctx = dbuf[8 * n_tok: 8 * n_tok + 4 * S].view(torch.int32)
@@ -177,10 +268,16 @@ def main():
         return (a[: 8 * n_tok].view(np.int64), a[8 * n_tok: 8 * n_tok + 4 * S].view(np.int32),
                 a[8 * n_tok + 4 * S:].view(np.int32).reshape(S, maxB))
 
+    plan = ops.StepPlan(out, q, k_pool, v_pool, d_table, d_ctx, w.scale, ws, key=step_k, value=step_v,
+                        slot_mapping=d_slots, partition_size=args.partition)
+    ring_done = [torch.cuda.Event() for _ in ring]
+    ring_used = [False] * len(ring)
+
     def prepare_step(i, append):
+        """Host part of a step: block manager -> pinned staging -> one async copy."""
         r = i % len(ring)
-        if ring_ev[r] is not None:
-            ring_ev[r].synchronize()
+        if ring_used[r]:
+            ring_done[r].synchronize()  # the copy that last read this staging slot has run
         slots_np, ctx_np, table_np = views(ring[r])
         if append:
             _, cow = bm.append_tokens(seqs, slots_out=slots_np)
@@ -188,59 +285,75 @@ def main():
                 raise RuntimeError("copy-on-write is not expected in this workload")
         bm.block_table(batch, maxB, pad=pad, table_out=table_np, ctx_out=ctx_np)
         dbuf.copy_(ring[r], non_blocking=True)
-        ev = torch.cuda.Event()
-        ev.record(stream)
-        ring_ev[r] = ev
+        ring_done[r].record(stream)
+        ring_used[r] = True
         return ctx_np.copy()
 
     if not grows:
         # the chunk workload: write the chunk once (untimed); every step then decodes in place
         prepare_step(0, True)
-        ops.reshape_and_cache(step_k, step_v, k_pool, v_pool, d_slots)
+        plan.cache_write()
         torch.cuda.synchronize()
 
-    ev_pairs = []
+    # decode is bracketed by two events in every timed step (its duration feeds
+    # the roofline); the small kernels are timed in a separate pass below
+    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
 
-    def step(i, timed):
+    def step(i, timed_idx=None):
         ctx_np = prepare_step(i, grows)
         mx = int(ctx_np.max())
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if timed else None
-        if timed:
-            e[0].record(stream)
         if grows:
-            ops.reshape_and_cache(step_k, step_v, k_pool, v_pool, d_slots)
-        if timed:
-            e[1].record(stream)
-        ops.decode_partitions(out, q, k_pool, v_pool, d_table, d_ctx, w.scale, mx, args.partition, ws)
-        if timed:
-            e[2].record(stream)
-        ops.decode_reduce(out, d_ctx, Hkv, mx, args.partition, ws)
-        if timed:
-            e[3].record(stream)
-            ev_pairs.append(e)
+            plan.cache_write()
+        if timed_idx is not None:
+            ev_dec[timed_idx][0].record(stream)
+        plan.decode_partitions(mx)
+        if timed_idx is not None:
+            ev_dec[timed_idx][1].record(stream)
+        plan.decode_reduce(mx)
         return decode_bytes(ctx_np, w)
 
     for i in range(args.warmup):
-        step(i, False)
+        step(i)
     torch.cuda.synchronize()
     total_bytes = 0.0
+    host_s = 0.0  # time the host spends issuing a step (the GPU runs behind it)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        total_bytes += step(args.warmup + i, True)
+        h0 = time.perf_counter()
+        total_bytes += step(args.warmup + i, i)
+        host_s += time.perf_counter() - h0
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
 
-    k1_ms = np.array([a[0].elapsed_time(a[1]) for a in ev_pairs])
-    k2_ms = np.array([a[1].elapsed_time(a[2]) for a in ev_pairs])
-    k3_ms = np.array([a[2].elapsed_time(a[3]) for a in ev_pairs])
+    # the small kernels and the whole kernel span of a step, outside the timed region
+    side = []
+    ctx_side = prepare_step(args.warmup + args.steps, False)
+    mx_side = int(ctx_side.max())
+    for _ in range(10):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record(stream)
+        if grows:
+            plan.cache_write()
+        e[1].record(stream)
+        plan.decode_partitions(mx_side)
+        e[2].record(stream)
+        plan.decode_reduce(mx_side)
+        e[3].record(stream)
+        side.append(e)
+    torch.cuda.synchronize()
+
+    k2_ms = np.array([a.elapsed_time(b) for a, b in ev_dec])
+    k1_ms = np.array([a[0].elapsed_time(a[1]) for a in side])
+    k3_ms = np.array([a[2].elapsed_time(a[3]) for a in side])
+    span_ms = np.array([a[0].elapsed_time(a[3]) for a in side])  # first kernel start to last kernel end
     bytes_per_launch = total_bytes / args.steps
     achieved = bytes_per_launch / (k2_ms.mean() * 1e-3) / 1e9
 
     # cold-cache decode: each launch after a 1 GiB write evicts L2 and the 256 MiB MALL
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     cold = []
-    ctx_now = prepare_step(10 ** 6, False)
+    ctx_now = prepare_step(args.warmup + args.steps + 1, False)
     mx = int(ctx_now.max())
     for _ in range(args.cold_iters):
         scratch.zero_()
@@ -320,7 +433,9 @@ def main():
                      "algorithmic_bytes_per_launch": round(bytes_per_launch, 1)},
         "kernels_ms": {"reshape_and_cache": round(float(k1_ms.mean()), 5),
                        "decode_partitions": round(float(k2_ms.mean()), 5),
-                       "decode_reduce": round(float(k3_ms.mean()), 5)},
+                       "decode_reduce": round(float(k3_ms.mean()), 5),
+                       "step_kernels_span": round(float(span_ms.mean()), 5)},
+        "host_ms_per_step": round(host_s / args.steps * 1e3, 4),
         "decode_partitions_cold": None if cold_gbs is None else {
             "median_ms": round(float(np.median(cold_ms)), 5), "p10_ms": round(float(np.percentile(cold_ms, 10)), 5),
             "p90_ms": round(float(np.percentile(cold_ms, 90)), 5), "gbs": round(cold_gbs, 2)},

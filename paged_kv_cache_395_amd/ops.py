@@ -150,3 +150,61 @@ def prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, scale, m
                                             _p(block_tables), block_tables.shape[1], _p(context_lens), S, Hq, Hkv, D,
                                             BLOCK_SIZE, NB, float(scale), int(max_context_len), _code(q),
                                             _stream(stream)))
+
+
+class StepPlan:
+    """One decode step (cache write, decode partitions, merge) on fixed buffers.
+
+    A serving loop launches the same kernels on the same buffers every step;
+    only the host bound ``max_context_len`` changes.  The plan checks every
+    tensor once, keeps the marshalled C arguments, and each call then costs
+    one ctypes call per launch.  The tensors must stay alive and keep their
+    storage for the plan's lifetime.
+    """
+
+    def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace,
+                 key=None, value=None, slot_mapping=None, partition_size=0, stream=None):
+        # the workspace is the caller's, sized for the largest max_context_len the plan will see
+        self._args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, 0,
+                                     partition_size, workspace)
+        self._lib = _lib.load()
+        self._stream = _stream(stream)
+        self._ws_bytes = self._args[18]
+        NB, Hkv, D = _pool_dims(k_cache)
+        S, Hq = q.shape[0], q.shape[1]
+        self._sizes = (S, Hq, Hkv, D)
+        self._reduce_head = (_p(out), _code(out), _p(context_lens), S, Hq, Hkv, D)
+        self._partition = int(partition_size)
+        self._write = None
+        if key is not None:
+            _dev(key, value, slot_mapping)
+            if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (Hkv, D):
+                raise ValueError("key / value must be [T, num_kv_heads, head_dim]")
+            if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
+                raise ValueError("slot_mapping must be int64 [T]")
+            if not (key.dtype == value.dtype == k_cache.dtype):
+                raise TypeError("key, value and the pools must share one dtype")
+            self._write = (_p(key), _p(value), _p(k_cache), _p(v_cache), _p(slot_mapping), key.shape[0], Hkv, D,
+                           BLOCK_SIZE, NB, _code(k_cache), self._stream)
+
+    def workspace_bytes(self, max_context_len: int) -> int:
+        S, Hq, Hkv, D = self._sizes
+        return decode_workspace_bytes(S, Hq, Hkv, D, max_context_len, self._partition)
+
+    def cache_write(self) -> None:
+        _lib.check(self._lib.pa_reshape_and_cache(*self._write))
+
+    def decode_partitions(self, max_context_len: int) -> None:
+        a = self._args
+        _lib.check(self._lib.pa_decode_partitions(*a[:15], int(max_context_len), *a[16:], self._stream))
+
+    def decode_reduce(self, max_context_len: int) -> None:
+        a = self._args
+        _lib.check(self._lib.pa_decode_reduce(*self._reduce_head, int(max_context_len), self._partition, a[17],
+                                              self._ws_bytes, self._stream))
+
+    def __call__(self, max_context_len: int) -> None:
+        if self._write is not None:
+            self.cache_write()
+        self.decode_partitions(max_context_len)
+        self.decode_reduce(max_context_len)
