@@ -125,12 +125,60 @@ def _per_dispatch(rows, name: str) -> tuple:
     return (sum(vals) / len(vals), len(vals)) if vals else (float("nan"), 0)
 
 
+def summarize_prefill(args, rec) -> None:
+    """Matrix-core utilisation of the chunked-prefill kernel from one rocprofv3
+    counter pass (SQ block) and one GRBM pass of the same command."""
+    wl = args.workload
+    rows = _csv_rows(args.prefill_pmc_dir, "counter_collection.csv")
+    grbm = _csv_rows(args.prefill_grbm_dir, "counter_collection.csv")
+
+    def avg(rs, counter):
+        v = [float(r["Counter_Value"]) for r in rs if "prefill_mfma_kernel" in r["Kernel_Name"]
+             and r["Counter_Name"] == counter]
+        return sum(v) / len(v) if v else float("nan"), len(v)
+
+    busy, n = avg(rows, "SQ_VALU_MFMA_BUSY_CYCLES")
+    cu, _ = avg(rows, "SQ_BUSY_CU_CYCLES")
+    mfma, _ = avg(rows, "SQ_INSTS_MFMA")
+    valu, _ = avg(rows, "SQ_INSTS_VALU")
+    lds, _ = avg(rows, "SQ_INSTS_LDS")
+    waits, _ = avg(rows, "SQ_WAIT_INST_ANY")
+    wcyc, _ = avg(rows, "SQ_WAVE_CYCLES")
+    gui, _ = avg(grbm, "GRBM_GUI_ACTIVE")
+    pf = rec["prefill"]
+    base = "python -u bench.py --workload %s --steps 2 --warmup 1 --cold-iters 0 --no-cpu-baseline" % wl
+    md = [f"# Matrix-core utilisation of `prefill_mfma_kernel`: {wl}", "",
+          "Two counter passes of the same command (one per counter block):", "", "```",
+          f"timeout -s KILL 180 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
+          f"SQ_INSTS_LDS SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY --output-format csv -d gpurun_out/pmc_prefill -o pf "
+          f"-- {base}",
+          f"timeout -s KILL 180 rocprofv3 --pmc GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/pmc_prefill_grbm "
+          f"-o pfg -- {base}", "```", "",
+          f"Per dispatch (mean of {n}):", "",
+          f"- GRBM_GUI_ACTIVE {gui:.4g} (summed over the 8 XCDs: {gui / 8:.4g} cycles of the GPU clock)",
+          f"- SQ_BUSY_CU_CYCLES {cu:.4g} (summed over CUs); SQ_VALU_MFMA_BUSY_CYCLES {busy:.4g} (summed over SIMDs)",
+          f"- matrix pipe busy = MFMA_BUSY / (4 x BUSY_CU) = {busy / (4 * cu):.3f} of the time each SIMD is active",
+          f"- instructions: MFMA {mfma:.4g}, VALU {valu:.4g} ({valu / mfma:.2f} per MFMA), LDS {lds:.4g}",
+          f"- SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES = {waits / wcyc:.3f} (waves stalled on a dependency)", "",
+          "Same workload, bench.py without the profiler:", "",
+          f"- {pf['ms']} ms for {pf['algorithmic_tflop']} TFLOP (4 D flops per attended (query, head, key)) = "
+          f"{pf['tflops']} TFLOP/s = {pf['frac_of_dense_mfma_peak']:.3f} of the 2.5 PFLOP/s dense bf16 peak",
+          "- the PV product runs twice (P split hi + lo), so the matrix pipe executes 1.5x the algorithmic flops", ""]
+    with open(os.path.join(ROOT, "profiles", f"prefill_{wl}_mfma.md"), "w") as f:
+        f.write("\n".join(md))
+    print("\n".join(md))
+
+
 def summarize(args) -> None:
     """Turn rocprofv3 output (the kernel trace and the FETCH_SIZE / WRITE_SIZE
     passes of the commands below) into the summaries kept under profiles/."""
     wl = args.workload
     with open(args.bench_json) as f:
         rec = json.load(f)
+    if args.prefill_pmc_dir:
+        summarize_prefill(args, rec)
+    if args.trace_dir is None:
+        return
     alg = rec["roofline"]["algorithmic_bytes_per_launch"]
     prof = os.path.join(ROOT, "profiles")
     base = "python -u bench.py --workload %s" % wl
@@ -150,6 +198,8 @@ def summarize(args) -> None:
               f"- kernels_ms: {rec['kernels_ms']}", f"- whole step: {rec['value']} GB/s, {rec['ms_per_step']} ms", ""]
     with open(os.path.join(prof, f"decode_{wl}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines))
+    if args.fetch_dir is None:
+        return
 
     fetch = _csv_rows(args.fetch_dir, "counter_collection.csv")
     write = _csv_rows(args.write_dir, "counter_collection.csv")
@@ -207,6 +257,8 @@ def main():
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
     ap.add_argument("--bench-json")
+    ap.add_argument("--prefill-pmc-dir")
+    ap.add_argument("--prefill-grbm-dir")
     args = ap.parse_args()
     if args.summarize:
         summarize(args)
@@ -366,16 +418,20 @@ def main():
     cold_ms = np.array([a.elapsed_time(b) for a, b in cold])
     cold_gbs = decode_bytes(ctx_now, w) / (np.median(cold_ms) * 1e-3) / 1e9 if len(cold_ms) else None
 
-    # plain streaming read of a 4 GiB buffer, for context
-    big = torch.ones(1 << 31, dtype=torch.bfloat16, device=dev)
-    big.sum()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
+    # HBM read ceiling: one streaming read of a 4 GiB buffer with decode's load style
+    big = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
+    big.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    ops.probe_read_bandwidth(big, sink)
+    probe = []
     for _ in range(5):
-        big.sum()
-    b.record(stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        ops.probe_read_bandwidth(big, sink)
+        b.record(stream)
+        probe.append((a, b))
     torch.cuda.synchronize()
-    read_gbs = 5 * big.numel() * 2 / (a.elapsed_time(b) * 1e-3) / 1e9
+    read_gbs = big.numel() / (np.median([a.elapsed_time(b) for a, b in probe]) * 1e-3) / 1e9
     del big, scratch
 
     extra_fields = {}

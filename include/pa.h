@@ -199,6 +199,17 @@ pa_status_t pa_prefill_chunk(void* out, pa_dtype_t out_dtype, const void* q, int
                              pa_dtype_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Measurement probe: reads `bytes` of device memory once with the load
+ * style decode uses (16-byte non-temporal buffer loads) and discards the
+ * data (a 4-byte write to *sink happens only for one improbable XOR of the
+ * input).  Timing it gives the HBM read ceiling against which decode's
+ * achieved bandwidth is set.  buf must be 16-byte aligned; `workgroups`
+ * sizes the grid (each reads 16 KiB per round).
+ * ---------------------------------------------------------------------- */
+pa_status_t pa_probe_read_bandwidth(const void* buf, int64_t bytes, uint32_t* sink, int32_t workgroups,
+                                    void* stream);
+
+/* ------------------------------------------------------------------------
  * Host block manager.  One pool of num_blocks blocks of 16 tokens; per
  * sequence a list of physical blocks; a free list; reference counts for
  * shared blocks.

@@ -319,4 +319,14 @@ pa_status_t pa_prefill_chunk(void* out, pa_dtype_t out_dtype, const void* q, int
   return hip_status(launch_prefill_chunk(a), "prefill launch");
 }
 
+pa_status_t pa_probe_read_bandwidth(const void* buf, int64_t bytes, uint32_t* sink, int32_t workgroups,
+                                    void* stream) {
+  if (bytes < 0 || workgroups <= 0) return fail(PA_EINVAL, "bytes must be >= 0 and workgroups > 0");
+  if (bytes == 0) return PA_OK;
+  if (!buf || !sink) return fail(PA_EINVAL, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return fail(PA_EINVAL, "buf must be 16-byte aligned");
+  return hip_status(launch_read_probe(buf, bytes, sink, workgroups, static_cast<hipStream_t>(stream)),
+                    "read probe launch");
+}
+
 }  // extern "C"

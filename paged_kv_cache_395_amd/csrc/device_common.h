@@ -94,6 +94,16 @@ __device__ inline float shfl(float v, int src) { return __shfl(v, src, kWave); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Max over the 4 lane groups of 16 (lanes n, n + 16, n + 32, n + 48), on
+// the permute network (no LDS round trip): swapping rows 1 <-> 0 and 3 <-> 2,
+// then the two wave halves, leaves every lane with the max of its column.
+__device__ inline float quad_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Lane group of 16 (0..3) and lane within it.
 __device__ inline int lane_id() { return threadIdx.x & (kWave - 1); }
 

@@ -64,4 +64,6 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t num_pairs,
                               int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
 
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t workgroups, hipStream_t stream);
+
 }  // namespace pa

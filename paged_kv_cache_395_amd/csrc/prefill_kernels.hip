@@ -7,14 +7,23 @@
 // Memory for KV Cache").
 //
 // Work split: rows are (query i, head n of the kv group), row = i * G + n.
-// One workgroup of WAVES waves owns WAVES * RT * 16 consecutive rows of one
-// (kv head, sequence) and walks the key blocks in order.  Each 16-token K/V
-// tile is fetched from HBM once per workgroup into double-buffered LDS and
-// read by every wave.  Products are written transposed as in decode:
-//   S^T[token][row] = K . Q^T   (16x16x32),   O^T[dim][row] += V^T . P^T (16x16x16)
-// with P split hi + lo in the input type.
+// One workgroup of 4 waves owns 128 consecutive rows (2 tiles of 16 per
+// wave) of one (kv head, sequence) and walks the keys in stages of 64 (4
+// blocks).  A stage's K and V tiles go from HBM straight into LDS
+// (16-byte direct-to-LDS loads, no register staging), double-buffered so
+// the next stage loads while this one computes; each K / V fragment is
+// read from LDS once per wave and used for both of its row tiles.
+// Products are written transposed as in decode, all on the 16x16x32
+// matrix instructions (the 16x16x16 forms run at half their rate):
+//   S^T[token][row] = K . Q^T                      (per 16-token block)
+//   O^T[dim][row]  += V^T . P^T                    (per pair of blocks, K = 32)
+// with P split hi + lo in the input type.  The grid is one-dimensional and
+// XCD-aware: all row tiles of one (sequence, kv head) run on one XCD, so
+// their shared K / V stream is fetched from HBM once into that XCD's L2.
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "device_common.h"
 #include "pa_internal.h"
@@ -47,22 +56,55 @@ __device__ inline void store_row4(void* out, int64_t idx, f32x4_t v) {
   }
 }
 
-template <typename T, int D, int WAVES, int RT, bool OUT_F32>
-__global__ void __launch_bounds__(WAVES * 64)
-prefill_mfma_kernel(PParams P) {
-  constexpr int DC = D / 32;
-  constexpr int NT = D / 16;
-  constexpr int kThreads = WAVES * 64;
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kStageBlocks = 4;                        // 16-token blocks per stage
+constexpr int kTabWindow = 2048;                       // block-table entries held in LDS
+constexpr int kXcds = 8;
+constexpr int kPrefillRowTiles = 2;      // 16-row tiles per wave
+constexpr int kPrefillWavesPerSimd = 2;  // register budget: two waves per SIMD
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait for this wave's outstanding memory loads (LDS-bound ones included).
+__device__ inline void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// RT 16-row tiles per wave; WPE waves per SIMD the register budget is cut for
+template <typename T, int D, bool OUT_F32, int RT, int WPE>
+__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
+  constexpr int kPfRT = RT;
+  constexpr int kPfRows = kPfWaves * kPfRT * 16;  // rows per workgroup
+  constexpr int DC = D / 32;                         // 16-byte chunks per lane per tile
+  constexpr int NT = D / 16;                         // 16-dim output tiles
   constexpr int kTileElems = kBlockTokens * D;
-  constexpr int kTileChunks = kTileElems / 8;  // 16-byte chunks per tile
-  constexpr int kRowsPerWave = RT * 16;
-  constexpr int kRowsPerWG = WAVES * kRowsPerWave;
-  constexpr int kStage = (kTileChunks + kThreads - 1) / kThreads;
+  constexpr int kTileBytes = kTileElems * 2;
+  constexpr int kRunsPerTile = kTileBytes / 1024;    // 1 KiB wave loads per tile
+  constexpr int kRunsPerStage = 2 * kStageBlocks * kRunsPerTile;
+  static_assert(kRunsPerStage % kPfWaves == 0, "stage loads split evenly over the waves");
+  constexpr int kStageU4 = 2 * kStageBlocks * kTileElems / 8;  // u32x4 per stage buffer
 
-  __shared__ u32x4_t s_k[2][kTileChunks];
-  __shared__ u32x4_t s_v[2][kTileChunks];
+  __shared__ u32x4_t s_buf0[kStageU4];
+  __shared__ u32x4_t s_buf1[kStageU4];
+  __shared__ int32_t s_tab[kTabWindow];
+  __shared__ int s_bad;
 
-  const int tile = blockIdx.x, g = blockIdx.y, s = blockIdx.z;
+  // XCD-aware work order: workgroup id % 8 picks the XCD; groups of 8
+  // (sequence, kv head) pairs are dealt one per XCD, each with all its tiles
+  const int id = blockIdx.x;
+  const int full = (num_pairs / kXcds) * kXcds;
+  int pair, tile;
+  if (id < full * tiles_per_pair) {
+    const int k = id / kXcds;
+    pair = (k / tiles_per_pair) * kXcds + id % kXcds;
+    tile = k % tiles_per_pair;
+  } else {
+    const int r = id - full * tiles_per_pair;
+    pair = full + r / tiles_per_pair;
+    tile = r % tiles_per_pair;
+  }
+  const int s = pair / P.hkv, g = pair - (pair / P.hkv) * P.hkv;
+
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, quad = lane >> 4;
@@ -70,13 +112,13 @@ prefill_mfma_kernel(PParams P) {
   const int C = P.chunk;
   const int R = C * G;
   const int ctx = P.ctxs[s];
-  const int row_wg0 = tile * kRowsPerWG;
+  const int row_wg0 = tile * kPfRows;
   if (row_wg0 >= R) return;
 
   if (ctx < C || ctx > P.max_ctx || ctx > P.max_blocks * kBlockTokens) {
     // contract violation: NaN rows for this workgroup's share
     const float nan = __builtin_nanf("");
-    for (int idx = threadIdx.x; idx < kRowsPerWG * D; idx += kThreads) {
+    for (int idx = threadIdx.x; idx < kPfRows * D; idx += kPfThreads) {
       const int row = row_wg0 + idx / D, d = idx % D;
       if (row >= R) break;
       const int i = row / G, hh = row - i * G;
@@ -87,166 +129,279 @@ prefill_mfma_kernel(PParams P) {
     return;
   }
 
-  // rows of this lane, one per row tile
-  int last[RT];
-  bool live[RT];
-  u32x4_t qb[RT][DC];
+  // rows of this lane (one per row tile), their last attended key, Q^T operands
+  int last[kPfRT];
+  bool live[kPfRT];
+  u32x4_t qb[kPfRT][DC];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int row = row_wg0 + w * kRowsPerWave + rt * 16 + n;
+  for (int rt = 0; rt < kPfRT; ++rt) {
+    const int row = row_wg0 + (w * kPfRT + rt) * 16 + n;
     live[rt] = row < R;
     const int i = live[rt] ? row / G : 0;
     const int hh = live[rt] ? row - i * G : 0;
-    last[rt] = ctx - C + i;
+    last[rt] = live[rt] ? ctx - C + i : -1;
 #pragma unroll
     for (int c = 0; c < DC; ++c) {
       qb[rt][c] = live[rt] ? load16(P.q + ((int64_t(s) * C + i) * P.hq + int64_t(g) * G + hh) * D + 8 * (4 * c + quad))
                            : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
-  const int row_wg_last = min(R, row_wg0 + kRowsPerWG) - 1;
-  const int nkb = (ctx - C + row_wg_last / G) / kBlockTokens + 1;  // key blocks any row of the WG needs
+  const int row_wg_last = min(R, row_wg0 + kPfRows) - 1;
+  const int first_masked = ctx - C + row_wg0 / G;          // smallest last-key of the workgroup's rows
+  const int nkb = (ctx - C + row_wg_last / G) / kBlockTokens + 1;  // key blocks any row needs
+  const int nst = (nkb + kStageBlocks - 1) / kStageBlocks;
   const int32_t* trow = P.tables + int64_t(s) * P.max_blocks;
   const int64_t blk_stride = int64_t(P.hkv) * kTileElems;
-  const uint16_t* kg = P.k + int64_t(g) * kTileElems;
-  const uint16_t* vg = P.v + int64_t(g) * kTileElems;
+  const char* kg = reinterpret_cast<const char*>(P.k + int64_t(g) * kTileElems);
+  const char* vg = reinterpret_cast<const char*>(P.v + int64_t(g) * kTileElems);
 
-  float m[RT], lsum[RT];
-  f32x4_t o[RT][NT];
+  float m[kPfRT], lsum[kPfRT];
+  f32x4_t o[kPfRT][NT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int rt = 0; rt < kPfRT; ++rt) {
     m[rt] = -INFINITY;
     lsum[rt] = 0.f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) o[rt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-  bool bad = false;
+  int bad = 0;
 
-  u32x4_t stk[kStage], stv[kStage];
-  auto fetch = [&](int kb) {
-    int phys = trow[kb];
-    if (phys < 0 || int64_t(phys) >= P.num_blocks) {
-      bad = true;
-      phys = 0;
-    }
-    const uint16_t* kt = kg + int64_t(phys) * blk_stride;
-    const uint16_t* vt = vg + int64_t(phys) * blk_stride;
-#pragma unroll
-    for (int e = 0; e < kStage; ++e) {
-      const int c = threadIdx.x + e * kThreads;
-      if (c < kTileChunks) {
-        stk[e] = load16(kt + c * 8);
-        stv[e] = load16(vt + c * 8);
-      }
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int e = 0; e < kStage; ++e) {
-      const int c = threadIdx.x + e * kThreads;
-      if (c < kTileChunks) {
-        s_k[buf][c] = stk[e];
-        s_v[buf][c] = stv[e];
-      }
-    }
+  int tab_base = 0;
+  auto fill_table = [&](int base) {  // all threads; caller synchronises
+    for (int j = threadIdx.x; j < kTabWindow && base + j < nkb; j += kPfThreads) s_tab[j] = trow[base + j];
   };
 
-  fetch(0);
-  stage(0);
-  __syncthreads();
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nkb) fetch(kb + 1);
+  // issue the direct-to-LDS loads of stage st into buf (this wave's share):
+  // one buffer resource per tile (base in scalar registers, range = the
+  // tile), so each load needs only the lane's 16-byte offset in a VGPR; a
+  // block past the key window or outside the pool gets an empty range and
+  // its LDS image is zero-filled without touching memory
+  const int lane_off = lane * 16;
+  auto issue_stage = [&](int st, u32x4_t* buf) {
+#pragma unroll
+    for (int j = 0; j < kRunsPerStage / kPfWaves; ++j) {
+      const int run = j * kPfWaves + w;
+      const int t8 = run / kRunsPerTile;  // 0..3 K tiles, 4..7 V tiles
+      const int part = run % kRunsPerTile;
+      const int blk = st * kStageBlocks + (t8 & 3);
+      int phys = blk < nkb ? s_tab[blk - tab_base] : 0;
+      phys = __builtin_amdgcn_readfirstlane(phys);
+      const bool in_pool = phys >= 0 && int64_t(phys) < P.num_blocks;
+      bad |= blk < nkb && !in_pool;
+      const bool ok = blk < nkb && in_pool;
+      const char* base = (t8 < kStageBlocks ? kg : vg) + int64_t(ok ? phys : 0) * blk_stride * 2;
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, ok ? kTileBytes : 0, kBufferRsrcWord3);
+      lds_void* dst = (lds_void*)(buf + t8 * (kTileElems / 8) + part * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, lane_off, part * 1024, 0, 0);
+    }
+  };
 
-    u32x4_t kc[DC], vc[DC];
+  // Scores are kept raw (q . k) and the scale is folded into the exponent:
+  // p = 2^(c s - m) with c = scale * log2(e) > 0 (a negative scale flips the
+  // sign bits of q, which is exact; a zero scale becomes a tiny positive one
+  // so masked keys stay at -inf), so the row max is taken over raw scores.
+  float c = P.scale_log2;
+  if (c < 0.f) {
+    c = -c;
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-      kc[c] = s_k[buf][c * 64 + lane];
-      vc[c] = s_v[buf][c * 64 + lane];
+    for (int rt = 0; rt < kPfRT; ++rt)
+#pragma unroll
+      for (int cc = 0; cc < DC; ++cc) qb[rt][cc] ^= u32x4_t{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+  }
+  c = fmaxf(c, 1e-30f);
+
+  typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+  // MASKED: the stage holds keys past some row's causal limit, past the
+  // context or past the key window; every other stage skips all mask work
+  auto compute_stage = [&](auto masked_tag, int st, const u32x4_t* buf) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    const int k0 = st * kStageBlocks * kBlockTokens;
+    const int nvalid = min(kStageBlocks, nkb - st * kStageBlocks);  // blocks of this stage in the key window
+    const u32x2_t* buf2 = reinterpret_cast<const u32x2_t*>(buf);
+    // ---- raw scores of the stage's 4 blocks for both row tiles
+    f32x4_t sc[kPfRT][kStageBlocks];
+#pragma unroll
+    for (int b = 0; b < kStageBlocks; ++b) {
+      u32x4_t kf[DC];
+#pragma unroll
+      for (int cc = 0; cc < DC; ++cc) kf[cc] = buf[b * (kTileElems / 8) + cc * 64 + lane];
+#pragma unroll
+      for (int rt = 0; rt < kPfRT; ++rt) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < DC; ++cc) acc = Mfma<T>::k32(kf[cc], qb[rt][cc], acc);
+        if constexpr (MASKED) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + b * kBlockTokens + 4 * quad + r;
+            acc[r] = (key <= last[rt] && b < nvalid) ? acc[r] : -INFINITY;
+          }
+        }
+        sc[rt][b] = acc;
+      }
     }
-    const int tok_base = kb * kBlockTokens + 4 * quad;
-    if (kb * kBlockTokens + kBlockTokens > ctx) {
-      const int valid = ctx - kb * kBlockTokens;
-      const int t0 = 4 * quad;
-      const uint32_t m01 = (t0 + 0 < valid ? 0x0000FFFFu : 0u) | (t0 + 1 < valid ? 0xFFFF0000u : 0u);
-      const uint32_t m23 = (t0 + 2 < valid ? 0x0000FFFFu : 0u) | (t0 + 3 < valid ? 0xFFFF0000u : 0u);
+    // ---- one reference-max check per stage: the max moves only past a 2^8
+    // margin (rare after the first stage), so the accumulator rescale is
+    // mostly skipped and the rest of the stage is straight-line code
+    float bm[kPfRT];
+    bool grow_any = false;
 #pragma unroll
-      for (int c = 0; c < DC; ++c) {
-        vc[c][0] &= m01;
-        vc[c][1] &= m23;
-        vc[c][2] &= m01;
-        vc[c][3] &= m23;
+    for (int rt = 0; rt < kPfRT; ++rt) {
+      float v = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < kStageBlocks; ++b)
+        v = fmaxf(v, fmaxf(fmaxf(sc[rt][b][0], sc[rt][b][1]), fmaxf(sc[rt][b][2], sc[rt][b][3])));
+      bm[rt] = quad_max(v) * c;
+      grow_any |= bm[rt] > m[rt] + 8.f;
+    }
+    if (__builtin_amdgcn_ballot_w64(grow_any)) {
+#pragma unroll
+      for (int rt = 0; rt < kPfRT; ++rt) {
+        const float mn = bm[rt] > m[rt] + 8.f ? bm[rt] : m[rt];
+        const float alpha = fast_exp2(m[rt] - mn);
+        lsum[rt] *= alpha;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) o[rt][t] *= alpha;
+        m[rt] = mn;
       }
     }
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int pr = 0; pr < kStageBlocks / 2; ++pr) {
+      // ---- probabilities; P goes straight into the B operands of the PV
+      // products: 8 values per lane = tokens 4 quad + 0..3 of the first
+      // block, then of the second (the k order the V operands below use)
+      u32x4_t ph[kPfRT], pl[kPfRT];
 #pragma unroll
-      for (int c = 0; c < DC; ++c) sc = Mfma<T>::k32(kc[c], qb[rt][c], sc);
-      float sv[4];
+      for (int rt = 0; rt < kPfRT; ++rt) {
+        const float neg_m = -m[rt];
+        uint16_t hi[8], lo[8];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = (tok_base + r <= last[rt]) ? sc[r] * P.scale_log2 : -INFINITY;
-      float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-      bm = fmaxf(bm, shfl_xor(bm, 16));
-      bm = fmaxf(bm, shfl_xor(bm, 32));
-      const float mn = fmaxf(m[rt], bm);
-      const float alpha = fast_exp2(m[rt] - mn);
-      float pr[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - mn);
-      lsum[rt] = lsum[rt] * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-      m[rt] = mn;
-      uint16_t hi[4], lo[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        hi[r] = T::from_float(pr[r]);
-        lo[r] = T::from_float(pr[r] - T::to_float(hi[r]));
+        for (int e = 0; e < 8; ++e) {
+          const float pv = fast_exp2(fmaf(sc[rt][2 * pr + e / 4][e % 4], c, neg_m));
+          lsum[rt] += pv;
+          hi[e] = T::from_float(pv);
+          lo[e] = T::from_float(pv - T::to_float(hi[e]));
+        }
+        ph[rt] = u32x4_t{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])};
+        pl[rt] = u32x4_t{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])};
       }
-      const uint32_t bh0 = pack2(hi[0], hi[1]), bh1 = pack2(hi[2], hi[3]);
-      const uint32_t bl0 = pack2(lo[0], lo[1]), bl1 = pack2(lo[2], lo[3]);
+      // ---- O^T += V^T P^T over the pair (K = 32).  V chunk cc of a tile
+      // holds, for lane (quad, n), tokens 4 quad + 0..3 of dim 32 cc + n
+      // (first 8 bytes) and of dim 32 cc + 16 + n (last 8 bytes); the A
+      // operand of output tile t takes the matching 8 bytes of both blocks.
+      const int b0 = 2 * pr, b1 = 2 * pr + 1;
+      uint32_t m0a = ~0u, m0b = ~0u, m1a = ~0u, m1b = ~0u;
+      if constexpr (MASKED) {
+        // blocks outside the window and slots past the context may hold
+        // anything (NaN included): zero them so 0 * garbage never reaches o
+        const int t0 = k0 + 4 * quad;
+        const int e0 = b0 < nvalid ? ctx - (t0 + b0 * kBlockTokens) : 0;  // valid tokens of the quad
+        const int e1 = b1 < nvalid ? ctx - (t0 + b1 * kBlockTokens) : 0;
+        m0a = (e0 > 0 ? 0x0000FFFFu : 0u) | (e0 > 1 ? 0xFFFF0000u : 0u);
+        m0b = (e0 > 2 ? 0x0000FFFFu : 0u) | (e0 > 3 ? 0xFFFF0000u : 0u);
+        m1a = (e1 > 0 ? 0x0000FFFFu : 0u) | (e1 > 1 ? 0xFFFF0000u : 0u);
+        m1b = (e1 > 2 ? 0x0000FFFFu : 0u) | (e1 > 3 ? 0xFFFF0000u : 0u);
+      }
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const uint32_t a0 = vc[t / 2][2 * (t % 2)];
-        const uint32_t a1 = vc[t / 2][2 * (t % 2) + 1];
-        f32x4_t acc = o[rt][t] * alpha;
-        acc = Mfma<T>::k16(a0, a1, bh0, bh1, acc);
-        o[rt][t] = Mfma<T>::k16(a0, a1, bl0, bl1, acc);
+        // 8-byte half (t % 2) of chunk t / 2, in both blocks
+        const int idx = ((t / 2) * 64 + lane) * 2 + (t % 2);
+        const u32x2_t h0 = buf2[(kStageBlocks + b0) * (kTileElems / 4) + idx];
+        const u32x2_t h1 = buf2[(kStageBlocks + b1) * (kTileElems / 4) + idx];
+        u32x4_t av = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
+        if constexpr (MASKED) av = av & u32x4_t{m0a, m0b, m1a, m1b};
+#pragma unroll
+        for (int rt = 0; rt < kPfRT; ++rt) {
+          o[rt][t] = Mfma<T>::k32(av, ph[rt], o[rt][t]);
+          o[rt][t] = Mfma<T>::k32(av, pl[rt], o[rt][t]);
+        }
       }
     }
-    if (kb + 1 < nkb) stage(buf ^ 1);
+  };
+  // Stages wholly below every row's causal limit and inside the key window
+  // (all but the last few) need no masks: they run double-buffered, the next
+  // stage loading while this one computes.  The masked tail runs one stage at
+  // a time.
+  const int nst_plain = min(nst, (first_masked + 1) / (kStageBlocks * kBlockTokens));
+  auto refill_table_for = [&](int st) {
+    // keep the table window over the blocks of stage st
+    if ((st + 1) * kStageBlocks - tab_base > kTabWindow) {
+      __syncthreads();
+      tab_base = st * kStageBlocks;
+      fill_table(tab_base);
+      __syncthreads();
+    }
+  };
+  if (threadIdx.x == 0) s_bad = 0;
+  fill_table(0);
+  __syncthreads();
+  if (nst_plain > 0) {
+    issue_stage(0, s_buf0);
+    wait_loads();
+    __syncthreads();
+  }
+  // two stages per iteration so each buffer has a fixed name (the compiler
+  // then knows the loads into one never alias reads of the other)
+  for (int st = 0; st < nst_plain; st += 2) {
+    if (st + 1 < nst_plain) {
+      refill_table_for(st + 1);
+      issue_stage(st + 1, s_buf1);
+    }
+    compute_stage(std::false_type{}, st, s_buf0);
+    wait_loads();
+    __syncthreads();
+    if (st + 1 >= nst_plain) break;
+    if (st + 2 < nst_plain) {
+      refill_table_for(st + 2);
+      issue_stage(st + 2, s_buf0);
+    }
+    compute_stage(std::false_type{}, st + 1, s_buf1);
+    wait_loads();
+    __syncthreads();
+  }
+  for (int st = nst_plain; st < nst; ++st) {
+    refill_table_for(st);
+    issue_stage(st, s_buf0);
+    wait_loads();
+    __syncthreads();
+    compute_stage(std::true_type{}, st, s_buf0);
     __syncthreads();
   }
 
+  // an out-of-pool table entry seen by any wave poisons every row
+  if (bad) s_bad = 1;
+  __syncthreads();
+  const bool any_bad = s_bad != 0;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
+  for (int rt = 0; rt < kPfRT; ++rt) {
     float l = lsum[rt];
     l += shfl_xor(l, 16);
     l += shfl_xor(l, 32);
     if (!live[rt]) continue;
-    const int row = row_wg0 + w * kRowsPerWave + rt * 16 + n;
+    const int row = row_wg0 + (w * kPfRT + rt) * 16 + n;
     const int i = row / G, hh = row - i * G;
     const int64_t obase = ((int64_t(s) * C + i) * P.hq + int64_t(g) * G + hh) * D;
-    const float inv = bad ? __builtin_nanf("") : 1.f / l;
+    const float inv = any_bad ? __builtin_nanf("") : 1.f / l;
 #pragma unroll
     for (int t = 0; t < NT; ++t) store_row4<T, OUT_F32>(P.out, obase + 16 * t + 4 * quad, o[rt][t] * inv);
   }
 }
 
-constexpr int kPrefillWaves = 4;
-constexpr int kPrefillRT = 2;
-
 template <typename T, int D>
 hipError_t launch_prefill_t(const PrefillArgs& a, const PParams& p) {
-  constexpr int rows_per_wg = kPrefillWaves * kPrefillRT * 16;
+  constexpr int RT = kPrefillRowTiles, WPE = kPrefillWavesPerSimd;
+  constexpr int rows = kPfWaves * RT * 16;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t R = int64_t(a.chunk) * G;
-  const dim3 grid(unsigned((R + rows_per_wg - 1) / rows_per_wg), unsigned(a.num_kv_heads), unsigned(a.num_seqs));
+  const int tiles = int((R + rows - 1) / rows);
+  const int pairs = a.num_seqs * a.num_kv_heads;
+  const dim3 grid(unsigned(int64_t(tiles) * pairs));
   if (a.out_f32) {
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, D, kPrefillWaves, kPrefillRT, true>), grid, dim3(kPrefillWaves * 64), 0,
-                       a.stream, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, D, true, RT, WPE>), grid, dim3(kPfThreads), 0, a.stream, p, tiles, pairs);
   } else {
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, D, kPrefillWaves, kPrefillRT, false>), grid, dim3(kPrefillWaves * 64), 0,
-                       a.stream, p);
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, D, false, RT, WPE>), grid, dim3(kPfThreads), 0, a.stream, p, tiles,
+                       pairs);
   }
   return hipGetLastError();
 }

@@ -152,6 +152,13 @@ def prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, scale, m
                                             _stream(stream)))
 
 
+def probe_read_bandwidth(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 4096, stream=None) -> None:
+    """Read all of ``buf`` once (HBM read-ceiling probe); ``sink`` is a small int32/uint8 device tensor."""
+    _dev(buf, sink)
+    _lib.check(_lib.load().pa_probe_read_bandwidth(_p(buf), buf.numel() * buf.element_size(), _p(sink),
+                                                   int(workgroups), _stream(stream)))
+
+
 class StepPlan:
     """One decode step (cache write, decode partitions, merge) on fixed buffers.
 

@@ -24,15 +24,36 @@ def run_prefill(p, out_f32=True):
 
 
 @pytest.mark.parametrize("kw", [dict(num_seqs=3, ctx=700, chunk=100), dict(num_seqs=2, ctx=300, chunk=37, Hq=16, Hkv=4),
-                                dict(num_seqs=2, ctx=64, chunk=64), dict(num_seqs=1, ctx=515, chunk=3, Hq=8, Hkv=8)],
-                         ids=["c100", "c37_g4", "whole", "g1"])
+                                dict(num_seqs=2, ctx=64, chunk=64), dict(num_seqs=1, ctx=515, chunk=3, Hq=8, Hkv=8),
+                                dict(num_seqs=2, ctx=333, chunk=70, dtype="f16"),
+                                dict(num_seqs=2, ctx=290, chunk=45, Hq=16, Hkv=2, head_dim=64),
+                                dict(num_seqs=1, ctx=40000, chunk=20, Hq=8, Hkv=1)],
+                         ids=["c100", "c37_g4", "whole", "g1", "f16", "d64", "table_window"])
 def test_prefill_reduced_matches_oracle(kw):
     p = Prepared(make_workload("longctx_bf16", **kw))
     say(f"[prefill] {kw}")
     _, out = run_prefill(p)
     k, v = p.oracle_pools()
-    ref = OA.prefill_chunk(p.w.q, k, v, p.table, p.ctx, p.w.scale, "bf16")
-    assert_close(out_f64(out), ref, "bf16", str(kw))
+    dt = p.w.dtype
+    ref = OA.prefill_chunk(p.w.q, k, v, p.table, p.ctx, p.w.scale, dt)
+    assert_close(out_f64(out), ref, dt, str(kw))
+
+
+def test_prefill_out_of_pool_entry_gives_nan_rows_only_for_its_sequence():
+    p = Prepared(make_workload("longctx_bf16", num_seqs=3, ctx=260, chunk=30))
+    w = p.w
+    d = p.device()
+    p.write_step(d)
+    table = d["table"].clone()
+    table[1, 3] = w.num_blocks + 5  # outside the pool: guarded, reported as NaN
+    q = to_dev(w.q, w.dtype)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ops.prefill_chunk(out, q, d["k"], d["v"], table, d["ctx"], w.scale, p.max_ctx)
+    got = out_f64(out)
+    assert np.all(np.isnan(got[1]))
+    k, v = p.oracle_pools()
+    ref = OA.prefill_chunk(w.q, k, v, p.table, p.ctx, w.scale, "bf16")
+    assert_close(got[[0, 2]], ref[[0, 2]], "bf16", "other sequences")
 
 
 def test_prefill_full_long_context_on_sampled_rows():

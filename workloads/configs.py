@@ -262,17 +262,18 @@ def _shared_prefix_bf16(rng, num_users=512, num_prompts=128, n_samples=4,
                    {"final_ctx": final_ctx, "blocks_needed": need})
 
 
-def _longctx_bf16(rng, num_seqs=16, ctx=32768, chunk=512, Hq=64, Hkv=8, NB=None):
+def _longctx_bf16(rng, num_seqs=16, ctx=32768, chunk=512, Hq=64, Hkv=8, NB=None, dtype="bf16", head_dim=128):
     if ctx < chunk:
         raise ValueError("the chunk lies inside the context")
     need = num_seqs * _blocks(ctx)
     if NB is None:
         NB = int(math.ceil(1.25 * need))
     program = [("add", s, ctx - chunk) for s in range(num_seqs)]
-    return _finish(rng, "longctx_bf16", "bf16", num_seqs, Hq, Hkv, 128, NB, 1.0 / math.sqrt(128), 512,
+    D = head_dim
+    return _finish(rng, "longctx_bf16", dtype, num_seqs, Hq, Hkv, D, NB, 1.0 / math.sqrt(D), 512,
                    chunk, program, np.arange(num_seqs),
                    f"{num_seqs} sequences at context {ctx} (the last {chunk} tokens appended as one chunk), "
-                   f"bf16, {Hq}/{Hkv} heads, head_dim 128, 512-token partitions",
+                   f"{dtype}, {Hq}/{Hkv} heads, head_dim {D}, 512-token partitions",
                    {"final_ctx": np.full(num_seqs, ctx, dtype=np.int64), "blocks_needed": need})
 
 
