@@ -38,7 +38,8 @@ def decode_bytes(ctx: np.ndarray, w) -> float:
     """Algorithmic bytes of one decode: K+V rows of every context token, q, out, table entries read."""
     e = ESIZE[w.dtype]
     kv = float(np.sum(ctx, dtype=np.int64)) * w.num_kv_heads * w.head_dim * 2 * e
-    qo = 2.0 * len(ctx) * w.num_q_heads * w.head_dim * e
+    nq = w.append if w.lengths.get("mode") == "multi" else 1  # queries per sequence
+    qo = 2.0 * len(ctx) * nq * w.num_q_heads * w.head_dim * e
     tab = float(np.sum((ctx + 15) // 16, dtype=np.int64)) * 4
     return kv + qo + tab
 
@@ -92,8 +93,12 @@ def cpu_baseline(w, budget_s: float = 15.0):
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         OA.reshape_and_cache(k, v, w.step_rows("k"), w.step_rows("v"), np.array(slots))
+        multi = w.lengths.get("mode") == "multi"
         for s in range(w.num_seqs):
-            OA.decode(w.decode_q, k, v, table, ctx, w.scale, w.dtype, seqs=[s])
+            if multi:  # the verification workload: each sequence's last w.append positions, causally
+                OA.prefill_chunk(w.q, k, v, table, ctx, w.scale, w.dtype, seqs=[s])
+            else:
+                OA.decode(w.decode_q, k, v, table, ctx, w.scale, w.dtype, seqs=[s])
             done.append(s)
             if time.perf_counter() - t0 > budget_s:
                 break
@@ -244,7 +249,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mha7b_f16",
-                    choices=["tiny_f32", "mha7b_f16", "gqa8b_bf16", "shared_prefix_bf16", "longctx_bf16"])
+                    choices=["tiny_f32", "mha7b_f16", "gqa8b_bf16", "shared_prefix_bf16", "longctx_bf16",
+                             "specdec_bf16"])
     ap.add_argument("--partition", type=int, default=0, help="tokens per context partition (0 = the library's choice)")
     ap.add_argument("--cold-iters", type=int, default=20, help="decode launches timed after a 1 GiB cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -287,8 +293,11 @@ def main():
         return torch.from_numpy(a).to(dev)
 
     S, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
-    grows = w.append == 1  # decode workloads append one token per step; the chunk workload decodes in place
-    extra = (args.warmup + args.steps + 1) if grows else 0
+    multi = w.lengths.get("mode") == "multi"  # each step appends and verifies w.append drafted tokens per sequence
+    # decode workloads append one token per step (the verification workload w.append); the chunk
+    # workload writes its chunk once and then decodes in place
+    grows = w.append == 1 or multi
+    extra = (args.warmup + args.steps + 2) * w.append if grows else 0
     maxB = w.max_blocks_per_seq(extra)
     pad = w.num_blocks + 1  # never read
     bm = BlockManager(w.num_blocks, free_order=w.free_order)
@@ -296,8 +305,8 @@ def main():
 
     k_pool, v_pool = to_dev(w.k_pool), to_dev(w.v_pool)
     step_k, step_v = to_dev(w.step_rows("k")), to_dev(w.step_rows("v"))
-    q = to_dev(w.decode_q)
-    out = torch.empty((S, Hq, D), dtype=tdt, device=dev)
+    q = to_dev(w.q) if multi else to_dev(w.decode_q)
+    out = torch.empty(tuple(q.shape), dtype=tdt, device=dev)
 
     # per-step host -> device staging: slots (int64 [n]) | ctx (int32 [S]) | table (int32 [S, maxB])
     n_tok = S * w.append
@@ -309,7 +318,8 @@ def main():
     d_table = dbuf[8 * n_tok + 4 * S:].view(torch.int32).view(S, maxB)
     final_ctx = int(w.lengths["final_ctx"].max()) + extra
     first_ctx = int(w.lengths["final_ctx"].max())
-    ws_need = max(ops.decode_workspace_bytes(S, Hq, Hkv, D, c, args.partition) for c in range(first_ctx, final_ctx + 1))
+    ws_need = max(ops.StepPlan.workspace_bytes_for(S, w.append if multi else 1, Hq, Hkv, D, c, args.partition)
+                  for c in range(first_ctx, final_ctx + 1))
     ws = torch.empty(max(1, ws_need), dtype=torch.uint8, device=dev)
     seqs = np.ascontiguousarray(w.step_seqs, dtype=np.int64)
     batch = np.ascontiguousarray(w.batch, dtype=np.int64)
@@ -411,7 +421,7 @@ def main():
         scratch.zero_()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
-        ops.decode_partitions(out, q, k_pool, v_pool, d_table, d_ctx, w.scale, mx, args.partition, ws)
+        plan.decode_partitions(mx)
         b.record(stream)
         cold.append((a, b))
     torch.cuda.synchronize()
@@ -442,7 +452,7 @@ def main():
         torch.cuda.synchronize()
         extra_fields["copy_probe_bytes"] = {"read": src.numel(), "write": dst.numel()}
         del src, dst
-    if w.append > 1:
+    if w.append > 1 and not multi:
         # the chunk workload also times its chunked prefill (matrix-core bound)
         qc = to_dev(w.q)
         oc = torch.empty(qc.shape, dtype=tdt, device=dev)

@@ -158,6 +158,35 @@ pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* q,
                       void* workspace, size_t workspace_bytes,
                       pa_dtype_t dtype, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Several queries per sequence: the last q_len positions of each context
+ * (ctx - q_len .. ctx - 1, their K/V already written), each attending
+ * causally to keys 0 .. its own position -- e.g. verifying q_len drafted
+ * tokens in one step.  This is the chunked-prefill computation
+ * (pa_prefill_chunk) for a chunk small enough that all q_len x group
+ * (query, head) pairs of a kv head fit the 16 matrix-core columns decode
+ * already pads to, so it runs at decode's bandwidth:
+ *   q    device [num_seqs][q_len][num_q_heads][head_dim] of dtype
+ *   out  device [num_seqs][q_len][num_q_heads][head_dim] of out_dtype
+ * Requires q_len * (num_q_heads / num_kv_heads) <= 16 and fp16 / bf16
+ * (PA_EUNSUPPORTED otherwise), context_lens[s] >= q_len (else NaN rows).
+ * q_len 1 is pa_decode.  Other arguments as pa_decode; the workspace is
+ * sized by pa_decode_multi_workspace_bytes.
+ * ---------------------------------------------------------------------- */
+size_t pa_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim, int32_t max_context_len,
+                                       int32_t partition_size);
+
+pa_status_t pa_decode_multi(void* out, pa_dtype_t out_dtype, const void* q, int32_t q_len,
+                            const void* k_cache, const void* v_cache,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens,
+                            int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                            float scale, int32_t max_context_len, int32_t partition_size,
+                            void* workspace, size_t workspace_bytes,
+                            pa_dtype_t dtype, void* stream);
+
 /* The two launches pa_decode makes, for callers that time or schedule them
  * separately.  pa_decode_partitions writes finished rows of single-partition
  * sequences to `out` and partial results of the others to `workspace`;

@@ -66,15 +66,20 @@ struct DecodeCheck {
   int32_t nparts;
 };
 
-pa_status_t check_decode(const void* out, pa_dtype_t out_dtype, const void* q, const void* k, const void* v,
-                         const int32_t* tables, int32_t max_blocks, const int32_t* ctx, int32_t S, int32_t Hq,
-                         int32_t Hkv, int32_t D, int32_t bs, int64_t NB, float scale, int32_t max_ctx,
+pa_status_t check_decode(const void* out, pa_dtype_t out_dtype, const void* q, int32_t q_len, const void* k,
+                         const void* v, const int32_t* tables, int32_t max_blocks, const int32_t* ctx, int32_t S,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int64_t NB, float scale, int32_t max_ctx,
                          int32_t partition, pa_dtype_t dtype, DecodeCheck* dc) {
   pa_status_t st = check_pool(Hkv, D, bs, NB, dtype);
   if (st != PA_OK) return st;
   if (S < 0) return fail(PA_EINVAL, "num_seqs must be >= 0");
   if (Hq <= 0 || Hq % Hkv != 0) return fail(PA_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", Hq, Hkv);
   if (Hq / Hkv > 16) return fail(PA_EUNSUPPORTED, "query group %d > 16", Hq / Hkv);
+  if (q_len < 1) return fail(PA_EINVAL, "q_len must be >= 1");
+  if (q_len > 1 && dtype == PA_F32) return fail(PA_EUNSUPPORTED, "several queries per sequence need fp16 or bf16");
+  if (q_len > 1 && (Hq / Hkv) * q_len > 16)
+    return fail(PA_EUNSUPPORTED, "q_len %d x query group %d > 16: use pa_prefill_chunk", q_len, Hq / Hkv);
+  if (int64_t(S) * q_len > 65535) return fail(PA_EUNSUPPORTED, "num_seqs x q_len must be <= 65535");
   if (!(out_dtype == PA_F32 || out_dtype == dtype))
     return fail(PA_EUNSUPPORTED, "out_dtype must be PA_F32 or the input dtype");
   if (max_ctx < 0) return fail(PA_EINVAL, "max_context_len must be >= 0");
@@ -111,16 +116,16 @@ void split_workspace(void* ws, int64_t S, int64_t Hq, int64_t D, int64_t nparts,
 
 enum class DecodePhase { kBoth, kPartitions, kReduce };
 
-pa_status_t run_decode(DecodePhase phase, void* out, pa_dtype_t out_dtype, const void* q, const void* k_cache,
-                       const void* v_cache, const int32_t* block_tables, int32_t max_blocks,
+pa_status_t run_decode(DecodePhase phase, void* out, pa_dtype_t out_dtype, const void* q, int32_t q_len,
+                       const void* k_cache, const void* v_cache, const int32_t* block_tables, int32_t max_blocks,
                        const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
                        int64_t NB, float scale, int32_t max_ctx, int32_t partition, void* workspace,
                        size_t workspace_bytes_given, pa_dtype_t dtype, void* stream) {
   DecodeCheck dc{};
-  pa_status_t st = check_decode(out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks, context_lens, S, Hq,
-                                Hkv, D, bs, NB, scale, max_ctx, partition, dtype, &dc);
+  pa_status_t st = check_decode(out, out_dtype, q, q_len, k_cache, v_cache, block_tables, max_blocks, context_lens,
+                                S, Hq, Hkv, D, bs, NB, scale, max_ctx, partition, dtype, &dc);
   if (st != PA_OK) return st;
-  const size_t need = ws_size(S, Hq, D, dc.nparts);
+  const size_t need = ws_size(int64_t(S) * q_len, Hq, D, dc.nparts);
   if (need > 0 && (workspace == nullptr || workspace_bytes_given < need))
     return fail(PA_EWORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes_given);
   if (S == 0) return PA_OK;
@@ -142,7 +147,8 @@ pa_status_t run_decode(DecodePhase phase, void* out, pa_dtype_t out_dtype, const
   a.max_context_len = max_ctx;
   a.partition = dc.partition;
   a.num_partitions = dc.nparts;
-  if (need > 0) split_workspace(workspace, S, Hq, D, dc.nparts, &a.ws_acc, &a.ws_m, &a.ws_l);
+  a.q_len = q_len;
+  if (need > 0) split_workspace(workspace, int64_t(S) * q_len, Hq, D, dc.nparts, &a.ws_acc, &a.ws_m, &a.ws_l);
   a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
   if (phase != DecodePhase::kReduce) {
@@ -218,13 +224,33 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   return ws_size(num_seqs, num_q_heads, head_dim, ceil_div(max_context_len, p));
 }
 
+size_t pa_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || q_len <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0)
+    return 0;
+  if (partition_size < 0 || partition_size % 16 != 0) return 0;
+  const int32_t p = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+  return ws_size(int64_t(num_seqs) * q_len, num_q_heads, head_dim, ceil_div(max_context_len, p));
+}
+
+pa_status_t pa_decode_multi(void* out, pa_dtype_t out_dtype, const void* q, int32_t q_len, const void* k_cache,
+                            const void* v_cache, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* context_lens, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                            int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                            int32_t max_context_len, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                            pa_dtype_t dtype, void* stream) {
+  return run_decode(DecodePhase::kBoth, out, out_dtype, q, q_len, k_cache, v_cache, block_tables, max_blocks_per_seq,
+                    context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                    max_context_len, partition_size, workspace, workspace_bytes, dtype, stream);
+}
+
 pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* context_lens,
                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, int64_t num_blocks, float scale, int32_t max_context_len,
                       int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype_t dtype,
                       void* stream) {
-  return run_decode(DecodePhase::kBoth, out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+  return run_decode(DecodePhase::kBoth, out, out_dtype, q, 1, k_cache, v_cache, block_tables, max_blocks_per_seq,
                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                     max_context_len, partition_size, workspace, workspace_bytes, dtype, stream);
 }
@@ -235,7 +261,7 @@ pa_status_t pa_decode_partitions(void* out, pa_dtype_t out_dtype, const void* q,
                                  int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                                  float scale, int32_t max_context_len, int32_t partition_size, void* workspace,
                                  size_t workspace_bytes, pa_dtype_t dtype, void* stream) {
-  return run_decode(DecodePhase::kPartitions, out, out_dtype, q, k_cache, v_cache, block_tables, max_blocks_per_seq,
+  return run_decode(DecodePhase::kPartitions, out, out_dtype, q, 1, k_cache, v_cache, block_tables, max_blocks_per_seq,
                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
                     max_context_len, partition_size, workspace, workspace_bytes, dtype, stream);
 }
@@ -271,6 +297,7 @@ pa_status_t pa_decode_reduce(void* out, pa_dtype_t out_dtype, const int32_t* con
   a.max_blocks = int32_t(ceil_div(max_context_len, 16));
   a.partition = p;
   a.num_partitions = int32_t(nparts);
+  a.q_len = 1;
   split_workspace(const_cast<void*>(workspace), num_seqs, num_q_heads, head_dim, nparts, &a.ws_acc, &a.ws_m, &a.ws_l);
   a.dtype = out_dtype == PA_F32 ? PA_F16 : out_dtype;
   a.stream = static_cast<hipStream_t>(stream);

@@ -26,6 +26,12 @@
 // hi + lo halves of the input type before the PV product so it keeps ~16
 // (bf16) / ~22 (fp16) mantissa bits; K, Q and V products are exact in fp32.
 // fp32 inputs use the vector ALUs (one workgroup per query head).
+//
+// Several queries per sequence (verifying C drafted tokens at positions
+// ctx - C .. ctx - 1) share each tile the same way: the accumulator columns
+// are the G * C (query, head) pairs of the kv group, and column (i, n) sees
+// keys up to position ctx - C + i, so G * C <= 16 runs at decode's
+// bandwidth with the causal limit applied per column.
 
 #include <math.h>
 
@@ -37,6 +43,8 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
+// "no max yet": finite so that 2^(s - m) of a masked score is 0, not NaN
+constexpr float kNoMax = -1e30f;
 
 struct KParams {
   void* out;
@@ -55,6 +63,7 @@ struct KParams {
   float scale_log2;
   int32_t max_blocks;
   int32_t hq, hkv, max_ctx, partition, nparts_max;
+  int32_t qlen;  // queries per sequence (1: plain decode)
 };
 
 template <typename T, bool OUT_F32>
@@ -115,13 +124,19 @@ decode_mfma_kernel(KParams P) {
   const int n = lane & 15;     // head column of this lane
   const int quad = lane >> 4;  // token quad / k-slice of this lane
   const int G = P.hq / P.hkv;
+  const int C = P.qlen;
+  const int ncol = G * C;  // accumulator columns in use: (query i, head n) = column i * G + n
   const int ctx = P.ctxs[s];
-  const int64_t row0 = int64_t(s) * P.hq + int64_t(g) * G;  // first q-head row of the group
+  // output / partial row of column c: query i = c / G, head g * G + c % G
+  auto col_row = [&](int c) {
+    return (int64_t(s) * C + c / G) * P.hq + int64_t(g) * G + c % G;
+  };
 
-  if (context_out_of_contract(ctx, P) || ctx == 0) {
+  if (context_out_of_contract(ctx, P) || ctx < C || ctx == 0) {
     if (part == 0) {
       const float v = ctx == 0 ? 0.f : __builtin_nanf("");
-      for (int idx = threadIdx.x; idx < G * D; idx += kThreads) store_out<T, OUT_F32>(P.out, row0 * D + idx, v);
+      for (int idx = threadIdx.x; idx < ncol * D; idx += kThreads)
+        store_out<T, OUT_F32>(P.out, col_row(idx / D) * D + idx % D, v);
     }
     return;
   }
@@ -132,16 +147,18 @@ decode_mfma_kernel(KParams P) {
   const int nparts = (ctx + P.partition - 1) / P.partition;
   const int32_t* trow = P.tables + int64_t(s) * P.max_blocks + tok0 / kBlockTokens;
 
-  // Q^T as the B operand: lane supplies head n, dims 8 * (4 i + quad) + 0..7.
+  // Q^T as the B operand: lane supplies column n, dims 8 * (4 i + quad) + 0..7.
   u32x4_t qb[DC];
 #pragma unroll
   for (int i = 0; i < DC; ++i) {
-    if (n < G) {
-      qb[i] = load16(P.q16 + (row0 + n) * D + 8 * (4 * i + quad));
+    if (n < ncol) {
+      qb[i] = load16(P.q16 + col_row(n) * D + 8 * (4 * i + quad));
     } else {
       qb[i] = u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+  // last key column n may attend (its query's position)
+  const int last_n = ctx - C + (n < ncol ? n / G : 0);
 
   const uint16_t* kg = P.k16 + int64_t(g) * kTileElems;
   const uint16_t* vg = P.v16 + int64_t(g) * kTileElems;
@@ -153,7 +170,9 @@ decode_mfma_kernel(KParams P) {
   // p = 2^(s - m) <= 256, which fp32 sums and the hi + lo split of P hold
   // exactly as well as p <= 1, and the accumulator rescale (a multiply of
   // all of o) is skipped on most tiles.
-  float m = -INFINITY;  // reference max of head n, same in every quad
+  // -1e30 rather than -inf: a column whose keys of a tile are all masked
+  // (only with C > 1) then gets p = 0, not 2^(-inf + inf)
+  float m = kNoMax;     // reference max of column n, same in every quad
   float lsum = 0.f;     // this lane's share of the sum of head n
   f32x4_t o[NT];
 #pragma unroll
@@ -189,10 +208,11 @@ decode_mfma_kernel(KParams P) {
 #pragma unroll
       for (int c = 0; c < DC; ++c) sc = Mfma<T>::k32(kt[c], qb[c], sc);
       const int jb = kWaves * (wb + i) + w;
-      const int valid = min(kBlockTokens, ntok - jb * kBlockTokens);
+      const int valid = min(kBlockTokens, ntok - jb * kBlockTokens);  // slots inside the context
+      const int lim = last_n - (tok0 + jb * kBlockTokens);             // last attended slot of column n
       float sv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sv[r] = (4 * quad + r < valid) ? sc[r] * P.scale_log2 : -INFINITY;
+      for (int r = 0; r < 4; ++r) sv[r] = (4 * quad + r <= lim) ? sc[r] * P.scale_log2 : -INFINITY;
       float bm = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
       bm = fmaxf(bm, shfl_xor(bm, 16));
       bm = fmaxf(bm, shfl_xor(bm, 32));
@@ -266,7 +286,7 @@ decode_mfma_kernel(KParams P) {
     s_m[w][n] = m;
     s_l[w][n] = lsum;
   }
-  if (n < G) {
+  if (n < ncol) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -274,7 +294,7 @@ decode_mfma_kernel(KParams P) {
   }
   __syncthreads();
   const bool any_bad = s_bad != 0;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < ncol * D; idx += kThreads) {
     const int h = idx / D, d = idx - (idx / D) * D;
     float M = s_m[0][h];
 #pragma unroll
@@ -288,9 +308,9 @@ decode_mfma_kernel(KParams P) {
     }
     if (any_bad) O = __builtin_nanf("");
     if (nparts == 1) {
-      store_out<T, OUT_F32>(P.out, (row0 + h) * D + d, O / L);
+      store_out<T, OUT_F32>(P.out, col_row(h) * D + d, O / L);
     } else {
-      const int64_t prow = (row0 + h) * P.nparts_max + part;
+      const int64_t prow = col_row(h) * P.nparts_max + part;
       P.ws_acc[prow * D + d] = O;
       if (d == 0) {
         P.ws_m[prow] = M;
@@ -468,12 +488,13 @@ decode_reduce_kernel(KParams P) {
   constexpr int kW = D / kWave;
   __shared__ float s_w[kReduceChunk];
   __shared__ float s_red[kW];
-  const int h = blockIdx.x, s = blockIdx.y;
+  const int h = blockIdx.x, sq = blockIdx.y;  // sq = s * qlen + query
+  const int s = sq / P.qlen;
   const int d = threadIdx.x;
   const int ctx = P.ctxs[s];
-  if (context_out_of_contract(ctx, P) || ctx <= P.partition) return;  // written by the partition kernel
+  if (context_out_of_contract(ctx, P) || ctx < P.qlen || ctx <= P.partition) return;  // written by the partition kernel
   const int nparts = (ctx + P.partition - 1) / P.partition;
-  const int64_t prow0 = (int64_t(s) * P.hq + h) * P.nparts_max;
+  const int64_t prow0 = (int64_t(sq) * P.hq + h) * P.nparts_max;
 
   float M = -INFINITY;
   for (int j = d; j < nparts; j += D) M = fmaxf(M, P.ws_m[prow0 + j]);
@@ -498,7 +519,7 @@ decode_reduce_kernel(KParams P) {
       O += wj * acc[int64_t(j0 + j) * D];
     }
   }
-  store_out<T, OUT_F32>(P.out, (int64_t(s) * P.hq + h) * D + d, O / L);
+  store_out<T, OUT_F32>(P.out, (int64_t(sq) * P.hq + h) * D + d, O / L);
 }
 
 KParams make_params(const DecodeArgs& a) {
@@ -523,6 +544,7 @@ KParams make_params(const DecodeArgs& a) {
   p.max_ctx = a.max_context_len;
   p.partition = a.partition;
   p.nparts_max = a.num_partitions;
+  p.qlen = a.q_len;
   return p;
 }
 
@@ -539,7 +561,7 @@ hipError_t launch_mfma(const DecodeArgs& a, const KParams& p) {
 
 template <typename T, int D>
 hipError_t launch_reduce(const DecodeArgs& a, const KParams& p) {
-  const dim3 grid(unsigned(a.num_q_heads), unsigned(a.num_seqs));
+  const dim3 grid(unsigned(a.num_q_heads), unsigned(a.num_seqs) * unsigned(a.q_len));
   if (a.out_f32) {
     hipLaunchKernelGGL((decode_reduce_kernel<T, D, true>), grid, dim3(D), 0, a.stream, p);
   } else {

@@ -27,9 +27,10 @@ struct DecodeArgs {
   int32_t max_context_len;
   int32_t partition;
   int32_t num_partitions;  // ceil(max_context_len / partition)
-  float* ws_acc;           // [S][Hq][num_partitions][D]
-  float* ws_m;             // [S][Hq][num_partitions]
-  float* ws_l;             // [S][Hq][num_partitions]
+  int32_t q_len;           // queries per sequence (1: plain decode)
+  float* ws_acc;           // [S][q_len][Hq][num_partitions][D]
+  float* ws_m;             // [S][q_len][Hq][num_partitions]
+  float* ws_l;             // [S][q_len][Hq][num_partitions]
   pa_dtype_t dtype;
   hipStream_t stream;
 };

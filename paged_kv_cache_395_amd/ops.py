@@ -133,6 +133,35 @@ def decode_reduce(out, context_lens, num_kv_heads, max_context_len, partition_si
                                             _stream(stream)))
 
 
+def decode_multi(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size=0,
+                 workspace=None, stream=None) -> None:
+    """Causal attention of the last q_len positions of each context, q [S, q_len, Hq, D], at decode's bandwidth
+    (q_len x group <= 16)."""
+    _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+    NB, Hkv, D = _pool_dims(k_cache)
+    if q.dim() != 4 or q.shape[3] != D:
+        raise ValueError("q must be [num_seqs, q_len, num_q_heads, head_dim]")
+    S, C, Hq = q.shape[0], q.shape[1], q.shape[2]
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks]")
+    if context_lens.dtype != torch.int32 or context_lens.shape != (S,):
+        raise ValueError("context_lens must be int32 [num_seqs]")
+    if not (q.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("q and the pools must share one dtype")
+    lib = _lib.load()
+    need = int(lib.pa_decode_multi_workspace_bytes(S, C, Hq, Hkv, D, int(max_context_len), int(partition_size)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _lib.check(lib.pa_decode_multi(_p(out), _code(out), _p(q), C, _p(k_cache), _p(v_cache), _p(block_tables),
+                                   block_tables.shape[1], _p(context_lens), S, Hq, Hkv, D, BLOCK_SIZE, NB,
+                                   float(scale), int(max_context_len), int(partition_size),
+                                   _p(workspace) if workspace is not None else None, ws_bytes, _code(q),
+                                   _stream(stream)))
+
+
 def prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, stream=None) -> None:
     """Causal attention of q [S, C, Hq, D] (the last C positions of each context) over the paged cache."""
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
@@ -166,22 +195,41 @@ class StepPlan:
     only the host bound ``max_context_len`` changes.  The plan checks every
     tensor once, keeps the marshalled C arguments, and each call then costs
     one ctypes call per launch.  The tensors must stay alive and keep their
-    storage for the plan's lifetime.
+    storage for the plan's lifetime.  A 4-D ``q`` [S, q_len, Hq, D] plans the
+    several-queries-per-sequence decode (pa_decode_multi: both launches in
+    one call, ``decode_partitions`` runs it and ``decode_reduce`` is a no-op).
     """
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace,
                  key=None, value=None, slot_mapping=None, partition_size=0, stream=None):
-        # the workspace is the caller's, sized for the largest max_context_len the plan will see
-        self._args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, 0,
-                                     partition_size, workspace)
         self._lib = _lib.load()
         self._stream = _stream(stream)
-        self._ws_bytes = self._args[18]
         NB, Hkv, D = _pool_dims(k_cache)
-        S, Hq = q.shape[0], q.shape[1]
-        self._sizes = (S, Hq, Hkv, D)
-        self._reduce_head = (_p(out), _code(out), _p(context_lens), S, Hq, Hkv, D)
         self._partition = int(partition_size)
+        self._multi = q.dim() == 4
+        if self._multi:
+            _dev(out, q, k_cache, v_cache, block_tables, context_lens)
+            if q.shape[3] != D or out.shape != q.shape:
+                raise ValueError("q / out must be [num_seqs, q_len, num_q_heads, head_dim]")
+            if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+                raise ValueError("block_tables and context_lens must be int32")
+            S, C, Hq = q.shape[0], q.shape[1], q.shape[2]
+            ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+            self._multi_head = (_p(out), _code(out), _p(q), C, _p(k_cache), _p(v_cache), _p(block_tables),
+                                block_tables.shape[1], _p(context_lens), S, Hq, Hkv, D, BLOCK_SIZE, NB, float(scale))
+            self._multi_tail = (self._partition, _p(workspace) if workspace is not None else None, ws_bytes,
+                                _code(q), self._stream)
+            self._sizes = (S, Hq, Hkv, D)
+            self._q_len = C
+        else:
+            # the workspace is the caller's, sized for the largest max_context_len the plan will see
+            self._args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, 0,
+                                         partition_size, workspace)
+            self._ws_bytes = self._args[18]
+            S, Hq = q.shape[0], q.shape[1]
+            self._sizes = (S, Hq, Hkv, D)
+            self._q_len = 1
+            self._reduce_head = (_p(out), _code(out), _p(context_lens), S, Hq, Hkv, D)
         self._write = None
         if key is not None:
             _dev(key, value, slot_mapping)
@@ -194,18 +242,31 @@ class StepPlan:
             self._write = (_p(key), _p(value), _p(k_cache), _p(v_cache), _p(slot_mapping), key.shape[0], Hkv, D,
                            BLOCK_SIZE, NB, _code(k_cache), self._stream)
 
+    @staticmethod
+    def workspace_bytes_for(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, max_context_len,
+                            partition_size=0) -> int:
+        """Workspace a plan of these sizes needs at max_context_len."""
+        return int(_lib.load().pa_decode_multi_workspace_bytes(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim,
+                                                               int(max_context_len), int(partition_size)))
+
     def workspace_bytes(self, max_context_len: int) -> int:
         S, Hq, Hkv, D = self._sizes
-        return decode_workspace_bytes(S, Hq, Hkv, D, max_context_len, self._partition)
+        return int(self._lib.pa_decode_multi_workspace_bytes(S, self._q_len, Hq, Hkv, D, int(max_context_len),
+                                                             self._partition))
 
     def cache_write(self) -> None:
         _lib.check(self._lib.pa_reshape_and_cache(*self._write))
 
     def decode_partitions(self, max_context_len: int) -> None:
+        if self._multi:
+            _lib.check(self._lib.pa_decode_multi(*self._multi_head, int(max_context_len), *self._multi_tail))
+            return
         a = self._args
         _lib.check(self._lib.pa_decode_partitions(*a[:15], int(max_context_len), *a[16:], self._stream))
 
     def decode_reduce(self, max_context_len: int) -> None:
+        if self._multi:
+            return
         a = self._args
         _lib.check(self._lib.pa_decode_reduce(*self._reduce_head, int(max_context_len), self._partition, a[17],
                                               self._ws_bytes, self._stream))

@@ -76,6 +76,37 @@ def test_decode_rejects_bad_arguments_before_launch(kw, status):
     assert L.pa_last_error()
 
 
+def multi_call(**kw):
+    a = dict(out=1, out_dtype=_lib.PA_F32, q=1, C=4, k=1, v=1, tables=1, maxb=4, ctx=1, S=1, Hq=8, Hkv=2, D=128,
+             bs=16, NB=10, scale=0.1, max_ctx=64, P=0, ws=None, ws_bytes=0, dtype=_lib.PA_BF16)
+    a.update(kw)
+    return L.pa_decode_multi(a["out"], a["out_dtype"], a["q"], a["C"], a["k"], a["v"], a["tables"], a["maxb"],
+                             a["ctx"], a["S"], a["Hq"], a["Hkv"], a["D"], a["bs"], a["NB"], a["scale"], a["max_ctx"],
+                             a["P"], a["ws"], a["ws_bytes"], a["dtype"], NULL)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(C=0), _lib.PA_EINVAL),
+    (dict(C=5), _lib.PA_EUNSUPPORTED),           # 5 queries x group 4 > 16 columns
+    (dict(C=2, dtype=_lib.PA_F32), _lib.PA_EUNSUPPORTED),
+    (dict(S=20000), _lib.PA_EUNSUPPORTED),       # num_seqs x q_len beyond the merge grid
+    (dict(max_ctx=600, maxb=40), _lib.PA_EWORKSPACE),
+])
+def test_multi_query_decode_rejects_bad_arguments(kw, status):
+    assert multi_call(**kw) == status
+    assert L.pa_last_error()
+
+
+def test_multi_query_workspace_scales_with_queries():
+    one = L.pa_decode_workspace_bytes(8, 32, 8, 128, 5000, 512)
+    assert L.pa_decode_multi_workspace_bytes(8, 1, 32, 8, 128, 5000, 512) == one
+    align = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    rows = 8 * 4 * 32 * 10
+    assert L.pa_decode_multi_workspace_bytes(8, 4, 32, 8, 128, 5000, 512) == align(rows * 128 * 4) + 2 * align(rows * 4)
+    assert L.pa_decode_multi(None, 0, None, 4, None, None, None, 4, None, 0, 8, 2, 128, 16, 10, 0.1, 64, 0, None, 0,
+                             _lib.PA_BF16, NULL) == _lib.PA_OK
+
+
 def test_decode_with_no_sequences_is_a_no_op():
     assert decode_call(S=0, out=None, q=None) == _lib.PA_OK
 

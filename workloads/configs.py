@@ -277,12 +277,28 @@ def _longctx_bf16(rng, num_seqs=16, ctx=32768, chunk=512, Hq=64, Hkv=8, NB=None,
                    {"final_ctx": np.full(num_seqs, ctx, dtype=np.int64), "blocks_needed": need})
 
 
+def _specdec_bf16(rng, num_seqs=256, median=1024, lo=16, hi=8192, q_len=4):
+    """Speculative verification: every sequence appends q_len drafted tokens and attends each causally."""
+    ctx = np.clip(np.rint(np.exp(math.log(median) + rng.standard_normal(num_seqs))), max(lo, q_len), hi)
+    ctx = ctx.astype(np.int64)
+    need = int(sum(_blocks(c) for c in ctx))
+    NB = int(math.ceil(1.25 * need))
+    program = [("add", s, int(ctx[s]) - q_len) for s in range(num_seqs)]
+    return _finish(rng, "specdec_bf16", "bf16", num_seqs, 32, 8, 128, NB, 1.0 / math.sqrt(128), 512, q_len,
+                   program, np.arange(num_seqs),
+                   f"Llama-3-8B-shaped GQA verification of {q_len} drafted tokens per sequence, bf16, batch "
+                   f"{num_seqs}, 32/8 heads, head_dim 128, ctx lognormal(median {median}, sigma 1) clipped to "
+                   f"[{max(lo, q_len)},{hi}]",
+                   {"final_ctx": ctx, "blocks_needed": need, "mode": "multi"})
+
+
 WORKLOADS = {
     "tiny_f32": (1001, _tiny_f32),
     "mha7b_f16": (1002, _mha7b_f16),
     "gqa8b_bf16": (1003, _gqa8b_bf16),
     "shared_prefix_bf16": (1004, _shared_prefix_bf16),
     "longctx_bf16": (1005, _longctx_bf16),
+    "specdec_bf16": (1006, _specdec_bf16),
 }
 
 
