@@ -105,6 +105,37 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* k_cac
                                  int64_t num_blocks, pa_dtype_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * One step's appends with the block tables and context lengths resident on
+ * the device: the cache write above, plus, for each token,
+ *     block_tables[row][pos / 16] = slot / 16
+ * (the block the slot lies in: a block opened on demand when pos % 16 == 0,
+ * the fresh copy after a copy-on-write, the unchanged block otherwise --
+ * [OS] "The Magic: No Pre-allocation", "Copy-on-Write: Sharing KV Cache"),
+ * and context_lens[r] = new_context_lens[r] for every row r.  A serving step
+ * then ships only its tokens' slots, rows and positions and the new lengths
+ * (about 1 KB for 64 sequences) instead of whole tables, and the decode that
+ * follows reads tables and lengths where this call left them.
+ *   key, value        device [num_tokens][num_kv_heads][head_dim] of dtype
+ *   slot_mapping      int64 [num_tokens]   (< 0: skip the token)
+ *   token_rows        int32 [num_tokens]   row of the token's sequence in
+ *                                          block_tables / context_lens
+ *   token_positions   int32 [num_tokens]   the token's position in its sequence
+ *   new_context_lens  int32 [num_seqs]
+ * These four may be device memory or pinned host memory (each value is read
+ * once).  block_tables (device int32 [num_seqs][max_blocks_per_seq]) and
+ * context_lens (device int32 [num_seqs]) are updated in place.  A token whose
+ * row or position falls outside the table is stored but does not touch the
+ * table.  Slots in one call must be distinct.
+ * ---------------------------------------------------------------------- */
+pa_status_t pa_append_step(const void* key, const void* value, void* k_cache, void* v_cache,
+                           const int64_t* slot_mapping, const int32_t* token_rows,
+                           const int32_t* token_positions, int32_t num_tokens,
+                           int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t* context_lens, const int32_t* new_context_lens, int32_t num_seqs,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, pa_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Copy whole physical blocks (K and V, all kv heads) src -> dst: the copy a
  * shared block gets before a sequence writes into it ([OS] "Copy-on-Write:
  * Sharing KV Cache").

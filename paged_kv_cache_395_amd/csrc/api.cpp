@@ -195,6 +195,43 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* k_cac
                     "reshape_and_cache launch");
 }
 
+pa_status_t pa_append_step(const void* key, const void* value, void* k_cache, void* v_cache,
+                           const int64_t* slot_mapping, const int32_t* token_rows, const int32_t* token_positions,
+                           int32_t num_tokens, int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t* context_lens, const int32_t* new_context_lens, int32_t num_seqs,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           pa_dtype_t dtype, void* stream) {
+  pa_status_t st = check_pool(num_kv_heads, head_dim, block_size, num_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (num_tokens < 0 || num_seqs < 0) return fail(PA_EINVAL, "num_tokens and num_seqs must be >= 0");
+  if (max_blocks_per_seq <= 0) return fail(PA_EINVAL, "max_blocks_per_seq must be positive");
+  if (num_tokens > 0 && (!key || !value || !k_cache || !v_cache || !slot_mapping || !token_rows || !token_positions ||
+                         !block_tables))
+    return fail(PA_EINVAL, "null pointer argument");
+  if (num_seqs > 0 && (!context_lens || !new_context_lens)) return fail(PA_EINVAL, "null pointer argument");
+  if (int64_t(num_tokens) + (int64_t(num_seqs) + 255) / 256 > INT32_MAX) return fail(PA_EUNSUPPORTED, "grid too large");
+  AppendStepArgs a{};
+  a.key = key;
+  a.value = value;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.slots = slot_mapping;
+  a.rows = token_rows;
+  a.positions = token_positions;
+  a.num_tokens = num_tokens;
+  a.tables = block_tables;
+  a.max_blocks = max_blocks_per_seq;
+  a.ctx = context_lens;
+  a.new_ctx = new_context_lens;
+  a.num_rows = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.elem_bytes = elem_bytes(dtype);
+  a.stream = static_cast<hipStream_t>(stream);
+  return hip_status(launch_append_step(a), "append_step launch");
+}
+
 pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t num_pairs,
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
                            pa_dtype_t dtype, void* stream) {

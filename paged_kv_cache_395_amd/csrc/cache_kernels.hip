@@ -51,6 +51,57 @@ reshape_and_cache_kernel(const E* __restrict__ key, const E* __restrict__ value,
   }
 }
 
+// One step's appends with the block tables and context lengths kept on the
+// device: workgroup t < T stores token t's K/V rows (every kv head) into its
+// slot and sets table[row][pos / 16] = slot / 16 (the block the slot lies in:
+// a new block when pos % 16 == 0, the fresh copy after a copy-on-write, the
+// same block otherwise); the workgroups after those copy new_ctx into ctx.
+// The token's (slot, row, pos) are read once, by thread 0, into LDS: they may
+// live in pinned host memory, where every read crosses the host link.
+template <typename E>
+__global__ void __launch_bounds__(256)
+append_step_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ kc, E* __restrict__ vc,
+                   const int64_t* slots, const int32_t* rows, const int32_t* positions, int32_t num_tokens,
+                   int32_t* tables, int32_t max_blocks, int32_t* ctx, const int32_t* new_ctx, int32_t num_rows,
+                   int32_t kv_heads, int32_t head_dim, int64_t num_blocks) {
+  typedef E vec8 __attribute__((ext_vector_type(8)));
+  const int t = blockIdx.x;
+  if (t >= num_tokens) {
+    const int i = (t - num_tokens) * blockDim.x + threadIdx.x;
+    if (i < num_rows) ctx[i] = new_ctx[i];
+    return;
+  }
+  __shared__ int64_t s_slot;
+  __shared__ int32_t s_row, s_pos;
+  if (threadIdx.x == 0) {
+    s_slot = slots[t];
+    s_row = rows[t];
+    s_pos = positions[t];
+  }
+  __syncthreads();
+  const int64_t slot = s_slot;
+  if (slot < 0 || slot >= num_blocks * kBlockTokens) return;  // skipped token, or outside the pool
+  const int row = s_row, pos = s_pos;
+  if (threadIdx.x == 0 && row >= 0 && row < num_rows && pos >= 0 && pos / kBlockTokens < max_blocks)
+    tables[int64_t(row) * max_blocks + pos / kBlockTokens] = int32_t(slot >> 4);
+  const int64_t blk = slot >> 4;
+  const int o = int(slot & 15);
+  const int runs_per_head = head_dim / 8;
+  for (int c = threadIdx.x; c < kv_heads * runs_per_head; c += blockDim.x) {
+    const int h = c / runs_per_head, j = c - h * runs_per_head;
+    const int64_t src = (int64_t(t) * kv_heads + h) * head_dim + 8 * j;
+    const int64_t tile = (blk * kv_heads + h) * int64_t(kBlockTokens * head_dim);
+    *reinterpret_cast<vec8*>(kc + tile + (j * kBlockTokens + o) * 8) = *reinterpret_cast<const vec8*>(key + src);
+    const vec8 vv = *reinterpret_cast<const vec8*>(value + src);
+    E* vt = vc + tile;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * j + e;
+      vt[(((d >> 5) * 4 + (o >> 2)) * 16 + (d & 15)) * 8 + ((d >> 4) & 1) * 4 + (o & 3)] = vv[e];
+    }
+  }
+}
+
 // Grid (chunks of one block, pairs, 2): z = 0 copies K, z = 1 copies V; each
 // thread moves 16 bytes.
 __global__ void __launch_bounds__(256)
@@ -84,6 +135,26 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                        static_cast<const uint32_t*>(key), static_cast<const uint32_t*>(value),
                        static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache), slots, num_tokens,
                        num_kv_heads, head_dim, num_blocks);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_append_step(const AppendStepArgs& a) {
+  const int64_t ctx_groups = (int64_t(a.num_rows) + 255) / 256;
+  const int64_t grid = int64_t(a.num_tokens) + ctx_groups;
+  if (grid == 0) return hipSuccess;
+  if (a.elem_bytes == 2) {
+    hipLaunchKernelGGL(append_step_kernel<uint16_t>, dim3(unsigned(grid)), dim3(256), 0, a.stream,
+                       static_cast<const uint16_t*>(a.key), static_cast<const uint16_t*>(a.value),
+                       static_cast<uint16_t*>(a.k_cache), static_cast<uint16_t*>(a.v_cache), a.slots, a.rows,
+                       a.positions, a.num_tokens, a.tables, a.max_blocks, a.ctx, a.new_ctx, a.num_rows,
+                       a.num_kv_heads, a.head_dim, a.num_blocks);
+  } else {
+    hipLaunchKernelGGL(append_step_kernel<uint32_t>, dim3(unsigned(grid)), dim3(256), 0, a.stream,
+                       static_cast<const uint32_t*>(a.key), static_cast<const uint32_t*>(a.value),
+                       static_cast<uint32_t*>(a.k_cache), static_cast<uint32_t*>(a.v_cache), a.slots, a.rows,
+                       a.positions, a.num_tokens, a.tables, a.max_blocks, a.ctx, a.new_ctx, a.num_rows,
+                       a.num_kv_heads, a.head_dim, a.num_blocks);
   }
   return hipGetLastError();
 }

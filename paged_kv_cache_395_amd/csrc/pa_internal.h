@@ -62,6 +62,28 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
                                     const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
                                     int32_t head_dim, int64_t num_blocks, int elem_bytes, hipStream_t stream);
 
+struct AppendStepArgs {
+  const void* key;
+  const void* value;
+  void* k_cache;
+  void* v_cache;
+  const int64_t* slots;
+  const int32_t* rows;
+  const int32_t* positions;
+  int32_t num_tokens;
+  int32_t* tables;
+  int32_t max_blocks;
+  int32_t* ctx;
+  const int32_t* new_ctx;
+  int32_t num_rows;
+  int32_t num_kv_heads, head_dim;
+  int64_t num_blocks;
+  int elem_bytes;
+  hipStream_t stream;
+};
+
+hipError_t launch_append_step(const AppendStepArgs& a);
+
 hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t num_pairs,
                               int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
 

@@ -60,6 +60,54 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -
                                                 _stream(stream)))
 
 
+def _dev_or_pinned(*ts):
+    for t in ts:
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError("step metadata must live on the GPU or in pinned host memory")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
+def _append_args(key, value, k_cache, v_cache, slot_mapping, token_rows, token_positions, block_tables,
+                 context_lens, new_context_lens, stream):
+    _dev(key, value, k_cache, v_cache, block_tables, context_lens)
+    _dev_or_pinned(slot_mapping, token_rows, token_positions, new_context_lens)
+    NB, Hkv, D = _pool_dims(k_cache)
+    if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (Hkv, D):
+        raise ValueError("key / value must be [T, num_kv_heads, head_dim]")
+    T = key.shape[0]
+    if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be int64 [T]")
+    for t in (token_rows, token_positions):
+        if t.dtype != torch.int32 or t.shape != (T,):
+            raise ValueError("token_rows / token_positions must be int32 [T]")
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks]")
+    S = block_tables.shape[0]
+    for t in (context_lens, new_context_lens):
+        if t.dtype != torch.int32 or t.shape != (S,):
+            raise ValueError("context_lens / new_context_lens must be int32 [num_seqs]")
+    if not (key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
+        raise TypeError("key, value and the pools must share one dtype")
+    return (_p(key), _p(value), _p(k_cache), _p(v_cache), _p(slot_mapping), _p(token_rows), _p(token_positions), T,
+            _p(block_tables), block_tables.shape[1], _p(context_lens), _p(new_context_lens), S, Hkv, D, BLOCK_SIZE,
+            NB, _code(k_cache), _stream(stream))
+
+
+def append_step(key, value, k_cache, v_cache, slot_mapping, token_rows, token_positions, block_tables, context_lens,
+                new_context_lens, stream=None) -> None:
+    """Cache write plus in-place update of device-resident tables and lengths.
+
+    Token t goes to slot ``slot_mapping[t]``; ``block_tables[token_rows[t]]
+    [token_positions[t] // 16]`` becomes ``slot_mapping[t] // 16``; then
+    ``context_lens`` takes ``new_context_lens``.  The four step vectors may be
+    device tensors or pinned host tensors.
+    """
+    _lib.check(_lib.load().pa_append_step(*_append_args(key, value, k_cache, v_cache, slot_mapping, token_rows,
+                                                        token_positions, block_tables, context_lens,
+                                                        new_context_lens, stream)))
+
+
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
     """Copy physical blocks src -> dst for each row (src, dst) of int64 ``pairs`` [n, 2]."""
     _dev(k_cache, v_cache, pairs)
@@ -198,10 +246,16 @@ class StepPlan:
     storage for the plan's lifetime.  A 4-D ``q`` [S, q_len, Hq, D] plans the
     several-queries-per-sequence decode (pa_decode_multi: both launches in
     one call, ``decode_partitions`` runs it and ``decode_reduce`` is a no-op).
+
+    With ``append=(token_rows, token_positions, new_context_lens)`` the cache
+    write is pa_append_step: ``block_tables`` and ``context_lens`` stay on the
+    device and the write patches them from the step's slots, so a step ships
+    only its tokens' slots / rows / positions and the new lengths (which may
+    sit in pinned host memory) instead of whole tables.
     """
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace,
-                 key=None, value=None, slot_mapping=None, partition_size=0, stream=None):
+                 key=None, value=None, slot_mapping=None, partition_size=0, stream=None, append=None):
         self._lib = _lib.load()
         self._stream = _stream(stream)
         NB, Hkv, D = _pool_dims(k_cache)
@@ -231,7 +285,12 @@ class StepPlan:
             self._q_len = 1
             self._reduce_head = (_p(out), _code(out), _p(context_lens), S, Hq, Hkv, D)
         self._write = None
-        if key is not None:
+        self._append = None
+        if key is not None and append is not None:
+            rows, positions, new_ctx = append
+            self._append = _append_args(key, value, k_cache, v_cache, slot_mapping, rows, positions, block_tables,
+                                        context_lens, new_ctx, stream)
+        elif key is not None:
             _dev(key, value, slot_mapping)
             if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (Hkv, D):
                 raise ValueError("key / value must be [T, num_kv_heads, head_dim]")
@@ -255,7 +314,10 @@ class StepPlan:
                                                              self._partition))
 
     def cache_write(self) -> None:
-        _lib.check(self._lib.pa_reshape_and_cache(*self._write))
+        if self._append is not None:
+            _lib.check(self._lib.pa_append_step(*self._append))
+        else:
+            _lib.check(self._lib.pa_reshape_and_cache(*self._write))
 
     def decode_partitions(self, max_context_len: int) -> None:
         if self._multi:
@@ -272,7 +334,7 @@ class StepPlan:
                                               self._ws_bytes, self._stream))
 
     def __call__(self, max_context_len: int) -> None:
-        if self._write is not None:
+        if self._write is not None or self._append is not None:
             self.cache_write()
         self.decode_partitions(max_context_len)
         self.decode_reduce(max_context_len)
