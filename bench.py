@@ -112,6 +112,166 @@ def cpu_baseline(w, budget_s: float = 15.0):
                       f"{dt:.1f} s; seqs/s {len(done) / dt:.2f}; numpy, BLAS 1 thread"}
 
 
+SERVING = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16", rows=256, num_blocks=10000,
+               host_blocks=8000, max_blocks=192, budget=4096, requests=1200, mean_gap=0.5, prompt_median=512,
+               prompt_hi=2048, output_median=256, output_hi=1024, seed=2024)
+SERVING_DESC = ("continuous batching: GQA 32/8 heads, head_dim 128, bf16, 256 rows, pool 10000 blocks (640 MiB; "
+                "too small for the peak, so requests are preempted), host swap pool 8000 blocks, Poisson arrivals "
+                "every 0.5 steps, prompts lognormal median 512 (<= 2048), outputs median 256 (<= 1024), "
+                "4096 batched tokens per step")
+
+
+def serving_cpu_baseline(c, trace, steps: int, budget_s: float = 15.0):
+    """The oracle scheduler over the same trace, plus oracle fp64 decode of a
+    bounded sample of rows at the last step, scaled to one whole step."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import attention as OA
+    from oracle.block_manager import RefBlockManager
+    from oracle.scheduler import RefScheduler
+    from workloads import to_storage
+
+    bm = RefBlockManager(c["num_blocks"])
+    bm.set_host_pool(c["host_blocks"])
+    sched = RefScheduler(bm, c["rows"], c["max_blocks"], c["budget"])
+    pending = list(trace)
+    t0 = time.perf_counter()
+    for step in range(steps):
+        while pending and pending[0][0] <= step:
+            _, i, p, t = pending.pop(0)
+            sched.submit(i, p, t)
+        st = sched.step()
+    t_sched = (time.perf_counter() - t0) / steps
+    # attention of a sample of rows over random pools of the real shape
+    rng = np.random.default_rng(5)
+    Hq, Hkv, D, dt = c["num_q_heads"], c["num_kv_heads"], c["head_dim"], c["dtype"]
+    rows = [r for r, s in enumerate(st["row_seq"]) if s >= 0]
+    table, ctx = np.zeros((len(rows), c["max_blocks"]), np.int32), np.zeros(len(rows), np.int32)
+    for j, r in enumerate(rows):
+        t, n = bm.block_table([st["row_seq"][r]], c["max_blocks"], pad=0)
+        table[j], ctx[j] = t[0], n[0]
+    used = sorted({int(b) for j in range(len(rows)) for b in table[j, : -(-int(ctx[j]) // 16)]})
+    remap = {b: i for i, b in enumerate(used)}
+    table = np.vectorize(lambda b: remap.get(int(b), 0))(table).astype(np.int32)
+    k = to_storage(rng.standard_normal((len(used), Hkv, 16 * D), dtype=np.float32), dt)
+    v = to_storage(rng.standard_normal((len(used), Hkv, 16 * D), dtype=np.float32), dt)
+    q = to_storage(rng.standard_normal((len(rows), Hq, D), dtype=np.float32), dt)
+    done = []
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        for j in range(len(rows)):
+            OA.decode(q, k, v, table, ctx, D ** -0.5, dt, seqs=[j])
+            done.append(j)
+            if time.perf_counter() - t1 > budget_s:
+                break
+        t_att = time.perf_counter() - t1
+    per_step = t_sched + t_att * len(rows) / len(done)
+    return {"value": round(1.0 / per_step, 4), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"oracle scheduler over the first {steps} steps of the same trace ({t_sched * 1e3:.2f} ms "
+                      f"per step) + fp64 oracle decode of {len(done)} of the {len(rows)} running rows at the "
+                      f"last step ({t_att:.1f} s), scaled to all rows; numpy, BLAS 1 thread"}
+
+
+def bench_serving(args) -> None:
+    """Continuous batching through the native scheduler and the driver."""
+    import torch
+
+    from paged_kv_cache_395_amd import ops
+    from paged_kv_cache_395_amd.driver import Driver
+    from workloads.serving import request_trace
+
+    c = dict(SERVING)
+    trace = request_trace(c["seed"], c["requests"], c["mean_gap"], c["prompt_median"], c["prompt_hi"],
+                          c["output_median"], c["output_hi"], lo=16)
+    trace = [(a, i, p, min(t, c["max_blocks"] * 16)) for a, i, p, t in trace]
+    torch.cuda.set_device(0)
+    Hq, Hkv, D = c["num_q_heads"], c["num_kv_heads"], c["head_dim"]
+    drv = Driver(c["num_blocks"], c["host_blocks"], Hq, Hkv, D, c["dtype"], c["rows"], c["max_blocks"],
+                 c["budget"], D ** -0.5)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(c["seed"])
+    for t in (drv.key, drv.value, drv.q, drv.k_pool, drv.v_pool):
+        t.copy_(torch.randn(t.shape, generator=g, device="cuda", dtype=torch.float32).to(t.dtype))
+    esize = ESIZE[c["dtype"]]
+    block_bytes = Hkv * 16 * D * esize * 2
+    pending = list(trace)
+    stats = {"decode_bytes": 0.0, "tokens": 0, "prompt_tokens": 0, "swap_blocks": 0, "swap_out": 0, "swap_in": 0, "recompute": 0,
+             "admitted": 0, "finished": 0, "rows": 0}
+    ev = []
+
+    def one(step, timed):
+        while pending and pending[0][0] <= step:
+            _, i, p, t = pending.pop(0)
+            drv.submit(i, p, t)
+        st = drv.schedule()
+        e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if timed else None
+        drv.launch(st, decode_events=e)
+        if timed:
+            ev.append(e)
+            ctx = st.context_lens.astype(np.float64)
+            stats["decode_bytes"] += float((ctx * Hkv * D * 2 * esize).sum() + (ctx > 0).sum() * Hq * D * (esize + 4))
+            generated = st.num_running - st.num_admitted  # one token each; the rest are admitted prompts
+            stats["tokens"] += generated
+            stats["prompt_tokens"] += len(st.slots) - generated
+            stats["swap_blocks"] += len(st.swap_out) + len(st.swap_in)
+            stats["swap_out"] += st.num_preempted_swap
+            stats["swap_in"] += st.num_swapped_in
+            stats["recompute"] += st.num_preempted_recompute
+            stats["admitted"] += st.num_admitted
+            stats["finished"] += len(st.finished)
+            stats["rows"] += st.num_running
+        return st
+
+    for i in range(args.warmup):
+        one(i, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        one(args.warmup + i, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    K = args.steps
+    achieved = stats["decode_bytes"] / (dec_ms.sum() * 1e-3) / 1e9
+    rec = {
+        "metric": "continuous-batching attention steps/s (decode KV GB/s) at 1 MI355X",
+        "value": round(K / elapsed, 2),
+        "unit": "steps/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(elapsed / K * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": c["dtype"], "data": "synthetic",
+        "config": {"workload": f"serving_bf16: {SERVING_DESC}", **{k: c[k] for k in ("rows", "num_blocks",
+                   "host_blocks", "budget", "num_q_heads", "num_kv_heads", "head_dim")}},
+        "generated_tokens_per_s": round(stats["tokens"] / elapsed, 1),
+        "prompt_tokens_written_per_s": round(stats["prompt_tokens"] / elapsed, 1),
+        "mean_running_rows": round(stats["rows"] / K, 1),
+        "decode_kv_gbs_whole_step": round(stats["decode_bytes"] / elapsed / 1e9, 1),
+        "swap": {"blocks": stats["swap_blocks"], "gb": round(stats["swap_blocks"] * block_bytes / 1e9, 3),
+                 "preempted_swap": stats["swap_out"], "swapped_in": stats["swap_in"],
+                 "preempted_recompute": stats["recompute"]},
+        "admitted": stats["admitted"], "finished": stats["finished"],
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "decode_mfma_kernel",
+                     "algorithmic_bytes_per_launch": round(stats["decode_bytes"] / K, 1)},
+    }
+    # the swap copy alone: one launch of 2048 block pairs each way
+    n = min(2048, c["host_blocks"], c["num_blocks"])
+    pairs_out = torch.from_numpy(np.stack([np.arange(n), np.arange(n)], axis=1).astype(np.int64)).cuda()
+    a, b, d = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    ops.swap_blocks(drv.k_host, drv.v_host, drv.k_pool, drv.v_pool, pairs_out)
+    a.record()
+    ops.swap_blocks(drv.k_host, drv.v_host, drv.k_pool, drv.v_pool, pairs_out)
+    b.record()
+    ops.swap_blocks(drv.k_pool, drv.v_pool, drv.k_host, drv.v_host, pairs_out)
+    d.record()
+    torch.cuda.synchronize()
+    rec["swap_copy_gbs"] = {"device_to_host": round(n * block_bytes / (a.elapsed_time(b) * 1e-3) / 1e9, 2),
+                            "host_to_device": round(n * block_bytes / (b.elapsed_time(d) * 1e-3) / 1e9, 2),
+                            "blocks": n}
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = serving_cpu_baseline(c, trace, args.warmup + args.steps)
+    print(json.dumps(rec), flush=True)
+
+
 DECODE_KERNEL = "decode_mfma_kernel"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
@@ -247,11 +407,12 @@ def summarize(args) -> None:
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None, help="timed steps (50; 200 for serving_bf16)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (5; 150 for serving_bf16, which fills its batch meanwhile)")
     ap.add_argument("--workload", default="mha7b_f16",
                     choices=["tiny_f32", "mha7b_f16", "gqa8b_bf16", "shared_prefix_bf16", "longctx_bf16",
-                             "specdec_bf16"])
+                             "specdec_bf16", "serving_bf16"])
     ap.add_argument("--partition", type=int, default=0, help="tokens per context partition (0 = the library's choice)")
     ap.add_argument("--cold-iters", type=int, default=20, help="decode launches timed after a 1 GiB cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -267,6 +428,11 @@ def main():
     ap.add_argument("--prefill-pmc-dir")
     ap.add_argument("--prefill-grbm-dir")
     args = ap.parse_args()
+    serving = args.workload == "serving_bf16"
+    if args.steps is None:
+        args.steps = 200 if serving else 50
+    if args.warmup is None:
+        args.warmup = 150 if serving else 5
     if args.summarize:
         summarize(args)
         return
@@ -276,6 +442,10 @@ def main():
         sys.stderr.write("bench.py measures one GPU only: every box here has one MI355X, and the paged "
                          "decode path is built and measured on a single GPU (run with --gpus 1).\n")
         sys.exit(2)
+
+    if args.workload == "serving_bf16":
+        bench_serving(args)
+        return
 
     import torch
 

@@ -147,6 +147,32 @@ pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, i
                            int64_t num_blocks, pa_dtype_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Move whole blocks (K and V, all kv heads) between two pools of the same
+ * geometry: the copy behind preempting a request by moving its blocks to CPU
+ * memory and bringing them back ([OS] "vLLM Architecture", the scheduler's
+ * third duty).  Block pairs[i][0] of the source pools goes to block
+ * pairs[i][1] of the destination pools.  Either side may be pinned host
+ * memory (swap out: device -> host; swap in: host -> device); the two sides
+ * must be different pools.
+ *   pairs   int64 [num_pairs][2] = (src, dst), device or pinned host memory;
+ *           destinations distinct.  A pair outside [0, src_blocks) x
+ *           [0, dst_blocks) is skipped.
+ * ---------------------------------------------------------------------- */
+pa_status_t pa_swap_blocks(void* dst_k, void* dst_v, int64_t dst_blocks, const void* src_k,
+                           const void* src_v, int64_t src_blocks, const int64_t* pairs,
+                           int32_t num_pairs, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, pa_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Set block_tables[row][idx] = block for each patch (row, idx, block): how a
+ * device-resident table follows a request that comes back from CPU memory
+ * into new blocks.  patches: int32 [num_patches][3], device or pinned host
+ * memory; a patch outside the table is skipped.
+ * ---------------------------------------------------------------------- */
+pa_status_t pa_patch_tables(int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                            const int32_t* patches, int32_t num_patches, void* stream);
+
+/* ------------------------------------------------------------------------
  * Decode attention over the paged cache: for every sequence s and q head h,
  *     out[s][h] = softmax(scale * q[s][h] . K_s^T) V_s
  * over the context_lens[s] tokens of s, reading K_s / V_s through the block
@@ -326,6 +352,96 @@ double pa_bm_usage(const pa_bm_t* bm);                              /* used / nu
 int32_t pa_bm_num_tokens(const pa_bm_t* bm, int64_t seq);           /* -1: unknown       */
 /* Copy the free list, head first, into out[0..cap); returns its length. */
 int64_t pa_bm_free_list(const pa_bm_t* bm, int32_t* out, int64_t cap);
+
+/* ------------------------------------------------------------------------
+ * Swap pool.  A second pool of num_host_blocks blocks in CPU memory, with its
+ * own ids, free queue (ascending at first) and reference counts, to which a
+ * preempted request's blocks move ([OS] "vLLM Architecture").  Set once.
+ *
+ * pa_bm_swap_out moves every block of seqs[0..n) to the host pool: one host
+ * block per distinct device block of the list (a block shared inside the
+ * list moves once and stays shared; a block also held by a sequence outside
+ * the list stays on the device for it, and the listed ones get a copy).
+ * pairs ([Σ blocks][2], (device, host)) receives the copies the device must
+ * make, in order; *num_pairs counts them.  Device blocks whose count drops to
+ * zero join the free queue.  A swapped-out sequence keeps its length; it
+ * cannot be appended to, forked, shared as a prefix or put in a block table
+ * until pa_bm_swap_in brings it back, into fresh device blocks (pairs =
+ * (host, device)).  Both are all-or-nothing (PA_ENOSPC when the target pool
+ * is short).  pa_bm_free_seq works in either residence.
+ * ---------------------------------------------------------------------- */
+pa_status_t pa_bm_set_host_pool(pa_bm_t* bm, int64_t num_host_blocks);
+pa_status_t pa_bm_swap_out(pa_bm_t* bm, const int64_t* seqs, int32_t n, int64_t* pairs, int32_t* num_pairs);
+pa_status_t pa_bm_swap_in(pa_bm_t* bm, const int64_t* seqs, int32_t n, int64_t* pairs, int32_t* num_pairs);
+int32_t pa_bm_is_swapped(const pa_bm_t* bm, int64_t seq);       /* 1 / 0; -1: unknown  */
+int64_t pa_bm_num_free_host(const pa_bm_t* bm);
+int32_t pa_bm_host_refcount(const pa_bm_t* bm, int64_t block);  /* -1: out of range   */
+
+/* ------------------------------------------------------------------------
+ * Continuous-batching step scheduler over a block manager ([OS] "Continuous
+ * Batching: The Other Half" and "vLLM Architecture"; [VIZ] "Continuous
+ * Batching").  Requests arrive with a prompt length and a final length; each
+ * step decides which requests run in which of max_rows batch rows and emits
+ * the host-side half of the step:
+ *   1. requests that reached their final length are freed (their rows and
+ *      blocks come back at once);
+ *   2. the blocks every running request's next token needs are reserved;
+ *      while they do not fit, the latest-arrived running request is
+ *      preempted: swapped out to the host pool, or, when the host pool
+ *      cannot hold it, freed and requeued with prompt = its tokens so far;
+ *   3. swapped-out requests come back, earliest arrival first, while a row
+ *      and their blocks (plus the reserve) are free; not one preempted in
+ *      this step;
+ *   4. only when nothing is swapped out, waiting requests are admitted,
+ *      earliest arrival first, while a row and their prompt's blocks are
+ *      free and the step's token count stays within max_batched_tokens (the
+ *      first admission of a step is always allowed); an admitted request's
+ *      prompt tokens are written this step;
+ *   5. every request running before the admissions appends one token.
+ * Priority is arrival (submit) order; a request keeps its row while it runs;
+ * a new or returning one takes the lowest free row.  The scheduler owns the
+ * sequences it creates (ids are the request ids); do not change them through
+ * the block manager while it runs.
+ *
+ * The device half of a step, in this order on one stream: swap out
+ * (pa_swap_blocks device -> host), swap in (host -> device), copy-on-write
+ * (pa_copy_blocks), table patches (pa_patch_tables), then pa_append_step with
+ * slots / token_rows / token_positions / context_lens, then decode over the
+ * max_rows rows (an empty row has length 0 and gives a zero row).
+ * The arrays in pa_sched_out_t belong to the scheduler and stay valid until
+ * its next step or destruction.
+ * ---------------------------------------------------------------------- */
+typedef struct pa_sched pa_sched_t;
+
+typedef struct {
+  int32_t num_tokens;             /* K/V rows to write this step               */
+  const int64_t* slots;           /* [num_tokens]                              */
+  const int32_t* token_rows;      /* [num_tokens]                              */
+  const int32_t* token_positions; /* [num_tokens]                              */
+  int32_t num_rows;               /* = max_rows                                */
+  const int32_t* context_lens;    /* [num_rows], 0 for an empty row            */
+  const int64_t* row_seq;         /* [num_rows], request id or -1              */
+  int32_t num_swap_out;
+  const int64_t* swap_out_pairs;  /* [num_swap_out][2] (device, host)          */
+  int32_t num_swap_in;
+  const int64_t* swap_in_pairs;   /* [num_swap_in][2] (host, device)           */
+  int32_t num_cow;
+  const int64_t* cow_pairs;       /* [num_cow][2] (src, dst) device blocks     */
+  int32_t num_patches;
+  const int32_t* table_patches;   /* [num_patches][3] (row, logical, physical) */
+  int32_t num_finished;
+  const int64_t* finished;        /* requests retired at the start of the step */
+  int32_t num_admitted, num_swapped_in, num_preempted_swap, num_preempted_recompute;
+  int32_t num_running, num_waiting, num_swapped;
+} pa_sched_out_t;
+
+pa_sched_t* pa_sched_create(pa_bm_t* bm, int32_t max_rows, int32_t max_blocks_per_seq,
+                            int32_t max_batched_tokens);
+void pa_sched_destroy(pa_sched_t* s);
+/* 1 <= prompt_tokens <= total_tokens; the request must fit the pool and the
+ * table width on its own. */
+pa_status_t pa_sched_submit(pa_sched_t* s, int64_t seq, int32_t prompt_tokens, int32_t total_tokens);
+pa_status_t pa_sched_step(pa_sched_t* s, pa_sched_out_t* out);
 
 #ifdef __cplusplus
 }

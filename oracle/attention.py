@@ -102,6 +102,16 @@ def copy_blocks(k_cache: np.ndarray, v_cache: np.ndarray, pairs: np.ndarray) -> 
         v_cache[dst] = v_cache[src]
 
 
+def swap_blocks(dst_k: np.ndarray, dst_v: np.ndarray, src_k: np.ndarray, src_v: np.ndarray, pairs) -> None:
+    """Copy block pairs[i][0] of the source pools into block pairs[i][1] of the
+    destination pools (a preempted request's blocks moving to CPU memory and
+    back: "PagedAttention: How vLLM Serves AI Like an Operating System",
+    section "vLLM Architecture")."""
+    for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):
+        dst_k[dst] = src_k[src]
+        dst_v[dst] = src_v[src]
+
+
 def gather_kv(k_cache, v_cache, table_row, ctx: int, dtype: str):
     """Contiguous fp64 K and V of one sequence, [Hkv, ctx, D] each.
 

@@ -31,6 +31,19 @@ Readings where the pages are silent:
   * a freed sequence releases its blocks in logical order;
   * every update is all-or-nothing: when the pool cannot supply the blocks an
     operation needs, it raises NoSpace and leaves the state untouched.
+
+Swap pool ([OS] "vLLM Architecture": a preempted request's blocks move to
+CPU memory).  Readings:
+  * the host pool is a second set of block ids with its own queue (ascending
+    at first) and reference counts;
+  * swapping a list of sequences out copies each distinct device block of
+    the list once, in list order and logical order; references held by the
+    listed sequences move to the host copy, a device block whose count drops
+    to zero is released; swapping in is the mirror image into fresh device
+    blocks;
+  * a swapped-out sequence keeps its length and cannot be appended to,
+    forked, used as a prefix or tabled until it is swapped back in; freeing
+    it releases its host blocks.
 """
 
 from collections import deque
@@ -56,7 +69,10 @@ class RefBlockManager:
             raise BadRequest("free_order must be a permutation of the pool")
         self.free = deque(order)
         self.ref = [0] * num_blocks
-        self.seqs = {}  # seq id -> {"blocks": [...], "n": tokens}
+        self.seqs = {}  # seq id -> {"blocks": [...], "n": tokens, "host": bool}
+        self.num_host_blocks = 0
+        self.host_free = deque()
+        self.host_ref = []
 
     # -- queries ---------------------------------------------------------
     def num_free(self) -> int:
@@ -85,6 +101,19 @@ class RefBlockManager:
         if self.ref[b] == 0:
             self.free.append(b)
 
+    def _on_host(self, seq) -> bool:
+        return bool(self.seqs[seq].get("host"))
+
+    def _take_host(self) -> int:
+        h = self.host_free.popleft()
+        self.host_ref[h] = 1
+        return h
+
+    def _drop_host(self, h: int) -> None:
+        self.host_ref[h] -= 1
+        if self.host_ref[h] == 0:
+            self.host_free.append(h)
+
     @staticmethod
     def _nblocks(n: int) -> int:
         return -(-n // BLOCK_SIZE)
@@ -99,8 +128,8 @@ class RefBlockManager:
         self.seqs[seq] = {"blocks": [self._take() for _ in range(need)], "n": num_tokens}
 
     def add_seq_with_prefix(self, seq, prefix_seq, prefix_tokens: int, tail_tokens: int) -> None:
-        if seq in self.seqs or prefix_seq not in self.seqs:
-            raise BadRequest("duplicate sequence or unknown prefix sequence")
+        if seq in self.seqs or prefix_seq not in self.seqs or self._on_host(prefix_seq):
+            raise BadRequest("duplicate sequence, or unknown or swapped-out prefix sequence")
         if prefix_tokens % BLOCK_SIZE or not 0 <= prefix_tokens <= self.seqs[prefix_seq]["n"] or tail_tokens < 0:
             raise BadRequest("a shared prefix is a whole number of blocks inside the prefix sequence")
         shared = self.seqs[prefix_seq]["blocks"][: prefix_tokens // BLOCK_SIZE]
@@ -113,8 +142,8 @@ class RefBlockManager:
         self.seqs[seq] = {"blocks": list(shared) + own, "n": prefix_tokens + tail_tokens}
 
     def fork(self, parent, child) -> None:
-        if parent not in self.seqs or child in self.seqs:
-            raise BadRequest("unknown parent or duplicate child")
+        if parent not in self.seqs or child in self.seqs or self._on_host(parent):
+            raise BadRequest("unknown or swapped-out parent, or duplicate child")
         blocks = list(self.seqs[parent]["blocks"])
         for b in blocks:
             self.ref[b] += 1
@@ -123,8 +152,12 @@ class RefBlockManager:
     def free_seq(self, seq) -> None:
         if seq not in self.seqs:
             raise BadRequest("unknown sequence")
-        for b in self.seqs.pop(seq)["blocks"]:
-            self._drop(b)
+        st = self.seqs.pop(seq)
+        for b in st["blocks"]:
+            if st.get("host"):
+                self._drop_host(b)
+            else:
+                self._drop(b)
 
     def append_tokens(self, seqs):
         """Append one token to each listed sequence, in list order.
@@ -135,11 +168,11 @@ class RefBlockManager:
         """
         seqs = [s for s in seqs]
         for s in seqs:
-            if s not in self.seqs:
-                raise BadRequest("unknown sequence")
+            if s not in self.seqs or self._on_host(s):
+                raise BadRequest("unknown or swapped-out sequence")
         # all-or-nothing: run the updates on a copy and commit on success
         saved = (deque(self.free), list(self.ref),
-                 {k: {"blocks": list(v["blocks"]), "n": v["n"]} for k, v in self.seqs.items()})
+                 {k: dict(v, blocks=list(v["blocks"])) for k, v in self.seqs.items()})
         try:
             slots, cows = [], []
             for s in seqs:
@@ -165,6 +198,82 @@ class RefBlockManager:
             self.free, self.ref, self.seqs = saved
             raise
 
+    # -- swap pool ---------------------------------------------------------
+    def set_host_pool(self, num_host_blocks: int) -> None:
+        if self.num_host_blocks or num_host_blocks < 0:
+            raise BadRequest("the host pool is set once, with a size >= 0")
+        self.num_host_blocks = int(num_host_blocks)
+        self.host_free = deque(range(num_host_blocks))
+        self.host_ref = [0] * num_host_blocks
+
+    def is_swapped(self, seq) -> bool:
+        return self._on_host(seq)
+
+    def num_free_host(self) -> int:
+        return len(self.host_free)
+
+    def host_refcount(self, block: int) -> int:
+        return self.host_ref[block]
+
+    def _check_swap_list(self, seqs, want_host: bool):
+        if len(set(seqs)) != len(seqs):
+            raise BadRequest("a sequence is listed twice")
+        for s in seqs:
+            if s not in self.seqs or self._on_host(s) != want_host:
+                raise BadRequest("unknown sequence or wrong residence")
+
+    def swap_out(self, seqs):
+        """Move the listed sequences' blocks to the host pool.
+
+        Returns the (device block, host block) copies, one per distinct device
+        block, in list order and logical order.
+        """
+        seqs = list(seqs)
+        self._check_swap_list(seqs, False)
+        distinct = {b for s in seqs for b in self.seqs[s]["blocks"]}
+        if len(distinct) > len(self.host_free):
+            raise NoSpace()
+        where, pairs = {}, []
+        for s in seqs:
+            st = self.seqs[s]
+            moved = []
+            for b in st["blocks"]:
+                if b in where:
+                    self.host_ref[where[b]] += 1
+                else:
+                    where[b] = self._take_host()
+                    pairs.append((b, where[b]))
+                self._drop(b)
+                moved.append(where[b])
+            st["blocks"], st["host"] = moved, True
+        return pairs
+
+    def swap_in(self, seqs):
+        """Bring swapped-out sequences back into fresh device blocks.
+
+        Returns the (host block, device block) copies, one per distinct host
+        block, in list order and logical order.
+        """
+        seqs = list(seqs)
+        self._check_swap_list(seqs, True)
+        distinct = {h for s in seqs for h in self.seqs[s]["blocks"]}
+        if len(distinct) > len(self.free):
+            raise NoSpace()
+        where, pairs = {}, []
+        for s in seqs:
+            st = self.seqs[s]
+            moved = []
+            for h in st["blocks"]:
+                if h in where:
+                    self.ref[where[h]] += 1
+                else:
+                    where[h] = self._take()
+                    pairs.append((h, where[h]))
+                self._drop_host(h)
+                moved.append(where[h])
+            st["blocks"], st["host"] = moved, False
+        return pairs
+
     def append_token(self, seq):
         slots, cows = self.append_tokens([seq])
         return slots[0], (cows[0] if cows else (-1, -1))
@@ -173,8 +282,8 @@ class RefBlockManager:
         """Rows of logical -> physical ids (padded with ``pad``) and context lengths."""
         table, ctx = [], []
         for s in seqs:
-            if s not in self.seqs:
-                raise BadRequest("unknown sequence")
+            if s not in self.seqs or self._on_host(s):
+                raise BadRequest("unknown or swapped-out sequence")
             blocks = self.seqs[s]["blocks"]
             if len(blocks) > max_blocks:
                 raise BadRequest("table too narrow")

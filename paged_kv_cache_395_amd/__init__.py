@@ -8,10 +8,11 @@ loads the library and raises if it has not been built.
 from . import _lib
 from ._lib import NoSpace, PAError, UnknownSequence  # noqa: F401
 from .block_manager import BlockManager  # noqa: F401
+from .scheduler import Scheduler  # noqa: F401
 
 _lib.load()
 
-__all__ = ["BlockManager", "PAError", "NoSpace", "UnknownSequence", "ops"]
+__all__ = ["BlockManager", "Scheduler", "PAError", "NoSpace", "UnknownSequence", "ops"]
 
 
 def __getattr__(name):

@@ -46,6 +46,9 @@ SIGNATURES = {
     "pa_append_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                                       _i32, _i64, ctypes.c_int, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, ctypes.c_int, _vp]),
+    "pa_swap_blocks": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                      _vp]),
+    "pa_patch_tables": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp]),
     "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -72,7 +75,31 @@ SIGNATURES = {
     "pa_bm_usage": (ctypes.c_double, [_vp]),
     "pa_bm_num_tokens": (_i32, [_vp, _i64]),
     "pa_bm_free_list": (_i64, [_vp, _vp, _i64]),
+    "pa_bm_set_host_pool": (ctypes.c_int, [_vp, _i64]),
+    "pa_bm_swap_out": (ctypes.c_int, [_vp, _vp, _i32, _vp, _pi32]),
+    "pa_bm_swap_in": (ctypes.c_int, [_vp, _vp, _i32, _vp, _pi32]),
+    "pa_bm_is_swapped": (_i32, [_vp, _i64]),
+    "pa_bm_num_free_host": (_i64, [_vp]),
+    "pa_bm_host_refcount": (_i32, [_vp, _i64]),
+    "pa_sched_create": (_vp, [_vp, _i32, _i32, _i32]),
+    "pa_sched_destroy": (None, [_vp]),
+    "pa_sched_submit": (ctypes.c_int, [_vp, _i64, _i32, _i32]),
+    "pa_sched_step": (ctypes.c_int, [_vp, _vp]),
 }
+
+
+
+class SchedOut(ctypes.Structure):
+    """pa_sched_out_t."""
+    _fields_ = [("num_tokens", _i32), ("slots", _pi64), ("token_rows", _pi32), ("token_positions", _pi32),
+                ("num_rows", _i32), ("context_lens", _pi32), ("row_seq", _pi64),
+                ("num_swap_out", _i32), ("swap_out_pairs", _pi64), ("num_swap_in", _i32), ("swap_in_pairs", _pi64),
+                ("num_cow", _i32), ("cow_pairs", _pi64), ("num_patches", _i32), ("table_patches", _pi32),
+                ("num_finished", _i32), ("finished", _pi64),
+                ("num_admitted", _i32), ("num_swapped_in", _i32), ("num_preempted_swap", _i32),
+                ("num_preempted_recompute", _i32), ("num_running", _i32), ("num_waiting", _i32),
+                ("num_swapped", _i32)]
+
 
 _lock = threading.Lock()
 _lib = None

@@ -73,6 +73,38 @@ class BlockManager:
         slots, cow = self.append_tokens([seq])
         return int(slots[0]), (tuple(int(x) for x in cow[0]) if len(cow) else (-1, -1))
 
+    # -- swap pool -----------------------------------------------------------
+    def set_host_pool(self, num_host_blocks: int) -> None:
+        _lib.check(self._l.pa_bm_set_host_pool(self._h, int(num_host_blocks)))
+
+    def _swap(self, fn, seqs):
+        seqs = np.ascontiguousarray(seqs, dtype=np.int64)
+        total = sum(-(-max(self.num_tokens(int(s)), 0) // 16) for s in seqs)
+        pairs = np.empty((max(total, 1), 2), dtype=np.int64)
+        n = ctypes.c_int32(0)
+        _lib.check(fn(self._h, _ptr(seqs), seqs.shape[0], _ptr(pairs), ctypes.byref(n)))
+        return pairs[: n.value]
+
+    def swap_out(self, seqs):
+        """Move the sequences' blocks to the host pool; returns (device, host) copies int64 [k, 2]."""
+        return self._swap(self._l.pa_bm_swap_out, seqs)
+
+    def swap_in(self, seqs):
+        """Bring swapped-out sequences back into fresh blocks; returns (host, device) copies int64 [k, 2]."""
+        return self._swap(self._l.pa_bm_swap_in, seqs)
+
+    def is_swapped(self, seq: int) -> bool:
+        r = int(self._l.pa_bm_is_swapped(self._h, int(seq)))
+        if r < 0:
+            raise _lib.UnknownSequence(_lib.PA_ENOENT, f"unknown sequence {seq}")
+        return bool(r)
+
+    def num_free_host(self) -> int:
+        return int(self._l.pa_bm_num_free_host(self._h))
+
+    def host_refcount(self, block: int) -> int:
+        return int(self._l.pa_bm_host_refcount(self._h, int(block)))
+
     # -- queries -------------------------------------------------------------
     def block_table(self, seqs, max_blocks: int, pad: int = -1, table_out: np.ndarray = None,
                     ctx_out: np.ndarray = None):

@@ -241,9 +241,35 @@ pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, i
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !pairs) return fail(PA_EINVAL, "null pointer argument");
   const int64_t block_bytes = int64_t(num_kv_heads) * 16 * head_dim * elem_bytes(dtype);
-  return hip_status(launch_copy_blocks(k_cache, v_cache, pairs, num_pairs, block_bytes, num_blocks,
-                                       static_cast<hipStream_t>(stream)),
+  return hip_status(launch_copy_blocks(k_cache, v_cache, k_cache, v_cache, pairs, num_pairs, block_bytes, num_blocks,
+                                       num_blocks, static_cast<hipStream_t>(stream)),
                     "copy_blocks launch");
+}
+
+pa_status_t pa_swap_blocks(void* dst_k, void* dst_v, int64_t dst_blocks, const void* src_k, const void* src_v,
+                           int64_t src_blocks, const int64_t* pairs, int32_t num_pairs, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, pa_dtype_t dtype, void* stream) {
+  pa_status_t st = check_pool(num_kv_heads, head_dim, block_size, dst_blocks, dtype);
+  if (st != PA_OK) return st;
+  if (src_blocks <= 0) return fail(PA_EINVAL, "src_blocks must be positive");
+  if (num_pairs < 0) return fail(PA_EINVAL, "num_pairs must be >= 0");
+  if (num_pairs == 0) return PA_OK;
+  if (!dst_k || !dst_v || !src_k || !src_v || !pairs) return fail(PA_EINVAL, "null pointer argument");
+  if (src_k == dst_k || src_v == dst_v) return fail(PA_EINVAL, "source and destination pools must differ");
+  const int64_t block_bytes = int64_t(num_kv_heads) * 16 * head_dim * elem_bytes(dtype);
+  return hip_status(launch_copy_blocks(dst_k, dst_v, src_k, src_v, pairs, num_pairs, block_bytes, src_blocks,
+                                       dst_blocks, static_cast<hipStream_t>(stream)),
+                    "swap_blocks launch");
+}
+
+pa_status_t pa_patch_tables(int32_t* block_tables, int32_t max_blocks_per_seq, int32_t num_seqs,
+                            const int32_t* patches, int32_t num_patches, void* stream) {
+  if (num_patches < 0 || num_seqs < 0 || max_blocks_per_seq <= 0) return fail(PA_EINVAL, "bad sizes");
+  if (num_patches == 0) return PA_OK;
+  if (!block_tables || !patches) return fail(PA_EINVAL, "null pointer argument");
+  return hip_status(launch_patch_tables(block_tables, max_blocks_per_seq, num_seqs, patches, num_patches,
+                                        static_cast<hipStream_t>(stream)),
+                    "patch_tables launch");
 }
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,

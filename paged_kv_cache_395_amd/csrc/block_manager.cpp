@@ -11,47 +11,89 @@
 // Interactive Visualization" (Page Table Visualization): a finished
 // sequence's pages return to the pool at once.
 
-#include <stdint.h>
+#include "bm_internal.h"
 
-#include <deque>
-#include <new>
-#include <unordered_map>
-#include <vector>
-
-#include "pa_internal.h"
-
-namespace {
-
-constexpr int32_t kBS = 16;
-
-struct Seq {
-  std::vector<int32_t> blocks;
-  int32_t tokens = 0;
-};
-
-}  // namespace
-
-struct pa_bm {
-  int64_t num_blocks = 0;
-  std::vector<int32_t> ref;
-  std::deque<int32_t> free_q;  // head = next block handed out, tail = most recently released
-  std::unordered_map<int64_t, Seq> seqs;
-
-  int32_t take() {
-    const int32_t b = free_q.front();
-    free_q.pop_front();
-    ref[b] = 1;
-    return b;
-  }
-  void drop(int32_t b) {
-    if (--ref[b] == 0) free_q.push_back(b);
-  }
-};
+#include <unordered_set>
 
 using pa::fail;
 
+namespace pa {
+
+int64_t append_need(const pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* cows) {
+  // Decide, without changing anything, how many blocks a batch of appends
+  // takes and how many of them are copy-on-write.  Per sequence track the
+  // token count and whether its last block is already private; per shared
+  // block track its count as earlier writers in the batch leave it.
+  struct SimSeq {
+    int32_t tokens;
+    bool last_private;
+  };
+  std::unordered_map<int64_t, SimSeq> sim;
+  std::unordered_map<int32_t, int32_t> sim_ref;
+  int64_t need = 0, nc = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return -fail(PA_ENOENT, "unknown sequence %lld", (long long)seqs[i]);
+    if (it->second.swapped) return -fail(PA_EINVAL, "sequence %lld is swapped out", (long long)seqs[i]);
+    auto si = sim.find(seqs[i]);
+    SimSeq st = si == sim.end() ? SimSeq{it->second.tokens, false} : si->second;
+    if (st.tokens == INT32_MAX) return -fail(PA_EINVAL, "sequence too long");
+    if (st.tokens % kBlockTokensHost == 0) {
+      ++need;
+      st.last_private = true;
+    } else if (!st.last_private) {
+      const int32_t last = it->second.blocks.back();
+      auto ri = sim_ref.find(last);
+      const int32_t r = ri == sim_ref.end() ? bm->ref[size_t(last)] : ri->second;
+      if (r > 1) {
+        ++need;
+        ++nc;
+        sim_ref[last] = r - 1;
+      }
+      st.last_private = true;
+    }
+    st.tokens += 1;
+    sim[seqs[i]] = st;
+  }
+  if (cows) *cows = nc;
+  return need;
+}
+
+}  // namespace pa
+
 namespace {
+
+constexpr int32_t kBS = pa::kBlockTokensHost;
+
 int64_t blocks_for(int64_t tokens) { return (tokens + kBS - 1) / kBS; }
+
+// Validate a list of sequences for a swap: all known, none listed twice,
+// each in the expected residence.
+pa_status_t check_swap_list(const pa_bm* bm, const int64_t* seqs, int32_t n, bool want_swapped, int64_t* blocks) {
+  if (n < 0 || (n > 0 && !seqs)) return fail(PA_EINVAL, "bad arguments");
+  std::unordered_set<int64_t> seen;
+  int64_t total = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown sequence %lld", (long long)seqs[i]);
+    if (!seen.insert(seqs[i]).second) return fail(PA_EINVAL, "sequence %lld listed twice", (long long)seqs[i]);
+    if (it->second.swapped != want_swapped)
+      return fail(PA_EINVAL, "sequence %lld is %s", (long long)seqs[i],
+                  want_swapped ? "not swapped out" : "already swapped out");
+    total += int64_t(it->second.blocks.size());
+  }
+  *blocks = total;
+  return PA_OK;
+}
+
+// Distinct blocks among the listed sequences' block lists.
+int64_t distinct_blocks(const pa_bm* bm, const int64_t* seqs, int32_t n) {
+  std::unordered_set<int32_t> d;
+  for (int32_t i = 0; i < n; ++i)
+    for (int32_t b : bm->seqs.find(seqs[i])->second.blocks) d.insert(b);
+  return int64_t(d.size());
+}
+
 }  // namespace
 
 extern "C" {
@@ -109,6 +151,7 @@ pa_status_t pa_bm_add_seq_with_prefix(pa_bm_t* bm, int64_t seq, int64_t prefix_s
   if (bm->seqs.count(seq)) return fail(PA_EINVAL, "sequence %lld already exists", (long long)seq);
   auto it = bm->seqs.find(prefix_seq);
   if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown prefix sequence %lld", (long long)prefix_seq);
+  if (it->second.swapped) return fail(PA_EINVAL, "prefix sequence %lld is swapped out", (long long)prefix_seq);
   if (prefix_tokens < 0 || prefix_tokens % kBS != 0 || prefix_tokens > it->second.tokens || tail_tokens < 0)
     return fail(PA_EINVAL, "a shared prefix is a whole number of blocks inside the prefix sequence");
   const int64_t need = blocks_for(tail_tokens);
@@ -128,6 +171,7 @@ pa_status_t pa_bm_fork(pa_bm_t* bm, int64_t parent, int64_t child) {
   if (!bm) return fail(PA_EINVAL, "null block manager");
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown parent %lld", (long long)parent);
+  if (it->second.swapped) return fail(PA_EINVAL, "parent %lld is swapped out", (long long)parent);
   if (bm->seqs.count(child)) return fail(PA_EINVAL, "sequence %lld already exists", (long long)child);
   Seq s = it->second;
   for (int32_t b : s.blocks) ++bm->ref[size_t(b)];
@@ -139,7 +183,11 @@ pa_status_t pa_bm_free_seq(pa_bm_t* bm, int64_t seq) {
   if (!bm) return fail(PA_EINVAL, "null block manager");
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown sequence %lld", (long long)seq);
-  for (int32_t b : it->second.blocks) bm->drop(b);
+  if (it->second.swapped) {
+    for (int32_t h : it->second.blocks) bm->drop_host(h);
+  } else {
+    for (int32_t b : it->second.blocks) bm->drop(b);
+  }
   bm->seqs.erase(it);
   return PA_OK;
 }
@@ -149,40 +197,9 @@ pa_status_t pa_bm_append_tokens(pa_bm_t* bm, const int64_t* seqs, int32_t n, int
   if (!bm) return fail(PA_EINVAL, "null block manager");
   if (n < 0 || (n > 0 && (!seqs || !slots))) return fail(PA_EINVAL, "bad arguments");
   if (num_cow) *num_cow = 0;
-  // Pass 1: decide, without changing anything, how many blocks the batch
-  // takes and whether any copy-on-write happens.  Per sequence track the
-  // token count and whether its last block is already private; per shared
-  // block track its count as earlier writers in the batch leave it.
-  struct SimSeq {
-    int32_t tokens;
-    bool last_private;
-  };
-  std::unordered_map<int64_t, SimSeq> sim;
-  std::unordered_map<int32_t, int32_t> sim_ref;
-  int64_t need = 0, cows = 0;
-  for (int32_t i = 0; i < n; ++i) {
-    auto it = bm->seqs.find(seqs[i]);
-    if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown sequence %lld", (long long)seqs[i]);
-    auto si = sim.find(seqs[i]);
-    SimSeq st = si == sim.end() ? SimSeq{it->second.tokens, false} : si->second;
-    if (st.tokens == INT32_MAX) return fail(PA_EINVAL, "sequence too long");
-    if (st.tokens % kBS == 0) {
-      ++need;
-      st.last_private = true;
-    } else if (!st.last_private) {
-      const int32_t last = it->second.blocks.back();
-      auto ri = sim_ref.find(last);
-      const int32_t r = ri == sim_ref.end() ? bm->ref[size_t(last)] : ri->second;
-      if (r > 1) {
-        ++need;
-        ++cows;
-        sim_ref[last] = r - 1;
-      }
-      st.last_private = true;
-    }
-    st.tokens += 1;
-    sim[seqs[i]] = st;
-  }
+  int64_t cows = 0;
+  const int64_t need = pa::append_need(bm, seqs, n, &cows);
+  if (need < 0) return pa_status_t(-need);
   if (need > int64_t(bm->free_q.size()))
     return fail(PA_ENOSPC, "need %lld blocks, %zu free", (long long)need, bm->free_q.size());
   if (cows > 0 && !cow_pairs) return fail(PA_EINVAL, "copy-on-write needed but cow_pairs is NULL");
@@ -218,6 +235,7 @@ pa_status_t pa_bm_block_table(const pa_bm_t* bm, const int64_t* seqs, int32_t n,
   for (int32_t i = 0; i < n; ++i) {
     auto it = bm->seqs.find(seqs[i]);
     if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown sequence %lld", (long long)seqs[i]);
+    if (it->second.swapped) return fail(PA_EINVAL, "sequence %lld is swapped out", (long long)seqs[i]);
     if (int64_t(it->second.blocks.size()) > max_blocks)
       return fail(PA_EINVAL, "sequence %lld holds %zu blocks > max_blocks %d", (long long)seqs[i],
                   it->second.blocks.size(), max_blocks);
@@ -231,6 +249,101 @@ pa_status_t pa_bm_block_table(const pa_bm_t* bm, const int64_t* seqs, int32_t n,
     context_lens[i] = s.tokens;
   }
   return PA_OK;
+}
+
+pa_status_t pa_bm_set_host_pool(pa_bm_t* bm, int64_t num_host_blocks) {
+  if (!bm) return fail(PA_EINVAL, "null block manager");
+  if (num_host_blocks < 0 || num_host_blocks > INT32_MAX) return fail(PA_EINVAL, "num_host_blocks out of range");
+  if (bm->num_host_blocks != 0) return fail(PA_EINVAL, "the host pool is already set");
+  bm->num_host_blocks = num_host_blocks;
+  bm->host_ref.assign(size_t(num_host_blocks), 0);
+  for (int64_t i = 0; i < num_host_blocks; ++i) bm->host_free.push_back(int32_t(i));
+  return PA_OK;
+}
+
+pa_status_t pa_bm_swap_out(pa_bm_t* bm, const int64_t* seqs, int32_t n, int64_t* pairs, int32_t* num_pairs) {
+  if (!bm) return fail(PA_EINVAL, "null block manager");
+  if (num_pairs) *num_pairs = 0;
+  int64_t total = 0;
+  pa_status_t st = check_swap_list(bm, seqs, n, false, &total);
+  if (st != PA_OK) return st;
+  if (total > 0 && !pairs) return fail(PA_EINVAL, "pairs is NULL");
+  const int64_t need = distinct_blocks(bm, seqs, n);
+  if (need > int64_t(bm->host_free.size()))
+    return fail(PA_ENOSPC, "need %lld host blocks, %zu free", (long long)need, bm->host_free.size());
+  std::unordered_map<int32_t, int32_t> moved;  // device block -> host block, within this call
+  int32_t np = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    Seq& s = bm->seqs.find(seqs[i])->second;
+    for (int32_t& b : s.blocks) {
+      auto mi = moved.find(b);
+      int32_t h;
+      if (mi == moved.end()) {
+        h = bm->take_host();
+        moved.emplace(b, h);
+        pairs[2 * np] = b;
+        pairs[2 * np + 1] = h;
+        ++np;
+      } else {
+        h = mi->second;
+        ++bm->host_ref[size_t(h)];
+      }
+      bm->drop(b);
+      b = h;
+    }
+    s.swapped = true;
+  }
+  if (num_pairs) *num_pairs = np;
+  return PA_OK;
+}
+
+pa_status_t pa_bm_swap_in(pa_bm_t* bm, const int64_t* seqs, int32_t n, int64_t* pairs, int32_t* num_pairs) {
+  if (!bm) return fail(PA_EINVAL, "null block manager");
+  if (num_pairs) *num_pairs = 0;
+  int64_t total = 0;
+  pa_status_t st = check_swap_list(bm, seqs, n, true, &total);
+  if (st != PA_OK) return st;
+  if (total > 0 && !pairs) return fail(PA_EINVAL, "pairs is NULL");
+  const int64_t need = distinct_blocks(bm, seqs, n);
+  if (need > int64_t(bm->free_q.size()))
+    return fail(PA_ENOSPC, "need %lld blocks, %zu free", (long long)need, bm->free_q.size());
+  std::unordered_map<int32_t, int32_t> moved;  // host block -> device block, within this call
+  int32_t np = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    Seq& s = bm->seqs.find(seqs[i])->second;
+    for (int32_t& h : s.blocks) {
+      auto mi = moved.find(h);
+      int32_t b;
+      if (mi == moved.end()) {
+        b = bm->take();
+        moved.emplace(h, b);
+        pairs[2 * np] = h;
+        pairs[2 * np + 1] = b;
+        ++np;
+      } else {
+        b = mi->second;
+        ++bm->ref[size_t(b)];
+      }
+      bm->drop_host(h);
+      h = b;
+    }
+    s.swapped = false;
+  }
+  if (num_pairs) *num_pairs = np;
+  return PA_OK;
+}
+
+int32_t pa_bm_is_swapped(const pa_bm_t* bm, int64_t seq) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? -1 : int32_t(it->second.swapped);
+}
+
+int64_t pa_bm_num_free_host(const pa_bm_t* bm) { return bm ? int64_t(bm->host_free.size()) : -1; }
+
+int32_t pa_bm_host_refcount(const pa_bm_t* bm, int64_t block) {
+  if (!bm || block < 0 || block >= bm->num_host_blocks) return -1;
+  return bm->host_ref[size_t(block)];
 }
 
 int64_t pa_bm_num_free(const pa_bm_t* bm) { return bm ? int64_t(bm->free_q.size()) : -1; }

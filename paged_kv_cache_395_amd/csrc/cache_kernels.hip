@@ -103,18 +103,33 @@ append_step_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __
 }
 
 // Grid (chunks of one block, pairs, 2): z = 0 copies K, z = 1 copies V; each
-// thread moves 16 bytes.
+// thread moves 16 bytes of block pairs[i][0] of the source pools into block
+// pairs[i][1] of the destination pools.  Copy-on-write passes one pool as
+// both; a swap passes the device pools and pinned host pools (either way).
 __global__ void __launch_bounds__(256)
-copy_blocks_kernel(char* __restrict__ kc, char* __restrict__ vc, const int64_t* __restrict__ pairs,
-                   int64_t block_bytes, int64_t num_blocks) {
-  char* base = blockIdx.z ? vc : kc;
+copy_blocks_kernel(char* __restrict__ dk, char* __restrict__ dv, const char* __restrict__ sk,
+                   const char* __restrict__ sv, const int64_t* __restrict__ pairs, int64_t block_bytes,
+                   int64_t src_blocks, int64_t dst_blocks) {
+  char* dst_base = blockIdx.z ? dv : dk;
+  const char* src_base = blockIdx.z ? sv : sk;
   const int64_t src = pairs[2 * int64_t(blockIdx.y)];
   const int64_t dst = pairs[2 * int64_t(blockIdx.y) + 1];
-  if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks) return;
+  if (src < 0 || src >= src_blocks || dst < 0 || dst >= dst_blocks) return;
   const int64_t off = (int64_t(blockIdx.x) * blockDim.x + threadIdx.x) * 16;
   if (off >= block_bytes) return;
-  *reinterpret_cast<u32x4_t*>(base + dst * block_bytes + off) =
-      *reinterpret_cast<const u32x4_t*>(base + src * block_bytes + off);
+  *reinterpret_cast<u32x4_t*>(dst_base + dst * block_bytes + off) =
+      *reinterpret_cast<const u32x4_t*>(src_base + src * block_bytes + off);
+}
+
+// One thread per patch (row, logical block, physical block).
+__global__ void __launch_bounds__(256)
+patch_tables_kernel(int32_t* __restrict__ tables, int32_t max_blocks, int32_t num_rows,
+                    const int32_t* __restrict__ patches, int32_t num_patches) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= num_patches) return;
+  const int32_t row = patches[3 * i], idx = patches[3 * i + 1], blk = patches[3 * i + 2];
+  if (row < 0 || row >= num_rows || idx < 0 || idx >= max_blocks) return;
+  tables[int64_t(row) * max_blocks + idx] = blk;
 }
 
 }  // namespace
@@ -159,18 +174,28 @@ hipError_t launch_append_step(const AppendStepArgs& a) {
   return hipGetLastError();
 }
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t num_pairs,
-                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream) {
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int64_t* pairs,
+                              int32_t num_pairs, int64_t block_bytes, int64_t src_blocks, int64_t dst_blocks,
+                              hipStream_t stream) {
   const unsigned chunks = unsigned((block_bytes / 16 + 255) / 256);
   for (int32_t first = 0; first < num_pairs; first += 65535) {
     const int32_t n = num_pairs - first < 65535 ? num_pairs - first : 65535;
     hipLaunchKernelGGL(copy_blocks_kernel, dim3(chunks, unsigned(n), 2), dim3(256), 0, stream,
-                       static_cast<char*>(k_cache), static_cast<char*>(v_cache), pairs + 2 * int64_t(first),
-                       block_bytes, num_blocks);
+                       static_cast<char*>(dst_k), static_cast<char*>(dst_v), static_cast<const char*>(src_k),
+                       static_cast<const char*>(src_v), pairs + 2 * int64_t(first), block_bytes, src_blocks,
+                       dst_blocks);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_patch_tables(int32_t* tables, int32_t max_blocks, int32_t num_rows, const int32_t* patches,
+                               int32_t num_patches, hipStream_t stream) {
+  if (num_patches == 0) return hipSuccess;
+  hipLaunchKernelGGL(patch_tables_kernel, dim3(unsigned((num_patches + 255) / 256)), dim3(256), 0, stream, tables,
+                     max_blocks, num_rows, patches, num_patches);
+  return hipGetLastError();
 }
 
 }  // namespace pa

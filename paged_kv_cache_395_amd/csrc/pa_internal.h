@@ -84,8 +84,11 @@ struct AppendStepArgs {
 
 hipError_t launch_append_step(const AppendStepArgs& a);
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t num_pairs,
-                              int64_t block_bytes, int64_t num_blocks, hipStream_t stream);
+hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int64_t* pairs,
+                              int32_t num_pairs, int64_t block_bytes, int64_t src_blocks, int64_t dst_blocks,
+                              hipStream_t stream);
+hipError_t launch_patch_tables(int32_t* tables, int32_t max_blocks, int32_t num_rows, const int32_t* patches,
+                               int32_t num_patches, hipStream_t stream);
 
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t workgroups, hipStream_t stream);
 

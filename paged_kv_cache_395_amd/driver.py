@@ -1,0 +1,150 @@
+"""Continuous-batching attention driver: the native scheduler's steps run on
+the device kernels over fixed buffers.
+
+Each step has a host half (``schedule``: the scheduler picks the batch,
+allocates slots, preempts and brings back requests) and a device half
+(``launch``, all on one stream): swap-out copies into the pinned host pool,
+swap-in copies back, copy-on-write, table patches, the cache write that also
+patches the device-resident tables and lengths, then decode over every batch
+row.  Between the two halves the caller fills ``key[:T]``, ``value[:T]``
+(the step's new K/V rows, in the order of ``Step.slots``) and ``q`` (one
+query per row).  Every computation runs in libpa's kernels; this module only
+stages metadata and marshals arguments.
+
+Pages: "PagedAttention: How vLLM Serves AI Like an Operating System",
+sections "Continuous Batching: The Other Half" and "vLLM Architecture"; the
+scheduling rules are the ones include/pa.h documents for pa_sched_step.
+"""
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+from .block_manager import BlockManager
+from .ops import BLOCK_SIZE, _code, _p
+from .scheduler import Scheduler
+
+_TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+class Driver:
+    def __init__(self, num_blocks, num_host_blocks, num_q_heads, num_kv_heads, head_dim, dtype, max_rows,
+                 max_blocks_per_seq, max_batched_tokens, scale, free_order=None, device="cuda", ring=4,
+                 partition_size=0):
+        self._l = _lib.load()
+        self.dtype = dtype
+        tdt = _TORCH[dtype]
+        dev = torch.device(device)
+        self.NB, self.NH = int(num_blocks), int(num_host_blocks)
+        self.Hq, self.Hkv, self.D = num_q_heads, num_kv_heads, head_dim
+        self.rows, self.maxB = int(max_rows), int(max_blocks_per_seq)
+        self.scale = float(scale)
+        self.partition = int(partition_size)
+        self.bm = BlockManager(num_blocks, free_order=free_order)
+        self.bm.set_host_pool(num_host_blocks)
+        self.sched = Scheduler(self.bm, max_rows, max_blocks_per_seq, max_batched_tokens)
+        tile = BLOCK_SIZE * head_dim
+        self.k_pool = torch.zeros((num_blocks, num_kv_heads, tile), dtype=tdt, device=dev)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        nh = max(self.NH, 1)
+        self.k_host = torch.zeros((nh, num_kv_heads, tile), dtype=tdt).pin_memory()
+        self.v_host = torch.zeros_like(self.k_host).pin_memory()
+        # tables and lengths stay on the device; unused entries point outside the pool
+        self.table = torch.full((max_rows, max_blocks_per_seq), num_blocks, dtype=torch.int32, device=dev)
+        self.ctx = torch.zeros(max_rows, dtype=torch.int32, device=dev)
+        # the first admission of a step may exceed the token budget by one whole request
+        self.cap = max_rows + max_batched_tokens + max_blocks_per_seq * BLOCK_SIZE
+        self.key = torch.zeros((self.cap, num_kv_heads, head_dim), dtype=tdt, device=dev)
+        self.value = torch.zeros_like(self.key)
+        self.q = torch.zeros((max_rows, num_q_heads, head_dim), dtype=tdt, device=dev)
+        self.out = torch.zeros((max_rows, num_q_heads, head_dim), dtype=torch.float32, device=dev)
+        max_ctx = max_blocks_per_seq * BLOCK_SIZE
+        ws = max(int(self._l.pa_decode_workspace_bytes(max_rows, num_q_heads, num_kv_heads, head_dim, c,
+                                                       self.partition)) for c in range(1, max_ctx + 1))
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream(dev)
+        self._s = ctypes.c_void_p(self.stream.cuda_stream)
+        # pinned staging, one set per in-flight step
+        pair_cap = 2 * max(num_blocks, nh)
+        self._ring = []
+        for _ in range(ring):
+            self._ring.append({
+                "slots": torch.empty(self.cap, dtype=torch.int64).pin_memory(),
+                "rows": torch.empty(self.cap, dtype=torch.int32).pin_memory(),
+                "pos": torch.empty(self.cap, dtype=torch.int32).pin_memory(),
+                "ctx": torch.empty(max_rows, dtype=torch.int32).pin_memory(),
+                "out_pairs": torch.empty((pair_cap, 2), dtype=torch.int64).pin_memory(),
+                "in_pairs": torch.empty((pair_cap, 2), dtype=torch.int64).pin_memory(),
+                "cow": torch.empty((max_rows, 2), dtype=torch.int64).pin_memory(),
+                "patches": torch.empty((max_rows * max_blocks_per_seq, 3), dtype=torch.int32).pin_memory(),
+                "done": torch.cuda.Event(), "used": False,
+            })
+        self._i = 0
+        self._code = _code(self.k_pool)
+        self.steps = 0
+
+    # -- host half -------------------------------------------------------------
+    def submit(self, seq: int, prompt_tokens: int, total_tokens: int) -> None:
+        self.sched.submit(seq, prompt_tokens, total_tokens)
+
+    def schedule(self):
+        """Run the scheduler for one step and stage its metadata; returns the Step."""
+        st = self.sched.step()
+        T = len(st.slots)
+        if T > self.cap:
+            raise RuntimeError(f"step writes {T} tokens, more than the staging capacity {self.cap}")
+        r = self._ring[self._i % len(self._ring)]
+        if r["used"]:
+            r["done"].synchronize()  # the launch that last read this staging set has run
+        r["slots"].numpy()[:T] = st.slots
+        r["rows"].numpy()[:T] = st.token_rows
+        r["pos"].numpy()[:T] = st.token_positions
+        r["ctx"].numpy()[:] = st.context_lens
+        r["out_pairs"].numpy()[: len(st.swap_out)] = st.swap_out
+        r["in_pairs"].numpy()[: len(st.swap_in)] = st.swap_in
+        r["cow"].numpy()[: len(st.cow)] = st.cow
+        r["patches"].numpy()[: len(st.patches)] = st.patches
+        return st
+
+    # -- device half -----------------------------------------------------------
+    def launch(self, st, decode_events=None) -> None:
+        """Enqueue the step's device work on the driver's stream (``decode_events``:
+        an optional pair of events recorded around the decode launch)."""
+        L, s, code = self._l, self._s, self._code
+        r = self._ring[self._i % len(self._ring)]
+        Hkv, D, NB, NH = self.Hkv, self.D, self.NB, max(self.NH, 1)
+        if len(st.swap_out):
+            _lib.check(L.pa_swap_blocks(_p(self.k_host), _p(self.v_host), NH, _p(self.k_pool), _p(self.v_pool), NB,
+                                        _p(r["out_pairs"]), len(st.swap_out), Hkv, D, BLOCK_SIZE, code, s))
+        if len(st.swap_in):
+            _lib.check(L.pa_swap_blocks(_p(self.k_pool), _p(self.v_pool), NB, _p(self.k_host), _p(self.v_host), NH,
+                                        _p(r["in_pairs"]), len(st.swap_in), Hkv, D, BLOCK_SIZE, code, s))
+        if len(st.cow):
+            _lib.check(L.pa_copy_blocks(_p(self.k_pool), _p(self.v_pool), _p(r["cow"]), len(st.cow), Hkv, D,
+                                        BLOCK_SIZE, NB, code, s))
+        if len(st.patches):
+            _lib.check(L.pa_patch_tables(_p(self.table), self.maxB, self.rows, _p(r["patches"]), len(st.patches), s))
+        _lib.check(L.pa_append_step(_p(self.key), _p(self.value), _p(self.k_pool), _p(self.v_pool), _p(r["slots"]),
+                                    _p(r["rows"]), _p(r["pos"]), len(st.slots), _p(self.table), self.maxB,
+                                    _p(self.ctx), _p(r["ctx"]), self.rows, Hkv, D, BLOCK_SIZE, NB, code, s))
+        r["done"].record(self.stream)
+        r["used"] = True
+        self._i += 1
+        # with every row empty the kernel still runs and writes zero rows
+        max_ctx = max(int(st.context_lens.max()), 1)
+        if decode_events is not None:
+            decode_events[0].record(self.stream)
+        _lib.check(L.pa_decode(_p(self.out), _lib.PA_F32, _p(self.q), _p(self.k_pool), _p(self.v_pool),
+                               _p(self.table), self.maxB, _p(self.ctx), self.rows, self.Hq, Hkv, D, BLOCK_SIZE, NB,
+                               self.scale, max_ctx, self.partition, _p(self.workspace), self.workspace.numel(),
+                               code, s))
+        if decode_events is not None:
+            decode_events[1].record(self.stream)
+        self.steps += 1
+
+    def step(self):
+        st = self.schedule()
+        self.launch(st)
+        return st

@@ -118,6 +118,38 @@ def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
                                           NB, _code(k_cache), _stream(stream)))
 
 
+def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
+    """Copy block pairs[i, 0] of the source pools into block pairs[i, 1] of the
+    destination pools; one side may be pinned host memory (a swap)."""
+    for t in (dst_k, dst_v, src_k, src_v, pairs):
+        if not (t.is_cuda or t.is_pinned()):
+            raise ValueError("pools and pairs must live on the GPU or in pinned host memory")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    NBd, Hkv, D = _pool_dims(dst_k)
+    NBs, Hkv_s, D_s = _pool_dims(src_k)
+    if (Hkv_s, D_s) != (Hkv, D) or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
+        raise ValueError("both sides must be pools of the same geometry")
+    if not (dst_k.dtype == dst_v.dtype == src_k.dtype == src_v.dtype):
+        raise TypeError("the pools must share one dtype")
+    if pairs.dtype != torch.int64 or pairs.dim() != 2 or pairs.shape[1] != 2:
+        raise ValueError("pairs must be int64 [n, 2]")
+    _lib.check(_lib.load().pa_swap_blocks(_p(dst_k), _p(dst_v), NBd, _p(src_k), _p(src_v), NBs, _p(pairs),
+                                          pairs.shape[0], Hkv, D, BLOCK_SIZE, _code(dst_k), _stream(stream)))
+
+
+def patch_tables(block_tables, patches, stream=None) -> None:
+    """block_tables[row, idx] = block for each (row, idx, block) row of int32 ``patches``."""
+    _dev(block_tables)
+    _dev_or_pinned(patches)
+    if block_tables.dtype != torch.int32 or block_tables.dim() != 2:
+        raise ValueError("block_tables must be int32 [num_seqs, max_blocks]")
+    if patches.dtype != torch.int32 or patches.dim() != 2 or patches.shape[1] != 3:
+        raise ValueError("patches must be int32 [n, 3]")
+    _lib.check(_lib.load().pa_patch_tables(_p(block_tables), block_tables.shape[1], block_tables.shape[0],
+                                           _p(patches), patches.shape[0], _stream(stream)))
+
+
 def decode_partition_size(num_seqs: int, num_kv_heads: int, max_context_len: int, partition_size: int = 0) -> int:
     """Tokens per context partition decode uses for these sizes (0 = the library's choice)."""
     return int(_lib.load().pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len, partition_size))

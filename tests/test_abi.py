@@ -163,6 +163,40 @@ def test_append_step_rejects_bad_arguments():
                             _lib.PA_BF16, NULL) == _lib.PA_OK
 
 
+def test_swap_and_patch_reject_bad_arguments():
+    def swap(dst=1, src=2, nb_src=10, n=3, D=128, pairs=1):
+        return L.pa_swap_blocks(dst, dst, 10, src, src, nb_src, pairs, n, 8, D, 16, _lib.PA_BF16, NULL)
+    assert swap(D=96) == _lib.PA_EUNSUPPORTED
+    assert swap(nb_src=0) == _lib.PA_EINVAL
+    assert swap(n=-1) == _lib.PA_EINVAL
+    assert swap(pairs=None) == _lib.PA_EINVAL
+    assert swap(src=1) == _lib.PA_EINVAL          # the same pool on both sides
+    assert swap(n=0, pairs=None) == _lib.PA_OK
+    assert L.pa_patch_tables(1, 0, 4, 1, 2, NULL) == _lib.PA_EINVAL
+    assert L.pa_patch_tables(None, 4, 4, 1, 2, NULL) == _lib.PA_EINVAL
+    assert L.pa_patch_tables(None, 4, 4, None, 0, NULL) == _lib.PA_OK
+
+
+def test_scheduler_and_host_pool_reject_bad_arguments():
+    assert not L.pa_sched_create(None, 4, 8, 64)
+    bm = L.pa_bm_create(8, 16, None)
+    assert not L.pa_sched_create(bm, 0, 8, 64)
+    assert L.pa_bm_set_host_pool(bm, -1) == _lib.PA_EINVAL
+    assert L.pa_bm_set_host_pool(bm, 4) == _lib.PA_OK
+    assert L.pa_bm_set_host_pool(bm, 4) == _lib.PA_EINVAL   # set once
+    assert L.pa_bm_num_free_host(bm) == 4
+    assert L.pa_bm_is_swapped(bm, 123) == -1
+    s = L.pa_sched_create(bm, 2, 4, 64)
+    assert s
+    assert L.pa_sched_submit(s, 1, 0, 5) == _lib.PA_EINVAL
+    assert L.pa_sched_submit(s, 1, 6, 5) == _lib.PA_EINVAL
+    assert L.pa_sched_submit(s, 1, 1, 65) == _lib.PA_EINVAL  # 5 blocks > table width 4
+    assert L.pa_sched_submit(s, 1, 1, 64) == _lib.PA_OK
+    assert L.pa_sched_step(s, None) == _lib.PA_EINVAL
+    L.pa_sched_destroy(s)
+    L.pa_bm_destroy(bm)
+
+
 def test_prefill_rejects_bad_arguments():
     def call(**kw):
         a = dict(dtype=_lib.PA_BF16, C=16, max_ctx=64, maxb=4, Hq=8, Hkv=2, out_dtype=_lib.PA_F32)

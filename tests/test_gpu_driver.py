@@ -1,0 +1,146 @@
+"""Continuous batching with preemption on the GPU: swap copies, table
+patches and the driver's whole step against the oracle.
+
+The oracle side runs the oracle scheduler and block manager, moves blocks
+with plain numpy copies and computes attention in fp64 from its own tables;
+the device side runs the native scheduler, the copy / patch / cache-write
+kernels and paged decode.  Step outputs of the two schedulers are asserted
+identical first; decode rows and, at the end, both pools are compared.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as OA
+from oracle.block_manager import RefBlockManager
+from oracle.scheduler import RefScheduler
+from paged_kv_cache_395_amd import ops
+from paged_kv_cache_395_amd.driver import Driver
+from tests._gpu import assert_close, out_f64, say, to_dev, to_host
+from tests.test_scheduler import as_lists
+from workloads import to_storage
+from workloads.serving import kv_rows, query_rows, request_trace
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_swap_blocks_both_ways_is_bit_exact(dtype):
+    rng = np.random.default_rng(61)
+    NB, NH, Hkv, D = 50, 30, 4, 128
+    k = to_storage(rng.standard_normal((NB, Hkv, 16 * D), dtype=np.float32), dtype)
+    v = to_storage(rng.standard_normal((NB, Hkv, 16 * D), dtype=np.float32), dtype)
+    hk = to_storage(rng.standard_normal((NH, Hkv, 16 * D), dtype=np.float32), dtype)
+    hv = to_storage(rng.standard_normal((NH, Hkv, 16 * D), dtype=np.float32), dtype)
+    dk, dv = to_dev(k, dtype), to_dev(v, dtype)
+    pk, pv = to_dev(hk, dtype).cpu().pin_memory(), to_dev(hv, dtype).cpu().pin_memory()
+    out_pairs = np.stack([rng.permutation(NB)[:20], rng.permutation(NH)[:20]], axis=1).astype(np.int64)
+    in_pairs = np.stack([rng.permutation(NH)[:25], rng.permutation(NB)[:25]], axis=1).astype(np.int64)
+    ops.swap_blocks(pk, pv, dk, dv, torch.from_numpy(out_pairs).pin_memory())   # out, pairs in host memory
+    torch.cuda.synchronize()
+    OA.swap_blocks(hk, hv, k, v, out_pairs)
+    assert np.array_equal(to_host(pk, dtype).view(np.uint8), hk.view(np.uint8))
+    assert np.array_equal(to_host(pv, dtype).view(np.uint8), hv.view(np.uint8))
+    ops.swap_blocks(dk, dv, pk, pv, torch.from_numpy(in_pairs).cuda())          # in, pairs on the device
+    torch.cuda.synchronize()
+    OA.swap_blocks(k, v, hk, hv, in_pairs)
+    assert np.array_equal(to_host(dk, dtype).view(np.uint8), k.view(np.uint8))
+    assert np.array_equal(to_host(dv, dtype).view(np.uint8), v.view(np.uint8))
+
+
+def test_patch_tables_sets_exactly_the_listed_entries():
+    table = np.arange(5 * 7, dtype=np.int32).reshape(5, 7)
+    d = torch.from_numpy(table.copy()).cuda()
+    patches = np.array([[0, 0, 100], [4, 6, 101], [2, 3, 102], [5, 0, 103], [1, 7, 104], [-1, 2, 105]],
+                       dtype=np.int32)
+    ops.patch_tables(d, torch.from_numpy(patches).pin_memory())
+    table[0, 0], table[4, 6], table[2, 3] = 100, 101, 102   # the last three fall outside the table
+    assert np.array_equal(d.cpu().numpy(), table)
+
+
+class OracleSide:
+    def __init__(self, NB, NH, Hkv, D, dtype, rows, maxB, budget, free_order):
+        self.bm = RefBlockManager(NB, free_order=free_order)
+        self.bm.set_host_pool(NH)
+        self.sched = RefScheduler(self.bm, rows, maxB, budget)
+        z = to_storage(np.zeros((NB, Hkv, 16 * D), dtype=np.float32), dtype)
+        self.k, self.v = z.copy(), z.copy()
+        zh = to_storage(np.zeros((max(NH, 1), Hkv, 16 * D), dtype=np.float32), dtype)
+        self.hk, self.hv = zh.copy(), zh.copy()
+        self.maxB = maxB
+
+    def apply(self, st, key, value):
+        OA.swap_blocks(self.hk, self.hv, self.k, self.v, st["swap_out"])
+        OA.swap_blocks(self.k, self.v, self.hk, self.hv, st["swap_in"])
+        OA.copy_blocks(self.k, self.v, st["cow"])
+        OA.reshape_and_cache(self.k, self.v, key, value, np.asarray(st["slots"], dtype=np.int64))
+
+    def tables(self, row_seq):
+        table = np.zeros((len(row_seq), self.maxB), dtype=np.int32)
+        ctx = np.zeros(len(row_seq), dtype=np.int32)
+        for r, s in enumerate(row_seq):
+            if s >= 0:
+                t, c = self.bm.block_table([s], self.maxB, pad=0)
+                table[r], ctx[r] = t[0], c[0]
+        return table, ctx
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,host_blocks", [
+    ("bf16", 8, 2, 128, 24),
+    ("f16", 4, 4, 64, 3),      # host pool too small for most victims: recompute path
+    ("f32", 4, 4, 64, 24),
+], ids=["bf16_gqa_swap", "f16_recompute", "f32_swap"])
+def test_driver_matches_the_oracle_through_preemption(dtype, Hq, Hkv, D, host_blocks):
+    seed = 71
+    NB, rows, maxB, budget = 20, 5, 8, 48
+    reqs = request_trace(seed, 16, mean_gap=3.0, prompt_median=20, prompt_hi=60, output_median=30, output_hi=60)
+    reqs = [(a, i, p, min(t, maxB * 16)) for a, i, p, t in reqs]
+    order = np.random.default_rng(seed).permutation(NB).astype(np.int32)
+    scale = D ** -0.5
+    drv = Driver(NB, host_blocks, Hq, Hkv, D, dtype, rows, maxB, budget, scale, free_order=order)
+    ora = OracleSide(NB, host_blocks, Hkv, D, dtype, rows, maxB, budget, order)
+    say(f"[driver] {dtype} Hq={Hq} Hkv={Hkv} D={D} host_blocks={host_blocks} requests={len(reqs)}")
+    pending = list(reqs)
+    counts = {"swap_out": 0, "swap_in": 0, "recompute": 0, "steps": 0}
+    for step in range(2000):
+        while pending and pending[0][0] <= step:
+            _, i, p, t = pending.pop(0)
+            drv.submit(i, p, t)
+            ora.sched.submit(i, p, t)
+        st = drv.schedule()
+        ost = ora.sched.step()
+        assert as_lists(st) == as_lists(ost), f"step {step}: schedulers differ"
+        T = len(st.slots)
+        key = np.empty((T, Hkv, D), dtype=ora.k.dtype)
+        val = np.empty_like(key)
+        for seq in set(int(st.row_seq[r]) for r in st.token_rows):
+            idx = [j for j in range(T) if int(st.row_seq[st.token_rows[j]]) == seq]
+            k_, v_ = kv_rows(seed, seq, [int(st.token_positions[j]) for j in idx], Hkv, D, dtype)
+            key[idx], val[idx] = k_, v_
+        q = np.zeros((rows, Hq, D), dtype=ora.k.dtype)
+        for r, s in enumerate(st.row_seq):
+            if s >= 0:
+                q[r] = query_rows(seed, int(s), step, Hq, D, dtype)
+        if T:
+            drv.key[:T].copy_(to_dev(key, dtype))
+            drv.value[:T].copy_(to_dev(val, dtype))
+        drv.q.copy_(to_dev(q, dtype))
+        drv.launch(st)
+        ora.apply(ost, key, val)
+        table, ctx = ora.tables(list(ost["row_seq"]))
+        want = OA.decode(q, ora.k, ora.v, table, ctx, scale, dtype)
+        torch.cuda.synchronize()
+        assert_close(out_f64(drv.out), want, dtype, f"step {step}")
+        counts["swap_out"] += st.num_preempted_swap
+        counts["swap_in"] += st.num_swapped_in
+        counts["recompute"] += st.num_preempted_recompute
+        counts["steps"] += 1
+        if st.idle and not pending:
+            break
+    say(f"[driver] {counts}")
+    assert not pending and st.idle
+    assert counts["swap_out"] + counts["recompute"] > 0, "the trace is meant to preempt"
+    assert np.array_equal(to_host(drv.k_pool, dtype).view(np.uint8), ora.k.view(np.uint8))
+    assert np.array_equal(to_host(drv.v_pool, dtype).view(np.uint8), ora.v.view(np.uint8))
+    if host_blocks:
+        assert np.array_equal(to_host(drv.k_host, dtype).view(np.uint8), ora.hk.view(np.uint8))

@@ -13,8 +13,10 @@ import pytest
 import oracle.attention
 import oracle.block_manager
 import oracle.layout
+import oracle.scheduler
 from tests import test_oracle_attention as PA
 from tests import test_oracle_block_manager as PB
+from tests import test_scheduler as PS
 
 MUTATIONS = [
     # (module, function or Class.method, original text, planted mistake, pin, pin args)
@@ -60,6 +62,24 @@ MUTATIONS = [
      "shared = self.seqs[prefix_seq][\"blocks\"][: prefix_tokens // BLOCK_SIZE]",
      "shared = self.seqs[prefix_seq][\"blocks\"][: prefix_tokens // BLOCK_SIZE - 1]",
      PB.test_prefix_caching_example, ()),
+    (oracle.scheduler, "RefScheduler.step", "arrival, s = self.running.pop()", "arrival, s = self.running.pop(0)",
+     PS.test_hand_worked_swap_trace, ("oracle",)),
+    (oracle.scheduler, "RefScheduler.step", "if bm.num_tokens(s) >= r[\"total\"]:",
+     "if bm.num_tokens(s) > r[\"total\"]:", PS.test_oracle_replay_reads_back_every_token, (PS.CASES[0],)),
+    (oracle.scheduler, "RefScheduler.step", "out[\"patches\"].append((row, j, b))",
+     "out[\"patches\"].append((row, j + 1, b))", PS.test_oracle_replay_reads_back_every_token, (PS.CASES[0],)),
+    (oracle.scheduler, "RefScheduler.step", "if not self.swapped:", "if True:",
+     PS.test_oracle_replay_reads_back_every_token, (PS.CASES[0],)),
+    (oracle.scheduler, "RefScheduler.step", "grow = 1 if n % BLOCK_SIZE == 0 else 0", "grow = 0",
+     PS.test_oracle_replay_reads_back_every_token, (PS.CASES[4],)),
+    (oracle.scheduler, "RefScheduler._need", "if st[\"n\"] % BLOCK_SIZE == 0:", "if st[\"n\"] % BLOCK_SIZE == 1:",
+     PS.test_oracle_replay_reads_back_every_token, (PS.CASES[0],)),
+    (oracle.block_manager, "RefBlockManager.swap_out", "pairs.append((b, where[b]))",
+     "pairs.append((where[b], b))", PS.test_oracle_replay_reads_back_every_token, (PS.CASES[0],)),
+    (oracle.block_manager, "RefBlockManager.swap_in", "self._drop_host(h)", "pass",
+     PS.test_oracle_replay_reads_back_every_token, (PS.CASES[0],)),
+    (oracle.block_manager, "RefBlockManager.swap_out", "self.host_ref[where[b]] += 1", "pass",
+     PS.test_swap_round_trip_with_shared_blocks_matches_the_oracle, ()),
 ]
 
 
