@@ -121,7 +121,7 @@ SERVING_DESC = ("continuous batching: GQA 32/8 heads, head_dim 128, bf16, 256 ro
                 "4096 batched tokens per step")
 
 
-def serving_cpu_baseline(c, trace, steps: int, budget_s: float = 15.0):
+def serving_cpu_baseline(c, trace, steps: int, budget_s: float = 15.0, prefix: bool = False):
     """The oracle scheduler over the same trace, plus oracle fp64 decode of a
     bounded sample of rows at the last step, scaled to one whole step."""
     from threadpoolctl import threadpool_limits
@@ -132,6 +132,8 @@ def serving_cpu_baseline(c, trace, steps: int, budget_s: float = 15.0):
     from workloads import to_storage
 
     bm = RefBlockManager(c["num_blocks"])
+    if prefix:
+        bm.enable_prefix_cache()
     bm.set_host_pool(c["host_blocks"])
     sched = RefScheduler(bm, c["rows"], c["max_blocks"], c["budget"])
     pending = list(trace)
@@ -139,7 +141,10 @@ def serving_cpu_baseline(c, trace, steps: int, budget_s: float = 15.0):
     for step in range(steps):
         while pending and pending[0][0] <= step:
             _, i, p, t = pending.pop(0)
-            sched.submit(i, p, t)
+            if prefix:
+                sched.submit(i, len(p), t, p)
+            else:
+                sched.submit(i, p, t)
         st = sched.step()
     t_sched = (time.perf_counter() - t0) / steps
     # attention of a sample of rows over random pools of the real shape
@@ -172,22 +177,34 @@ def serving_cpu_baseline(c, trace, steps: int, budget_s: float = 15.0):
                       f"last step ({t_att:.1f} s), scaled to all rows; numpy, BLAS 1 thread"}
 
 
+SERVING_PREFIX = dict(SERVING, prompts=8, system_len=512, tail_median=128, tail_hi=1024)
+SERVING_PREFIX_DESC = ("continuous batching with automatic prefix caching: the serving_bf16 shapes, pool and "
+                       "arrivals, prompts = one of 8 shared 512-token system prompts + a lognormal tail "
+                       "(median 128, <= 1024), outputs median 256 (<= 1024); admission shares cached prompt blocks")
+
+
 def bench_serving(args) -> None:
     """Continuous batching through the native scheduler and the driver."""
     import torch
 
     from paged_kv_cache_395_amd import ops
     from paged_kv_cache_395_amd.driver import Driver
-    from workloads.serving import request_trace
+    from workloads.serving import prefix_requests, request_trace
 
-    c = dict(SERVING)
-    trace = request_trace(c["seed"], c["requests"], c["mean_gap"], c["prompt_median"], c["prompt_hi"],
-                          c["output_median"], c["output_hi"], lo=16)
-    trace = [(a, i, p, min(t, c["max_blocks"] * 16)) for a, i, p, t in trace]
+    prefix = args.workload == "serving_prefix_bf16"
+    c = dict(SERVING_PREFIX if prefix else SERVING)
+    if prefix:
+        trace = prefix_requests(c["seed"], c["requests"], c["prompts"], c["system_len"], c["tail_median"],
+                                c["tail_hi"], c["output_median"], c["output_hi"], c["mean_gap"])
+        trace = [(a, i, ids, min(t, c["max_blocks"] * 16)) for a, i, ids, t in trace]
+    else:
+        trace = request_trace(c["seed"], c["requests"], c["mean_gap"], c["prompt_median"], c["prompt_hi"],
+                              c["output_median"], c["output_hi"], lo=16)
+        trace = [(a, i, p, min(t, c["max_blocks"] * 16)) for a, i, p, t in trace]
     torch.cuda.set_device(0)
     Hq, Hkv, D = c["num_q_heads"], c["num_kv_heads"], c["head_dim"]
     drv = Driver(c["num_blocks"], c["host_blocks"], Hq, Hkv, D, c["dtype"], c["rows"], c["max_blocks"],
-                 c["budget"], D ** -0.5)
+                 c["budget"], D ** -0.5, prefix_cache=prefix)
     g = torch.Generator(device="cuda")
     g.manual_seed(c["seed"])
     for t in (drv.key, drv.value, drv.q, drv.k_pool, drv.v_pool):
@@ -195,14 +212,17 @@ def bench_serving(args) -> None:
     esize = ESIZE[c["dtype"]]
     block_bytes = Hkv * 16 * D * esize * 2
     pending = list(trace)
-    stats = {"decode_bytes": 0.0, "tokens": 0, "prompt_tokens": 0, "swap_blocks": 0, "swap_out": 0, "swap_in": 0, "recompute": 0,
+    stats = {"decode_bytes": 0.0, "tokens": 0, "prompt_tokens": 0, "cached_tokens": 0, "swap_blocks": 0, "swap_out": 0, "swap_in": 0, "recompute": 0,
              "admitted": 0, "finished": 0, "rows": 0}
     ev = []
 
     def one(step, timed):
         while pending and pending[0][0] <= step:
             _, i, p, t = pending.pop(0)
-            drv.submit(i, p, t)
+            if prefix:
+                drv.submit(i, len(p), t, p)
+            else:
+                drv.submit(i, p, t)
         st = drv.schedule()
         e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if timed else None
         drv.launch(st, decode_events=e)
@@ -213,6 +233,7 @@ def bench_serving(args) -> None:
             generated = st.num_running - st.num_admitted  # one token each; the rest are admitted prompts
             stats["tokens"] += generated
             stats["prompt_tokens"] += len(st.slots) - generated
+            stats["cached_tokens"] += st.num_cached_tokens
             stats["swap_blocks"] += len(st.swap_out) + len(st.swap_in)
             stats["swap_out"] += st.num_preempted_swap
             stats["swap_in"] += st.num_swapped_in
@@ -239,10 +260,12 @@ def bench_serving(args) -> None:
         "unit": "steps/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(elapsed / K * 1e3, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": c["dtype"], "data": "synthetic",
-        "config": {"workload": f"serving_bf16: {SERVING_DESC}", **{k: c[k] for k in ("rows", "num_blocks",
+        "config": {"workload": (f"serving_prefix_bf16: {SERVING_PREFIX_DESC}" if prefix
+                                else f"serving_bf16: {SERVING_DESC}"), **{k: c[k] for k in ("rows", "num_blocks",
                    "host_blocks", "budget", "num_q_heads", "num_kv_heads", "head_dim")}},
         "generated_tokens_per_s": round(stats["tokens"] / elapsed, 1),
         "prompt_tokens_written_per_s": round(stats["prompt_tokens"] / elapsed, 1),
+        "prompt_tokens_from_prefix_cache_per_s": round(stats["cached_tokens"] / elapsed, 1),
         "mean_running_rows": round(stats["rows"] / K, 1),
         "decode_kv_gbs_whole_step": round(stats["decode_bytes"] / elapsed / 1e9, 1),
         "swap": {"blocks": stats["swap_blocks"], "gb": round(stats["swap_blocks"] * block_bytes / 1e9, 3),
@@ -268,7 +291,7 @@ def bench_serving(args) -> None:
                             "host_to_device": round(n * block_bytes / (b.elapsed_time(d) * 1e-3) / 1e9, 2),
                             "blocks": n}
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = serving_cpu_baseline(c, trace, args.warmup + args.steps)
+        rec["cpu_baseline"] = serving_cpu_baseline(c, trace, args.warmup + args.steps, prefix=prefix)
     print(json.dumps(rec), flush=True)
 
 
@@ -412,7 +435,7 @@ def main():
                     help="untimed steps first (5; 150 for serving_bf16, which fills its batch meanwhile)")
     ap.add_argument("--workload", default="mha7b_f16",
                     choices=["tiny_f32", "mha7b_f16", "gqa8b_bf16", "shared_prefix_bf16", "longctx_bf16",
-                             "specdec_bf16", "serving_bf16"])
+                             "specdec_bf16", "serving_bf16", "serving_prefix_bf16"])
     ap.add_argument("--partition", type=int, default=0, help="tokens per context partition (0 = the library's choice)")
     ap.add_argument("--cold-iters", type=int, default=20, help="decode launches timed after a 1 GiB cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -428,7 +451,7 @@ def main():
     ap.add_argument("--prefill-pmc-dir")
     ap.add_argument("--prefill-grbm-dir")
     args = ap.parse_args()
-    serving = args.workload == "serving_bf16"
+    serving = args.workload in ("serving_bf16", "serving_prefix_bf16")
     if args.steps is None:
         args.steps = 200 if serving else 50
     if args.warmup is None:
@@ -443,7 +466,7 @@ def main():
                          "decode path is built and measured on a single GPU (run with --gpus 1).\n")
         sys.exit(2)
 
-    if args.workload == "serving_bf16":
+    if args.workload in ("serving_bf16", "serving_prefix_bf16"):
         bench_serving(args)
         return
 

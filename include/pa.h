@@ -354,6 +354,32 @@ int32_t pa_bm_num_tokens(const pa_bm_t* bm, int64_t seq);           /* -1: unkno
 int64_t pa_bm_free_list(const pa_bm_t* bm, int32_t* out, int64_t cap);
 
 /* ------------------------------------------------------------------------
+ * Automatic prefix caching ([OS] "Copy-on-Write: Sharing KV Cache", Prefix
+ * Caching; [NL] item 5, Prefix Caching): requests that start with the same
+ * tokens share the blocks of that prefix without naming each other.
+ * Turn it on once, before the first sequence.  pa_bm_add_seq_tokens adds a
+ * sequence from its token ids: each full 16-token block is identified by its
+ * whole prefix (a hash of the previous block's identity and its own 16 ids,
+ * confirmed against the stored ids); the leading run of blocks that are
+ * already cached is shared (count + 1), the rest are fresh, and fresh full
+ * blocks become cached.  *cached_tokens (a multiple of 16) tells the caller
+ * how many leading tokens are already in the cache: only tokens from there
+ * on need their K/V computed and written.  A cached block whose count drops
+ * to zero is not freed but kept, least recently released first in line for
+ * eviction; it can still be claimed by a later match, and allocation takes
+ * it (dropping its identity) only when the free queue is empty.
+ * pa_bm_num_free counts free plus evictable blocks; pa_bm_num_cached_free
+ * the evictable ones.  With caching on, pa_bm_free_seq releases a sequence's
+ * blocks deepest first, so a prefix is evicted from its end.  A new block
+ * whose prefix identity is already held by an evictable block takes the
+ * identity over; the old block goes to the free queue.
+ * ---------------------------------------------------------------------- */
+pa_status_t pa_bm_enable_prefix_cache(pa_bm_t* bm);
+pa_status_t pa_bm_add_seq_tokens(pa_bm_t* bm, int64_t seq, const int32_t* tokens, int32_t num_tokens,
+                                 int32_t* cached_tokens);
+int64_t pa_bm_num_cached_free(const pa_bm_t* bm);
+
+/* ------------------------------------------------------------------------
  * Swap pool.  A second pool of num_host_blocks blocks in CPU memory, with its
  * own ids, free queue (ascending at first) and reference counts, to which a
  * preempted request's blocks move ([OS] "vLLM Architecture").  Set once.
@@ -395,7 +421,8 @@ int32_t pa_bm_host_refcount(const pa_bm_t* bm, int64_t block);  /* -1: out of ra
  *   4. only when nothing is swapped out, waiting requests are admitted,
  *      earliest arrival first, while a row and their prompt's blocks are
  *      free and the step's token count stays within max_batched_tokens (the
- *      first admission of a step is always allowed); an admitted request's
+ *      first admission of a step is always allowed; the count includes
+ *      prompt tokens found in the prefix cache); an admitted request's
  *      prompt tokens are written this step;
  *   5. every request running before the admissions appends one token.
  * Priority is arrival (submit) order; a request keeps its row while it runs;
@@ -428,19 +455,31 @@ typedef struct {
   int32_t num_cow;
   const int64_t* cow_pairs;       /* [num_cow][2] (src, dst) device blocks     */
   int32_t num_patches;
-  const int32_t* table_patches;   /* [num_patches][3] (row, logical, physical) */
+  const int32_t* table_patches;   /* [num_patches][3] (row, logical, physical): swapped-in
+                                     requests, and cached prefix blocks of admitted ones */
   int32_t num_finished;
   const int64_t* finished;        /* requests retired at the start of the step */
   int32_t num_admitted, num_swapped_in, num_preempted_swap, num_preempted_recompute;
   int32_t num_running, num_waiting, num_swapped;
+  int32_t num_cached_tokens;      /* admitted prompt tokens found in the prefix cache (not written) */
 } pa_sched_out_t;
 
 pa_sched_t* pa_sched_create(pa_bm_t* bm, int32_t max_rows, int32_t max_blocks_per_seq,
                             int32_t max_batched_tokens);
 void pa_sched_destroy(pa_sched_t* s);
-/* 1 <= prompt_tokens <= total_tokens; the request must fit the pool and the
- * table width on its own. */
+/* seq >= 0; 1 <= prompt_tokens <= total_tokens; the request must fit the
+ * pool and the table width on its own. */
 pa_status_t pa_sched_submit(pa_sched_t* s, int64_t seq, int32_t prompt_tokens, int32_t total_tokens);
+/* The same with the prompt's token ids (prompt_ids[prompt_tokens], copied),
+ * for a block manager with prefix caching on: admission then shares the
+ * cached blocks of the prompt's longest cached prefix (pa_bm_add_seq_tokens),
+ * counts only the blocks it takes (fresh, or claimed back from the evictable
+ * list), lists only the prompt tokens after the cached ones for writing, and
+ * lists the cached blocks' table entries as patches (no token write sets
+ * them).
+ * A request preempted for recompute comes back by count, without its ids. */
+pa_status_t pa_sched_submit_tokens(pa_sched_t* s, int64_t seq, const int32_t* prompt_ids,
+                                   int32_t prompt_tokens, int32_t total_tokens);
 pa_status_t pa_sched_step(pa_sched_t* s, pa_sched_out_t* out);
 
 #ifdef __cplusplus

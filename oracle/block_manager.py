@@ -46,7 +46,7 @@ CPU memory).  Readings:
     it releases its host blocks.
 """
 
-from collections import deque
+from collections import OrderedDict, deque
 
 BLOCK_SIZE = 16
 
@@ -73,16 +73,20 @@ class RefBlockManager:
         self.num_host_blocks = 0
         self.host_free = deque()
         self.host_ref = []
+        self.prefix_cache = False
+        self.cache = {}            # whole prefix (tuple of token ids up to a block's end) -> block
+        self.block_key = {}        # block -> its prefix
+        self.lru = OrderedDict()   # cached blocks nobody holds; the first is evicted first
 
     # -- queries ---------------------------------------------------------
     def num_free(self) -> int:
-        return len(self.free)
+        return len(self.free) + len(self.lru)
 
     def refcount(self, block: int) -> int:
         return self.ref[block]
 
     def usage(self) -> float:
-        return (self.num_blocks - len(self.free)) / self.num_blocks
+        return (self.num_blocks - self.num_free()) / self.num_blocks
 
     def blocks_of(self, seq):
         return list(self.seqs[seq]["blocks"])
@@ -92,14 +96,28 @@ class RefBlockManager:
 
     # -- helpers -----------------------------------------------------------
     def _take(self) -> int:
-        b = self.free.popleft()
+        if self.free:
+            b = self.free.popleft()
+        else:  # evict the cached block released longest ago
+            b, _ = self.lru.popitem(last=False)
+            del self.cache[self.block_key.pop(b)]
         self.ref[b] = 1
         return b
 
     def _drop(self, b: int) -> None:
         self.ref[b] -= 1
         if self.ref[b] == 0:
-            self.free.append(b)
+            if b in self.block_key:
+                self.lru[b] = None
+            else:
+                self.free.append(b)
+
+    def _snapshot(self):
+        return (deque(self.free), list(self.ref), {k: dict(v, blocks=list(v["blocks"])) for k, v in self.seqs.items()},
+                dict(self.cache), dict(self.block_key), OrderedDict(self.lru))
+
+    def _restore(self, saved) -> None:
+        self.free, self.ref, self.seqs, self.cache, self.block_key, self.lru = saved
 
     def _on_host(self, seq) -> bool:
         return bool(self.seqs[seq].get("host"))
@@ -123,7 +141,7 @@ class RefBlockManager:
         if seq in self.seqs or num_tokens < 0:
             raise BadRequest("duplicate sequence or negative length")
         need = self._nblocks(num_tokens)
-        if need > len(self.free):
+        if need > self.num_free():
             raise NoSpace()
         self.seqs[seq] = {"blocks": [self._take() for _ in range(need)], "n": num_tokens}
 
@@ -134,7 +152,7 @@ class RefBlockManager:
             raise BadRequest("a shared prefix is a whole number of blocks inside the prefix sequence")
         shared = self.seqs[prefix_seq]["blocks"][: prefix_tokens // BLOCK_SIZE]
         need = self._nblocks(tail_tokens)
-        if need > len(self.free):
+        if need > self.num_free():
             raise NoSpace()
         for b in shared:
             self.ref[b] += 1
@@ -153,10 +171,12 @@ class RefBlockManager:
         if seq not in self.seqs:
             raise BadRequest("unknown sequence")
         st = self.seqs.pop(seq)
-        for b in st["blocks"]:
-            if st.get("host"):
-                self._drop_host(b)
-            else:
+        if st.get("host"):
+            for h in st["blocks"]:
+                self._drop_host(h)
+        else:
+            # with prefix caching the deepest block goes first, so a prefix is evicted from its end
+            for b in (reversed(st["blocks"]) if self.prefix_cache else st["blocks"]):
                 self._drop(b)
 
     def append_tokens(self, seqs):
@@ -171,21 +191,20 @@ class RefBlockManager:
             if s not in self.seqs or self._on_host(s):
                 raise BadRequest("unknown or swapped-out sequence")
         # all-or-nothing: run the updates on a copy and commit on success
-        saved = (deque(self.free), list(self.ref),
-                 {k: dict(v, blocks=list(v["blocks"])) for k, v in self.seqs.items()})
+        saved = self._snapshot()
         try:
             slots, cows = [], []
             for s in seqs:
                 st = self.seqs[s]
                 pos = st["n"]
                 if pos % BLOCK_SIZE == 0:
-                    if not self.free:
+                    if not self.num_free():
                         raise NoSpace()
                     st["blocks"].append(self._take())
                 else:
                     last = st["blocks"][-1]
                     if self.ref[last] > 1:
-                        if not self.free:
+                        if not self.num_free():
                             raise NoSpace()
                         fresh = self._take()
                         self.ref[last] -= 1
@@ -195,8 +214,67 @@ class RefBlockManager:
                 st["n"] = pos + 1
             return slots, cows
         except NoSpace:
-            self.free, self.ref, self.seqs = saved
+            self._restore(saved)
             raise
+
+    # -- prefix cache ------------------------------------------------------
+    def enable_prefix_cache(self) -> None:
+        if self.prefix_cache or self.seqs:
+            raise BadRequest("turn prefix caching on once, before the first sequence")
+        self.prefix_cache = True
+
+    def num_cached_free(self) -> int:
+        return len(self.lru)
+
+    def prefix_hits(self, tokens):
+        """The cached blocks of the longest cached prefix of ``tokens``, and how
+        many of them wait in the evictable list.  Changes nothing."""
+        tokens = [int(t) for t in tokens]
+        hits = []
+        for i in range(len(tokens) // BLOCK_SIZE):
+            b = self.cache.get(tuple(tokens[: BLOCK_SIZE * (i + 1)]))
+            if b is None:
+                break
+            hits.append(b)
+        return hits, sum(1 for b in hits if b in self.lru)
+
+    def add_seq_tokens(self, seq, tokens) -> int:
+        """New sequence from its token ids, sharing the cached blocks of its
+        longest cached prefix; returns how many leading tokens were cached."""
+        if not self.prefix_cache:
+            raise BadRequest("prefix caching is off")
+        if seq in self.seqs:
+            raise BadRequest("duplicate sequence")
+        tokens = [int(t) for t in tokens]
+        n = len(tokens)
+        full, total = n // BLOCK_SIZE, self._nblocks(n)
+        prefixes = [tuple(tokens[: BLOCK_SIZE * (i + 1)]) for i in range(full)]
+        hits = []
+        for p in prefixes:
+            if p not in self.cache:
+                break
+            hits.append(self.cache[p])
+        claimed = sum(1 for b in hits if b in self.lru)
+        if total - len(hits) > self.num_free() - claimed:
+            raise NoSpace()
+        for b in hits:
+            self.lru.pop(b, None)
+            self.ref[b] += 1
+        blocks = list(hits)
+        for i in range(len(hits), total):
+            b = self._take()
+            blocks.append(b)
+            if i < full:
+                old = self.cache.get(prefixes[i])
+                if old is not None:  # an evictable block held this prefix: the new one takes it over
+                    del self.block_key[old]
+                    if old in self.lru:
+                        del self.lru[old]
+                        self.free.append(old)
+                self.cache[prefixes[i]] = b
+                self.block_key[b] = prefixes[i]
+        self.seqs[seq] = {"blocks": blocks, "n": n}
+        return len(hits) * BLOCK_SIZE
 
     # -- swap pool ---------------------------------------------------------
     def set_host_pool(self, num_host_blocks: int) -> None:
@@ -257,7 +335,7 @@ class RefBlockManager:
         seqs = list(seqs)
         self._check_swap_list(seqs, True)
         distinct = {h for s in seqs for h in self.seqs[s]["blocks"]}
-        if len(distinct) > len(self.free):
+        if len(distinct) > self.num_free():
             raise NoSpace()
         where, pairs = {}, []
         for s in seqs:

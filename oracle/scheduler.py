@@ -29,7 +29,14 @@ Readings where the pages are silent (the same rules the library documents):
     request that was running before the admissions appends one token;
   * the step's token list holds the admitted prompts (admission order) and
     then the appended tokens (priority order); swapped-in requests' table
-    entries are listed as (row, logical block, physical block) patches.
+    entries are listed as (row, logical block, physical block) patches;
+  * a request submitted with its prompt's token ids (prefix caching on) is
+    admitted through the prefix cache: it needs only the blocks it takes
+    (fresh ones, and cached ones claimed back from the evictable list), only
+    its prompt tokens after the cached ones are written, and its cached
+    blocks' table entries are listed as patches; the token
+    budget still counts its whole prompt; a request preempted for recompute
+    comes back by count, without ids.
 """
 
 from bisect import insort
@@ -56,14 +63,17 @@ class RefScheduler:
         self.swapped = []      # sorted (arrival, seq)
         self.rows = [-1] * max_rows
 
-    def submit(self, seq, prompt_tokens: int, total_tokens: int) -> None:
-        if not 1 <= prompt_tokens <= total_tokens:
-            raise BadRequest("need 1 <= prompt <= total")
+    def submit(self, seq, prompt_tokens: int, total_tokens: int, prompt_ids=None) -> None:
+        if not 1 <= prompt_tokens <= total_tokens or seq < 0:
+            raise BadRequest("need 1 <= prompt <= total and a request id >= 0")
+        if prompt_ids is not None and (not self.bm.prefix_cache or len(prompt_ids) != prompt_tokens):
+            raise BadRequest("token ids need prefix caching on and one id per prompt token")
         if _blocks(total_tokens) > min(self.max_blocks, self.bm.num_blocks):
             raise BadRequest("request can never fit")
         if seq in self.req or seq in self.bm.seqs:
             raise BadRequest("duplicate request")
-        self.req[seq] = {"arrival": self.arrivals, "prompt": prompt_tokens, "total": total_tokens, "row": -1}
+        self.req[seq] = {"arrival": self.arrivals, "prompt": prompt_tokens, "total": total_tokens, "row": -1,
+                         "ids": None if prompt_ids is None else [int(t) for t in prompt_ids]}
         self.waiting.append((self.arrivals, seq))
         self.arrivals += 1
 
@@ -91,7 +101,7 @@ class RefScheduler:
         bm = self.bm
         out = {"slots": [], "token_rows": [], "token_positions": [], "swap_out": [], "swap_in": [], "cow": [],
                "patches": [], "finished": [], "num_admitted": 0, "num_swapped_in": 0, "num_preempted_swap": 0,
-               "num_preempted_recompute": 0}
+               "num_preempted_recompute": 0, "num_cached_tokens": 0}
 
         # 1. retire
         for arrival, s in list(self.running):
@@ -118,6 +128,7 @@ class RefScheduler:
                 out["num_preempted_swap"] += 1
             else:
                 r["prompt"] = bm.num_tokens(s)
+                r["ids"] = None  # readmitted by count
                 bm.free_seq(s)
                 insort(self.waiting, (arrival, s))
                 out["num_preempted_recompute"] += 1
@@ -153,13 +164,27 @@ class RefScheduler:
                 arrival, s = self.waiting[0]
                 r = self.req[s]
                 row = self._free_row()
-                if row < 0 or _blocks(r["prompt"]) + reserve > bm.num_free():
+                if row < 0:
+                    break
+                take = _blocks(r["prompt"])
+                if r["ids"] is not None:  # cached prefix blocks are shared; claiming an evictable one uses it up
+                    hits, claimed = bm.prefix_hits(r["ids"])
+                    take = take - len(hits) + claimed
+                if take + reserve > bm.num_free():
                     break
                 if admitted and r["prompt"] > left:
                     break
-                bm.add_seq(s, r["prompt"])
+                first = 0
+                if r["ids"] is not None:
+                    first = bm.add_seq_tokens(s, r["ids"])
+                    out["num_cached_tokens"] += first
+                    r["ids"] = None
+                else:
+                    bm.add_seq(s, r["prompt"])
                 blocks = bm.seqs[s]["blocks"]
-                for p in range(r["prompt"]):
+                for j in range(first // BLOCK_SIZE):  # cached blocks are not written: their entries are patched
+                    out["patches"].append((row, j, blocks[j]))
+                for p in range(first, r["prompt"]):
                     out["slots"].append(blocks[p // BLOCK_SIZE] * BLOCK_SIZE + p % BLOCK_SIZE)
                     out["token_rows"].append(row)
                     out["token_positions"].append(p)

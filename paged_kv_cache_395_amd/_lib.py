@@ -75,6 +75,9 @@ SIGNATURES = {
     "pa_bm_usage": (ctypes.c_double, [_vp]),
     "pa_bm_num_tokens": (_i32, [_vp, _i64]),
     "pa_bm_free_list": (_i64, [_vp, _vp, _i64]),
+    "pa_bm_enable_prefix_cache": (ctypes.c_int, [_vp]),
+    "pa_bm_add_seq_tokens": (ctypes.c_int, [_vp, _i64, _vp, _i32, _pi32]),
+    "pa_bm_num_cached_free": (_i64, [_vp]),
     "pa_bm_set_host_pool": (ctypes.c_int, [_vp, _i64]),
     "pa_bm_swap_out": (ctypes.c_int, [_vp, _vp, _i32, _vp, _pi32]),
     "pa_bm_swap_in": (ctypes.c_int, [_vp, _vp, _i32, _vp, _pi32]),
@@ -84,6 +87,7 @@ SIGNATURES = {
     "pa_sched_create": (_vp, [_vp, _i32, _i32, _i32]),
     "pa_sched_destroy": (None, [_vp]),
     "pa_sched_submit": (ctypes.c_int, [_vp, _i64, _i32, _i32]),
+    "pa_sched_submit_tokens": (ctypes.c_int, [_vp, _i64, _vp, _i32, _i32]),
     "pa_sched_step": (ctypes.c_int, [_vp, _vp]),
 }
 
@@ -98,7 +102,7 @@ class SchedOut(ctypes.Structure):
                 ("num_finished", _i32), ("finished", _pi64),
                 ("num_admitted", _i32), ("num_swapped_in", _i32), ("num_preempted_swap", _i32),
                 ("num_preempted_recompute", _i32), ("num_running", _i32), ("num_waiting", _i32),
-                ("num_swapped", _i32)]
+                ("num_swapped", _i32), ("num_cached_tokens", _i32)]
 
 
 _lock = threading.Lock()

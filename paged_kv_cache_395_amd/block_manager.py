@@ -73,6 +73,21 @@ class BlockManager:
         slots, cow = self.append_tokens([seq])
         return int(slots[0]), (tuple(int(x) for x in cow[0]) if len(cow) else (-1, -1))
 
+    # -- prefix cache ----------------------------------------------------------
+    def enable_prefix_cache(self) -> None:
+        _lib.check(self._l.pa_bm_enable_prefix_cache(self._h))
+
+    def add_seq_tokens(self, seq: int, tokens) -> int:
+        """New sequence from its token ids; returns how many leading tokens were already cached."""
+        tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        cached = ctypes.c_int32(0)
+        _lib.check(self._l.pa_bm_add_seq_tokens(self._h, int(seq), _ptr(tokens), tokens.shape[0],
+                                                ctypes.byref(cached)))
+        return cached.value
+
+    def num_cached_free(self) -> int:
+        return int(self._l.pa_bm_num_cached_free(self._h))
+
     # -- swap pool -----------------------------------------------------------
     def set_host_pool(self, num_host_blocks: int) -> None:
         _lib.check(self._l.pa_bm_set_host_pool(self._h, int(num_host_blocks)))

@@ -86,6 +86,39 @@ pa_status_t check_swap_list(const pa_bm* bm, const int64_t* seqs, int32_t n, boo
   return PA_OK;
 }
 
+// Key of a full block: a hash of the prefix hash before it and its 16 token
+// ids (FNV-1a 64 over their bytes, then the SplitMix64 finalizer to spread
+// the bits).  A match is confirmed against the stored parent hash and token
+// ids, so only a collision of whole-prefix hashes could mislead it.
+uint64_t block_key(uint64_t parent, const int32_t* tok) {
+  uint64_t h = 1469598103934665603ull;
+  auto mix = [&h](uint64_t x, int bytes) {
+    for (int i = 0; i < bytes; ++i) {
+      h ^= (x >> (8 * i)) & 0xffu;
+      h *= 1099511628211ull;
+    }
+  };
+  mix(parent, 8);
+  for (int i = 0; i < kBS; ++i) mix(uint32_t(tok[i]), 4);
+  h ^= h >> 30;
+  h *= 0xbf58476d1ce4e5b9ull;
+  h ^= h >> 27;
+  h *= 0x94d049bb133111ebull;
+  h ^= h >> 31;
+  return h;
+}
+
+// The cached block holding exactly this (parent, tokens), or -1.
+int32_t lookup(const pa_bm* bm, uint64_t k, uint64_t parent, const int32_t* tok) {
+  auto it = bm->cached.find(k);
+  if (it == bm->cached.end()) return -1;
+  const int32_t b = it->second;
+  if (bm->parent_key[size_t(b)] != parent) return -1;
+  for (int i = 0; i < kBS; ++i)
+    if (bm->key_tokens[size_t(b) * kBS + i] != tok[i]) return -1;
+  return b;
+}
+
 // Distinct blocks among the listed sequences' block lists.
 int64_t distinct_blocks(const pa_bm* bm, const int64_t* seqs, int32_t n) {
   std::unordered_set<int32_t> d;
@@ -95,6 +128,37 @@ int64_t distinct_blocks(const pa_bm* bm, const int64_t* seqs, int32_t n) {
 }
 
 }  // namespace
+
+namespace pa {
+
+int64_t prefix_probe(const pa_bm* bm, const int32_t* tokens, int32_t num_tokens, std::vector<int32_t>* hits,
+                     std::vector<uint64_t>* keys, std::vector<uint64_t>* parents) {
+  const int32_t full = num_tokens / kBS;
+  keys->assign(size_t(full), 0);
+  parents->assign(size_t(full), 0);
+  hits->clear();
+  uint64_t parent = 0;
+  bool hitting = true;
+  int64_t claimed = 0;
+  for (int32_t i = 0; i < full; ++i) {
+    const int32_t* tok = tokens + int64_t(i) * kBS;
+    (*parents)[size_t(i)] = parent;
+    (*keys)[size_t(i)] = block_key(parent, tok);
+    if (hitting) {
+      const int32_t b = lookup(bm, (*keys)[size_t(i)], parent, tok);
+      if (b >= 0) {
+        hits->push_back(b);
+        claimed += bm->in_lru[size_t(b)];
+      } else {
+        hitting = false;
+      }
+    }
+    parent = (*keys)[size_t(i)];
+  }
+  return claimed;
+}
+
+}  // namespace pa
 
 extern "C" {
 
@@ -135,8 +199,8 @@ pa_status_t pa_bm_add_seq(pa_bm_t* bm, int64_t seq, int32_t num_tokens) {
   if (num_tokens < 0) return fail(PA_EINVAL, "negative length");
   if (bm->seqs.count(seq)) return fail(PA_EINVAL, "sequence %lld already exists", (long long)seq);
   const int64_t need = blocks_for(num_tokens);
-  if (need > int64_t(bm->free_q.size()))
-    return fail(PA_ENOSPC, "need %lld blocks, %zu free", (long long)need, bm->free_q.size());
+  if (need > bm->available())
+    return fail(PA_ENOSPC, "need %lld blocks, %lld free", (long long)need, (long long)bm->available());
   Seq s;
   s.tokens = num_tokens;
   s.blocks.reserve(size_t(need));
@@ -155,8 +219,8 @@ pa_status_t pa_bm_add_seq_with_prefix(pa_bm_t* bm, int64_t seq, int64_t prefix_s
   if (prefix_tokens < 0 || prefix_tokens % kBS != 0 || prefix_tokens > it->second.tokens || tail_tokens < 0)
     return fail(PA_EINVAL, "a shared prefix is a whole number of blocks inside the prefix sequence");
   const int64_t need = blocks_for(tail_tokens);
-  if (need > int64_t(bm->free_q.size()))
-    return fail(PA_ENOSPC, "need %lld blocks, %zu free", (long long)need, bm->free_q.size());
+  if (need > bm->available())
+    return fail(PA_ENOSPC, "need %lld blocks, %lld free", (long long)need, (long long)bm->available());
   Seq s;
   s.tokens = prefix_tokens + tail_tokens;
   const int32_t shared = prefix_tokens / kBS;
@@ -183,10 +247,14 @@ pa_status_t pa_bm_free_seq(pa_bm_t* bm, int64_t seq) {
   if (!bm) return fail(PA_EINVAL, "null block manager");
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown sequence %lld", (long long)seq);
+  const std::vector<int32_t>& bl = it->second.blocks;
   if (it->second.swapped) {
-    for (int32_t h : it->second.blocks) bm->drop_host(h);
+    for (int32_t h : bl) bm->drop_host(h);
+  } else if (bm->prefix_cache) {
+    // deepest block first, so a cached prefix is evicted from its end
+    for (auto b = bl.rbegin(); b != bl.rend(); ++b) bm->drop(*b);
   } else {
-    for (int32_t b : it->second.blocks) bm->drop(b);
+    for (int32_t b : bl) bm->drop(b);
   }
   bm->seqs.erase(it);
   return PA_OK;
@@ -200,8 +268,8 @@ pa_status_t pa_bm_append_tokens(pa_bm_t* bm, const int64_t* seqs, int32_t n, int
   int64_t cows = 0;
   const int64_t need = pa::append_need(bm, seqs, n, &cows);
   if (need < 0) return pa_status_t(-need);
-  if (need > int64_t(bm->free_q.size()))
-    return fail(PA_ENOSPC, "need %lld blocks, %zu free", (long long)need, bm->free_q.size());
+  if (need > bm->available())
+    return fail(PA_ENOSPC, "need %lld blocks, %lld free", (long long)need, (long long)bm->available());
   if (cows > 0 && !cow_pairs) return fail(PA_EINVAL, "copy-on-write needed but cow_pairs is NULL");
   // Pass 2: apply; cannot fail.
   int32_t nc = 0;
@@ -305,8 +373,8 @@ pa_status_t pa_bm_swap_in(pa_bm_t* bm, const int64_t* seqs, int32_t n, int64_t* 
   if (st != PA_OK) return st;
   if (total > 0 && !pairs) return fail(PA_EINVAL, "pairs is NULL");
   const int64_t need = distinct_blocks(bm, seqs, n);
-  if (need > int64_t(bm->free_q.size()))
-    return fail(PA_ENOSPC, "need %lld blocks, %zu free", (long long)need, bm->free_q.size());
+  if (need > bm->available())
+    return fail(PA_ENOSPC, "need %lld blocks, %lld free", (long long)need, (long long)bm->available());
   std::unordered_map<int32_t, int32_t> moved;  // host block -> device block, within this call
   int32_t np = 0;
   for (int32_t i = 0; i < n; ++i) {
@@ -346,7 +414,74 @@ int32_t pa_bm_host_refcount(const pa_bm_t* bm, int64_t block) {
   return bm->host_ref[size_t(block)];
 }
 
-int64_t pa_bm_num_free(const pa_bm_t* bm) { return bm ? int64_t(bm->free_q.size()) : -1; }
+pa_status_t pa_bm_enable_prefix_cache(pa_bm_t* bm) {
+  if (!bm) return fail(PA_EINVAL, "null block manager");
+  if (bm->prefix_cache) return fail(PA_EINVAL, "prefix caching is already on");
+  if (!bm->seqs.empty()) return fail(PA_EINVAL, "turn prefix caching on before adding sequences");
+  const size_t nb = size_t(bm->num_blocks);
+  bm->prefix_cache = true;
+  bm->key.assign(nb, 0);
+  bm->parent_key.assign(nb, 0);
+  bm->key_tokens.assign(nb * kBS, 0);
+  bm->keyed.assign(nb, 0);
+  bm->in_lru.assign(nb, 0);
+  bm->lru_pos.assign(nb, bm->lru.end());
+  return PA_OK;
+}
+
+
+pa_status_t pa_bm_add_seq_tokens(pa_bm_t* bm, int64_t seq, const int32_t* tokens, int32_t num_tokens,
+                                 int32_t* cached_tokens) {
+  if (!bm) return fail(PA_EINVAL, "null block manager");
+  if (!bm->prefix_cache) return fail(PA_EINVAL, "prefix caching is off (pa_bm_enable_prefix_cache)");
+  if (num_tokens < 0 || (num_tokens > 0 && !tokens)) return fail(PA_EINVAL, "bad arguments");
+  if (bm->seqs.count(seq)) return fail(PA_EINVAL, "sequence %lld already exists", (long long)seq);
+  const int32_t full = num_tokens / kBS;
+  const int64_t total = blocks_for(num_tokens);
+  // the leading run of full blocks already cached
+  std::vector<uint64_t> keys, parents;
+  std::vector<int32_t> hits;
+  const int64_t from_lru = pa::prefix_probe(bm, tokens, num_tokens, &hits, &keys, &parents);
+  const int64_t need = total - int64_t(hits.size());
+  if (need > bm->available() - from_lru)
+    return fail(PA_ENOSPC, "need %lld blocks, %lld free", (long long)need, (long long)(bm->available() - from_lru));
+  Seq s;
+  s.tokens = num_tokens;
+  s.blocks.reserve(size_t(total));
+  for (int32_t b : hits) {
+    if (bm->in_lru[size_t(b)]) bm->lru_remove(b);
+    ++bm->ref[size_t(b)];
+    s.blocks.push_back(b);
+  }
+  for (int64_t i = int64_t(hits.size()); i < total; ++i) {
+    const int32_t b = bm->take();
+    s.blocks.push_back(b);
+    if (i < full) {  // a full prompt block: key it (the caller writes its tokens this step)
+      const uint64_t k = keys[size_t(i)];
+      auto it = bm->cached.find(k);
+      if (it != bm->cached.end()) {  // a stale entry for the same prefix: the new block replaces it
+        const int32_t old = it->second;
+        bm->keyed[size_t(old)] = 0;
+        if (bm->in_lru[size_t(old)]) {
+          bm->lru_remove(old);
+          bm->free_q.push_back(old);
+        }
+      }
+      bm->cached[k] = b;
+      bm->key[size_t(b)] = k;
+      bm->parent_key[size_t(b)] = parents[size_t(i)];
+      for (int t = 0; t < kBS; ++t) bm->key_tokens[size_t(b) * kBS + t] = tokens[i * kBS + t];
+      bm->keyed[size_t(b)] = 1;
+    }
+  }
+  bm->seqs.emplace(seq, std::move(s));
+  if (cached_tokens) *cached_tokens = int32_t(hits.size()) * kBS;
+  return PA_OK;
+}
+
+int64_t pa_bm_num_cached_free(const pa_bm_t* bm) { return bm ? int64_t(bm->lru.size()) : -1; }
+
+int64_t pa_bm_num_free(const pa_bm_t* bm) { return bm ? bm->available() : -1; }
 
 int32_t pa_bm_refcount(const pa_bm_t* bm, int64_t block) {
   if (!bm || block < 0 || block >= bm->num_blocks) return -1;
@@ -355,7 +490,7 @@ int32_t pa_bm_refcount(const pa_bm_t* bm, int64_t block) {
 
 double pa_bm_usage(const pa_bm_t* bm) {
   if (!bm) return -1.0;
-  return double(bm->num_blocks - int64_t(bm->free_q.size())) / double(bm->num_blocks);
+  return double(bm->num_blocks - bm->available()) / double(bm->num_blocks);
 }
 
 int32_t pa_bm_num_tokens(const pa_bm_t* bm, int64_t seq) {

@@ -40,6 +40,7 @@ struct Req {
   int32_t prompt;  // tokens written when admitted
   int32_t total;   // the request is done once its sequence holds this many tokens
   int32_t row;
+  std::vector<int32_t> ids;  // prompt token ids, when given (admission then reuses cached prefix blocks)
 };
 
 void insert_by_arrival(std::vector<Req>& v, const Req& r) {
@@ -71,7 +72,7 @@ struct pa_sched {
     return -1;
   }
   const Seq& seq_of(int64_t id) const { return bm->seqs.find(id)->second; }
-  int64_t free_blocks() const { return int64_t(bm->free_q.size()); }
+  int64_t free_blocks() const { return bm->available(); }
   int64_t running_need() const {
     std::vector<int64_t> ids;
     ids.reserve(running.size());
@@ -104,7 +105,13 @@ pa_sched_t* pa_sched_create(pa_bm_t* bm, int32_t max_rows, int32_t max_blocks_pe
 void pa_sched_destroy(pa_sched_t* s) { delete s; }
 
 pa_status_t pa_sched_submit(pa_sched_t* s, int64_t seq, int32_t prompt_tokens, int32_t total_tokens) {
+  return pa_sched_submit_tokens(s, seq, nullptr, prompt_tokens, total_tokens);
+}
+
+pa_status_t pa_sched_submit_tokens(pa_sched_t* s, int64_t seq, const int32_t* prompt_ids, int32_t prompt_tokens,
+                                   int32_t total_tokens) {
   if (!s) return fail(PA_EINVAL, "null scheduler");
+  if (seq < 0) return fail(PA_EINVAL, "request ids must be >= 0");
   if (prompt_tokens < 1 || total_tokens < prompt_tokens)
     return fail(PA_EINVAL, "need 1 <= prompt_tokens <= total_tokens");
   const int64_t nb = blocks_for(total_tokens);
@@ -112,8 +119,11 @@ pa_status_t pa_sched_submit(pa_sched_t* s, int64_t seq, int32_t prompt_tokens, i
     return fail(PA_EINVAL, "a request of %d tokens can never fit (%lld blocks)", total_tokens, (long long)nb);
   if (s->known.count(seq) || s->bm->seqs.count(seq))
     return fail(PA_EINVAL, "sequence %lld already exists", (long long)seq);
+  if (prompt_ids && !s->bm->prefix_cache) return fail(PA_EINVAL, "token ids need prefix caching on");
   s->known.insert(seq);
-  s->waiting.push_back(Req{seq, s->next_arrival++, prompt_tokens, total_tokens, -1});
+  Req r{seq, s->next_arrival++, prompt_tokens, total_tokens, -1, {}};
+  if (prompt_ids) r.ids.assign(prompt_ids, prompt_ids + prompt_tokens);
+  s->waiting.push_back(std::move(r));
   return PA_OK;
 }
 
@@ -167,7 +177,8 @@ pa_status_t pa_sched_step(pa_sched_t* s, pa_sched_out_t* out) {
       insert_by_arrival(s->swapped, v);
       ++o.num_preempted_swap;
     } else {
-      v.prompt = sq.tokens;  // recomputed from its tokens so far when readmitted
+      v.prompt = sq.tokens;  // recomputed from its tokens so far when readmitted (by count: no ids)
+      v.ids.clear();
       pa_bm_free_seq(bm, v.seq);
       insert_by_arrival(s->waiting, v);
       ++o.num_preempted_recompute;
@@ -209,16 +220,38 @@ pa_status_t pa_sched_step(pa_sched_t* s, pa_sched_out_t* out) {
   std::unordered_set<int64_t> admitted;
   if (s->swapped.empty()) {
     int64_t budget = int64_t(s->max_batched_tokens) - int64_t(s->running.size());
+    std::vector<int32_t> hits;
+    std::vector<uint64_t> keys, parents;
     while (!s->waiting.empty()) {
-      Req r = s->waiting.front();
+      Req& r = s->waiting.front();
       const int32_t row = s->free_row();
       if (row < 0) break;
-      if (blocks_for(r.prompt) + reserved > s->free_blocks()) break;
+      // blocks the admission takes: fresh ones, plus cached ones it claims back from the evictable list
+      int64_t take = blocks_for(r.prompt), write_from = 0;
+      const bool by_ids = !r.ids.empty();
+      if (by_ids) {
+        const int64_t claimed = pa::prefix_probe(bm, r.ids.data(), r.prompt, &hits, &keys, &parents);
+        take = take - int64_t(hits.size()) + claimed;
+      }
+      if (take + reserved > s->free_blocks()) break;
       if (!admitted.empty() && r.prompt > budget) break;  // the first admission of a step is always allowed
-      pa_status_t st = pa_bm_add_seq(bm, r.seq, r.prompt);
+      pa_status_t st;
+      if (by_ids) {
+        int32_t cached = 0;
+        st = pa_bm_add_seq_tokens(bm, r.seq, r.ids.data(), r.prompt, &cached);
+        write_from = cached;
+        o.num_cached_tokens += cached;
+      } else {
+        st = pa_bm_add_seq(bm, r.seq, r.prompt);
+      }
       if (st != PA_OK) return st;
       const Seq& sq = s->seq_of(r.seq);
-      for (int32_t p = 0; p < r.prompt; ++p) {
+      for (int64_t j = 0; j < write_from / kBS; ++j) {  // cached blocks get no token write: patch the table
+        s->patches.push_back(row);
+        s->patches.push_back(int32_t(j));
+        s->patches.push_back(sq.blocks[size_t(j)]);
+      }
+      for (int32_t p = int32_t(write_from); p < r.prompt; ++p) {
         s->slots.push_back(int64_t(sq.blocks[size_t(p / kBS)]) * kBS + p % kBS);
         s->rows.push_back(row);
         s->positions.push_back(p);
@@ -227,8 +260,10 @@ pa_status_t pa_sched_step(pa_sched_t* s, pa_sched_out_t* out) {
       r.row = row;
       s->row_seq[size_t(row)] = r.seq;
       admitted.insert(r.seq);
-      insert_by_arrival(s->running, r);
+      Req moved = std::move(r);
+      moved.ids.clear();  // only admission reads them
       s->waiting.erase(s->waiting.begin());
+      insert_by_arrival(s->running, moved);
       ++o.num_admitted;
     }
   }

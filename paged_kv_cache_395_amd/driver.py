@@ -32,7 +32,7 @@ _TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 class Driver:
     def __init__(self, num_blocks, num_host_blocks, num_q_heads, num_kv_heads, head_dim, dtype, max_rows,
                  max_blocks_per_seq, max_batched_tokens, scale, free_order=None, device="cuda", ring=4,
-                 partition_size=0):
+                 partition_size=0, prefix_cache=False):
         self._l = _lib.load()
         self.dtype = dtype
         tdt = _TORCH[dtype]
@@ -43,6 +43,8 @@ class Driver:
         self.scale = float(scale)
         self.partition = int(partition_size)
         self.bm = BlockManager(num_blocks, free_order=free_order)
+        if prefix_cache:
+            self.bm.enable_prefix_cache()
         self.bm.set_host_pool(num_host_blocks)
         self.sched = Scheduler(self.bm, max_rows, max_blocks_per_seq, max_batched_tokens)
         tile = BLOCK_SIZE * head_dim
@@ -86,8 +88,8 @@ class Driver:
         self.steps = 0
 
     # -- host half -------------------------------------------------------------
-    def submit(self, seq: int, prompt_tokens: int, total_tokens: int) -> None:
-        self.sched.submit(seq, prompt_tokens, total_tokens)
+    def submit(self, seq: int, prompt_tokens: int, total_tokens: int, prompt_ids=None) -> None:
+        self.sched.submit(seq, prompt_tokens, total_tokens, prompt_ids)
 
     def schedule(self):
         """Run the scheduler for one step and stage its metadata; returns the Step."""

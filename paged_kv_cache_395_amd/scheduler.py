@@ -38,6 +38,7 @@ class Step:
     num_running: int
     num_waiting: int
     num_swapped: int
+    num_cached_tokens: int
 
     @property
     def idle(self) -> bool:
@@ -68,8 +69,16 @@ class Scheduler:
         except Exception:  # interpreter shutdown
             pass
 
-    def submit(self, seq: int, prompt_tokens: int, total_tokens: int) -> None:
-        _lib.check(self._l.pa_sched_submit(self._h, int(seq), int(prompt_tokens), int(total_tokens)))
+    def submit(self, seq: int, prompt_tokens: int, total_tokens: int, prompt_ids=None) -> None:
+        """Queue a request; with ``prompt_ids`` (and prefix caching on) admission reuses cached prefix blocks."""
+        if prompt_ids is None:
+            _lib.check(self._l.pa_sched_submit(self._h, int(seq), int(prompt_tokens), int(total_tokens)))
+            return
+        ids = np.ascontiguousarray(prompt_ids, dtype=np.int32)
+        if ids.shape != (int(prompt_tokens),):
+            raise ValueError("prompt_ids must hold prompt_tokens ids")
+        _lib.check(self._l.pa_sched_submit_tokens(self._h, int(seq), ids.ctypes.data_as(ctypes.c_void_p),
+                                                  int(prompt_tokens), int(total_tokens)))
 
     def step(self) -> Step:
         o = self._out
@@ -87,4 +96,5 @@ class Scheduler:
             finished=_arr(o.finished, o.num_finished, np.int64),
             num_admitted=o.num_admitted, num_swapped_in=o.num_swapped_in,
             num_preempted_swap=o.num_preempted_swap, num_preempted_recompute=o.num_preempted_recompute,
-            num_running=o.num_running, num_waiting=o.num_waiting, num_swapped=o.num_swapped)
+            num_running=o.num_running, num_waiting=o.num_waiting, num_swapped=o.num_swapped,
+            num_cached_tokens=o.num_cached_tokens)

@@ -144,3 +144,70 @@ def test_driver_matches_the_oracle_through_preemption(dtype, Hq, Hkv, D, host_bl
     assert np.array_equal(to_host(drv.v_pool, dtype).view(np.uint8), ora.v.view(np.uint8))
     if host_blocks:
         assert np.array_equal(to_host(drv.k_host, dtype).view(np.uint8), ora.hk.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype,host_blocks", [("bf16", 16), ("f16", 2)], ids=["bf16_swap", "f16_recompute"])
+def test_driver_with_prefix_cache_matches_the_oracle(dtype, host_blocks):
+    """Requests on three shared system prompts, admitted through the prefix
+    cache: only uncached prompt tokens are written, cached blocks reach the
+    device tables as patches, and every row's attention matches the oracle.
+    The oracle's pools are also checked against K/V regenerated from each
+    row's own token prefix, so shared blocks must hold exactly that prefix."""
+    from workloads.serving import kv_rows_by_key, prefix_requests, token_keys
+
+    seed = 83
+    Hq, Hkv, D = 8, 2, 128
+    NB, rows, maxB, budget = 28, 6, 10, 96
+    reqs = prefix_requests(seed, 24, 3, 48, 12, 40, 20, 50, mean_gap=2.0, vocab=500)
+    reqs = [(a, i, ids, min(t, maxB * 16)) for a, i, ids, t in reqs]
+    prompt = {i: ids for _, i, ids, _ in reqs}
+    scale = D ** -0.5
+    drv = Driver(NB, host_blocks, Hq, Hkv, D, dtype, rows, maxB, budget, scale, prefix_cache=True)
+    ora = OracleSide(NB, host_blocks, Hkv, D, dtype, rows, maxB, budget, None)
+    ora.bm.enable_prefix_cache()
+    say(f"[driver-prefix] {dtype} host_blocks={host_blocks} requests={len(reqs)}")
+    pending = list(reqs)
+    counts = {"cached": 0, "preempted": 0}
+    for step in range(3000):
+        while pending and pending[0][0] <= step:
+            _, i, ids, t = pending.pop(0)
+            drv.submit(i, len(ids), t, ids)
+            ora.sched.submit(i, len(ids), t, ids)
+        st = drv.schedule()
+        ost = ora.sched.step()
+        assert as_lists(st) == as_lists(ost), f"step {step}: schedulers differ"
+        T = len(st.slots)
+        keys = [token_keys(int(st.row_seq[st.token_rows[j]]), [int(st.token_positions[j])],
+                           prompt[int(st.row_seq[st.token_rows[j]])])[0] for j in range(T)]
+        key, val = kv_rows_by_key(seed, keys, Hkv, D, dtype)
+        q = np.zeros((rows, Hq, D), dtype=ora.k.dtype)
+        for r, s in enumerate(st.row_seq):
+            if s >= 0:
+                q[r] = query_rows(seed, int(s), step, Hq, D, dtype)
+        if T:
+            drv.key[:T].copy_(to_dev(key, dtype))
+            drv.value[:T].copy_(to_dev(val, dtype))
+        drv.q.copy_(to_dev(q, dtype))
+        drv.launch(st)
+        ora.apply(ost, key, val)
+        table, ctx = ora.tables(list(ost["row_seq"]))
+        if step % 7 == 0:  # the oracle's own pools hold each row's prefix
+            for r, s in enumerate(ost["row_seq"]):
+                if s >= 0:
+                    K, V = OA.gather_kv(ora.k, ora.v, table[r], int(ctx[r]), dtype)
+                    k_want, v_want = kv_rows_by_key(seed, token_keys(s, range(int(ctx[r])), prompt[s]), Hkv, D,
+                                                    dtype)
+                    assert np.array_equal(K, OA.to_f64(k_want, dtype).transpose(1, 0, 2)), f"step {step} row {r}"
+                    assert np.array_equal(V, OA.to_f64(v_want, dtype).transpose(1, 0, 2)), f"step {step} row {r}"
+        want = OA.decode(q, ora.k, ora.v, table, ctx, scale, dtype)
+        torch.cuda.synchronize()
+        assert_close(out_f64(drv.out), want, dtype, f"step {step}")
+        counts["cached"] += st.num_cached_tokens
+        counts["preempted"] += st.num_preempted_swap + st.num_preempted_recompute
+        if st.idle and not pending:
+            break
+    say(f"[driver-prefix] {counts}")
+    assert not pending and st.idle
+    assert counts["cached"] > 0 and counts["preempted"] > 0
+    assert np.array_equal(to_host(drv.k_pool, dtype).view(np.uint8), ora.k.view(np.uint8))
+    assert np.array_equal(to_host(drv.v_pool, dtype).view(np.uint8), ora.v.view(np.uint8))

@@ -16,6 +16,7 @@ import oracle.layout
 import oracle.scheduler
 from tests import test_oracle_attention as PA
 from tests import test_oracle_block_manager as PB
+from tests import test_prefix_cache as PC
 from tests import test_scheduler as PS
 
 MUTATIONS = [
@@ -80,6 +81,23 @@ MUTATIONS = [
      PS.test_oracle_replay_reads_back_every_token, (PS.CASES[0],)),
     (oracle.block_manager, "RefBlockManager.swap_out", "self.host_ref[where[b]] += 1", "pass",
      PS.test_swap_round_trip_with_shared_blocks_matches_the_oracle, ()),
+    (oracle.scheduler, "RefScheduler.step", "out[\"patches\"].append((row, j, blocks[j]))", "pass",
+     PS.test_prefix_cached_admission_reads_back_every_token, (PS.PREFIX_CASES[0],)),
+    (oracle.scheduler, "RefScheduler.step", "take = take - len(hits) + claimed", "take = take - len(hits)",
+     PS.test_prefix_cached_admission_reads_back_every_token, (PS.PREFIX_CASES[1],)),
+    (oracle.block_manager, "RefBlockManager._drop", "self.lru[b] = None", "self.free.append(b)",
+     PC.test_released_prefixes_wait_in_lru_and_are_evicted_from_their_end, ("oracle",)),
+    (oracle.block_manager, "RefBlockManager.free_seq", "reversed(st[\"blocks\"]) if self.prefix_cache",
+     "st[\"blocks\"] if self.prefix_cache", PC.test_released_prefixes_wait_in_lru_and_are_evicted_from_their_end,
+     ("oracle",)),
+    (oracle.block_manager, "RefBlockManager.add_seq_tokens", "tuple(tokens[: BLOCK_SIZE * (i + 1)])",
+     "tuple(tokens[BLOCK_SIZE * i: BLOCK_SIZE * (i + 1)])", PC.test_a_block_is_shared_only_under_the_same_prefix,
+     ("oracle",)),
+    (oracle.block_manager, "RefBlockManager.add_seq_tokens", "if i < full:", "if i <= full:",
+     PC.test_only_full_blocks_are_cached_and_a_miss_ends_the_run, ("oracle",)),
+    (oracle.block_manager, "RefBlockManager._take", "b, _ = self.lru.popitem(last=False)",
+     "b, _ = self.lru.popitem(last=True)", PC.test_released_prefixes_wait_in_lru_and_are_evicted_from_their_end,
+     ("oracle",)),
 ]
 
 

@@ -19,7 +19,7 @@ from tests._golden import load
 FIELDS = ["slots", "token_rows", "token_positions", "context_lens", "row_seq", "swap_out", "swap_in", "cow",
           "patches", "finished"]
 COUNTS = ["num_admitted", "num_swapped_in", "num_preempted_swap", "num_preempted_recompute", "num_running",
-          "num_waiting", "num_swapped"]
+          "num_waiting", "num_swapped", "num_cached_tokens"]
 
 
 def as_lists(step) -> dict:
@@ -46,11 +46,13 @@ class LabelWorld:
     """Device and host pools of (seq, pos) labels plus a device-side table,
     driven only by a step's outputs, in the order the device runs them."""
 
-    def __init__(self, num_blocks, num_host_blocks, max_rows, max_blocks):
+    def __init__(self, num_blocks, num_host_blocks, max_rows, max_blocks, label=None):
         self.dev = [[None] * 16 for _ in range(num_blocks)]
         self.host = [[None] * 16 for _ in range(num_host_blocks)]
         self.table = [[-1] * max_blocks for _ in range(max_rows)]
         self.max_blocks = max_blocks
+        # what token p of request s holds: (s, p) unless its content is shared
+        self.label = label or (lambda s, p: (s, p))
 
     def apply(self, st: dict):
         for d, h in st["swap_out"]:
@@ -63,7 +65,7 @@ class LabelWorld:
             self.table[r][j] = b
         for slot, r, p in zip(st["slots"], st["token_rows"], st["token_positions"]):
             seq = st["row_seq"][r]
-            self.dev[slot // 16][slot % 16] = (seq, p)
+            self.dev[slot // 16][slot % 16] = self.label(seq, p)
             self.table[r][p // 16] = slot // 16
 
     def check_rows(self, st: dict):
@@ -73,7 +75,7 @@ class LabelWorld:
                 continue
             for p in range(n):
                 got = self.dev[self.table[r][p // 16]][p % 16]
-                assert got == (seq, p), f"row {r} seq {seq} pos {p} reads {got}"
+                assert got == self.label(seq, p), f"row {r} seq {seq} pos {p} reads {got}"
 
 
 def random_trace(rng, n_req, max_prompt, max_total):
@@ -363,3 +365,84 @@ def test_swap_out_is_all_or_nothing_when_the_host_pool_is_short():
         with pytest.raises((NoSpace, NativeNoSpace)):
             bm.swap_out([1])
         assert not bm.is_swapped(1) and bm.num_free_host() == 2 and bm.num_free() == 5
+
+
+# -- admission through the prefix cache -------------------------------------
+def prefix_trace(rng, n_req, n_prompts, max_sys, max_tail, max_out):
+    """Requests on a few shared system prompts: (arrival, id, prompt ids, total)."""
+    systems = [list(rng.integers(0, 1000, size=int(rng.integers(16, max_sys + 1)))) for _ in range(n_prompts)]
+    reqs = []
+    for i in range(n_req):
+        ids = systems[int(rng.integers(n_prompts))] + list(rng.integers(0, 1000, size=int(rng.integers(1, max_tail))))
+        reqs.append((int(rng.integers(0, 3 * n_req)), i, ids, len(ids) + int(rng.integers(0, max_out))))
+    return sorted(reqs, key=lambda r: (r[0], r[1]))
+
+
+def run_prefix_trace(sched, reqs, on_step=None):
+    pending = list(reqs)
+    history = []
+    for step in range(5000):
+        while pending and pending[0][0] <= step:
+            _, i, ids, total = pending.pop(0)
+            sched.submit(i, len(ids), total, ids)
+        st = sched.step()
+        st = st if isinstance(st, dict) else as_lists(st)
+        history.append(st)
+        if on_step:
+            on_step(step, st)
+        if st["num_running"] == 0 and st["num_waiting"] == 0 and st["num_swapped"] == 0 and not pending:
+            return history
+    raise AssertionError("trace did not drain")
+
+
+PREFIX_CASES = [  # (seed, requests, prompts, max system, max tail, max output, blocks, host blocks, rows, budget)
+    (31, 40, 3, 80, 30, 60, 30, 20, 6, 128),
+    (32, 60, 2, 130, 20, 40, 24, 6, 8, 96),     # tight: swaps, recomputes and evictions
+    (33, 30, 5, 40, 50, 90, 40, 40, 4, 256),
+]
+
+
+@pytest.mark.parametrize("case", PREFIX_CASES, ids=[f"seed{c[0]}" for c in PREFIX_CASES])
+def test_prefix_cached_admission_reads_back_every_token(case):
+    """Replay with content labels: a prompt token's label is its whole prefix,
+    so a row that shares a cached block must read exactly its own prefix."""
+    seed, n, npr, msys, mtail, mout, nb, nh, rows, budget = case
+    rng = np.random.default_rng(seed)
+    reqs = prefix_trace(rng, n, npr, msys, mtail, mout)
+    prompt = {i: ids for _, i, ids, _ in reqs}
+    maxb = -(-max(t for *_, t in reqs) // 16)
+    bm = RefBlockManager(nb)
+    bm.enable_prefix_cache()
+    bm.set_host_pool(nh)
+    sched = RefScheduler(bm, rows, maxb, budget)
+
+    def label(s, p):
+        return ("prefix", tuple(prompt[s][: p + 1])) if p < len(prompt[s]) else (s, p)
+
+    world = LabelWorld(nb, max(nh, 1), rows, maxb, label)
+    cached = [0]
+
+    def on_step(step, st):
+        world.apply(st)
+        world.check_rows(st)
+        cached[0] += st["num_cached_tokens"]
+
+    run_prefix_trace(sched, reqs, on_step)
+    assert cached[0] > 0, "the trace is meant to hit the prefix cache"
+
+
+@pytest.mark.parametrize("case", PREFIX_CASES, ids=[f"seed{c[0]}" for c in PREFIX_CASES])
+def test_native_prefix_cached_admission_matches_the_oracle(case):
+    seed, n, npr, msys, mtail, mout, nb, nh, rows, budget = case
+    rng = np.random.default_rng(seed)
+    reqs = prefix_trace(rng, n, npr, msys, mtail, mout)
+    maxb = -(-max(t for *_, t in reqs) // 16)
+    ref_bm, nat_bm = RefBlockManager(nb), BlockManager(nb)
+    for bm in (ref_bm, nat_bm):
+        bm.enable_prefix_cache()
+        bm.set_host_pool(nh)
+    h_ref = run_prefix_trace(RefScheduler(ref_bm, rows, maxb, budget), reqs)
+    h_nat = run_prefix_trace(Scheduler(nat_bm, rows, maxb, budget), reqs)
+    assert len(h_ref) == len(h_nat)
+    for k, (a, b) in enumerate(zip(h_ref, h_nat)):
+        assert as_lists(a) == b, f"step {k} differs"
