@@ -41,7 +41,8 @@ def decode_bytes(ctx: np.ndarray, w) -> float:
     kv = float(np.sum(ctx, dtype=np.int64)) * w.num_kv_heads * w.head_dim * 2 * e
     nq = w.append if w.lengths.get("mode") == "multi" else 1  # queries per sequence
     qo = 2.0 * len(ctx) * nq * w.num_q_heads * w.head_dim * e
-    tab = float(np.sum((ctx + 15) // 16, dtype=np.int64)) * 4
+    bs = w.block_size
+    tab = float(np.sum((ctx + bs - 1) // bs, dtype=np.int64)) * 4
     return kv + qo + tab
 
 
@@ -84,7 +85,7 @@ def cpu_baseline(w, budget_s: float = 15.0):
     from oracle.block_manager import RefBlockManager
     from workloads import run_program
 
-    ref = RefBlockManager(w.num_blocks, free_order=w.free_order)
+    ref = RefBlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
     run_program(ref, w.program)
     slots, _ = ref.append_tokens(list(w.step_seqs))
     table, ctx = ref.block_table(list(w.batch), w.max_blocks_per_seq(), pad=0)
@@ -467,7 +468,8 @@ def main():
                     help="untimed steps first (5; 150 for serving_bf16, which fills its batch meanwhile)")
     ap.add_argument("--workload", default="mha7b_f16",
                     choices=["tiny_f32", "mha7b_f16", "gqa8b_bf16", "shared_prefix_bf16", "longctx_bf16",
-                             "specdec_bf16", "serving_bf16", "serving_prefix_bf16"])
+                             "specdec_bf16", "serving_bf16", "serving_prefix_bf16", "mha7b_f16_bs32",
+                             "mha7b_f16_bs64", "gqa8b_bf16_bs32"])
     ap.add_argument("--partition", type=int, default=0, help="tokens per context partition (0 = the library's choice)")
     ap.add_argument("--cold-iters", type=int, default=20, help="decode launches timed after a 1 GiB cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -526,7 +528,7 @@ def main():
     extra = (args.warmup + args.steps + 2) * w.append if grows else 0
     maxB = w.max_blocks_per_seq(extra)
     pad = w.num_blocks + 1  # never read
-    bm = BlockManager(w.num_blocks, free_order=w.free_order)
+    bm = BlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
     run_program(bm, w.program)
 
     k_pool, v_pool = to_dev(w.k_pool), to_dev(w.v_pool)

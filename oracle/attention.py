@@ -31,7 +31,7 @@ patterns; the oracle widens those exact values to fp64 itself.
 
 import numpy as np
 
-from .layout import BLOCK_SIZE, tile_index
+from .layout import BLOCK_SIZE, block_index
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
@@ -73,19 +73,21 @@ def reshape_and_cache(k_cache: np.ndarray, v_cache: np.ndarray, key: np.ndarray,
                       slot_mapping: np.ndarray) -> None:
     """Write each new token's K and V rows into its slot, in place, bit for bit.
 
-    key / value are [T, Hkv, D]; slot t names physical block slot // 16 and
-    offset slot % 16 (on-demand filling of blocks as tokens are stored: [OS]
-    "PagedAttention: Virtual Memory for KV Cache", How It Works).  Negative
-    slots are skipped.
+    key / value are [T, Hkv, D]; slot t names physical block slot // bs and
+    offset slot % bs, bs = the pool's block size (16 unless a variant pool of
+    32 or 64 tokens per block is passed) (on-demand filling of blocks as
+    tokens are stored: [OS] "PagedAttention: Virtual Memory for KV Cache", How
+    It Works).  Negative slots are skipped.
     """
     T, Hkv, D = key.shape
-    kidx = tile_index("k", D)
-    vidx = tile_index("v", D)
+    bs = k_cache.shape[2] // D
+    kidx = block_index("k", D, bs)
+    vidx = block_index("v", D, bs)
     for t in range(T):
         slot = int(slot_mapping[t])
         if slot < 0:
             continue
-        b, o = divmod(slot, BLOCK_SIZE)
+        b, o = divmod(slot, bs)
         for h in range(Hkv):
             k_cache[b, h, kidx[o]] = key[t, h]
             v_cache[b, h, vidx[o]] = value[t, h]
@@ -112,24 +114,25 @@ def swap_blocks(dst_k: np.ndarray, dst_v: np.ndarray, src_k: np.ndarray, src_v: 
         dst_v[dst] = src_v[src]
 
 
-def gather_kv(k_cache, v_cache, table_row, ctx: int, dtype: str):
+def gather_kv(k_cache, v_cache, table_row, ctx: int, dtype: str, block_size: int = BLOCK_SIZE):
     """Contiguous fp64 K and V of one sequence, [Hkv, ctx, D] each.
 
     Logical block j of the sequence is physical block table_row[j]; token
-    position p is offset p % 16 of logical block p // 16.  Only the first
-    ceil(ctx / 16) table entries are read.
+    position p is offset p % bs of logical block p // bs.  Only the first
+    ceil(ctx / bs) table entries are read.
     """
-    NB, Hkv, tile = k_cache.shape
-    D = tile // BLOCK_SIZE
-    nb = -(-ctx // BLOCK_SIZE)
+    NB, Hkv, run = k_cache.shape
+    bs = block_size
+    D = run // bs
+    nb = -(-ctx // bs)
     phys = np.asarray(table_row[:nb], dtype=np.int64)
-    kidx = tile_index("k", D)
-    vidx = tile_index("v", D)
-    # [nb, Hkv, 16, D] in (logical block, head, token, dim) order
+    kidx = block_index("k", D, bs)
+    vidx = block_index("v", D, bs)
+    # [nb, Hkv, bs, D] in (logical block, head, token, dim) order
     K = to_f64(k_cache[phys][:, :, kidx], dtype)
     V = to_f64(v_cache[phys][:, :, vidx], dtype)
-    K = K.transpose(1, 0, 2, 3).reshape(Hkv, nb * BLOCK_SIZE, D)[:, :ctx]
-    V = V.transpose(1, 0, 2, 3).reshape(Hkv, nb * BLOCK_SIZE, D)[:, :ctx]
+    K = K.transpose(1, 0, 2, 3).reshape(Hkv, nb * bs, D)[:, :ctx]
+    V = V.transpose(1, 0, 2, 3).reshape(Hkv, nb * bs, D)[:, :ctx]
     return K, V
 
 
@@ -149,6 +152,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, dtype:
     """
     S, Hq, D = q.shape
     Hkv = k_cache.shape[1]
+    bs = k_cache.shape[2] // D
     G = Hq // Hkv
     out = np.zeros((S, Hq, D), dtype=np.float64)
     qf = to_f64(q, dtype)
@@ -156,7 +160,7 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, dtype:
         n = int(context_lens[s])
         if n == 0:
             continue
-        K, V = gather_kv(k_cache, v_cache, block_tables[s], n, dtype)
+        K, V = gather_kv(k_cache, v_cache, block_tables[s], n, dtype, bs)
         for h in (range(Hq) if heads is None else heads):
             g = h // G
             z = scale * (K[g] @ qf[s, h])
@@ -174,13 +178,14 @@ def prefill_chunk(q, k_cache, v_cache, block_tables, context_lens, scale: float,
     """
     S, C, Hq, D = q.shape
     Hkv = k_cache.shape[1]
+    bs = k_cache.shape[2] // D
     G = Hq // Hkv
     out = np.zeros((S, C, Hq, D), dtype=np.float64)
     for s in (range(S) if seqs is None else seqs):
         n = int(context_lens[s])
         if n < C:
             raise ValueError("the chunk must lie inside the context")
-        K, V = gather_kv(k_cache, v_cache, block_tables[s], n, dtype)
+        K, V = gather_kv(k_cache, v_cache, block_tables[s], n, dtype, bs)
         qf = to_f64(q[s], dtype)
         for i in (range(C) if rows is None else rows):
             last = n - C + i

@@ -5,7 +5,7 @@ Pages cited (by title and section):
   [VIZ] "vLLM Architecture and PagedAttention - Interactive Visualization"
 
 What it models:
-  * one pool of fixed 16-token blocks; a per-sequence block table maps
+  * one pool of fixed blocks of 16 tokens (32 and 64 as variants); a per-sequence block table maps
     logical block i to a physical block; the free list holds blocks no
     sequence uses ([OS] "PagedAttention: Virtual Memory for KV Cache", How It
     Works and the memory-layout example with its free list);
@@ -61,8 +61,9 @@ class BadRequest(Exception):
 
 class RefBlockManager:
     def __init__(self, num_blocks: int, block_size: int = BLOCK_SIZE, free_order=None):
-        if block_size != BLOCK_SIZE:
-            raise BadRequest("block_size must be 16")
+        if block_size not in (16, 32, 64):
+            raise BadRequest("block_size must be 16, 32 or 64")
+        self.bs = int(block_size)
         self.num_blocks = int(num_blocks)
         order = list(range(num_blocks)) if free_order is None else [int(b) for b in free_order]
         if sorted(order) != list(range(num_blocks)):
@@ -132,9 +133,8 @@ class RefBlockManager:
         if self.host_ref[h] == 0:
             self.host_free.append(h)
 
-    @staticmethod
-    def _nblocks(n: int) -> int:
-        return -(-n // BLOCK_SIZE)
+    def _nblocks(self, n: int) -> int:
+        return -(-n // self.bs)
 
     # -- updates -----------------------------------------------------------
     def add_seq(self, seq, num_tokens: int) -> None:
@@ -148,9 +148,9 @@ class RefBlockManager:
     def add_seq_with_prefix(self, seq, prefix_seq, prefix_tokens: int, tail_tokens: int) -> None:
         if seq in self.seqs or prefix_seq not in self.seqs or self._on_host(prefix_seq):
             raise BadRequest("duplicate sequence, or unknown or swapped-out prefix sequence")
-        if prefix_tokens % BLOCK_SIZE or not 0 <= prefix_tokens <= self.seqs[prefix_seq]["n"] or tail_tokens < 0:
+        if prefix_tokens % self.bs or not 0 <= prefix_tokens <= self.seqs[prefix_seq]["n"] or tail_tokens < 0:
             raise BadRequest("a shared prefix is a whole number of blocks inside the prefix sequence")
-        shared = self.seqs[prefix_seq]["blocks"][: prefix_tokens // BLOCK_SIZE]
+        shared = self.seqs[prefix_seq]["blocks"][: prefix_tokens // self.bs]
         need = self._nblocks(tail_tokens)
         if need > self.num_free():
             raise NoSpace()
@@ -197,7 +197,7 @@ class RefBlockManager:
             for s in seqs:
                 st = self.seqs[s]
                 pos = st["n"]
-                if pos % BLOCK_SIZE == 0:
+                if pos % self.bs == 0:
                     if not self.num_free():
                         raise NoSpace()
                     st["blocks"].append(self._take())
@@ -210,7 +210,7 @@ class RefBlockManager:
                         self.ref[last] -= 1
                         st["blocks"][-1] = fresh
                         cows.append((last, fresh))
-                slots.append(st["blocks"][pos // BLOCK_SIZE] * BLOCK_SIZE + pos % BLOCK_SIZE)
+                slots.append(st["blocks"][pos // self.bs] * self.bs + pos % self.bs)
                 st["n"] = pos + 1
             return slots, cows
         except NoSpace:
@@ -231,8 +231,8 @@ class RefBlockManager:
         many of them wait in the evictable list.  Changes nothing."""
         tokens = [int(t) for t in tokens]
         hits = []
-        for i in range(len(tokens) // BLOCK_SIZE):
-            b = self.cache.get(tuple(tokens[: BLOCK_SIZE * (i + 1)]))
+        for i in range(len(tokens) // self.bs):
+            b = self.cache.get(tuple(tokens[: self.bs * (i + 1)]))
             if b is None:
                 break
             hits.append(b)
@@ -247,8 +247,8 @@ class RefBlockManager:
             raise BadRequest("duplicate sequence")
         tokens = [int(t) for t in tokens]
         n = len(tokens)
-        full, total = n // BLOCK_SIZE, self._nblocks(n)
-        prefixes = [tuple(tokens[: BLOCK_SIZE * (i + 1)]) for i in range(full)]
+        full, total = n // self.bs, self._nblocks(n)
+        prefixes = [tuple(tokens[: self.bs * (i + 1)]) for i in range(full)]
         hits = []
         for p in prefixes:
             if p not in self.cache:
@@ -274,7 +274,7 @@ class RefBlockManager:
                 self.cache[prefixes[i]] = b
                 self.block_key[b] = prefixes[i]
         self.seqs[seq] = {"blocks": blocks, "n": n}
-        return len(hits) * BLOCK_SIZE
+        return len(hits) * self.bs
 
     # -- swap pool ---------------------------------------------------------
     def set_host_pool(self, num_host_blocks: int) -> None:

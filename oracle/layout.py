@@ -15,6 +15,10 @@ V tile  element (token t, dim d) sits at
         i.e. [D/32][4 token quads][16 dims][2 dim halves][4 tokens]
 
 D must be a multiple of 32.
+
+Blocks of 32 or 64 tokens (variants; the pages fix 16): the (block, kv head)
+run of bs * D elements is bs / 16 such tiles one after another, token t of
+the block in tile t // 16 at token t % 16.
 """
 
 import numpy as np
@@ -41,4 +45,16 @@ def tile_index(which: str, head_dim: int) -> np.ndarray:
     for t in range(BLOCK_SIZE):
         for d in range(head_dim):
             idx[t, d] = f(t, d)
+    return idx
+
+
+def block_index(which: str, head_dim: int, block_size: int = BLOCK_SIZE) -> np.ndarray:
+    """[block_size, D] int64 array: position of every (token, dim) inside one
+    (block, kv head) run of block_size * D elements."""
+    if block_size % BLOCK_SIZE:
+        raise ValueError("block_size must be a multiple of 16")
+    tile = tile_index(which, head_dim)
+    idx = np.empty((block_size, head_dim), dtype=np.int64)
+    for t in range(block_size):
+        idx[t] = (t // BLOCK_SIZE) * BLOCK_SIZE * head_dim + tile[t % BLOCK_SIZE]
     return idx

@@ -41,11 +41,7 @@ Readings where the pages are silent (the same rules the library documents):
 
 from bisect import insort
 
-from .block_manager import BLOCK_SIZE, BadRequest
-
-
-def _blocks(n: int) -> int:
-    return -(-n // BLOCK_SIZE)
+from .block_manager import BadRequest
 
 
 class RefScheduler:
@@ -68,7 +64,7 @@ class RefScheduler:
             raise BadRequest("need 1 <= prompt <= total and a request id >= 0")
         if prompt_ids is not None and (not self.bm.prefix_cache or len(prompt_ids) != prompt_tokens):
             raise BadRequest("token ids need prefix caching on and one id per prompt token")
-        if _blocks(total_tokens) > min(self.max_blocks, self.bm.num_blocks):
+        if self.bm._nblocks(total_tokens) > min(self.max_blocks, self.bm.num_blocks):
             raise BadRequest("request can never fit")
         if seq in self.req or seq in self.bm.seqs:
             raise BadRequest("duplicate request")
@@ -84,7 +80,7 @@ class RefScheduler:
         refs = {}
         for _, s in self.running:
             st = self.bm.seqs[s]
-            if st["n"] % BLOCK_SIZE == 0:
+            if st["n"] % self.bm.bs == 0:
                 need += 1
             else:
                 last = st["blocks"][-1]
@@ -143,7 +139,7 @@ class RefScheduler:
             if row < 0:
                 break
             n = bm.num_tokens(s)
-            grow = 1 if n % BLOCK_SIZE == 0 else 0
+            grow = 1 if n % bm.bs == 0 else 0
             if len(bm.seqs[s]["blocks"]) + grow + reserve > bm.num_free():
                 break
             out["swap_in"] += bm.swap_in([s])
@@ -166,7 +162,7 @@ class RefScheduler:
                 row = self._free_row()
                 if row < 0:
                     break
-                take = _blocks(r["prompt"])
+                take = bm._nblocks(r["prompt"])
                 if r["ids"] is not None:  # cached prefix blocks are shared; claiming an evictable one uses it up
                     hits, claimed = bm.prefix_hits(r["ids"])
                     take = take - len(hits) + claimed
@@ -182,10 +178,10 @@ class RefScheduler:
                 else:
                     bm.add_seq(s, r["prompt"])
                 blocks = bm.seqs[s]["blocks"]
-                for j in range(first // BLOCK_SIZE):  # cached blocks are not written: their entries are patched
+                for j in range(first // bm.bs):  # cached blocks are not written: their entries are patched
                     out["patches"].append((row, j, blocks[j]))
                 for p in range(first, r["prompt"]):
-                    out["slots"].append(blocks[p // BLOCK_SIZE] * BLOCK_SIZE + p % BLOCK_SIZE)
+                    out["slots"].append(blocks[p // bm.bs] * bm.bs + p % bm.bs)
                     out["token_rows"].append(row)
                     out["token_positions"].append(p)
                 left -= r["prompt"]

@@ -16,10 +16,9 @@ def _ptr(a: np.ndarray):
 
 
 class BlockManager:
-    """Pool of ``num_blocks`` 16-token blocks with a free list, reference
-    counts and copy-on-write (see include/pa.h for the exact rules)."""
-
-    BLOCK_SIZE = 16
+    """Pool of ``num_blocks`` blocks of ``block_size`` (16, 32 or 64) tokens with
+    a free list, reference counts and copy-on-write (see include/pa.h for the
+    exact rules)."""
 
     def __init__(self, num_blocks: int, block_size: int = 16, free_order=None):
         self._l = _lib.load()
@@ -33,6 +32,7 @@ class BlockManager:
             raise _lib.PAError(_lib.PA_EINVAL, self._l.pa_last_error().decode())
         self._h = ctypes.c_void_p(h)
         self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
 
     def close(self) -> None:
         if getattr(self, "_h", None):
@@ -94,7 +94,7 @@ class BlockManager:
 
     def _swap(self, fn, seqs):
         seqs = np.ascontiguousarray(seqs, dtype=np.int64)
-        total = sum(-(-max(self.num_tokens(int(s)), 0) // 16) for s in seqs)
+        total = sum(-(-max(self.num_tokens(int(s)), 0) // self.block_size) for s in seqs)
         pairs = np.empty((max(total, 1), 2), dtype=np.int64)
         n = ctypes.c_int32(0)
         _lib.check(fn(self._h, _ptr(seqs), seqs.shape[0], _ptr(pairs), ctypes.byref(n)))
@@ -152,6 +152,6 @@ class BlockManager:
         n = self.num_tokens(seq)
         if n < 0:
             raise _lib.UnknownSequence(_lib.PA_ENOENT, f"unknown sequence {seq}")
-        nb = -(-n // 16)
+        nb = -(-n // self.block_size)
         table, _ = self.block_table([seq], max(nb, 1))
         return table[0, :nb].tolist()

@@ -25,9 +25,15 @@ pa_status_t hip_status(hipError_t e, const char* what) {
   return fail(PA_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// log2 of 16-token tiles per block for the supported block sizes, else -1.
+int32_t tile_shift_of(int32_t block_size) {
+  return block_size == 16 ? 0 : block_size == 32 ? 1 : block_size == 64 ? 2 : -1;
+}
+
 pa_status_t check_pool(int32_t kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype_t dtype) {
   if (!known_dtype(dtype)) return fail(PA_EUNSUPPORTED, "unknown dtype %d", int(dtype));
-  if (block_size != 16) return fail(PA_EUNSUPPORTED, "block_size must be 16 (got %d)", block_size);
+  if (tile_shift_of(block_size) < 0)
+    return fail(PA_EUNSUPPORTED, "block_size must be 16, 32 or 64 (got %d)", block_size);
   if (head_dim != 64 && head_dim != 128) return fail(PA_EUNSUPPORTED, "head_dim must be 64 or 128 (got %d)", head_dim);
   if (kv_heads <= 0) return fail(PA_EINVAL, "num_kv_heads must be positive (got %d)", kv_heads);
   if (num_blocks <= 0) return fail(PA_EINVAL, "num_blocks must be positive");
@@ -83,7 +89,7 @@ pa_status_t check_decode(const void* out, pa_dtype_t out_dtype, const void* q, i
   if (!(out_dtype == PA_F32 || out_dtype == dtype))
     return fail(PA_EUNSUPPORTED, "out_dtype must be PA_F32 or the input dtype");
   if (max_ctx < 0) return fail(PA_EINVAL, "max_context_len must be >= 0");
-  if (max_blocks < 0 || int64_t(max_blocks) * 16 < max_ctx)
+  if (max_blocks < 0 || int64_t(max_blocks) * bs < max_ctx)
     return fail(PA_EINVAL, "max_blocks_per_seq (%d) cannot hold max_context_len (%d)", max_blocks, max_ctx);
   if (!isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");
   if (partition < 0 || partition % 16 != 0) return fail(PA_EINVAL, "partition_size must be 0 or a positive multiple of 16");
@@ -148,6 +154,7 @@ pa_status_t run_decode(DecodePhase phase, void* out, pa_dtype_t out_dtype, const
   a.partition = dc.partition;
   a.num_partitions = dc.nparts;
   a.q_len = q_len;
+  a.tile_shift = tile_shift_of(bs);
   if (need > 0) split_workspace(workspace, int64_t(S) * q_len, Hq, D, dc.nparts, &a.ws_acc, &a.ws_m, &a.ws_l);
   a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
@@ -191,7 +198,8 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* k_cac
   if (num_tokens == 0) return PA_OK;
   if (!key || !value || !k_cache || !v_cache || !slot_mapping) return fail(PA_EINVAL, "null pointer argument");
   return hip_status(launch_reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, num_tokens, num_kv_heads,
-                                             head_dim, num_blocks, elem_bytes(dtype), static_cast<hipStream_t>(stream)),
+                                             head_dim, num_blocks, tile_shift_of(block_size), elem_bytes(dtype),
+                                             static_cast<hipStream_t>(stream)),
                     "reshape_and_cache launch");
 }
 
@@ -227,6 +235,7 @@ pa_status_t pa_append_step(const void* key, const void* value, void* k_cache, vo
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
   a.num_blocks = num_blocks;
+  a.tile_shift = tile_shift_of(block_size);
   a.elem_bytes = elem_bytes(dtype);
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(launch_append_step(a), "append_step launch");
@@ -240,7 +249,7 @@ pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, i
   if (num_pairs < 0) return fail(PA_EINVAL, "num_pairs must be >= 0");
   if (num_pairs == 0) return PA_OK;
   if (!k_cache || !v_cache || !pairs) return fail(PA_EINVAL, "null pointer argument");
-  const int64_t block_bytes = int64_t(num_kv_heads) * 16 * head_dim * elem_bytes(dtype);
+  const int64_t block_bytes = int64_t(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
   return hip_status(launch_copy_blocks(k_cache, v_cache, k_cache, v_cache, pairs, num_pairs, block_bytes, num_blocks,
                                        num_blocks, static_cast<hipStream_t>(stream)),
                     "copy_blocks launch");
@@ -256,7 +265,7 @@ pa_status_t pa_swap_blocks(void* dst_k, void* dst_v, int64_t dst_blocks, const v
   if (num_pairs == 0) return PA_OK;
   if (!dst_k || !dst_v || !src_k || !src_v || !pairs) return fail(PA_EINVAL, "null pointer argument");
   if (src_k == dst_k || src_v == dst_v) return fail(PA_EINVAL, "source and destination pools must differ");
-  const int64_t block_bytes = int64_t(num_kv_heads) * 16 * head_dim * elem_bytes(dtype);
+  const int64_t block_bytes = int64_t(num_kv_heads) * block_size * head_dim * elem_bytes(dtype);
   return hip_status(launch_copy_blocks(dst_k, dst_v, src_k, src_v, pairs, num_pairs, block_bytes, src_blocks,
                                        dst_blocks, static_cast<hipStream_t>(stream)),
                     "swap_blocks launch");
@@ -381,7 +390,7 @@ pa_status_t pa_prefill_chunk(void* out, pa_dtype_t out_dtype, const void* q, int
   if (num_q_heads / num_kv_heads > 16) return fail(PA_EUNSUPPORTED, "query group %d > 16", num_q_heads / num_kv_heads);
   if (!(out_dtype == PA_F32 || out_dtype == dtype)) return fail(PA_EUNSUPPORTED, "out_dtype must be PA_F32 or the input dtype");
   if (max_context_len < chunk_len) return fail(PA_EINVAL, "max_context_len must be >= chunk_len");
-  if (max_blocks_per_seq < 0 || int64_t(max_blocks_per_seq) * 16 < max_context_len)
+  if (max_blocks_per_seq < 0 || int64_t(max_blocks_per_seq) * block_size < max_context_len)
     return fail(PA_EINVAL, "max_blocks_per_seq cannot hold max_context_len");
   if (!isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");
   if (num_seqs == 0 || chunk_len == 0) return PA_OK;
@@ -404,6 +413,7 @@ pa_status_t pa_prefill_chunk(void* out, pa_dtype_t out_dtype, const void* q, int
   a.num_blocks = num_blocks;
   a.scale_log2 = scale * kLog2e;
   a.max_context_len = max_context_len;
+  a.tile_shift = tile_shift_of(block_size);
   a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(launch_prefill_chunk(a), "prefill launch");

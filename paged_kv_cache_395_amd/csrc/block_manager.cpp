@@ -38,7 +38,7 @@ int64_t append_need(const pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* co
     auto si = sim.find(seqs[i]);
     SimSeq st = si == sim.end() ? SimSeq{it->second.tokens, false} : si->second;
     if (st.tokens == INT32_MAX) return -fail(PA_EINVAL, "sequence too long");
-    if (st.tokens % kBlockTokensHost == 0) {
+    if (st.tokens % bm->bs == 0) {
       ++need;
       st.last_private = true;
     } else if (!st.last_private) {
@@ -63,9 +63,7 @@ int64_t append_need(const pa_bm* bm, const int64_t* seqs, int32_t n, int64_t* co
 
 namespace {
 
-constexpr int32_t kBS = pa::kBlockTokensHost;
-
-int64_t blocks_for(int64_t tokens) { return (tokens + kBS - 1) / kBS; }
+int64_t blocks_for(int64_t tokens, int32_t bs) { return (tokens + bs - 1) / bs; }
 
 // Validate a list of sequences for a swap: all known, none listed twice,
 // each in the expected residence.
@@ -86,11 +84,11 @@ pa_status_t check_swap_list(const pa_bm* bm, const int64_t* seqs, int32_t n, boo
   return PA_OK;
 }
 
-// Key of a full block: a hash of the prefix hash before it and its 16 token
+// Key of a full block: a hash of the prefix hash before it and its token
 // ids (FNV-1a 64 over their bytes, then the SplitMix64 finalizer to spread
 // the bits).  A match is confirmed against the stored parent hash and token
 // ids, so only a collision of whole-prefix hashes could mislead it.
-uint64_t block_key(uint64_t parent, const int32_t* tok) {
+uint64_t block_key(uint64_t parent, const int32_t* tok, int32_t bs) {
   uint64_t h = 1469598103934665603ull;
   auto mix = [&h](uint64_t x, int bytes) {
     for (int i = 0; i < bytes; ++i) {
@@ -99,7 +97,7 @@ uint64_t block_key(uint64_t parent, const int32_t* tok) {
     }
   };
   mix(parent, 8);
-  for (int i = 0; i < kBS; ++i) mix(uint32_t(tok[i]), 4);
+  for (int i = 0; i < bs; ++i) mix(uint32_t(tok[i]), 4);
   h ^= h >> 30;
   h *= 0xbf58476d1ce4e5b9ull;
   h ^= h >> 27;
@@ -114,8 +112,8 @@ int32_t lookup(const pa_bm* bm, uint64_t k, uint64_t parent, const int32_t* tok)
   if (it == bm->cached.end()) return -1;
   const int32_t b = it->second;
   if (bm->parent_key[size_t(b)] != parent) return -1;
-  for (int i = 0; i < kBS; ++i)
-    if (bm->key_tokens[size_t(b) * kBS + i] != tok[i]) return -1;
+  for (int i = 0; i < bm->bs; ++i)
+    if (bm->key_tokens[size_t(b) * bm->bs + i] != tok[i]) return -1;
   return b;
 }
 
@@ -133,7 +131,7 @@ namespace pa {
 
 int64_t prefix_probe(const pa_bm* bm, const int32_t* tokens, int32_t num_tokens, std::vector<int32_t>* hits,
                      std::vector<uint64_t>* keys, std::vector<uint64_t>* parents) {
-  const int32_t full = num_tokens / kBS;
+  const int32_t full = num_tokens / bm->bs;
   keys->assign(size_t(full), 0);
   parents->assign(size_t(full), 0);
   hits->clear();
@@ -141,9 +139,9 @@ int64_t prefix_probe(const pa_bm* bm, const int32_t* tokens, int32_t num_tokens,
   bool hitting = true;
   int64_t claimed = 0;
   for (int32_t i = 0; i < full; ++i) {
-    const int32_t* tok = tokens + int64_t(i) * kBS;
+    const int32_t* tok = tokens + int64_t(i) * bm->bs;
     (*parents)[size_t(i)] = parent;
-    (*keys)[size_t(i)] = block_key(parent, tok);
+    (*keys)[size_t(i)] = block_key(parent, tok, bm->bs);
     if (hitting) {
       const int32_t b = lookup(bm, (*keys)[size_t(i)], parent, tok);
       if (b >= 0) {
@@ -163,8 +161,8 @@ int64_t prefix_probe(const pa_bm* bm, const int32_t* tokens, int32_t num_tokens,
 extern "C" {
 
 pa_bm_t* pa_bm_create(int64_t num_blocks, int32_t block_size, const int32_t* free_order) {
-  if (num_blocks <= 0 || num_blocks > INT32_MAX || block_size != kBS) {
-    fail(PA_EINVAL, "pa_bm_create: num_blocks must be in [1, 2^31) and block_size 16");
+  if (num_blocks <= 0 || num_blocks > INT32_MAX || !(block_size == 16 || block_size == 32 || block_size == 64)) {
+    fail(PA_EINVAL, "pa_bm_create: num_blocks must be in [1, 2^31) and block_size 16, 32 or 64");
     return nullptr;
   }
   pa_bm* bm = new (std::nothrow) pa_bm;
@@ -173,6 +171,7 @@ pa_bm_t* pa_bm_create(int64_t num_blocks, int32_t block_size, const int32_t* fre
     return nullptr;
   }
   bm->num_blocks = num_blocks;
+  bm->bs = block_size;
   bm->ref.assign(size_t(num_blocks), 0);
   if (free_order) {
     std::vector<char> seen(size_t(num_blocks), 0);
@@ -198,7 +197,7 @@ pa_status_t pa_bm_add_seq(pa_bm_t* bm, int64_t seq, int32_t num_tokens) {
   if (!bm) return fail(PA_EINVAL, "null block manager");
   if (num_tokens < 0) return fail(PA_EINVAL, "negative length");
   if (bm->seqs.count(seq)) return fail(PA_EINVAL, "sequence %lld already exists", (long long)seq);
-  const int64_t need = blocks_for(num_tokens);
+  const int64_t need = blocks_for(num_tokens, bm->bs);
   if (need > bm->available())
     return fail(PA_ENOSPC, "need %lld blocks, %lld free", (long long)need, (long long)bm->available());
   Seq s;
@@ -216,14 +215,14 @@ pa_status_t pa_bm_add_seq_with_prefix(pa_bm_t* bm, int64_t seq, int64_t prefix_s
   auto it = bm->seqs.find(prefix_seq);
   if (it == bm->seqs.end()) return fail(PA_ENOENT, "unknown prefix sequence %lld", (long long)prefix_seq);
   if (it->second.swapped) return fail(PA_EINVAL, "prefix sequence %lld is swapped out", (long long)prefix_seq);
-  if (prefix_tokens < 0 || prefix_tokens % kBS != 0 || prefix_tokens > it->second.tokens || tail_tokens < 0)
+  if (prefix_tokens < 0 || prefix_tokens % bm->bs != 0 || prefix_tokens > it->second.tokens || tail_tokens < 0)
     return fail(PA_EINVAL, "a shared prefix is a whole number of blocks inside the prefix sequence");
-  const int64_t need = blocks_for(tail_tokens);
+  const int64_t need = blocks_for(tail_tokens, bm->bs);
   if (need > bm->available())
     return fail(PA_ENOSPC, "need %lld blocks, %lld free", (long long)need, (long long)bm->available());
   Seq s;
   s.tokens = prefix_tokens + tail_tokens;
-  const int32_t shared = prefix_tokens / kBS;
+  const int32_t shared = prefix_tokens / bm->bs;
   s.blocks.assign(it->second.blocks.begin(), it->second.blocks.begin() + shared);
   for (int32_t b : s.blocks) ++bm->ref[size_t(b)];
   for (int64_t i = 0; i < need; ++i) s.blocks.push_back(bm->take());
@@ -276,7 +275,7 @@ pa_status_t pa_bm_append_tokens(pa_bm_t* bm, const int64_t* seqs, int32_t n, int
   for (int32_t i = 0; i < n; ++i) {
     Seq& s = bm->seqs.find(seqs[i])->second;
     const int32_t pos = s.tokens;
-    if (pos % kBS == 0) {
+    if (pos % bm->bs == 0) {
       s.blocks.push_back(bm->take());
     } else {
       const int32_t last = s.blocks.back();
@@ -289,7 +288,7 @@ pa_status_t pa_bm_append_tokens(pa_bm_t* bm, const int64_t* seqs, int32_t n, int
         ++nc;
       }
     }
-    slots[i] = int64_t(s.blocks[size_t(pos / kBS)]) * kBS + pos % kBS;
+    slots[i] = int64_t(s.blocks[size_t(pos / bm->bs)]) * bm->bs + pos % bm->bs;
     s.tokens = pos + 1;
   }
   if (num_cow) *num_cow = nc;
@@ -422,7 +421,7 @@ pa_status_t pa_bm_enable_prefix_cache(pa_bm_t* bm) {
   bm->prefix_cache = true;
   bm->key.assign(nb, 0);
   bm->parent_key.assign(nb, 0);
-  bm->key_tokens.assign(nb * kBS, 0);
+  bm->key_tokens.assign(nb * size_t(bm->bs), 0);
   bm->keyed.assign(nb, 0);
   bm->in_lru.assign(nb, 0);
   bm->lru_pos.assign(nb, bm->lru.end());
@@ -436,8 +435,8 @@ pa_status_t pa_bm_add_seq_tokens(pa_bm_t* bm, int64_t seq, const int32_t* tokens
   if (!bm->prefix_cache) return fail(PA_EINVAL, "prefix caching is off (pa_bm_enable_prefix_cache)");
   if (num_tokens < 0 || (num_tokens > 0 && !tokens)) return fail(PA_EINVAL, "bad arguments");
   if (bm->seqs.count(seq)) return fail(PA_EINVAL, "sequence %lld already exists", (long long)seq);
-  const int32_t full = num_tokens / kBS;
-  const int64_t total = blocks_for(num_tokens);
+  const int32_t full = num_tokens / bm->bs;
+  const int64_t total = blocks_for(num_tokens, bm->bs);
   // the leading run of full blocks already cached
   std::vector<uint64_t> keys, parents;
   std::vector<int32_t> hits;
@@ -470,12 +469,12 @@ pa_status_t pa_bm_add_seq_tokens(pa_bm_t* bm, int64_t seq, const int32_t* tokens
       bm->cached[k] = b;
       bm->key[size_t(b)] = k;
       bm->parent_key[size_t(b)] = parents[size_t(i)];
-      for (int t = 0; t < kBS; ++t) bm->key_tokens[size_t(b) * kBS + t] = tokens[i * kBS + t];
+      for (int t = 0; t < bm->bs; ++t) bm->key_tokens[size_t(b) * bm->bs + t] = tokens[i * bm->bs + t];
       bm->keyed[size_t(b)] = 1;
     }
   }
   bm->seqs.emplace(seq, std::move(s));
-  if (cached_tokens) *cached_tokens = int32_t(hits.size()) * kBS;
+  if (cached_tokens) *cached_tokens = int32_t(hits.size()) * bm->bs;
   return PA_OK;
 }
 

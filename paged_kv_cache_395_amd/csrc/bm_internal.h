@@ -13,10 +13,6 @@
 
 #include "pa_internal.h"
 
-namespace pa {
-constexpr int32_t kBlockTokensHost = 16;
-}
-
 struct Seq {
   std::vector<int32_t> blocks;  // device block ids; host block ids while swapped out
   int32_t tokens = 0;
@@ -25,6 +21,7 @@ struct Seq {
 
 struct pa_bm {
   int64_t num_blocks = 0;
+  int32_t bs = 16;  // tokens per block: 16, 32 or 64
   std::vector<int32_t> ref;
   std::deque<int32_t> free_q;  // head = next block handed out, tail = most recently released
   std::unordered_map<int64_t, Seq> seqs;

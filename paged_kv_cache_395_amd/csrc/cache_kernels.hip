@@ -13,6 +13,14 @@
 namespace pa {
 namespace {
 
+// Element offset of the 16-token tile that holds `slot`, for kv head h: a
+// (block, kv head) run is 2^sh consecutive tiles of 16 * D elements.
+__device__ inline int64_t slot_tile(int64_t slot, int h, int kv_heads, int head_dim, int sh) {
+  const int64_t blk = slot >> (4 + sh);
+  const int64_t sub = (slot >> 4) & ((1 << sh) - 1);
+  return (((blk * kv_heads + h) << sh) + sub) * int64_t(kBlockTokens * head_dim);
+}
+
 // One thread moves one 8-element run (dims 8j..8j+7 of one kv head) of one
 // token.  K: the run is contiguous in the tile ([D/8][16][8]), one vector
 // store.  V: the 8 dims scatter to 8 positions of the [D/32][4][16][2][4]
@@ -21,7 +29,7 @@ template <typename E>
 __global__ void __launch_bounds__(256)
 reshape_and_cache_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ kc,
                          E* __restrict__ vc, const int64_t* __restrict__ slots, int32_t num_tokens,
-                         int32_t kv_heads, int32_t head_dim, int64_t num_blocks) {
+                         int32_t kv_heads, int32_t head_dim, int64_t num_blocks, int32_t sh) {
   typedef E vec8 __attribute__((ext_vector_type(8)));
   const int runs_per_head = head_dim / 8;
   const int runs_per_token = kv_heads * runs_per_head;
@@ -32,11 +40,10 @@ reshape_and_cache_kernel(const E* __restrict__ key, const E* __restrict__ value,
   const int h = rem / runs_per_head;
   const int j = rem - h * runs_per_head;
   const int64_t slot = slots[t];
-  if (slot < 0 || slot >= num_blocks * kBlockTokens) return;  // skipped token, or outside the pool
-  const int64_t blk = slot >> 4;
+  if (slot < 0 || slot >= (num_blocks << (4 + sh))) return;  // skipped token, or outside the pool
   const int o = int(slot & 15);
   const int64_t src = (int64_t(t) * kv_heads + h) * head_dim + 8 * j;
-  const int64_t tile = (blk * kv_heads + h) * int64_t(kBlockTokens * head_dim);
+  const int64_t tile = slot_tile(slot, h, kv_heads, head_dim, sh);
 
   const vec8 kv = *reinterpret_cast<const vec8*>(key + src);
   *reinterpret_cast<vec8*>(kc + tile + (j * kBlockTokens + o) * 8) = kv;
@@ -63,7 +70,7 @@ __global__ void __launch_bounds__(256)
 append_step_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ kc, E* __restrict__ vc,
                    const int64_t* slots, const int32_t* rows, const int32_t* positions, int32_t num_tokens,
                    int32_t* tables, int32_t max_blocks, int32_t* ctx, const int32_t* new_ctx, int32_t num_rows,
-                   int32_t kv_heads, int32_t head_dim, int64_t num_blocks) {
+                   int32_t kv_heads, int32_t head_dim, int64_t num_blocks, int32_t sh) {
   typedef E vec8 __attribute__((ext_vector_type(8)));
   const int t = blockIdx.x;
   if (t >= num_tokens) {
@@ -80,17 +87,16 @@ append_step_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __
   }
   __syncthreads();
   const int64_t slot = s_slot;
-  if (slot < 0 || slot >= num_blocks * kBlockTokens) return;  // skipped token, or outside the pool
+  if (slot < 0 || slot >= (num_blocks << (4 + sh))) return;  // skipped token, or outside the pool
   const int row = s_row, pos = s_pos;
-  if (threadIdx.x == 0 && row >= 0 && row < num_rows && pos >= 0 && pos / kBlockTokens < max_blocks)
-    tables[int64_t(row) * max_blocks + pos / kBlockTokens] = int32_t(slot >> 4);
-  const int64_t blk = slot >> 4;
+  if (threadIdx.x == 0 && row >= 0 && row < num_rows && pos >= 0 && (pos >> (4 + sh)) < max_blocks)
+    tables[int64_t(row) * max_blocks + (pos >> (4 + sh))] = int32_t(slot >> (4 + sh));
   const int o = int(slot & 15);
   const int runs_per_head = head_dim / 8;
   for (int c = threadIdx.x; c < kv_heads * runs_per_head; c += blockDim.x) {
     const int h = c / runs_per_head, j = c - h * runs_per_head;
     const int64_t src = (int64_t(t) * kv_heads + h) * head_dim + 8 * j;
-    const int64_t tile = (blk * kv_heads + h) * int64_t(kBlockTokens * head_dim);
+    const int64_t tile = slot_tile(slot, h, kv_heads, head_dim, sh);
     *reinterpret_cast<vec8*>(kc + tile + (j * kBlockTokens + o) * 8) = *reinterpret_cast<const vec8*>(key + src);
     const vec8 vv = *reinterpret_cast<const vec8*>(value + src);
     E* vt = vc + tile;
@@ -136,7 +142,8 @@ patch_tables_kernel(int32_t* __restrict__ tables, int32_t max_blocks, int32_t nu
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                                    int32_t head_dim, int64_t num_blocks, int elem_bytes, hipStream_t stream) {
+                                    int32_t head_dim, int64_t num_blocks, int32_t tile_shift, int elem_bytes,
+                                    hipStream_t stream) {
   if (num_tokens == 0) return hipSuccess;
   const int64_t runs = int64_t(num_tokens) * num_kv_heads * (head_dim / 8);
   const dim3 grid(unsigned((runs + 255) / 256));
@@ -144,12 +151,12 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
     hipLaunchKernelGGL(reshape_and_cache_kernel<uint16_t>, grid, dim3(256), 0, stream,
                        static_cast<const uint16_t*>(key), static_cast<const uint16_t*>(value),
                        static_cast<uint16_t*>(k_cache), static_cast<uint16_t*>(v_cache), slots, num_tokens,
-                       num_kv_heads, head_dim, num_blocks);
+                       num_kv_heads, head_dim, num_blocks, tile_shift);
   } else {
     hipLaunchKernelGGL(reshape_and_cache_kernel<uint32_t>, grid, dim3(256), 0, stream,
                        static_cast<const uint32_t*>(key), static_cast<const uint32_t*>(value),
                        static_cast<uint32_t*>(k_cache), static_cast<uint32_t*>(v_cache), slots, num_tokens,
-                       num_kv_heads, head_dim, num_blocks);
+                       num_kv_heads, head_dim, num_blocks, tile_shift);
   }
   return hipGetLastError();
 }
@@ -163,13 +170,13 @@ hipError_t launch_append_step(const AppendStepArgs& a) {
                        static_cast<const uint16_t*>(a.key), static_cast<const uint16_t*>(a.value),
                        static_cast<uint16_t*>(a.k_cache), static_cast<uint16_t*>(a.v_cache), a.slots, a.rows,
                        a.positions, a.num_tokens, a.tables, a.max_blocks, a.ctx, a.new_ctx, a.num_rows,
-                       a.num_kv_heads, a.head_dim, a.num_blocks);
+                       a.num_kv_heads, a.head_dim, a.num_blocks, a.tile_shift);
   } else {
     hipLaunchKernelGGL(append_step_kernel<uint32_t>, dim3(unsigned(grid)), dim3(256), 0, a.stream,
                        static_cast<const uint32_t*>(a.key), static_cast<const uint32_t*>(a.value),
                        static_cast<uint32_t*>(a.k_cache), static_cast<uint32_t*>(a.v_cache), a.slots, a.rows,
                        a.positions, a.num_tokens, a.tables, a.max_blocks, a.ctx, a.new_ctx, a.num_rows,
-                       a.num_kv_heads, a.head_dim, a.num_blocks);
+                       a.num_kv_heads, a.head_dim, a.num_blocks, a.tile_shift);
   }
   return hipGetLastError();
 }

@@ -64,6 +64,9 @@ struct KParams {
   int32_t max_blocks;
   int32_t hq, hkv, max_ctx, partition, nparts_max;
   int32_t qlen;  // queries per sequence (1: plain decode)
+  // log2 of 16-token tiles per block: a (block, kv head) run of the pool is
+  // 2^tile_shift consecutive tiles; the table has one entry per block
+  int32_t tile_shift;
 };
 
 template <typename T, bool OUT_F32>
@@ -78,7 +81,7 @@ __device__ inline void store_out(void* out, int64_t idx, float v) {
 // A context length the grid / table cannot cover is a caller error: report it
 // as NaN rows instead of reading out of bounds.
 __device__ inline bool context_out_of_contract(int ctx, const KParams& P) {
-  return ctx < 0 || ctx > P.max_ctx || ctx > P.max_blocks * kBlockTokens;
+  return ctx < 0 || ctx > P.max_ctx || int64_t(ctx) > (int64_t(P.max_blocks) * kBlockTokens << P.tile_shift);
 }
 
 // ------------------------------------------------------------------------
@@ -145,7 +148,9 @@ decode_mfma_kernel(KParams P) {
   const int ntok = min(P.partition, ctx - tok0);
   const int nblk = (ntok + kBlockTokens - 1) / kBlockTokens;
   const int nparts = (ctx + P.partition - 1) / P.partition;
-  const int32_t* trow = P.tables + int64_t(s) * P.max_blocks + tok0 / kBlockTokens;
+  const int sh = P.tile_shift;
+  const int tile0 = tok0 / kBlockTokens;  // the partition's first tile in the sequence
+  const int32_t* trow = P.tables + int64_t(s) * P.max_blocks;
 
   // Q^T as the B operand: lane supplies column n, dims 8 * (4 i + quad) + 0..7.
   u32x4_t qb[DC];
@@ -160,9 +165,9 @@ decode_mfma_kernel(KParams P) {
   // last key column n may attend (its query's position)
   const int last_n = ctx - C + (n < ncol ? n / G : 0);
 
-  const uint16_t* kg = P.k16 + int64_t(g) * kTileElems;
-  const uint16_t* vg = P.v16 + int64_t(g) * kTileElems;
-  const int64_t blk_stride = int64_t(P.hkv) * kTileElems;
+  const uint16_t* kg = P.k16 + (int64_t(g) << sh) * kTileElems;
+  const uint16_t* vg = P.v16 + (int64_t(g) << sh) * kTileElems;
+  const int64_t blk_stride = (int64_t(P.hkv) << sh) * kTileElems;
   const int voff = lane * 16;
 
   // Online softmax in the exp2 domain.  The reference max m of head n is
@@ -182,13 +187,15 @@ decode_mfma_kernel(KParams P) {
   const int ntw_all = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;  // tiles of this wave
   for (int wb = 0; wb < ntw_all; wb += kWave) {
     const int ntw = min(kWave, ntw_all - wb);
-    const int tbl = lane < ntw ? trow[kWaves * (wb + lane) + w] : 0;
+    const int tbl = lane < ntw ? trow[(tile0 + kWaves * (wb + lane) + w) >> sh] : 0;
 
     auto rsrc = [&](int i, const uint16_t* base) {
       const int phys = __builtin_amdgcn_readlane(tbl, i < ntw ? i : 0);
+      const int sub = (tile0 + kWaves * (wb + i) + w) & ((1 << sh) - 1);  // tile inside the block
       const bool ok = i < ntw && phys >= 0 && int64_t(phys) < P.num_blocks;
       bad |= i < ntw && !ok;  // an entry outside the pool: NaN result, nothing read
-      return tile_rsrc(base + int64_t(ok ? phys : 0) * blk_stride, ok ? kTileElems * 2 : 0);
+      return tile_rsrc(base + int64_t(ok ? phys : 0) * blk_stride + (ok ? sub : 0) * kTileElems,
+                       ok ? kTileElems * 2 : 0);
     };
     auto load = [&](int i, u32x4_t* kd, u32x4_t* vd) {
       const auto rk = rsrc(i, kg);
@@ -357,13 +364,15 @@ decode_f32_kernel(KParams P) {
   const int ntok = min(P.partition, ctx - tok0);
   const int nblk = (ntok + kBlockTokens - 1) / kBlockTokens;
   const int nparts = (ctx + P.partition - 1) / P.partition;
-  const int32_t* trow = P.tables + int64_t(s) * P.max_blocks + tok0 / kBlockTokens;
+  const int sh = P.tile_shift;
+  const int tile0 = tok0 / kBlockTokens;
+  const int32_t* trow = P.tables + int64_t(s) * P.max_blocks;
 
   f32x8_t qv[DC];
 #pragma unroll
   for (int i = 0; i < DC; ++i) qv[i] = *reinterpret_cast<const f32x8_t*>(P.q32 + row * D + 8 * (4 * i + quad));
 
-  const int64_t blk_stride = int64_t(P.hkv) * kTile;
+  const int64_t blk_stride = (int64_t(P.hkv) << sh) * kTile;
   float m = -INFINITY, lsum = 0.f;
   float acc[DC][2];
 #pragma unroll
@@ -371,13 +380,14 @@ decode_f32_kernel(KParams P) {
   bool bad = false;
 
   for (int jb = w; jb < nblk; jb += kWaves) {
-    int phys = trow[jb];
+    int phys = trow[(tile0 + jb) >> sh];
     if (phys < 0 || int64_t(phys) >= P.num_blocks) {
       bad = true;
       phys = 0;
     }
-    const float* kt = P.k32 + int64_t(phys) * blk_stride + int64_t(g) * kTile + lane * 8;
-    const float* vt = P.v32 + int64_t(phys) * blk_stride + int64_t(g) * kTile + lane * 8;
+    const int64_t tile = ((int64_t(g) << sh) + ((tile0 + jb) & ((1 << sh) - 1))) * kTile;
+    const float* kt = P.k32 + int64_t(phys) * blk_stride + tile + lane * 8;
+    const float* vt = P.v32 + int64_t(phys) * blk_stride + tile + lane * 8;
     f32x8_t kk[DC], vv[DC];
 #pragma unroll
     for (int i = 0; i < DC; ++i) kk[i] = *reinterpret_cast<const f32x8_t*>(kt + i * 512);
@@ -545,6 +555,7 @@ KParams make_params(const DecodeArgs& a) {
   p.partition = a.partition;
   p.nparts_max = a.num_partitions;
   p.qlen = a.q_len;
+  p.tile_shift = a.tile_shift;
   return p;
 }
 

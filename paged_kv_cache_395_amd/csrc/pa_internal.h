@@ -28,6 +28,7 @@ struct DecodeArgs {
   int32_t partition;
   int32_t num_partitions;  // ceil(max_context_len / partition)
   int32_t q_len;           // queries per sequence (1: plain decode)
+  int32_t tile_shift;      // log2(block_size / 16)
   float* ws_acc;           // [S][q_len][Hq][num_partitions][D]
   float* ws_m;             // [S][q_len][Hq][num_partitions]
   float* ws_l;             // [S][q_len][Hq][num_partitions]
@@ -52,6 +53,7 @@ struct PrefillArgs {
   int64_t num_blocks;
   float scale_log2;
   int32_t max_context_len;
+  int32_t tile_shift;  // log2(block_size / 16)
   pa_dtype_t dtype;
   hipStream_t stream;
 };
@@ -60,7 +62,8 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a);
 
 hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_cache, void* v_cache,
                                     const int64_t* slots, int32_t num_tokens, int32_t num_kv_heads,
-                                    int32_t head_dim, int64_t num_blocks, int elem_bytes, hipStream_t stream);
+                                    int32_t head_dim, int64_t num_blocks, int32_t tile_shift, int elem_bytes,
+                                    hipStream_t stream);
 
 struct AppendStepArgs {
   const void* key;
@@ -78,6 +81,7 @@ struct AppendStepArgs {
   int32_t num_rows;
   int32_t num_kv_heads, head_dim;
   int64_t num_blocks;
+  int32_t tile_shift;  // log2(block_size / 16)
   int elem_bytes;
   hipStream_t stream;
 };

@@ -42,6 +42,7 @@ struct PParams {
   float scale_log2;
   int32_t max_blocks;
   int32_t chunk, hq, hkv, max_ctx;
+  int32_t tile_shift;  // log2 of 16-token tiles per block (one table entry per block)
 };
 
 template <typename T, bool OUT_F32>
@@ -115,7 +116,7 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   const int row_wg0 = tile * kPfRows;
   if (row_wg0 >= R) return;
 
-  if (ctx < C || ctx > P.max_ctx || ctx > P.max_blocks * kBlockTokens) {
+  if (ctx < C || ctx > P.max_ctx || int64_t(ctx) > (int64_t(P.max_blocks) * kBlockTokens << P.tile_shift)) {
     // contract violation: NaN rows for this workgroup's share
     const float nan = __builtin_nanf("");
     for (int idx = threadIdx.x; idx < kPfRows * D; idx += kPfThreads) {
@@ -151,9 +152,10 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   const int nkb = (ctx - C + row_wg_last / G) / kBlockTokens + 1;  // key blocks any row needs
   const int nst = (nkb + kStageBlocks - 1) / kStageBlocks;
   const int32_t* trow = P.tables + int64_t(s) * P.max_blocks;
-  const int64_t blk_stride = int64_t(P.hkv) * kTileElems;
-  const char* kg = reinterpret_cast<const char*>(P.k + int64_t(g) * kTileElems);
-  const char* vg = reinterpret_cast<const char*>(P.v + int64_t(g) * kTileElems);
+  const int sh = P.tile_shift;
+  const int64_t blk_stride = (int64_t(P.hkv) << sh) * kTileElems;
+  const char* kg = reinterpret_cast<const char*>(P.k + (int64_t(g) << sh) * kTileElems);
+  const char* vg = reinterpret_cast<const char*>(P.v + (int64_t(g) << sh) * kTileElems);
 
   float m[kPfRT], lsum[kPfRT];
   f32x4_t o[kPfRT][NT];
@@ -168,7 +170,8 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
 
   int tab_base = 0;
   auto fill_table = [&](int base) {  // all threads; caller synchronises
-    for (int j = threadIdx.x; j < kTabWindow && base + j < nkb; j += kPfThreads) s_tab[j] = trow[base + j];
+    // one entry per 16-token tile (a block of 2^sh tiles repeats its entry)
+    for (int j = threadIdx.x; j < kTabWindow && base + j < nkb; j += kPfThreads) s_tab[j] = trow[(base + j) >> sh];
   };
 
   // issue the direct-to-LDS loads of stage st into buf (this wave's share):
@@ -189,7 +192,9 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
       const bool in_pool = phys >= 0 && int64_t(phys) < P.num_blocks;
       bad |= blk < nkb && !in_pool;
       const bool ok = blk < nkb && in_pool;
-      const char* base = (t8 < kStageBlocks ? kg : vg) + int64_t(ok ? phys : 0) * blk_stride * 2;
+      const int sub = blk & ((1 << sh) - 1);  // tile inside the block
+      const char* base = (t8 < kStageBlocks ? kg : vg) + (int64_t(ok ? phys : 0) * blk_stride +
+                                                          (ok ? sub : 0) * kTileElems) * 2;
       const __amdgpu_buffer_rsrc_t r =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, ok ? kTileBytes : 0, kBufferRsrcWord3);
       lds_void* dst = (lds_void*)(buf + t8 * (kTileElems / 8) + part * 64);
@@ -424,6 +429,7 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a) {
   p.hq = a.num_q_heads;
   p.hkv = a.num_kv_heads;
   p.max_ctx = a.max_context_len;
+  p.tile_shift = a.tile_shift;
   if (a.dtype == PA_BF16) return a.head_dim == 64 ? launch_prefill_t<Bf16, 64>(a, p) : launch_prefill_t<Bf16, 128>(a, p);
   return a.head_dim == 64 ? launch_prefill_t<F16, 64>(a, p) : launch_prefill_t<F16, 128>(a, p);
 }

@@ -32,8 +32,6 @@ using pa::fail;
 
 namespace {
 
-constexpr int32_t kBS = pa::kBlockTokensHost;
-
 struct Req {
   int64_t seq;
   int64_t arrival;
@@ -49,7 +47,7 @@ void insert_by_arrival(std::vector<Req>& v, const Req& r) {
   v.insert(pos, r);
 }
 
-int64_t blocks_for(int64_t tokens) { return (tokens + kBS - 1) / kBS; }
+int64_t blocks_for(int64_t tokens, int32_t bs) { return (tokens + bs - 1) / bs; }
 
 }  // namespace
 
@@ -114,7 +112,7 @@ pa_status_t pa_sched_submit_tokens(pa_sched_t* s, int64_t seq, const int32_t* pr
   if (seq < 0) return fail(PA_EINVAL, "request ids must be >= 0");
   if (prompt_tokens < 1 || total_tokens < prompt_tokens)
     return fail(PA_EINVAL, "need 1 <= prompt_tokens <= total_tokens");
-  const int64_t nb = blocks_for(total_tokens);
+  const int64_t nb = blocks_for(total_tokens, s->bm->bs);
   if (nb > s->max_blocks || nb > s->bm->num_blocks)
     return fail(PA_EINVAL, "a request of %d tokens can never fit (%lld blocks)", total_tokens, (long long)nb);
   if (s->known.count(seq) || s->bm->seqs.count(seq))
@@ -195,7 +193,7 @@ pa_status_t pa_sched_step(pa_sched_t* s, pa_sched_out_t* out) {
     if (row < 0) break;
     const Seq& sq = s->seq_of(r.seq);
     const int64_t nb = int64_t(sq.blocks.size());
-    const int64_t grow = sq.tokens % kBS == 0 ? 1 : 0;
+    const int64_t grow = sq.tokens % bm->bs == 0 ? 1 : 0;
     if (nb + grow + reserved > s->free_blocks()) break;
     s->scratch_pairs.resize(2 * size_t(nb) + 2);
     int32_t np = 0;
@@ -227,7 +225,7 @@ pa_status_t pa_sched_step(pa_sched_t* s, pa_sched_out_t* out) {
       const int32_t row = s->free_row();
       if (row < 0) break;
       // blocks the admission takes: fresh ones, plus cached ones it claims back from the evictable list
-      int64_t take = blocks_for(r.prompt), write_from = 0;
+      int64_t take = blocks_for(r.prompt, bm->bs), write_from = 0;
       const bool by_ids = !r.ids.empty();
       if (by_ids) {
         const int64_t claimed = pa::prefix_probe(bm, r.ids.data(), r.prompt, &hits, &keys, &parents);
@@ -246,13 +244,13 @@ pa_status_t pa_sched_step(pa_sched_t* s, pa_sched_out_t* out) {
       }
       if (st != PA_OK) return st;
       const Seq& sq = s->seq_of(r.seq);
-      for (int64_t j = 0; j < write_from / kBS; ++j) {  // cached blocks get no token write: patch the table
+      for (int64_t j = 0; j < write_from / bm->bs; ++j) {  // cached blocks get no token write: patch the table
         s->patches.push_back(row);
         s->patches.push_back(int32_t(j));
         s->patches.push_back(sq.blocks[size_t(j)]);
       }
       for (int32_t p = int32_t(write_from); p < r.prompt; ++p) {
-        s->slots.push_back(int64_t(sq.blocks[size_t(p / kBS)]) * kBS + p % kBS);
+        s->slots.push_back(int64_t(sq.blocks[size_t(p / bm->bs)]) * bm->bs + p % bm->bs);
         s->rows.push_back(row);
         s->positions.push_back(p);
       }

@@ -23,7 +23,7 @@ import torch
 
 from . import _lib
 from .block_manager import BlockManager
-from .ops import BLOCK_SIZE, _code, _p
+from .ops import _code, _p
 from .scheduler import Scheduler
 
 _TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
@@ -32,7 +32,7 @@ _TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 class Driver:
     def __init__(self, num_blocks, num_host_blocks, num_q_heads, num_kv_heads, head_dim, dtype, max_rows,
                  max_blocks_per_seq, max_batched_tokens, scale, free_order=None, device="cuda", ring=4,
-                 partition_size=0, prefix_cache=False):
+                 partition_size=0, prefix_cache=False, block_size=16):
         self._l = _lib.load()
         self.dtype = dtype
         tdt = _TORCH[dtype]
@@ -42,12 +42,13 @@ class Driver:
         self.rows, self.maxB = int(max_rows), int(max_blocks_per_seq)
         self.scale = float(scale)
         self.partition = int(partition_size)
-        self.bm = BlockManager(num_blocks, free_order=free_order)
+        self.bs = int(block_size)
+        self.bm = BlockManager(num_blocks, block_size=block_size, free_order=free_order)
         if prefix_cache:
             self.bm.enable_prefix_cache()
         self.bm.set_host_pool(num_host_blocks)
         self.sched = Scheduler(self.bm, max_rows, max_blocks_per_seq, max_batched_tokens)
-        tile = BLOCK_SIZE * head_dim
+        tile = self.bs * head_dim
         self.k_pool = torch.zeros((num_blocks, num_kv_heads, tile), dtype=tdt, device=dev)
         self.v_pool = torch.zeros_like(self.k_pool)
         nh = max(self.NH, 1)
@@ -57,12 +58,12 @@ class Driver:
         self.table = torch.full((max_rows, max_blocks_per_seq), num_blocks, dtype=torch.int32, device=dev)
         self.ctx = torch.zeros(max_rows, dtype=torch.int32, device=dev)
         # the first admission of a step may exceed the token budget by one whole request
-        self.cap = max_rows + max_batched_tokens + max_blocks_per_seq * BLOCK_SIZE
+        self.cap = max_rows + max_batched_tokens + max_blocks_per_seq * self.bs
         self.key = torch.zeros((self.cap, num_kv_heads, head_dim), dtype=tdt, device=dev)
         self.value = torch.zeros_like(self.key)
         self.q = torch.zeros((max_rows, num_q_heads, head_dim), dtype=tdt, device=dev)
         self.out = torch.zeros((max_rows, num_q_heads, head_dim), dtype=torch.float32, device=dev)
-        max_ctx = max_blocks_per_seq * BLOCK_SIZE
+        max_ctx = max_blocks_per_seq * self.bs
         ws = max(int(self._l.pa_decode_workspace_bytes(max_rows, num_q_heads, num_kv_heads, head_dim, c,
                                                        self.partition)) for c in range(1, max_ctx + 1))
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
@@ -119,18 +120,18 @@ class Driver:
         Hkv, D, NB, NH = self.Hkv, self.D, self.NB, max(self.NH, 1)
         if len(st.swap_out):
             _lib.check(L.pa_swap_blocks(_p(self.k_host), _p(self.v_host), NH, _p(self.k_pool), _p(self.v_pool), NB,
-                                        _p(r["out_pairs"]), len(st.swap_out), Hkv, D, BLOCK_SIZE, code, s))
+                                        _p(r["out_pairs"]), len(st.swap_out), Hkv, D, self.bs, code, s))
         if len(st.swap_in):
             _lib.check(L.pa_swap_blocks(_p(self.k_pool), _p(self.v_pool), NB, _p(self.k_host), _p(self.v_host), NH,
-                                        _p(r["in_pairs"]), len(st.swap_in), Hkv, D, BLOCK_SIZE, code, s))
+                                        _p(r["in_pairs"]), len(st.swap_in), Hkv, D, self.bs, code, s))
         if len(st.cow):
             _lib.check(L.pa_copy_blocks(_p(self.k_pool), _p(self.v_pool), _p(r["cow"]), len(st.cow), Hkv, D,
-                                        BLOCK_SIZE, NB, code, s))
+                                        self.bs, NB, code, s))
         if len(st.patches):
             _lib.check(L.pa_patch_tables(_p(self.table), self.maxB, self.rows, _p(r["patches"]), len(st.patches), s))
         _lib.check(L.pa_append_step(_p(self.key), _p(self.value), _p(self.k_pool), _p(self.v_pool), _p(r["slots"]),
                                     _p(r["rows"]), _p(r["pos"]), len(st.slots), _p(self.table), self.maxB,
-                                    _p(self.ctx), _p(r["ctx"]), self.rows, Hkv, D, BLOCK_SIZE, NB, code, s))
+                                    _p(self.ctx), _p(r["ctx"]), self.rows, Hkv, D, self.bs, NB, code, s))
         r["done"].record(self.stream)
         r["used"] = True
         self._i += 1
@@ -139,7 +140,7 @@ class Driver:
         if decode_events is not None:
             decode_events[0].record(self.stream)
         _lib.check(L.pa_decode(_p(self.out), _lib.PA_F32, _p(self.q), _p(self.k_pool), _p(self.v_pool),
-                               _p(self.table), self.maxB, _p(self.ctx), self.rows, self.Hq, Hkv, D, BLOCK_SIZE, NB,
+                               _p(self.table), self.maxB, _p(self.ctx), self.rows, self.Hq, Hkv, D, self.bs, NB,
                                self.scale, max_ctx, self.partition, _p(self.workspace), self.workspace.numel(),
                                code, s))
         if decode_events is not None:

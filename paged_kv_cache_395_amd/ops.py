@@ -39,16 +39,31 @@ def _p(t: torch.Tensor) -> ctypes.c_void_p:
     return ctypes.c_void_p(t.data_ptr())
 
 
-def _pool_dims(k_cache: torch.Tensor):
-    if k_cache.dim() != 3 or k_cache.shape[2] % BLOCK_SIZE:
-        raise ValueError("pools are [num_blocks, num_kv_heads, 16 * head_dim]")
-    return k_cache.shape[0], k_cache.shape[1], k_cache.shape[2] // BLOCK_SIZE
+BLOCK_SIZES = (16, 32, 64)
+
+
+def _pool_dims(k_cache: torch.Tensor, head_dim: int = None):
+    """(num_blocks, num_kv_heads, head_dim, block_size) of a pool
+    [num_blocks, num_kv_heads, block_size * head_dim].  Without ``head_dim``
+    (whole-block copies, where only the block's bytes matter) the first block
+    size that leaves a supported head_dim is taken."""
+    if k_cache.dim() != 3:
+        raise ValueError("pools are [num_blocks, num_kv_heads, block_size * head_dim]")
+    run = k_cache.shape[2]
+    if head_dim is not None:
+        if run % head_dim or run // head_dim not in BLOCK_SIZES:
+            raise ValueError(f"pool rows of {run} elements do not hold 16, 32 or 64 tokens of head_dim {head_dim}")
+        return k_cache.shape[0], k_cache.shape[1], head_dim, run // head_dim
+    for bs in BLOCK_SIZES:
+        if run % bs == 0 and run // bs in (64, 128):
+            return k_cache.shape[0], k_cache.shape[1], run // bs, bs
+    raise ValueError("pools are [num_blocks, num_kv_heads, block_size * head_dim]")
 
 
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
     """Write key/value [T, Hkv, D] into their slots (int64 [T]) of the pools."""
     _dev(key, value, k_cache, v_cache, slot_mapping)
-    NB, Hkv, D = _pool_dims(k_cache)
+    NB, Hkv, D, bs = _pool_dims(k_cache, key.shape[-1])
     if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (Hkv, D):
         raise ValueError("key / value must be [T, num_kv_heads, head_dim]")
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
@@ -56,7 +71,7 @@ def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -
     if not (key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
         raise TypeError("key, value and the pools must share one dtype")
     _lib.check(_lib.load().pa_reshape_and_cache(_p(key), _p(value), _p(k_cache), _p(v_cache), _p(slot_mapping),
-                                                key.shape[0], Hkv, D, BLOCK_SIZE, NB, _code(k_cache),
+                                                key.shape[0], Hkv, D, bs, NB, _code(k_cache),
                                                 _stream(stream)))
 
 
@@ -72,7 +87,7 @@ def _append_args(key, value, k_cache, v_cache, slot_mapping, token_rows, token_p
                  context_lens, new_context_lens, stream):
     _dev(key, value, k_cache, v_cache, block_tables, context_lens)
     _dev_or_pinned(slot_mapping, token_rows, token_positions, new_context_lens)
-    NB, Hkv, D = _pool_dims(k_cache)
+    NB, Hkv, D, bs = _pool_dims(k_cache, key.shape[-1])
     if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (Hkv, D):
         raise ValueError("key / value must be [T, num_kv_heads, head_dim]")
     T = key.shape[0]
@@ -90,7 +105,7 @@ def _append_args(key, value, k_cache, v_cache, slot_mapping, token_rows, token_p
     if not (key.dtype == value.dtype == k_cache.dtype == v_cache.dtype):
         raise TypeError("key, value and the pools must share one dtype")
     return (_p(key), _p(value), _p(k_cache), _p(v_cache), _p(slot_mapping), _p(token_rows), _p(token_positions), T,
-            _p(block_tables), block_tables.shape[1], _p(context_lens), _p(new_context_lens), S, Hkv, D, BLOCK_SIZE,
+            _p(block_tables), block_tables.shape[1], _p(context_lens), _p(new_context_lens), S, Hkv, D, bs,
             NB, _code(k_cache), _stream(stream))
 
 
@@ -99,7 +114,7 @@ def append_step(key, value, k_cache, v_cache, slot_mapping, token_rows, token_po
     """Cache write plus in-place update of device-resident tables and lengths.
 
     Token t goes to slot ``slot_mapping[t]``; ``block_tables[token_rows[t]]
-    [token_positions[t] // 16]`` becomes ``slot_mapping[t] // 16``; then
+    [token_positions[t] // block_size]`` becomes ``slot_mapping[t] // block_size``; then
     ``context_lens`` takes ``new_context_lens``.  The four step vectors may be
     device tensors or pinned host tensors.
     """
@@ -111,10 +126,10 @@ def append_step(key, value, k_cache, v_cache, slot_mapping, token_rows, token_po
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
     """Copy physical blocks src -> dst for each row (src, dst) of int64 ``pairs`` [n, 2]."""
     _dev(k_cache, v_cache, pairs)
-    NB, Hkv, D = _pool_dims(k_cache)
+    NB, Hkv, D, bs = _pool_dims(k_cache)
     if pairs.dtype != torch.int64 or pairs.dim() != 2 or pairs.shape[1] != 2:
         raise ValueError("pairs must be int64 [n, 2]")
-    _lib.check(_lib.load().pa_copy_blocks(_p(k_cache), _p(v_cache), _p(pairs), pairs.shape[0], Hkv, D, BLOCK_SIZE,
+    _lib.check(_lib.load().pa_copy_blocks(_p(k_cache), _p(v_cache), _p(pairs), pairs.shape[0], Hkv, D, bs,
                                           NB, _code(k_cache), _stream(stream)))
 
 
@@ -126,16 +141,16 @@ def swap_blocks(dst_k, dst_v, src_k, src_v, pairs, stream=None) -> None:
             raise ValueError("pools and pairs must live on the GPU or in pinned host memory")
         if not t.is_contiguous():
             raise ValueError("all tensors must be contiguous")
-    NBd, Hkv, D = _pool_dims(dst_k)
-    NBs, Hkv_s, D_s = _pool_dims(src_k)
-    if (Hkv_s, D_s) != (Hkv, D) or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
+    NBd, Hkv, D, bs = _pool_dims(dst_k)
+    NBs, Hkv_s, D_s, bs_s = _pool_dims(src_k)
+    if (Hkv_s, D_s, bs_s) != (Hkv, D, bs) or dst_v.shape != dst_k.shape or src_v.shape != src_k.shape:
         raise ValueError("both sides must be pools of the same geometry")
     if not (dst_k.dtype == dst_v.dtype == src_k.dtype == src_v.dtype):
         raise TypeError("the pools must share one dtype")
     if pairs.dtype != torch.int64 or pairs.dim() != 2 or pairs.shape[1] != 2:
         raise ValueError("pairs must be int64 [n, 2]")
     _lib.check(_lib.load().pa_swap_blocks(_p(dst_k), _p(dst_v), NBd, _p(src_k), _p(src_v), NBs, _p(pairs),
-                                          pairs.shape[0], Hkv, D, BLOCK_SIZE, _code(dst_k), _stream(stream)))
+                                          pairs.shape[0], Hkv, D, bs, _code(dst_k), _stream(stream)))
 
 
 def patch_tables(block_tables, patches, stream=None) -> None:
@@ -164,7 +179,7 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, h
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size,
                  workspace):
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
-    NB, Hkv, D = _pool_dims(k_cache)
+    NB, Hkv, D, bs = _pool_dims(k_cache, q.shape[-1])
     if q.dim() != 3 or q.shape[2] != D:
         raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
     S, Hq = q.shape[0], q.shape[1]
@@ -182,7 +197,7 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
     ws_ptr = _p(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return (_p(out), _code(out), _p(q), _p(k_cache), _p(v_cache), _p(block_tables), block_tables.shape[1],
-            _p(context_lens), S, Hq, Hkv, D, BLOCK_SIZE, NB, float(scale), int(max_context_len),
+            _p(context_lens), S, Hq, Hkv, D, bs, NB, float(scale), int(max_context_len),
             int(partition_size), ws_ptr, ws_bytes, _code(q)), workspace
 
 
@@ -218,7 +233,7 @@ def decode_multi(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
     """Causal attention of the last q_len positions of each context, q [S, q_len, Hq, D], at decode's bandwidth
     (q_len x group <= 16)."""
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
-    NB, Hkv, D = _pool_dims(k_cache)
+    NB, Hkv, D, bs = _pool_dims(k_cache, q.shape[-1])
     if q.dim() != 4 or q.shape[3] != D:
         raise ValueError("q must be [num_seqs, q_len, num_q_heads, head_dim]")
     S, C, Hq = q.shape[0], q.shape[1], q.shape[2]
@@ -236,7 +251,7 @@ def decode_multi(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _lib.check(lib.pa_decode_multi(_p(out), _code(out), _p(q), C, _p(k_cache), _p(v_cache), _p(block_tables),
-                                   block_tables.shape[1], _p(context_lens), S, Hq, Hkv, D, BLOCK_SIZE, NB,
+                                   block_tables.shape[1], _p(context_lens), S, Hq, Hkv, D, bs, NB,
                                    float(scale), int(max_context_len), int(partition_size),
                                    _p(workspace) if workspace is not None else None, ws_bytes, _code(q),
                                    _stream(stream)))
@@ -245,7 +260,7 @@ def decode_multi(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
 def prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, stream=None) -> None:
     """Causal attention of q [S, C, Hq, D] (the last C positions of each context) over the paged cache."""
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
-    NB, Hkv, D = _pool_dims(k_cache)
+    NB, Hkv, D, bs = _pool_dims(k_cache, q.shape[-1])
     if q.dim() != 4 or q.shape[3] != D:
         raise ValueError("q must be [num_seqs, chunk_len, num_q_heads, head_dim]")
     S, C, Hq = q.shape[0], q.shape[1], q.shape[2]
@@ -257,7 +272,7 @@ def prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, scale, m
         raise ValueError("context_lens must be int32 [num_seqs]")
     _lib.check(_lib.load().pa_prefill_chunk(_p(out), _code(out), _p(q), C, _p(k_cache), _p(v_cache),
                                             _p(block_tables), block_tables.shape[1], _p(context_lens), S, Hq, Hkv, D,
-                                            BLOCK_SIZE, NB, float(scale), int(max_context_len), _code(q),
+                                            bs, NB, float(scale), int(max_context_len), _code(q),
                                             _stream(stream)))
 
 
@@ -290,7 +305,7 @@ class StepPlan:
                  key=None, value=None, slot_mapping=None, partition_size=0, stream=None, append=None):
         self._lib = _lib.load()
         self._stream = _stream(stream)
-        NB, Hkv, D = _pool_dims(k_cache)
+        NB, Hkv, D, bs = _pool_dims(k_cache, q.shape[-1])
         self._partition = int(partition_size)
         self._multi = q.dim() == 4
         if self._multi:
@@ -302,7 +317,7 @@ class StepPlan:
             S, C, Hq = q.shape[0], q.shape[1], q.shape[2]
             ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
             self._multi_head = (_p(out), _code(out), _p(q), C, _p(k_cache), _p(v_cache), _p(block_tables),
-                                block_tables.shape[1], _p(context_lens), S, Hq, Hkv, D, BLOCK_SIZE, NB, float(scale))
+                                block_tables.shape[1], _p(context_lens), S, Hq, Hkv, D, bs, NB, float(scale))
             self._multi_tail = (self._partition, _p(workspace) if workspace is not None else None, ws_bytes,
                                 _code(q), self._stream)
             self._sizes = (S, Hq, Hkv, D)
@@ -331,7 +346,7 @@ class StepPlan:
             if not (key.dtype == value.dtype == k_cache.dtype):
                 raise TypeError("key, value and the pools must share one dtype")
             self._write = (_p(key), _p(value), _p(k_cache), _p(v_cache), _p(slot_mapping), key.shape[0], Hkv, D,
-                           BLOCK_SIZE, NB, _code(k_cache), self._stream)
+                           bs, NB, _code(k_cache), self._stream)
 
     @staticmethod
     def workspace_bytes_for(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, max_context_len,

@@ -58,8 +58,8 @@ class Prepared:
 
     def __init__(self, w, pad_id=None, extra_tokens=0):
         self.w = w
-        self.ref_bm = RefBlockManager(w.num_blocks, free_order=w.free_order)
-        self.bm = BlockManager(w.num_blocks, free_order=w.free_order)
+        self.ref_bm = RefBlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
+        self.bm = BlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
         run_program(self.ref_bm, w.program)
         run_program(self.bm, w.program)
         seqs = w.step_seqs

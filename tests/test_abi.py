@@ -53,6 +53,18 @@ def decode_call(**kw):
                        a["ws_bytes"], a["dtype"], NULL)
 
 
+def test_block_sizes_16_32_64_are_accepted_and_others_refused():
+    for bs, want in [(16, _lib.PA_OK), (32, _lib.PA_OK), (64, _lib.PA_OK), (8, _lib.PA_EUNSUPPORTED),
+                     (128, _lib.PA_EUNSUPPORTED), (24, _lib.PA_EUNSUPPORTED)]:
+        assert L.pa_reshape_and_cache(None, None, None, None, None, 0, 8, 128, bs, 10, _lib.PA_BF16, NULL) == want
+        bm = L.pa_bm_create(8, bs, None)
+        assert bool(bm) == (want == _lib.PA_OK)
+        if bm:
+            L.pa_bm_destroy(bm)
+    # the table must hold max_context_len at the block size given
+    assert decode_call(bs=32, maxb=2, max_ctx=65) == _lib.PA_EINVAL
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(D=96), _lib.PA_EUNSUPPORTED),
     (dict(bs=8), _lib.PA_EUNSUPPORTED),
@@ -145,7 +157,7 @@ def test_cache_write_and_copy_reject_bad_arguments():
     assert L.pa_reshape_and_cache(1, 1, 1, 1, 1, -1, 8, 128, 16, 10, _lib.PA_BF16, NULL) == _lib.PA_EINVAL
     assert L.pa_reshape_and_cache(None, 1, 1, 1, 1, 4, 8, 128, 16, 10, _lib.PA_BF16, NULL) == _lib.PA_EINVAL
     assert L.pa_reshape_and_cache(None, None, None, None, None, 0, 8, 128, 16, 10, _lib.PA_BF16, NULL) == _lib.PA_OK
-    assert L.pa_copy_blocks(1, 1, 1, 2, 8, 128, 32, 10, _lib.PA_F16, NULL) == _lib.PA_EUNSUPPORTED
+    assert L.pa_copy_blocks(1, 1, 1, 2, 8, 128, 8, 10, _lib.PA_F16, NULL) == _lib.PA_EUNSUPPORTED
     assert L.pa_copy_blocks(None, None, None, 0, 8, 128, 16, 10, _lib.PA_F16, NULL) == _lib.PA_OK
 
 
@@ -153,7 +165,8 @@ def test_append_step_rejects_bad_arguments():
     def call(T=4, maxb=8, S=2, D=128, bs=16, key=1, ctx=1):
         return L.pa_append_step(key, 1, 1, 1, 1, 1, 1, T, 1, maxb, ctx, 1, S, 8, D, bs, 10, _lib.PA_BF16, NULL)
     assert call(D=100) == _lib.PA_EUNSUPPORTED
-    assert call(bs=32) == _lib.PA_EUNSUPPORTED
+    assert call(bs=8) == _lib.PA_EUNSUPPORTED
+    assert call(bs=48) == _lib.PA_EUNSUPPORTED
     assert call(T=-1) == _lib.PA_EINVAL
     assert call(S=-1) == _lib.PA_EINVAL
     assert call(maxb=0) == _lib.PA_EINVAL

@@ -64,8 +64,8 @@ def test_parallel_sampling_and_prefix_examples():
 @pytest.mark.parametrize("name", list(WORKLOADS))
 def test_workload_programs_match(name):
     w = make_workload(name) if name != "longctx_bf16" else make_workload(name, num_seqs=4, ctx=4096)
-    ref = RefBlockManager(w.num_blocks, free_order=w.free_order)
-    nat = BlockManager(w.num_blocks, free_order=w.free_order)
+    ref = RefBlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
+    nat = BlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
     run_program(ref, w.program)
     run_program(nat, w.program)
     same_state(ref, nat, w.batch)

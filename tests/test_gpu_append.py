@@ -28,8 +28,8 @@ def step_vectors(bm, seqs_in_batch, append):
 
 def run_steps(w, steps, pinned, seed):
     rng = np.random.default_rng(seed)
-    bm = BlockManager(w.num_blocks, free_order=w.free_order)
-    ref = RefBlockManager(w.num_blocks, free_order=w.free_order)
+    bm = BlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
+    ref = RefBlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
     run_program(bm, w.program)
     run_program(ref, w.program)
     S, Hkv, D, A = w.num_seqs, w.num_kv_heads, w.head_dim, w.append
@@ -158,7 +158,7 @@ def test_step_plan_with_resident_tables_matches_the_oracle():
     """StepPlan in append mode: the per-step write keeps tables on the device
     and the decode that follows reads them."""
     w = make_workload("gqa8b_bf16", num_seqs=16)
-    bm = BlockManager(w.num_blocks, free_order=w.free_order)
+    bm = BlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
     run_program(bm, w.program)
     S, Hkv, Hq, D = w.num_seqs, w.num_kv_heads, w.num_q_heads, w.head_dim
     steps = 5

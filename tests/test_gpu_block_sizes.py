@@ -1,0 +1,98 @@
+"""Blocks of 32 and 64 tokens on the GPU: every kernel that addresses the
+pool (cache write, device-resident append, decode, several-query decode,
+chunked prefill, block copies and swaps) against the oracle, which pages the
+same values in blocks of the same size.  Partitions of 48 tokens start in
+the middle of a block."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as OA
+from paged_kv_cache_395_amd import ops
+from tests._gpu import Prepared, assert_close, out_f64, say, to_dev, to_host
+from workloads import make_workload, to_storage
+
+pytestmark = pytest.mark.gpu
+
+CASES = [("tiny_f32", dict(block_size=32)), ("tiny_f32", dict(block_size=64)),
+         ("mha7b_f16", dict(num_seqs=6, lo=1, hi=1100, block_size=32)),
+         ("gqa8b_bf16", dict(num_seqs=12, hi=1500, block_size=32)),
+         ("gqa8b_bf16", dict(num_seqs=12, hi=1500, block_size=64))]
+IDS = ["f32_bs32", "f32_bs64", "f16_bs32", "bf16_bs32", "bf16_bs64"]
+
+
+@pytest.mark.parametrize("name,kw", CASES, ids=IDS)
+def test_cache_write_and_decode_match_the_oracle(name, kw):
+    p = Prepared(make_workload(name, **kw))
+    say(f"[block-size] {name} {kw}")
+    d = p.device()
+    p.write_step(d)
+    torch.cuda.synchronize()
+    k_ref, v_ref = p.oracle_pools()
+    assert np.array_equal(to_host(d["k"], p.w.dtype).view(np.uint8), k_ref.view(np.uint8))
+    assert np.array_equal(to_host(d["v"], p.w.dtype).view(np.uint8), v_ref.view(np.uint8))
+    ref = p.oracle_decode()
+    for partition in (0, 48, 256):
+        out = p.gpu_decode(d, partition=partition)
+        assert_close(out_f64(out), ref, p.w.dtype, f"{name} {kw} P={partition}")
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_full_size_decode_on_larger_blocks(bs):
+    p = Prepared(make_workload("mha7b_f16", block_size=bs))
+    say(f"[block-size] mha7b_f16 full bs={bs}")
+    d = p.device()
+    p.write_step(d)
+    out = p.gpu_decode(d)
+    torch.cuda.synchronize()
+    seqs = list(range(0, p.w.num_seqs, 7))
+    ref = p.oracle_decode(seqs=seqs)
+    assert_close(out_f64(out)[seqs], ref[seqs], "f16", f"bs={bs}")
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_prefill_and_several_queries_on_larger_blocks(bs):
+    p = Prepared(make_workload("longctx_bf16", num_seqs=2, ctx=700, chunk=100, block_size=bs))
+    w = p.w
+    d = p.device()
+    p.write_step(d)
+    q = to_dev(w.q, w.dtype)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ops.prefill_chunk(out, q, d["k"], d["v"], d["table"], d["ctx"], w.scale, p.max_ctx)
+    k, v = p.oracle_pools()
+    assert_close(out_f64(out), OA.prefill_chunk(w.q, k, v, p.table, p.ctx, w.scale, "bf16"), "bf16", f"prefill bs={bs}")
+
+    m = Prepared(make_workload("specdec_bf16", num_seqs=10, hi=1200, block_size=bs))
+    dm = m.device()
+    m.write_step(dm)
+    qm = to_dev(m.w.q, "bf16")
+    om = torch.empty(qm.shape, dtype=torch.float32, device="cuda")
+    ops.decode_multi(om, qm, dm["k"], dm["v"], dm["table"], dm["ctx"], m.w.scale, m.max_ctx, 48)
+    km, vm = m.oracle_pools()
+    assert_close(out_f64(om), OA.prefill_chunk(m.w.q, km, vm, m.table, m.ctx, m.w.scale, "bf16"), "bf16",
+                 f"multi bs={bs}")
+
+
+def test_append_step_and_block_copies_on_32_token_blocks():
+    from tests.test_gpu_append import run_steps
+    w = make_workload("gqa8b_bf16", num_seqs=16, block_size=32)
+    say("[block-size] append steps bs=32")
+    dk, dv, k_ref, v_ref, d_table, d_ctx, table, ctx = run_steps(w, 40, True, seed=91)
+    q = to_storage(np.random.default_rng(92).standard_normal((16, 32, 128), dtype=np.float32), "bf16")
+    out = torch.empty((16, 32, 128), dtype=torch.float32, device="cuda")
+    ops.decode(out, to_dev(q, "bf16"), dk, dv, d_table, d_ctx, w.scale, int(ctx.max()))
+    assert_close(out_f64(out), OA.decode(q, k_ref, v_ref, table, ctx, w.scale, "bf16"), "bf16", "append bs=32")
+    # copies and swaps move whole 32-token blocks
+    rng = np.random.default_rng(93)
+    perm = rng.permutation(w.num_blocks)
+    pairs = np.stack([perm[:30], perm[30:60]], axis=1).astype(np.int64)
+    ops.copy_blocks(dk, dv, torch.from_numpy(pairs).cuda())
+    OA.copy_blocks(k_ref, v_ref, pairs)
+    hk = torch.zeros((40,) + tuple(dk.shape[1:]), dtype=dk.dtype).pin_memory()
+    hv = torch.zeros_like(hk).pin_memory()
+    out_pairs = np.stack([perm[60:80], np.arange(20)], axis=1).astype(np.int64)
+    ops.swap_blocks(hk, hv, dk, dv, torch.from_numpy(out_pairs).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(dk, "bf16"), k_ref) and np.array_equal(to_host(dv, "bf16"), v_ref)
+    assert np.array_equal(to_host(hk, "bf16")[:20], k_ref[perm[60:80]])
+    assert np.array_equal(to_host(hv, "bf16")[:20], v_ref[perm[60:80]])

@@ -24,7 +24,7 @@ from workloads import make_workload, run_program, to_storage
 
 # ---------------------------------------------------------------- helpers
 
-def paged_from_logical(logical_k, logical_v, num_blocks, dtype, free_order=None, fill=0.0):
+def paged_from_logical(logical_k, logical_v, num_blocks, dtype, free_order=None, fill=0.0, block_size=16):
     """Place per-sequence logical K/V ([n, Hkv, D] storage arrays) into a pool.
 
     The block manager hands out slots token by token; the oracle's cache write
@@ -32,9 +32,9 @@ def paged_from_logical(logical_k, logical_v, num_blocks, dtype, free_order=None,
     """
     Hkv, D = logical_k[0].shape[1:]
     sd = logical_k[0].dtype
-    k_pool = np.full((num_blocks, Hkv, 16 * D), fill, dtype=sd)
-    v_pool = np.full((num_blocks, Hkv, 16 * D), fill, dtype=sd)
-    bm = RefBlockManager(num_blocks, free_order=free_order)
+    k_pool = np.full((num_blocks, Hkv, block_size * D), fill, dtype=sd)
+    v_pool = np.full((num_blocks, Hkv, block_size * D), fill, dtype=sd)
+    bm = RefBlockManager(num_blocks, block_size=block_size, free_order=free_order)
     for s in range(len(logical_k)):
         bm.add_seq(s, 0)
     # interleave sequences token by token so their blocks interleave in the pool
@@ -46,7 +46,7 @@ def paged_from_logical(logical_k, logical_v, num_blocks, dtype, free_order=None,
         key = np.stack([logical_k[s][t] for s in seqs])
         val = np.stack([logical_v[s][t] for s in seqs])
         A.reshape_and_cache(k_pool, v_pool, key, val, np.array(slots))
-    maxb = max(1, max(-(-len(k) // 16) for k in logical_k))
+    maxb = max(1, max(-(-len(k) // block_size) for k in logical_k))
     table, ctx = bm.block_table(range(len(logical_k)), maxb, pad=-1)
     return k_pool, v_pool, np.array(table, dtype=np.int32), np.array(ctx, dtype=np.int32), bm
 
@@ -87,6 +87,39 @@ def test_tile_layout_is_a_bijection(D):
     for which in ("k", "v"):
         idx = L.tile_index(which, D)
         assert sorted(idx.ravel().tolist()) == list(range(16 * D))
+
+
+def test_larger_blocks_are_runs_of_tiles_at_hand_derived_offsets():
+    """A 32- or 64-token block is 2 or 4 consecutive 16-token tiles, in token order."""
+    D = 64
+    k32, v32 = L.block_index("k", D, 32), L.block_index("v", D, 32)
+    assert k32[17, 5] == 1024 + 13            # tile 1, K(t=1, d=5) = (0 * 16 + 1) * 8 + 5
+    assert v32[20, 40] == 1024 + 704          # tile 1, V(t=4, d=40) = ((1 * 4 + 1) * 16 + 8) * 8 + 0 + 0
+    assert k32[3, 9] == L.k_offset(3, 9)      # tile 0 is the 16-token tile itself
+    k64 = L.block_index("k", D, 64)
+    assert k64[63, 63] == 3 * 1024 + L.k_offset(15, 63)
+    for bs in (32, 64):
+        for which in ("k", "v"):
+            idx = L.block_index(which, D, bs)
+            assert sorted(idx.ravel().tolist()) == list(range(bs * D))
+
+
+@pytest.mark.parametrize("bs", [32, 64])
+def test_block_size_changes_nothing_in_the_result(bs):
+    """The same logical K/V paged in 16-token and larger blocks attend identically."""
+    rng = np.random.default_rng(19)
+    lens = [70, 5, 129, 33]
+    ks, vs = random_logical(rng, lens, 2, 64, "bf16")
+    q = to_storage(rng.standard_normal((4, 8, 64), dtype=np.float32), "bf16")
+    a = paged_from_logical(ks, vs, 30, "bf16", rng.permutation(30))
+    b = paged_from_logical(ks, vs, 30, "bf16", rng.permutation(30), block_size=bs)
+    for s, n in enumerate(lens):
+        Ka, Va = A.gather_kv(a[0], a[1], a[2][s], n, "bf16")
+        Kb, Vb = A.gather_kv(b[0], b[1], b[2][s], n, "bf16", bs)
+        assert np.array_equal(Ka, Kb) and np.array_equal(Va, Vb)
+    # equal inputs; only the fp64 summation order of the library matmul may differ with the array strides
+    np.testing.assert_allclose(A.decode(q, *a[:4], 0.125, "bf16"), A.decode(q, *b[:4], 0.125, "bf16"),
+                               rtol=0, atol=1e-12)
 
 
 def test_cache_write_lands_at_the_layout_offsets():
@@ -147,13 +180,13 @@ def test_output_rounding_to_storage_is_nearest(dtype):
 
 # ---------------------------------------------------------------- brute force
 
-@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-def test_decode_matches_brute_force_on_the_tiny_shape(dtype):
+@pytest.mark.parametrize("dtype,bs", [("f32", 16), ("f16", 16), ("bf16", 16), ("f32", 32), ("bf16", 64)])
+def test_decode_matches_brute_force_on_the_tiny_shape(dtype, bs):
     rng = np.random.default_rng(11)
     lens = [20, 37, 16, 1]
     ks, vs = random_logical(rng, lens, 4, 64, dtype)
     q = to_storage(rng.standard_normal((4, 4, 64), dtype=np.float32), dtype)
-    k_pool, v_pool, table, ctx, _ = paged_from_logical(ks, vs, 20, dtype, rng.permutation(20))
+    k_pool, v_pool, table, ctx, _ = paged_from_logical(ks, vs, 20, dtype, rng.permutation(20), block_size=bs)
     got = A.decode(q, k_pool, v_pool, table, ctx, 1 / 8, dtype)
     want = brute_decode(q, ks, vs, 1 / 8, dtype)
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
@@ -161,25 +194,29 @@ def test_decode_matches_brute_force_on_the_tiny_shape(dtype):
 
 @settings(max_examples=25, deadline=None)
 @given(S=st.integers(1, 4), G=st.sampled_from([1, 2, 4]), Hkv=st.integers(1, 2), D=st.sampled_from([32, 64]),
-       lens=st.lists(st.integers(1, 40), min_size=4, max_size=4), seed=st.integers(0, 2 ** 31 - 1))
-def test_decode_matches_brute_force_hypothesis(S, G, Hkv, D, lens, seed):
+       lens=st.lists(st.integers(1, 40), min_size=4, max_size=4), seed=st.integers(0, 2 ** 31 - 1),
+       bs=st.sampled_from([16, 32, 64]))
+def test_decode_matches_brute_force_hypothesis(S, G, Hkv, D, lens, seed, bs):
     rng = np.random.default_rng(seed)
     lens = lens[:S]
     ks, vs = random_logical(rng, lens, Hkv, D, "f32")
     q = rng.standard_normal((S, G * Hkv, D)).astype(np.float32)
-    nb = sum(-(-n // 16) for n in lens) + 3
-    k_pool, v_pool, table, ctx, _ = paged_from_logical(ks, vs, nb, "f32", rng.permutation(nb), fill=np.nan)
+    nb = sum(-(-n // bs) for n in lens) + 3
+    k_pool, v_pool, table, ctx, _ = paged_from_logical(ks, vs, nb, "f32", rng.permutation(nb), fill=np.nan,
+                                                        block_size=bs)
     scale = 1 / math.sqrt(D)
     got = A.decode(q, k_pool, v_pool, table, ctx, scale, "f32")
     want = brute_decode(q, ks, vs, scale, "f32")
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
 
 
-def test_prefill_matches_brute_force():
+@pytest.mark.parametrize("bs", [16, 32])
+def test_prefill_matches_brute_force(bs):
     rng = np.random.default_rng(5)
     lens, C, Hkv, G, D = [40, 23], 7, 2, 2, 32
     ks, vs = random_logical(rng, lens, Hkv, D, "bf16")
-    k_pool, v_pool, table, ctx, _ = paged_from_logical(ks, vs, 10, "bf16", rng.permutation(10), fill=0)
+    k_pool, v_pool, table, ctx, _ = paged_from_logical(ks, vs, 10, "bf16", rng.permutation(10), fill=0,
+                                                        block_size=bs)
     q = to_storage(rng.standard_normal((2, C, Hkv * G, D), dtype=np.float32), "bf16")
     got = A.prefill_chunk(q, k_pool, v_pool, table, ctx, 0.25, "bf16")
     for s, n in enumerate(lens):

@@ -156,8 +156,8 @@ class Workload:
         return -(-longest // self.block_size)
 
 
-def _blocks(n: int) -> int:
-    return -(-int(n) // BLOCK_SIZE)
+def _blocks(n: int, bs: int = BLOCK_SIZE) -> int:
+    return -(-int(n) // bs)
 
 
 def run_program(bm, program) -> None:
@@ -180,10 +180,10 @@ def run_program(bm, program) -> None:
 
 
 def _finish(rng, name, dtype, S, Hq, Hkv, D, NB, scale, P, append, program, batch,
-            description, lengths) -> Workload:
+            description, lengths, block_size=BLOCK_SIZE) -> Workload:
     free_order = rng.permutation(NB).astype(np.int32)
-    k_pool = _normal_storage(rng, (NB, Hkv, BLOCK_SIZE * D), dtype)
-    v_pool = _normal_storage(rng, (NB, Hkv, BLOCK_SIZE * D), dtype)
+    k_pool = _normal_storage(rng, (NB, Hkv, block_size * D), dtype)
+    v_pool = _normal_storage(rng, (NB, Hkv, block_size * D), dtype)
     q = _normal_storage(rng, (S, append, Hq, D), dtype, chunk_rows=max(1, 65536 // max(1, append)))
     step_k = _normal_storage(rng, (S, append, Hkv, D), dtype, chunk_rows=max(1, 65536 // max(1, append)))
     step_v = _normal_storage(rng, (S, append, Hkv, D), dtype, chunk_rows=max(1, 65536 // max(1, append)))
@@ -191,39 +191,42 @@ def _finish(rng, name, dtype, S, Hq, Hkv, D, NB, scale, P, append, program, batc
                     head_dim=D, num_blocks=NB, scale=scale, partition_size=P, append=append,
                     free_order=free_order, program=program, batch=np.asarray(batch, dtype=np.int64),
                     k_pool=k_pool, v_pool=v_pool, q=q, step_k=step_k, step_v=step_v,
-                    description=description, lengths=lengths)
+                    block_size=block_size, description=description, lengths=lengths)
 
 
-def _decode_from_lengths(rng, name, dtype, ctx, Hq, Hkv, D, P, NB=None, description=""):
+def _decode_from_lengths(rng, name, dtype, ctx, Hq, Hkv, D, P, NB=None, description="", block_size=BLOCK_SIZE):
     """Independent sequences: sequence s caches ctx[s]-1 tokens, the step appends one."""
     ctx = np.asarray(ctx, dtype=np.int64)
     S = len(ctx)
-    need = int(sum(_blocks(c) for c in ctx))
+    need = int(sum(_blocks(c, block_size) for c in ctx))
     if NB is None:
         NB = int(math.ceil(1.25 * need))
     program = [("add", s, int(ctx[s]) - 1) for s in range(S)]
+    if block_size != BLOCK_SIZE:
+        description += f"; {block_size}-token blocks"
     return _finish(rng, name, dtype, S, Hq, Hkv, D, NB, 1.0 / math.sqrt(D), P, 1, program,
-                   np.arange(S), description, {"final_ctx": ctx, "blocks_needed": need})
+                   np.arange(S), description, {"final_ctx": ctx, "blocks_needed": need}, block_size)
 
 
-def _tiny_f32(rng, ctx=(20, 37, 16, 1)):
+def _tiny_f32(rng, ctx=(20, 37, 16, 1), block_size=BLOCK_SIZE):
     return _decode_from_lengths(
         rng, "tiny_f32", "f32", ctx, 4, 4, 64, 512, NB=20,
-        description="4 sequences, fp32, 4/4 heads, head_dim 64, 20-block pool, 1 new token each")
+        description="4 sequences, fp32, 4/4 heads, head_dim 64, 20-block pool, 1 new token each",
+        block_size=block_size)
 
 
-def _mha7b_f16(rng, num_seqs=64, lo=128, hi=2048):
+def _mha7b_f16(rng, num_seqs=64, lo=128, hi=2048, block_size=BLOCK_SIZE, name="mha7b_f16"):
     ctx = rng.integers(lo, hi + 1, size=num_seqs)
     return _decode_from_lengths(
-        rng, "mha7b_f16", "f16", ctx, 32, 32, 128, 512,
+        rng, name, "f16", ctx, 32, 32, 128, 512,
         description=f"7B-shaped decode, fp16, batch {num_seqs}, 32/32 heads, head_dim 128, "
-                    f"ctx U[{lo},{hi}], pool 1.25x need")
+                    f"ctx U[{lo},{hi}], pool 1.25x need", block_size=block_size)
 
 
-def _gqa8b_bf16(rng, num_seqs=256, median=1024, lo=16, hi=8192):
+def _gqa8b_bf16(rng, num_seqs=256, median=1024, lo=16, hi=8192, block_size=BLOCK_SIZE, name="gqa8b_bf16"):
     ctx = np.clip(np.rint(np.exp(math.log(median) + rng.standard_normal(num_seqs))), lo, hi).astype(np.int64)
     return _decode_from_lengths(
-        rng, "gqa8b_bf16", "bf16", ctx, 32, 8, 128, 512,
+        rng, name, "bf16", ctx, 32, 8, 128, 512, block_size=block_size,
         description=f"Llama-3-8B-shaped GQA decode, bf16, batch {num_seqs}, 32/8 heads, head_dim 128, "
                     f"ctx lognormal(median {median}, sigma 1) clipped to [{lo},{hi}]")
 
@@ -262,10 +265,11 @@ def _shared_prefix_bf16(rng, num_users=512, num_prompts=128, n_samples=4,
                    {"final_ctx": final_ctx, "blocks_needed": need})
 
 
-def _longctx_bf16(rng, num_seqs=16, ctx=32768, chunk=512, Hq=64, Hkv=8, NB=None, dtype="bf16", head_dim=128):
+def _longctx_bf16(rng, num_seqs=16, ctx=32768, chunk=512, Hq=64, Hkv=8, NB=None, dtype="bf16", head_dim=128,
+                  block_size=BLOCK_SIZE):
     if ctx < chunk:
         raise ValueError("the chunk lies inside the context")
-    need = num_seqs * _blocks(ctx)
+    need = num_seqs * _blocks(ctx, block_size)
     if NB is None:
         NB = int(math.ceil(1.25 * need))
     program = [("add", s, ctx - chunk) for s in range(num_seqs)]
@@ -273,23 +277,24 @@ def _longctx_bf16(rng, num_seqs=16, ctx=32768, chunk=512, Hq=64, Hkv=8, NB=None,
     return _finish(rng, "longctx_bf16", dtype, num_seqs, Hq, Hkv, D, NB, 1.0 / math.sqrt(D), 512,
                    chunk, program, np.arange(num_seqs),
                    f"{num_seqs} sequences at context {ctx} (the last {chunk} tokens appended as one chunk), "
-                   f"{dtype}, {Hq}/{Hkv} heads, head_dim {D}, 512-token partitions",
-                   {"final_ctx": np.full(num_seqs, ctx, dtype=np.int64), "blocks_needed": need})
+                   f"{dtype}, {Hq}/{Hkv} heads, head_dim {D}, 512-token partitions"
+                   + ("" if block_size == BLOCK_SIZE else f", {block_size}-token blocks"),
+                   {"final_ctx": np.full(num_seqs, ctx, dtype=np.int64), "blocks_needed": need}, block_size)
 
 
-def _specdec_bf16(rng, num_seqs=256, median=1024, lo=16, hi=8192, q_len=4):
+def _specdec_bf16(rng, num_seqs=256, median=1024, lo=16, hi=8192, q_len=4, block_size=BLOCK_SIZE):
     """Speculative verification: every sequence appends q_len drafted tokens and attends each causally."""
     ctx = np.clip(np.rint(np.exp(math.log(median) + rng.standard_normal(num_seqs))), max(lo, q_len), hi)
     ctx = ctx.astype(np.int64)
-    need = int(sum(_blocks(c) for c in ctx))
+    need = int(sum(_blocks(c, block_size) for c in ctx))
     NB = int(math.ceil(1.25 * need))
     program = [("add", s, int(ctx[s]) - q_len) for s in range(num_seqs)]
     return _finish(rng, "specdec_bf16", "bf16", num_seqs, 32, 8, 128, NB, 1.0 / math.sqrt(128), 512, q_len,
                    program, np.arange(num_seqs),
                    f"Llama-3-8B-shaped GQA verification of {q_len} drafted tokens per sequence, bf16, batch "
                    f"{num_seqs}, 32/8 heads, head_dim 128, ctx lognormal(median {median}, sigma 1) clipped to "
-                   f"[{max(lo, q_len)},{hi}]",
-                   {"final_ctx": ctx, "blocks_needed": need, "mode": "multi"})
+                   f"[{max(lo, q_len)},{hi}]" + ("" if block_size == BLOCK_SIZE else f", {block_size}-token blocks"),
+                   {"final_ctx": ctx, "blocks_needed": need, "mode": "multi"}, block_size)
 
 
 WORKLOADS = {
@@ -299,6 +304,10 @@ WORKLOADS = {
     "shared_prefix_bf16": (1004, _shared_prefix_bf16),
     "longctx_bf16": (1005, _longctx_bf16),
     "specdec_bf16": (1006, _specdec_bf16),
+    # block-size variants of the 7B and GQA decode workloads (same contexts: same seeds)
+    "mha7b_f16_bs32": (1002, lambda rng, **kw: _mha7b_f16(rng, block_size=32, name="mha7b_f16_bs32", **kw)),
+    "mha7b_f16_bs64": (1002, lambda rng, **kw: _mha7b_f16(rng, block_size=64, name="mha7b_f16_bs64", **kw)),
+    "gqa8b_bf16_bs32": (1003, lambda rng, **kw: _gqa8b_bf16(rng, block_size=32, name="gqa8b_bf16_bs32", **kw)),
 }
 
 
