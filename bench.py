@@ -347,6 +347,13 @@ def _per_dispatch(rows, name: str) -> tuple:
     return (sum(vals) / len(vals), len(vals)) if vals else (float("nan"), 0)
 
 
+def _largest_dispatch(rows, name: str) -> float:
+    """The copy probe: the largest of the run's copy dispatches (the others
+    are the small table / length copies of the set-up)."""
+    vals = [float(r["Counter_Value"]) for r in rows if name in r["Kernel_Name"]]
+    return max(vals) if vals else float("nan")
+
+
 def summarize_prefill(args, rec) -> None:
     """Matrix-core utilisation of the chunked-prefill kernel from one rocprofv3
     counter pass (SQ block) and one GRBM pass of the same command."""
@@ -427,8 +434,8 @@ def summarize(args) -> None:
     write = _csv_rows(args.write_dir, "counter_collection.csv")
     f_dec, n_dec = _per_dispatch(fetch, DECODE_KERNEL)
     w_dec, _ = _per_dispatch(write, DECODE_KERNEL)
-    f_cp, _ = _per_dispatch(fetch, COPY_KERNEL)
-    w_cp, _ = _per_dispatch(write, COPY_KERNEL)
+    f_cp = _largest_dispatch(fetch, COPY_KERNEL)
+    w_cp = _largest_dispatch(write, COPY_KERNEL)
     probe_kib = 1024 * 1024
     fs, ws = probe_kib / f_cp, probe_kib / w_cp  # each counter against a copy of known size
     hbm_f, hbm_w = f_dec * 1024 * fs, w_dec * 1024 * ws
