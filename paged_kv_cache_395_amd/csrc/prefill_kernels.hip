@@ -181,20 +181,31 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   // its LDS image is zero-filled without touching memory
   const int lane_off = lane * 16;
   auto issue_stage = [&](int st, u32x4_t* buf) {
+    // The stage's 4 key tiles, looked up once per wave in vector registers
+    // (lane l: tile l % 4): the byte offset of the tile from its pool run, or
+    // -1 when the tile is past the key window or its table entry is outside
+    // the pool.  Each load below then only picks its tile's offset with two
+    // lane reads instead of redoing the lookup and the 64-bit address product
+    // in scalar code for every 1 KiB run.
+    const int blk_l = st * kStageBlocks + (lane & (kStageBlocks - 1));
+    const int phys_l = blk_l < nkb ? s_tab[blk_l - tab_base] : 0;
+    const bool in_pool_l = phys_l >= 0 && int64_t(phys_l) < P.num_blocks;
+    bad |= blk_l < nkb && !in_pool_l;
+    const int64_t off_l =
+        blk_l < nkb && in_pool_l
+            ? (int64_t(phys_l) * blk_stride + int64_t(blk_l & ((1 << sh) - 1)) * kTileElems) * 2  // tile in its block
+            : int64_t(-1);
+    const uint32_t off_lo = uint32_t(uint64_t(off_l)), off_hi = uint32_t(uint64_t(off_l) >> 32);
 #pragma unroll
     for (int j = 0; j < kRunsPerStage / kPfWaves; ++j) {
       const int run = j * kPfWaves + w;
       const int t8 = run / kRunsPerTile;  // 0..3 K tiles, 4..7 V tiles
       const int part = run % kRunsPerTile;
-      const int blk = st * kStageBlocks + (t8 & 3);
-      int phys = blk < nkb ? s_tab[blk - tab_base] : 0;
-      phys = __builtin_amdgcn_readfirstlane(phys);
-      const bool in_pool = phys >= 0 && int64_t(phys) < P.num_blocks;
-      bad |= blk < nkb && !in_pool;
-      const bool ok = blk < nkb && in_pool;
-      const int sub = blk & ((1 << sh) - 1);  // tile inside the block
-      const char* base = (t8 < kStageBlocks ? kg : vg) + (int64_t(ok ? phys : 0) * blk_stride +
-                                                          (ok ? sub : 0) * kTileElems) * 2;
+      const int b = t8 & (kStageBlocks - 1);
+      const int64_t off = int64_t((uint64_t(__builtin_amdgcn_readlane(off_hi, b)) << 32) |
+                                  uint64_t(__builtin_amdgcn_readlane(off_lo, b)));
+      const bool ok = off >= 0;
+      const char* base = (t8 < kStageBlocks ? kg : vg) + (ok ? off : 0);
       const __amdgpu_buffer_rsrc_t r =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, ok ? kTileBytes : 0, kBufferRsrcWord3);
       lds_void* dst = (lds_void*)(buf + t8 * (kTileElems / 8) + part * 64);
