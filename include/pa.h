@@ -15,12 +15,17 @@
  * The KV cache is cut into fixed blocks of 16 tokens that can sit anywhere
  * in one pool; a per-sequence block table maps logical block i to a
  * physical block ([OS] "PagedAttention: Virtual Memory for KV Cache", How It
- * Works and the memory-layout example).  block_size must be 16.
+ * Works and the memory-layout example).  block_size is 16, the pages'
+ * size; 32 and 64 are supported as variants (every entry point takes
+ * block_size, the same for all calls on one pool), anything else is
+ * PA_EUNSUPPORTED.  Below, bs = block_size.
  *
  * Pools.  k_cache and v_cache are separate device arrays
- *     [num_blocks][num_kv_heads][16 * head_dim]      (elements of `dtype`)
- * and one (block, kv head) tile is one contiguous run of 16 * head_dim
- * elements.  Inside a tile (t = token offset 0..15, d = dim):
+ *     [num_blocks][num_kv_heads][bs * head_dim]      (elements of `dtype`)
+ * and one (block, kv head) run is bs * head_dim contiguous elements: bs / 16
+ * tiles of 16 tokens one after another (tokens 0-15 of the block in the
+ * first, 16-31 in the second, ...).  Inside a tile (t = token offset
+ * 0..15, d = dim):
  *     K(t, d) at  ((d / 8) * 16 + t) * 8 + d % 8
  *                 i.e. [head_dim/8][16 tokens][8 dims]
  *     V(t, d) at  (((d / 32) * 4 + t / 4) * 16 + d % 16) * 8
@@ -30,12 +35,12 @@
  * loads that land directly in matrix-core operand registers.  head_dim must
  * be a multiple of 32; the kernels support 64 and 128.
  *
- * Slots.  Token position p of a sequence lives in logical block p / 16 at
- * offset p % 16; its slot is  physical_block * 16 + p % 16  (int64).  A
+ * Slots.  Token position p of a sequence lives in logical block p / bs at
+ * offset p % bs; its slot is  physical_block * bs + p % bs  (int64).  A
  * negative slot means "skip this token".
  *
  * Block tables.  int32 [num_seqs][max_blocks_per_seq], row-major; only the
- * first ceil(context_len / 16) entries of a row are read.  context_lens is
+ * first ceil(context_len / bs) entries of a row are read.  context_lens is
  * int32 [num_seqs] and counts every cached token including the one(s) the
  * step just wrote.
  *
@@ -107,8 +112,8 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* k_cac
 /* ------------------------------------------------------------------------
  * One step's appends with the block tables and context lengths resident on
  * the device: the cache write above, plus, for each token,
- *     block_tables[row][pos / 16] = slot / 16
- * (the block the slot lies in: a block opened on demand when pos % 16 == 0,
+ *     block_tables[row][pos / bs] = slot / bs
+ * (the block the slot lies in: a block opened on demand when pos % bs == 0,
  * the fresh copy after a copy-on-write, the unchanged block otherwise --
  * [OS] "The Magic: No Pre-allocation", "Copy-on-Write: Sharing KV Cache"),
  * and context_lens[r] = new_context_lens[r] for every row r.  A serving step
@@ -296,11 +301,11 @@ pa_status_t pa_probe_read_bandwidth(const void* buf, int64_t bytes, uint32_t* si
                                     void* stream);
 
 /* ------------------------------------------------------------------------
- * Host block manager.  One pool of num_blocks blocks of 16 tokens; per
- * sequence a list of physical blocks; a free list; reference counts for
- * shared blocks.
+ * Host block manager.  One pool of num_blocks blocks of block_size (16, 32
+ * or 64) tokens; per sequence a list of physical blocks; a free list;
+ * reference counts for shared blocks.
  *   - allocation on demand: a token at offset 0 of a fresh block takes a
- *     new block, so n tokens hold ceil(n/16) blocks and waste at most 15
+ *     new block, so n tokens hold ceil(n/bs) blocks and waste at most bs - 1
  *     slots ([OS] "The Magic: No Pre-allocation");
  *   - release on finish ([VIZ] "Page Table Visualization");
  *   - sharing by fork (parallel sampling) and by a common prefix (system
@@ -321,7 +326,7 @@ void pa_bm_destroy(pa_bm_t* bm);
 /* New sequence holding num_tokens (>= 0) tokens in fresh blocks. */
 pa_status_t pa_bm_add_seq(pa_bm_t* bm, int64_t seq, int32_t num_tokens);
 
-/* New sequence sharing the first prefix_tokens (a multiple of 16, within the
+/* New sequence sharing the first prefix_tokens (a multiple of bs, within the
  * prefix sequence) of prefix_seq, plus tail_tokens in fresh blocks. */
 pa_status_t pa_bm_add_seq_with_prefix(pa_bm_t* bm, int64_t seq, int64_t prefix_seq,
                                       int32_t prefix_tokens, int32_t tail_tokens);
@@ -358,11 +363,11 @@ int64_t pa_bm_free_list(const pa_bm_t* bm, int32_t* out, int64_t cap);
  * Caching; [NL] item 5, Prefix Caching): requests that start with the same
  * tokens share the blocks of that prefix without naming each other.
  * Turn it on once, before the first sequence.  pa_bm_add_seq_tokens adds a
- * sequence from its token ids: each full 16-token block is identified by its
- * whole prefix (a hash of the previous block's identity and its own 16 ids,
+ * sequence from its token ids: each full block is identified by its whole
+ * prefix (a hash of the previous block's identity and its own bs ids,
  * confirmed against the stored ids); the leading run of blocks that are
  * already cached is shared (count + 1), the rest are fresh, and fresh full
- * blocks become cached.  *cached_tokens (a multiple of 16) tells the caller
+ * blocks become cached.  *cached_tokens (a multiple of bs) tells the caller
  * how many leading tokens are already in the cache: only tokens from there
  * on need their K/V computed and written.  A cached block whose count drops
  * to zero is not freed but kept, least recently released first in line for

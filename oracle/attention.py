@@ -20,7 +20,8 @@ Readings where the pages are silent (each is listed with its reason in the
 design notes):
   * context_lens counts the token the step just wrote (it sits at ctx - 1).
   * q head h reads kv head h // (Hq / Hkv) (contiguous GQA groups).
-  * a slot is physical_block * 16 + offset; a negative slot is skipped.
+  * a slot is physical_block * bs + offset (bs = 16, the pages' size; 32 and
+    64 as variants); a negative slot is skipped.
   * a chunk of C queries occupies the last C positions of the context, and
     query i attends keys 0 .. ctx - C + i.
   * ctx == 0 yields a zero output row.
