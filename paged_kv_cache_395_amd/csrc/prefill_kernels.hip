@@ -83,17 +83,10 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   constexpr int kRunsPerTile = kTileBytes / 1024;    // 1 KiB wave loads per tile
   constexpr int kRunsPerStage = 2 * kStageBlocks * kRunsPerTile;
   static_assert(kRunsPerStage % kPfWaves == 0, "stage loads split evenly over the waves");
-  constexpr int kHalfRuns = kStageBlocks * kRunsPerTile;        // 1 KiB loads of a stage's K (or V) tiles
-  static_assert(kHalfRuns % kPfWaves == 0, "K and V loads split evenly over the waves");
-  constexpr int kHalfU4 = kStageBlocks * kTileElems / 8;        // u32x4 per stage's K (or V) tiles
+  constexpr int kStageU4 = 2 * kStageBlocks * kTileElems / 8;  // u32x4 per stage buffer
 
-  // K and V tiles of two stages, in four separate arrays: the software
-  // pipeline below loads into one while it reads others, and distinct arrays
-  // let the compiler see that no load aliases a read
-  __shared__ u32x4_t s_k0[kHalfU4];
-  __shared__ u32x4_t s_k1[kHalfU4];
-  __shared__ u32x4_t s_v0[kHalfU4];
-  __shared__ u32x4_t s_v1[kHalfU4];
+  __shared__ u32x4_t s_buf0[kStageU4];
+  __shared__ u32x4_t s_buf1[kStageU4];
   __shared__ int32_t s_tab[kTabWindow];
   __shared__ int s_bad;
 
@@ -181,13 +174,13 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
     for (int j = threadIdx.x; j < kTabWindow && base + j < nkb; j += kPfThreads) s_tab[j] = trow[(base + j) >> sh];
   };
 
-  // issue the direct-to-LDS loads of the K (or V) tiles of stage st into buf
-  // (this wave's share): one buffer resource per tile (base in scalar
-  // registers, range = the tile), so each load needs only the lane's 16-byte
-  // offset in a VGPR; a tile past the key window or outside the pool gets an
-  // empty range and its LDS image is zero-filled without touching memory
+  // issue the direct-to-LDS loads of stage st into buf (this wave's share):
+  // one buffer resource per tile (base in scalar registers, range = the
+  // tile), so each load needs only the lane's 16-byte offset in a VGPR; a
+  // block past the key window or outside the pool gets an empty range and
+  // its LDS image is zero-filled without touching memory
   const int lane_off = lane * 16;
-  auto issue_half = [&](int st, bool v_half, u32x4_t* buf) {
+  auto issue_stage = [&](int st, u32x4_t* buf) {
     // The stage's 4 key tiles, looked up once per wave in vector registers
     // (lane l: tile l % 4): the byte offset of the tile from its pool run, or
     // -1 when the tile is past the key window or its table entry is outside
@@ -204,17 +197,18 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
             : int64_t(-1);
     const uint32_t off_lo = uint32_t(uint64_t(off_l)), off_hi = uint32_t(uint64_t(off_l) >> 32);
 #pragma unroll
-    for (int j = 0; j < kHalfRuns / kPfWaves; ++j) {
+    for (int j = 0; j < kRunsPerStage / kPfWaves; ++j) {
       const int run = j * kPfWaves + w;
-      const int t = run / kRunsPerTile;  // tile 0..3 of the stage
+      const int t8 = run / kRunsPerTile;  // 0..3 K tiles, 4..7 V tiles
       const int part = run % kRunsPerTile;
-      const int64_t off = int64_t((uint64_t(__builtin_amdgcn_readlane(off_hi, t)) << 32) |
-                                  uint64_t(__builtin_amdgcn_readlane(off_lo, t)));
+      const int b = t8 & (kStageBlocks - 1);
+      const int64_t off = int64_t((uint64_t(__builtin_amdgcn_readlane(off_hi, b)) << 32) |
+                                  uint64_t(__builtin_amdgcn_readlane(off_lo, b)));
       const bool ok = off >= 0;
-      const char* base = (v_half ? vg : kg) + (ok ? off : 0);
+      const char* base = (t8 < kStageBlocks ? kg : vg) + (ok ? off : 0);
       const __amdgpu_buffer_rsrc_t r =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, ok ? kTileBytes : 0, kBufferRsrcWord3);
-      lds_void* dst = (lds_void*)(buf + t * (kTileElems / 8) + part * 64);
+      lds_void* dst = (lds_void*)(buf + t8 * (kTileElems / 8) + part * 64);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, lane_off, part * 1024, 0, 0);
     }
   };
@@ -234,19 +228,20 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   c = fmaxf(c, 1e-30f);
 
   typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
-  typedef f32x4_t Scores[kPfRT][kStageBlocks];
   // MASKED: the stage holds keys past some row's causal limit, past the
-  // context or past the key window; every other stage skips all mask work.
-  // ---- raw scores of a stage's 4 key tiles for both row tiles
-  auto qk_stage = [&](auto masked_tag, int st, const u32x4_t* kbuf, Scores& sc) {
+  // context or past the key window; every other stage skips all mask work
+  auto compute_stage = [&](auto masked_tag, int st, const u32x4_t* buf) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int k0 = st * kStageBlocks * kBlockTokens;
     const int nvalid = min(kStageBlocks, nkb - st * kStageBlocks);  // blocks of this stage in the key window
+    const u32x2_t* buf2 = reinterpret_cast<const u32x2_t*>(buf);
+    // ---- raw scores of the stage's 4 blocks for both row tiles
+    f32x4_t sc[kPfRT][kStageBlocks];
 #pragma unroll
     for (int b = 0; b < kStageBlocks; ++b) {
       u32x4_t kf[DC];
 #pragma unroll
-      for (int cc = 0; cc < DC; ++cc) kf[cc] = kbuf[b * (kTileElems / 8) + cc * 64 + lane];
+      for (int cc = 0; cc < DC; ++cc) kf[cc] = buf[b * (kTileElems / 8) + cc * 64 + lane];
 #pragma unroll
       for (int rt = 0; rt < kPfRT; ++rt) {
         f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -262,13 +257,6 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
         sc[rt][b] = acc;
       }
     }
-  };
-  // ---- softmax of a stage's scores and its PV products
-  auto softmax_pv = [&](auto masked_tag, int st, const Scores& sc, const u32x4_t* vbuf) {
-    constexpr bool MASKED = decltype(masked_tag)::value;
-    const int k0 = st * kStageBlocks * kBlockTokens;
-    const int nvalid = min(kStageBlocks, nkb - st * kStageBlocks);
-    const u32x2_t* buf2 = reinterpret_cast<const u32x2_t*>(vbuf);
     // ---- one reference-max check per stage: the max moves only past a 2^8
     // margin (rare after the first stage), so the accumulator rescale is
     // mostly skipped and the rest of the stage is straight-line code
@@ -335,8 +323,8 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
       for (int t = 0; t < NT; ++t) {
         // 8-byte half (t % 2) of chunk t / 2, in both blocks
         const int idx = ((t / 2) * 64 + lane) * 2 + (t % 2);
-        const u32x2_t h0 = buf2[b0 * (kTileElems / 4) + idx];
-        const u32x2_t h1 = buf2[b1 * (kTileElems / 4) + idx];
+        const u32x2_t h0 = buf2[(kStageBlocks + b0) * (kTileElems / 4) + idx];
+        const u32x2_t h1 = buf2[(kStageBlocks + b1) * (kTileElems / 4) + idx];
         u32x4_t av = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
         if constexpr (MASKED) av = av & u32x4_t{m0a, m0b, m1a, m1b};
 #pragma unroll
@@ -348,19 +336,15 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
     }
   };
   // Stages wholly below every row's causal limit and inside the key window
-  // (all but the last few) need no masks.  They run software-pipelined by
-  // one stage: while the softmax and PV products of stage st run, the QK
-  // products of stage st + 1 (whose K tiles landed a step earlier) are
-  // already issued, so the matrix cores have independent work while the
-  // vector units compute the softmax; meanwhile the K tiles of st + 2 and
-  // the V tiles of st + 1 are loading.  The masked tail runs one stage at a
-  // time.
+  // (all but the last few) need no masks: they run double-buffered, the next
+  // stage loading while this one computes.  The masked tail runs one stage at
+  // a time.
   const int nst_plain = min(nst, (first_masked + 1) / (kStageBlocks * kBlockTokens));
-  auto refill_window = [&](int st_lo, int st_hi) {
-    // keep the table window over the blocks of stages st_lo .. st_hi
-    if ((st_hi + 1) * kStageBlocks - tab_base > kTabWindow) {
+  auto refill_table_for = [&](int st) {
+    // keep the table window over the blocks of stage st
+    if ((st + 1) * kStageBlocks - tab_base > kTabWindow) {
       __syncthreads();
-      tab_base = st_lo * kStageBlocks;
+      tab_base = st * kStageBlocks;
       fill_table(tab_base);
       __syncthreads();
     }
@@ -368,44 +352,36 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   if (threadIdx.x == 0) s_bad = 0;
   fill_table(0);
   __syncthreads();
-  Scores sc_a, sc_b;
   if (nst_plain > 0) {
-    issue_half(0, false, s_k0);
-    issue_half(0, true, s_v0);
-    if (nst_plain > 1) issue_half(1, false, s_k1);
+    issue_stage(0, s_buf0);
     wait_loads();
     __syncthreads();
-    qk_stage(std::false_type{}, 0, s_k0, sc_a);
-    __syncthreads();  // every wave is done with K(0) before K(2) replaces it
   }
-  // step st: sc_cur = QK(st), k_next = K(st + 1), v_cur = V(st); k_free and
-  // v_next were read in the previous step and take K(st + 2) and V(st + 1)
-  auto step = [&](int st, Scores& sc_cur, Scores& sc_next, u32x4_t* k_free, const u32x4_t* k_next,
-                  u32x4_t* v_next, const u32x4_t* v_cur) {
-    refill_window(st + 1, st + 2);
-    if (st + 2 < nst_plain) issue_half(st + 2, false, k_free);
+  // two stages per iteration so each buffer has a fixed name (the compiler
+  // then knows the loads into one never alias reads of the other)
+  for (int st = 0; st < nst_plain; st += 2) {
     if (st + 1 < nst_plain) {
-      issue_half(st + 1, true, v_next);
-      qk_stage(std::false_type{}, st + 1, k_next, sc_next);
+      refill_table_for(st + 1);
+      issue_stage(st + 1, s_buf1);
     }
-    softmax_pv(std::false_type{}, st, sc_cur, v_cur);
+    compute_stage(std::false_type{}, st, s_buf0);
     wait_loads();
     __syncthreads();
-  };
-  // two stages per iteration so every buffer has a fixed name
-  for (int st = 0; st < nst_plain; st += 2) {
-    step(st, sc_a, sc_b, s_k0, s_k1, s_v1, s_v0);
     if (st + 1 >= nst_plain) break;
-    step(st + 1, sc_b, sc_a, s_k1, s_k0, s_v0, s_v1);
+    if (st + 2 < nst_plain) {
+      refill_table_for(st + 2);
+      issue_stage(st + 2, s_buf0);
+    }
+    compute_stage(std::false_type{}, st + 1, s_buf1);
+    wait_loads();
+    __syncthreads();
   }
   for (int st = nst_plain; st < nst; ++st) {
-    refill_window(st, st);
-    issue_half(st, false, s_k0);
-    issue_half(st, true, s_v0);
+    refill_table_for(st);
+    issue_stage(st, s_buf0);
     wait_loads();
     __syncthreads();
-    qk_stage(std::true_type{}, st, s_k0, sc_a);
-    softmax_pv(std::true_type{}, st, sc_a, s_v0);
+    compute_stage(std::true_type{}, st, s_buf0);
     __syncthreads();
   }
 
