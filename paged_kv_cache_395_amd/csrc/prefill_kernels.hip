@@ -180,13 +180,6 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   // block past the key window or outside the pool gets an empty range and
   // its LDS image is zero-filled without touching memory
   const int lane_off = lane * 16;
-  // This lane's odd 8-byte V half (in 8-byte units), hidden from the
-  // compiler: left visible, it fuses a lane's even and odd halves of a chunk
-  // into one 16-byte LDS read and then spends register copies assembling
-  // each PV operand from two such reads; kept apart, each operand is read
-  // as its two 8-byte halves (one per block) straight into its registers.
-  int v_odd = 2 * lane + 1;
-  asm volatile("" : "+v"(v_odd));
   auto issue_stage = [&](int st, u32x4_t* buf) {
     // The stage's 4 key tiles, looked up once per wave in vector registers
     // (lane l: tile l % 4): the byte offset of the tile from its pool run, or
@@ -215,11 +208,7 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
       const char* base = (t8 < kStageBlocks ? kg : vg) + (ok ? off : 0);
       const __amdgpu_buffer_rsrc_t r =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, ok ? kTileBytes : 0, kBufferRsrcWord3);
-      // K tiles one after another; V tiles chunk-major (1 KiB chunk `part`
-      // of the stage's 4 blocks side by side), so the two blocks' halves of
-      // one PV operand are 1 KiB apart and are read by one instruction
-      lds_void* dst = (lds_void*)(t8 < kStageBlocks ? buf + t8 * (kTileElems / 8) + part * 64
-                                                    : buf + kStageBlocks * (kTileElems / 8) + (part * kStageBlocks + b) * 64);
+      lds_void* dst = (lds_void*)(buf + t8 * (kTileElems / 8) + part * 64);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, lane_off, part * 1024, 0, 0);
     }
   };
@@ -333,9 +322,9 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         // 8-byte half (t % 2) of chunk t / 2, in both blocks
-        const int idx = kStageBlocks * (kTileElems / 4) + (t / 2) * kStageBlocks * 128 + (t % 2 ? v_odd : 2 * lane);
-        const u32x2_t h0 = buf2[idx + b0 * 128];
-        const u32x2_t h1 = buf2[idx + b1 * 128];
+        const int idx = ((t / 2) * 64 + lane) * 2 + (t % 2);
+        const u32x2_t h0 = buf2[(kStageBlocks + b0) * (kTileElems / 4) + idx];
+        const u32x2_t h1 = buf2[(kStageBlocks + b1) * (kTileElems / 4) + idx];
         u32x4_t av = u32x4_t{h0[0], h0[1], h1[0], h1[1]};
         if constexpr (MASKED) av = av & u32x4_t{m0a, m0b, m1a, m1b};
 #pragma unroll
