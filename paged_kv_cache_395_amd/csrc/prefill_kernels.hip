@@ -81,8 +81,7 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   constexpr int kTileElems = kBlockTokens * D;
   constexpr int kTileBytes = kTileElems * 2;
   constexpr int kRunsPerTile = kTileBytes / 1024;    // 1 KiB wave loads per tile
-  constexpr int kRunsPerStage = 2 * kStageBlocks * kRunsPerTile;
-  static_assert(kRunsPerStage % kPfWaves == 0, "stage loads split evenly over the waves");
+  static_assert(kStageBlocks == kPfWaves, "each wave loads one block of a stage");
   constexpr int kStageU4 = 2 * kStageBlocks * kTileElems / 8;  // u32x4 per stage buffer
 
   __shared__ u32x4_t s_buf0[kStageU4];
@@ -147,6 +146,12 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
                            : u32x4_t{0u, 0u, 0u, 0u};
     }
   }
+  // Wait for the Q operands here, on every path.  Left to the compiler, the
+  // wait lands at their first use inside the key loop, where a path that
+  // skips the first stage's load makes it count the next stage's tile
+  // loads too: every other stage then waited for its successor's tiles
+  // before its first product (a third of the kernel's time).
+  wait_loads();
   const int row_wg_last = min(R, row_wg0 + kPfRows) - 1;
   const int first_masked = ctx - C + row_wg0 / G;          // smallest last-key of the workgroup's rows
   const int nkb = (ctx - C + row_wg_last / G) / kBlockTokens + 1;  // key blocks any row needs
@@ -174,42 +179,30 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
     for (int j = threadIdx.x; j < kTabWindow && base + j < nkb; j += kPfThreads) s_tab[j] = trow[(base + j) >> sh];
   };
 
-  // issue the direct-to-LDS loads of stage st into buf (this wave's share):
-  // one buffer resource per tile (base in scalar registers, range = the
-  // tile), so each load needs only the lane's 16-byte offset in a VGPR; a
-  // block past the key window or outside the pool gets an empty range and
-  // its LDS image is zero-filled without touching memory
+  // direct-to-LDS loads of the stage's tiles: each lane moves 16 bytes
   const int lane_off = lane * 16;
   auto issue_stage = [&](int st, u32x4_t* buf) {
-    // The stage's 4 key tiles, looked up once per wave in vector registers
-    // (lane l: tile l % 4): the byte offset of the tile from its pool run, or
-    // -1 when the tile is past the key window or its table entry is outside
-    // the pool.  Each load below then only picks its tile's offset with two
-    // lane reads instead of redoing the lookup and the 64-bit address product
-    // in scalar code for every 1 KiB run.
-    const int blk_l = st * kStageBlocks + (lane & (kStageBlocks - 1));
-    const int phys_l = blk_l < nkb ? s_tab[blk_l - tab_base] : 0;
-    const bool in_pool_l = phys_l >= 0 && int64_t(phys_l) < P.num_blocks;
-    bad |= blk_l < nkb && !in_pool_l;
-    const int64_t off_l =
-        blk_l < nkb && in_pool_l
-            ? (int64_t(phys_l) * blk_stride + int64_t(blk_l & ((1 << sh) - 1)) * kTileElems) * 2  // tile in its block
-            : int64_t(-1);
-    const uint32_t off_lo = uint32_t(uint64_t(off_l)), off_hi = uint32_t(uint64_t(off_l) >> 32);
+    // Wave w loads block w of the stage: its K tile and its V tile, each as
+    // kRunsPerTile 1 KiB runs.  One lookup and one buffer resource per tile
+    // (base in scalar registers, range = the tile), so each load needs only
+    // the lane's 16-byte offset and the run's scalar offset; a block past the
+    // key window or outside the pool gets an empty range and its LDS image
+    // is zero-filled without touching memory.
+    const int blk = st * kStageBlocks + w;
+    const int phys = blk < nkb ? __builtin_amdgcn_readfirstlane(s_tab[blk - tab_base]) : 0;
+    const bool in_pool = phys >= 0 && int64_t(phys) < P.num_blocks;
+    bad |= blk < nkb && !in_pool;
+    const bool ok = blk < nkb && in_pool;
+    const int64_t off = ok ? (int64_t(phys) * blk_stride + int64_t(blk & ((1 << sh) - 1)) * kTileElems) * 2 : 0;
 #pragma unroll
-    for (int j = 0; j < kRunsPerStage / kPfWaves; ++j) {
-      const int run = j * kPfWaves + w;
-      const int t8 = run / kRunsPerTile;  // 0..3 K tiles, 4..7 V tiles
-      const int part = run % kRunsPerTile;
-      const int b = t8 & (kStageBlocks - 1);
-      const int64_t off = int64_t((uint64_t(__builtin_amdgcn_readlane(off_hi, b)) << 32) |
-                                  uint64_t(__builtin_amdgcn_readlane(off_lo, b)));
-      const bool ok = off >= 0;
-      const char* base = (t8 < kStageBlocks ? kg : vg) + (ok ? off : 0);
-      const __amdgpu_buffer_rsrc_t r =
-          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, ok ? kTileBytes : 0, kBufferRsrcWord3);
-      lds_void* dst = (lds_void*)(buf + t8 * (kTileElems / 8) + part * 64);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, lane_off, part * 1024, 0, 0);
+    for (int h = 0; h < 2; ++h) {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>((h ? vg : kg) + off), 0,
+                                                                         ok ? kTileBytes : 0, kBufferRsrcWord3);
+#pragma unroll
+      for (int part = 0; part < kRunsPerTile; ++part) {
+        lds_void* dst = (lds_void*)(buf + (h * kStageBlocks + w) * (kTileElems / 8) + part * 64);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, lane_off, part * 1024, 0, 0);
+      }
     }
   };
 
