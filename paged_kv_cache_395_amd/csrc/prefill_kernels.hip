@@ -334,8 +334,9 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   // a time.
   const int nst_plain = min(nst, (first_masked + 1) / (kStageBlocks * kBlockTokens));
   auto refill_table_for = [&](int st) {
-    // keep the table window over the blocks of stage st
-    if ((st + 1) * kStageBlocks - tab_base > kTabWindow) {
+    // keep the table window over the blocks of stage st (it only moves
+    // forward; the check both ways keeps a stale window from being read)
+    if (st * kStageBlocks < tab_base || (st + 1) * kStageBlocks - tab_base > kTabWindow) {
       __syncthreads();
       tab_base = st * kStageBlocks;
       fill_table(tab_base);
