@@ -65,8 +65,9 @@ reshape_and_cache_kernel(const E* __restrict__ key, const E* __restrict__ value,
 // same block otherwise); the workgroups after those copy new_ctx into ctx.
 // The token's (slot, row, pos) are read once, by thread 0, into LDS: they may
 // live in pinned host memory, where every read crosses the host link.
+constexpr int kAppendThreads = 512;  // one 8-element run per thread for 32 kv heads x 128 dims
 template <typename E>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kAppendThreads)
 append_step_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ kc, E* __restrict__ vc,
                    const int64_t* slots, const int32_t* rows, const int32_t* positions, int32_t num_tokens,
                    int32_t* tables, int32_t max_blocks, int32_t* ctx, const int32_t* new_ctx, int32_t num_rows,
@@ -80,6 +81,17 @@ append_step_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __
   }
   __shared__ int64_t s_slot;
   __shared__ int32_t s_row, s_pos;
+  // the thread's first K/V run is read before the metadata wait, so the
+  // device reads overlap the (slower) read of the slot from host memory
+  const int runs_per_head = head_dim / 8;
+  const int nruns = kv_heads * runs_per_head;
+  vec8 kv0 = {}, vv0 = {};
+  if (int(threadIdx.x) < nruns) {
+    const int h = threadIdx.x / runs_per_head, j = threadIdx.x - h * runs_per_head;
+    const int64_t src = (int64_t(t) * kv_heads + h) * head_dim + 8 * j;
+    kv0 = *reinterpret_cast<const vec8*>(key + src);
+    vv0 = *reinterpret_cast<const vec8*>(value + src);
+  }
   if (threadIdx.x == 0) {
     s_slot = slots[t];
     s_row = rows[t];
@@ -92,13 +104,14 @@ append_step_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __
   if (threadIdx.x == 0 && row >= 0 && row < num_rows && pos >= 0 && (pos >> (4 + sh)) < max_blocks)
     tables[int64_t(row) * max_blocks + (pos >> (4 + sh))] = int32_t(slot >> (4 + sh));
   const int o = int(slot & 15);
-  const int runs_per_head = head_dim / 8;
-  for (int c = threadIdx.x; c < kv_heads * runs_per_head; c += blockDim.x) {
+  for (int c = threadIdx.x; c < nruns; c += blockDim.x) {
     const int h = c / runs_per_head, j = c - h * runs_per_head;
     const int64_t src = (int64_t(t) * kv_heads + h) * head_dim + 8 * j;
     const int64_t tile = slot_tile(slot, h, kv_heads, head_dim, sh);
-    *reinterpret_cast<vec8*>(kc + tile + (j * kBlockTokens + o) * 8) = *reinterpret_cast<const vec8*>(key + src);
-    const vec8 vv = *reinterpret_cast<const vec8*>(value + src);
+    const bool first = c == int(threadIdx.x);
+    *reinterpret_cast<vec8*>(kc + tile + (j * kBlockTokens + o) * 8) =
+        first ? kv0 : *reinterpret_cast<const vec8*>(key + src);
+    const vec8 vv = first ? vv0 : *reinterpret_cast<const vec8*>(value + src);
     E* vt = vc + tile;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -162,17 +175,17 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
 }
 
 hipError_t launch_append_step(const AppendStepArgs& a) {
-  const int64_t ctx_groups = (int64_t(a.num_rows) + 255) / 256;
+  const int64_t ctx_groups = (int64_t(a.num_rows) + kAppendThreads - 1) / kAppendThreads;
   const int64_t grid = int64_t(a.num_tokens) + ctx_groups;
   if (grid == 0) return hipSuccess;
   if (a.elem_bytes == 2) {
-    hipLaunchKernelGGL(append_step_kernel<uint16_t>, dim3(unsigned(grid)), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL(append_step_kernel<uint16_t>, dim3(unsigned(grid)), dim3(kAppendThreads), 0, a.stream,
                        static_cast<const uint16_t*>(a.key), static_cast<const uint16_t*>(a.value),
                        static_cast<uint16_t*>(a.k_cache), static_cast<uint16_t*>(a.v_cache), a.slots, a.rows,
                        a.positions, a.num_tokens, a.tables, a.max_blocks, a.ctx, a.new_ctx, a.num_rows,
                        a.num_kv_heads, a.head_dim, a.num_blocks, a.tile_shift);
   } else {
-    hipLaunchKernelGGL(append_step_kernel<uint32_t>, dim3(unsigned(grid)), dim3(256), 0, a.stream,
+    hipLaunchKernelGGL(append_step_kernel<uint32_t>, dim3(unsigned(grid)), dim3(kAppendThreads), 0, a.stream,
                        static_cast<const uint32_t*>(a.key), static_cast<const uint32_t*>(a.value),
                        static_cast<uint32_t*>(a.k_cache), static_cast<uint32_t*>(a.v_cache), a.slots, a.rows,
                        a.positions, a.num_tokens, a.tables, a.max_blocks, a.ctx, a.new_ctx, a.num_rows,
