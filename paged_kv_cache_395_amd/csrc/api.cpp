@@ -394,7 +394,10 @@ pa_status_t pa_prefill_chunk(void* out, pa_dtype_t out_dtype, const void* q, int
     return fail(PA_EINVAL, "max_blocks_per_seq cannot hold max_context_len");
   if (!isfinite(scale)) return fail(PA_EINVAL, "scale must be finite");
   if (num_seqs == 0 || chunk_len == 0) return PA_OK;
-  if (num_seqs > 65535 || num_kv_heads > 65535) return fail(PA_EUNSUPPORTED, "grid too large");
+  // rows (query, head of the group) and workgroups are counted in int on the device
+  const int64_t rows = int64_t(chunk_len) * (num_q_heads / num_kv_heads);
+  if (rows > INT32_MAX / 2 || (rows / 16 + 1) * num_seqs * num_kv_heads > INT32_MAX)
+    return fail(PA_EUNSUPPORTED, "grid too large");
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens) return fail(PA_EINVAL, "null pointer argument");
   PrefillArgs a{};
   a.out = out;

@@ -405,7 +405,7 @@ hipError_t launch_prefill_t(const PrefillArgs& a, const PParams& p) {
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t R = int64_t(a.chunk) * G;
   const int tiles = int((R + rows - 1) / rows);
-  const int pairs = a.num_seqs * a.num_kv_heads;
+  const int pairs = a.num_seqs * a.num_kv_heads;  // the caller bounds tiles x pairs by INT32_MAX
   const dim3 grid(unsigned(int64_t(tiles) * pairs));
   if (a.out_f32) {
     hipLaunchKernelGGL((prefill_mfma_kernel<T, D, true, RT, WPE>), grid, dim3(kPfThreads), 0, a.stream, p, tiles, pairs);

@@ -221,6 +221,8 @@ def test_prefill_rejects_bad_arguments():
     assert call(maxb=2) == _lib.PA_EINVAL
     assert call(Hq=7) == _lib.PA_EINVAL
     assert call(out_dtype=_lib.PA_F16) == _lib.PA_EUNSUPPORTED
+    # rows of a chunk (query x head of the group) beyond what the device counts in int
+    assert call(C=1 << 28, max_ctx=1 << 28, maxb=1 << 24, Hq=32, Hkv=2) == _lib.PA_EUNSUPPORTED
 
 
 def test_package_exposes_the_binding():
