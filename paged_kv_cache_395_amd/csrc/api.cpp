@@ -96,7 +96,8 @@ pa_status_t check_decode(const void* out, pa_dtype_t out_dtype, const void* q, i
   partition = choose_partition(S, Hkv, max_ctx, partition);
   if (S > 0 && (!out || !q || !k || !v || !tables || !ctx)) return fail(PA_EINVAL, "null pointer argument");
   const int64_t nparts = max_ctx == 0 ? 1 : ceil_div(max_ctx, partition);
-  if (nparts > 65535 * 64) return fail(PA_EUNSUPPORTED, "too many partitions");
+  // partitions index the third grid dimension of the mfma path (at most 65535)
+  if (nparts > 65535) return fail(PA_EUNSUPPORTED, "%lld partitions > 65535: use a larger partition_size", (long long)nparts);
   if (S > 65535 || Hq > 65535) return fail(PA_EUNSUPPORTED, "num_seqs and num_q_heads must be <= 65535");
   dc->partition = partition;
   dc->nparts = int32_t(nparts);

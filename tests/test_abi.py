@@ -81,6 +81,7 @@ def test_block_sizes_16_32_64_are_accepted_and_others_refused():
     (dict(max_ctx=600, maxb=40, P=256), _lib.PA_EWORKSPACE),
     (dict(P=-16), _lib.PA_EINVAL),
     (dict(scale=float("inf")), _lib.PA_EINVAL),
+    (dict(max_ctx=16 * 65536, maxb=65536, P=16), _lib.PA_EUNSUPPORTED),  # 65536 partitions > one grid dimension
 ])
 def test_decode_rejects_bad_arguments_before_launch(kw, status):
     st = decode_call(**kw)
