@@ -192,7 +192,9 @@ pa_status_t pa_patch_tables(int32_t* block_tables, int32_t max_blocks_per_seq, i
  *                   to let the library choose (pa_decode_partition_size
  *                   reports the choice).  Sequences longer than one
  *                   partition are split; the pieces are merged exactly by
- *                   a log-sum-exp reduction.
+ *                   a log-sum-exp reduction.  At most 65535 partitions
+ *                   (ceil(max_context_len / partition)); more give
+ *                   PA_EUNSUPPORTED.
  *   workspace       device scratch of at least
  *                   pa_decode_workspace_bytes(...) bytes (may be NULL when
  *                   that is 0); its contents are private to the call.
@@ -278,7 +280,9 @@ pa_status_t pa_decode_reduce(void* out, pa_dtype_t out_dtype, const int32_t* con
  *   out  device [num_seqs][chunk_len][num_q_heads][head_dim] of out_dtype
  *   q    device [num_seqs][chunk_len][num_q_heads][head_dim] of dtype
  * Requires context_lens[s] >= chunk_len (else that sequence's rows are NaN).
- * dtype PA_F16 / PA_BF16 only (matrix cores, fp32 accumulation).
+ * dtype PA_F16 / PA_BF16 only (matrix cores, fp32 accumulation).  A chunk
+ * whose rows (chunk_len x query group) or workgroup count would exceed the
+ * device's int counters gives PA_EUNSUPPORTED.
  * ---------------------------------------------------------------------- */
 pa_status_t pa_prefill_chunk(void* out, pa_dtype_t out_dtype, const void* q, int32_t chunk_len,
                              const void* k_cache, const void* v_cache,
