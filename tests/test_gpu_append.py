@@ -201,3 +201,37 @@ def test_step_plan_with_resident_tables_matches_the_oracle():
         assert_close(out_f64(out), want, w.dtype, f"step {step}")
     assert np.array_equal(d_table.cpu().numpy(), t_now)
     assert np.array_equal(d_ctx.cpu().numpy(), c_now)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_wide_tokens_take_several_runs_per_thread(dtype):
+    """64 kv heads x 128 dims is 1,024 eight-element runs per token, twice the
+    workgroup: each thread stores the run it read before the slot arrived and
+    then reads and stores a second one."""
+    rng = np.random.default_rng(61 if dtype == "bf16" else 62)
+    NB, Hkv, D = 12, 64, 128
+    k = to_storage(rng.standard_normal((NB, Hkv, 16 * D), dtype=np.float32), dtype)
+    v = to_storage(rng.standard_normal((NB, Hkv, 16 * D), dtype=np.float32), dtype)
+    key = to_storage(rng.standard_normal((5, Hkv, D), dtype=np.float32), dtype)
+    val = to_storage(rng.standard_normal((5, Hkv, D), dtype=np.float32), dtype)
+    # row 0 writes positions 0..2 of its block 7, row 1 positions 16..17 of its block 2
+    slots = np.array([7 * 16 + 0, 7 * 16 + 1, 7 * 16 + 2, 2 * 16 + 0, 2 * 16 + 1], dtype=np.int64)
+    rows = np.array([0, 0, 0, 1, 1], dtype=np.int32)
+    positions = np.array([0, 1, 2, 16, 17], dtype=np.int32)
+    new_ctx = np.array([3, 18], dtype=np.int32)
+    table = np.full((2, 3), NB + 4, dtype=np.int32)
+    table[1, 0] = 9
+    d_table = torch.from_numpy(table.copy()).cuda()
+    d_ctx = torch.zeros(2, dtype=torch.int32, device="cuda")
+    dk, dv = to_dev(k, dtype), to_dev(v, dtype)
+    ops.append_step(to_dev(key, dtype), to_dev(val, dtype), dk, dv,
+                    *[torch.from_numpy(a).cuda() for a in (slots, rows, positions)], d_table, d_ctx,
+                    torch.from_numpy(new_ctx).cuda())
+    k_ref, v_ref = k.copy(), v.copy()
+    OA.reshape_and_cache(k_ref, v_ref, key, val, slots)
+    table[0, 0], table[1, 1] = 7, 2
+    assert np.array_equal(d_table.cpu().numpy(), table)
+    assert np.array_equal(d_ctx.cpu().numpy(), new_ctx)
+    bits = np.uint16 if dtype == "bf16" else np.uint32
+    assert np.array_equal(to_host(dk, dtype).view(bits), k_ref.view(bits))
+    assert np.array_equal(to_host(dv, dtype).view(bits), v_ref.view(bits))
