@@ -77,8 +77,8 @@ def load_traffic(workload: str, bytes_per_launch: float):
 
 
 def _host_threads() -> int:
-    """Host cores this process may use: the machine's CPU share when the
-    environment states it (OMP_NUM_THREADS), else the affinity mask."""
+    """Host cores this process may use: the CPU share the environment
+    states (OMP_NUM_THREADS), else the affinity mask."""
     env = os.environ.get("OMP_NUM_THREADS", "")
     n = int(env) if env.isdigit() and int(env) > 0 else 0
     return min(n, len(os.sched_getaffinity(0))) if n else len(os.sched_getaffinity(0))
@@ -513,8 +513,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        sys.stderr.write("bench.py measures one GPU only: every box here has one MI355X, and the paged "
-                         "decode path is built and measured on a single GPU (run with --gpus 1).\n")
+        sys.stderr.write("bench.py measures one GPU only: the paged decode path runs on one GPU's share "
+                         "of the work and several GPUs are not supported (run with --gpus 1).\n")
         sys.exit(2)
 
     if args.workload in ("serving_bf16", "serving_prefix_bf16"):
