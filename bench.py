@@ -389,9 +389,9 @@ def summarize_prefill(args, rec) -> None:
     md = [f"# Matrix-core utilisation of `prefill_mfma_kernel`: {wl}", "",
           "Two counter passes of the same command (one per counter block):", "", "```",
           f"timeout -s KILL 180 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
-          f"SQ_INSTS_LDS SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY --output-format csv -d gpurun_out/pmc_prefill -o pf "
+          f"SQ_INSTS_LDS SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY --output-format csv -d {args.prefill_pmc_dir} -o pf "
           f"-- {base}",
-          f"timeout -s KILL 180 rocprofv3 --pmc GRBM_GUI_ACTIVE --output-format csv -d gpurun_out/pmc_prefill_grbm "
+          f"timeout -s KILL 180 rocprofv3 --pmc GRBM_GUI_ACTIVE --output-format csv -d {args.prefill_grbm_dir} "
           f"-o pfg -- {base}", "```", "",
           f"Per dispatch (mean of {n}):", "",
           f"- GRBM_GUI_ACTIVE {gui:.4g} (summed over the 8 XCDs: {gui / 8:.4g} cycles of the GPU clock)",
@@ -421,9 +421,9 @@ def summarize(args) -> None:
     alg = rec["roofline"]["algorithmic_bytes_per_launch"]
     prof = os.path.join(ROOT, "profiles")
     base = "python -u bench.py --workload %s" % wl
-    trace_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d gpurun_out/trace_{wl} -o trace -- "
+    trace_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {args.trace_dir} -o trace -- "
                  f"{base} --steps 20 --warmup 3 --cold-iters 3 --no-cpu-baseline")
-    pmc_cmd = (f"timeout -s KILL 120 rocprofv3 --pmc {{counter}} --output-format csv -d gpurun_out/pmc_{{tag}}_{wl} "
+    pmc_cmd = (f"timeout -s KILL 120 rocprofv3 --pmc {{counter}} --output-format csv -d {{out_dir}} "
                f"-o {{tag}} -- {base} --steps 3 --warmup 1 --cold-iters 0 --no-cpu-baseline --copy-probe-mib 1024")
     lines = [f"# Kernel trace: {wl}", "", f"{rec['config']['workload']}", "",
              "Command (from the repository root, one MI355X):", "", "```", trace_cmd, "```", "",
@@ -455,8 +455,8 @@ def summarize(args) -> None:
            "fetch_scale": fs, "write_scale": ws, "hbm_fetch_bytes_per_launch": hbm_f,
            "hbm_write_bytes_per_launch": hbm_w, "hbm_bytes_per_launch": hbm_f + hbm_w,
            "algorithmic_bytes_per_launch": alg,
-           "commands": [pmc_cmd.format(counter="FETCH_SIZE", tag="fetch"),
-                        pmc_cmd.format(counter="WRITE_SIZE", tag="write")]}
+           "commands": [pmc_cmd.format(counter="FETCH_SIZE", out_dir=args.fetch_dir, tag="fetch"),
+                        pmc_cmd.format(counter="WRITE_SIZE", out_dir=args.write_dir, tag="write")]}
     with open(os.path.join(prof, f"decode_partitions_{wl}_traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
     md = [f"# HBM traffic of `{DECODE_KERNEL}`: {wl}", "",
