@@ -485,12 +485,14 @@ decode_f32_kernel(KParams P) {
 // ------------------------------------------------------------------------
 // Log-sum-exp merge of the partition partials.  Grid (Hq, S), D threads:
 //   M = max_j m_j,  w_j = 2^(m_j - M),  out = sum_j w_j acc_j / sum_j w_j l_j
-// Thread d owns output dim d; the weights of up to kReduceChunk partitions
-// at a time are computed once into LDS and every partition's row is read
-// with one coalesced load.  Sums run in partition order, so the result is
-// deterministic.
+// Thread d owns output dim d.  A row of up to kReduceFew partitions loads
+// all its partials at once; longer rows compute the weights of up to
+// kReduceChunk partitions at a time once into LDS and read every
+// partition's row with one coalesced load.  Sums run in partition order, so
+// the result is deterministic.
 // ------------------------------------------------------------------------
 constexpr int kReduceChunk = 256;
+constexpr int kReduceFew = 8;  // rows with at most this many partitions take the one-pass path
 
 template <typename T, int D, bool OUT_F32>
 __global__ void __launch_bounds__(D)
@@ -505,6 +507,32 @@ decode_reduce_kernel(KParams P) {
   if (context_out_of_contract(ctx, P) || ctx < P.qlen || ctx <= P.partition) return;  // written by the partition kernel
   const int nparts = (ctx + P.partition - 1) / P.partition;
   const int64_t prow0 = (int64_t(sq) * P.hq + h) * P.nparts_max;
+
+  if (nparts <= kReduceFew) {
+    // few partitions (the common case): every partial of the row is loaded
+    // at once, with no barrier, so the merge costs one round trip to memory
+    // (slots past the row's last partition reload that one and weigh 0)
+    float mj[kReduceFew], lj[kReduceFew], aj[kReduceFew];
+#pragma unroll
+    for (int j = 0; j < kReduceFew; ++j) {
+      const int jj = min(j, nparts - 1);
+      mj[j] = P.ws_m[prow0 + jj];
+      lj[j] = P.ws_l[prow0 + jj];
+      aj[j] = P.ws_acc[(prow0 + jj) * D + d];
+    }
+    float M = mj[0];
+#pragma unroll
+    for (int j = 1; j < kReduceFew; ++j) M = fmaxf(M, mj[j]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int j = 0; j < kReduceFew; ++j) {
+      const float wj = j < nparts ? fast_exp2(mj[j] - M) : 0.f;
+      L += wj * lj[j];
+      O += wj * aj[j];
+    }
+    store_out<T, OUT_F32>(P.out, (int64_t(sq) * P.hq + h) * D + d, O / L);
+    return;
+  }
 
   float M = -INFINITY;
   for (int j = d; j < nparts; j += D) M = fmaxf(M, P.ws_m[prow0 + j]);
