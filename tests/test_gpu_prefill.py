@@ -8,7 +8,7 @@ import torch
 from oracle import attention as OA
 from paged_kv_cache_395_amd import ops
 from tests._gpu import Prepared, assert_close, out_f64, say, to_dev
-from workloads import make_workload
+from workloads import make_workload, to_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +81,24 @@ def test_prefill_output_dtype_and_determinism():
     assert torch.equal(out, out2)
     _, outb = run_prefill(p, out_f32=False)
     assert torch.equal(outb, out.to(torch.bfloat16))
+
+
+def test_prefill_follows_scores_that_keep_growing_along_the_context():
+    """Every key block is scaled by 2^(logical block // 8): scores double every
+    two 64-key stages, so the running max moves again and again through the
+    unmasked stages and the accumulated output is rescaled each time (the
+    scaling is by powers of two, exact in bf16, so both sides see the same
+    values)."""
+    p = Prepared(make_workload("longctx_bf16", num_seqs=2, ctx=1000, chunk=48, Hq=16, Hkv=2))
+    w = p.w
+    bits = w.k_pool.astype(np.uint32) << np.uint32(16)
+    k32 = bits.view(np.float32)
+    for s in range(w.num_seqs):
+        for lb in range(-(-int(p.ctx[s]) // 16)):
+            k32[p.table[s, lb]] *= np.float32(2.0 ** (lb // 8))
+    w.k_pool[...] = to_storage(k32, "bf16")
+    say("[prefill] growing scores")
+    _, out = run_prefill(p)
+    k, v = p.oracle_pools()
+    ref = OA.prefill_chunk(w.q, k, v, p.table, p.ctx, w.scale, "bf16")
+    assert_close(out_f64(out), ref, "bf16", "growing scores")
