@@ -3,7 +3,8 @@
 Every workload at full size with the launch configuration the benchmark
 uses (the library's default partitions), reduced sizes with ragged tails, the
 output-dtype path, partition-size agreement, and the closed-form / paging
-properties: single-token contexts, dominant keys, zero queries, physical
+properties: single-token contexts, dominant keys, zero queries, scores growing
+along the context (rescales and far-apart partition maxima), physical
 relabelling, determinism, NaN poison in unread memory, zero-length
 contexts and out-of-pool table entries.
 """
@@ -15,7 +16,7 @@ import torch
 
 from oracle import attention as OA
 from tests._gpu import Prepared, assert_close, out_f64, say, to_dev, to_host
-from workloads import make_workload
+from workloads import make_workload, to_storage
 
 pytestmark = pytest.mark.gpu
 
@@ -234,3 +235,37 @@ def test_zero_length_context_gives_a_zero_row_and_bad_entries_give_nan():
     ctx[7] = p.max_ctx + 1
     out = out_f64(p.gpu_decode(d, ctx=ctx))
     assert np.all(np.isnan(out[7]))
+
+
+def _scale_blocks_along_context(p, per=8):
+    """Multiply every key block by 2^(logical block // per) (exact for these
+    types), so scores grow along each context."""
+    w = p.w
+    if w.dtype == "bf16":
+        k = (w.k_pool.astype(np.uint32) << np.uint32(16)).view(np.float32)
+    else:
+        k = w.k_pool.astype(np.float32)
+    done = set()
+    for s in range(len(p.ctx)):
+        for lb in range(-(-int(p.ctx[s]) // w.block_size)):
+            b = int(p.table[s, lb])
+            assert b not in done, "a shared block would be scaled twice"
+            done.add(b)
+            k[b] *= np.float32(2.0 ** (lb // per))
+    w.k_pool[...] = to_storage(k, w.dtype) if w.dtype != "f32" else k
+
+
+@pytest.mark.parametrize("name,kw", [("mha7b_f16", dict(num_seqs=5, lo=300, hi=1100)),
+                                     ("gqa8b_bf16", dict(num_seqs=8, hi=1500))], ids=["f16", "bf16"])
+@pytest.mark.parametrize("partition", [64, 0])
+def test_scores_growing_along_the_context(name, kw, partition):
+    """The running max moves again and again inside a partition (lazy
+    rescale) and the partitions' maxima differ by orders of magnitude (LSE
+    merge)."""
+    p = Prepared(make_workload(name, **kw))
+    _scale_blocks_along_context(p)
+    say(f"[decode] growing scores {name} P={partition}")
+    d = p.device()
+    p.write_step(d)
+    out = p.gpu_decode(d, partition=partition)
+    assert_close(out_f64(out), p.oracle_decode(), p.w.dtype, f"{name} growing scores")
