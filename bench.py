@@ -696,7 +696,22 @@ def main():
         probe.append((a, b))
     torch.cuda.synchronize()
     read_gbs = big.numel() / (np.median([a.elapsed_time(b) for a, b in probe]) * 1e-3) / 1e9
-    del big, scratch
+    # gather ceiling: the same buffer read as decode tiles (16 tokens of one kv head) in a random order
+    tile_bytes = 16 * w.head_dim * ESIZE[w.dtype]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    order = torch.randperm(big.numel() // tile_bytes, generator=gen, device=dev, dtype=torch.int32)
+    ops.probe_gather_bandwidth(big, order, tile_bytes, sink)
+    probe = []
+    for _ in range(5):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        ops.probe_gather_bandwidth(big, order, tile_bytes, sink)
+        b.record(stream)
+        probe.append((a, b))
+    torch.cuda.synchronize()
+    gather_gbs = order.numel() * tile_bytes / (np.median([a.elapsed_time(b) for a, b in probe]) * 1e-3) / 1e9
+    del big, scratch, order
 
     extra_fields = {}
     if args.copy_probe_mib:
@@ -760,6 +775,7 @@ def main():
             "median_ms": round(float(np.median(cold_ms)), 5), "p10_ms": round(float(np.percentile(cold_ms, 10)), 5),
             "p90_ms": round(float(np.percentile(cold_ms, 90)), 5), "gbs": round(cold_gbs, 2)},
         "hbm_read_ceiling_gbs": round(read_gbs, 1),
+        "hbm_gather_ceiling_gbs": round(gather_gbs, 1),
         **extra_fields,
     }
     if not args.no_cpu_baseline:

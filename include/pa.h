@@ -305,6 +305,20 @@ pa_status_t pa_probe_read_bandwidth(const void* buf, int64_t bytes, uint32_t* si
                                     void* stream);
 
 /* ------------------------------------------------------------------------
+ * Measurement probe for the access pattern of paged decode: reads the
+ * tiles tiles[0 .. num_tiles) of tile_bytes bytes each (tile i is
+ * buf + i * tile_bytes; a multiple of 1024 up to 64 KiB) with the same
+ * 16-byte non-temporal loads, wave by wave with two tiles in flight, and
+ * discards the data like pa_probe_read_bandwidth.  A random permutation of
+ * the tiles of a large buffer gives the ceiling of a gather of scattered
+ * blocks.  tiles: int32, device memory; an index outside
+ * [0, buf_bytes / tile_bytes) is skipped without a memory access.  buf must
+ * be 16-byte aligned; `workgroups` (4 waves each) sizes the grid.
+ * ---------------------------------------------------------------------- */
+pa_status_t pa_probe_gather_bandwidth(const void* buf, int64_t buf_bytes, const int32_t* tiles, int64_t num_tiles,
+                                      int32_t tile_bytes, uint32_t* sink, int32_t workgroups, void* stream);
+
+/* ------------------------------------------------------------------------
  * Host block manager.  One pool of num_blocks blocks of block_size (16, 32
  * or 64) tokens; per sequence a list of physical blocks; a free list;
  * reference counts for shared blocks.

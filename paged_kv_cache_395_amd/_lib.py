@@ -62,6 +62,7 @@ SIGNATURES = {
     "pa_prefill_chunk": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                         _i32, _i32, _i64, _f32, _i32, ctypes.c_int, _vp]),
     "pa_probe_read_bandwidth": (ctypes.c_int, [_vp, _i64, _vp, _i32, _vp]),
+    "pa_probe_gather_bandwidth": (ctypes.c_int, [_vp, _i64, _vp, _i64, _i32, _vp, _i32, _vp]),
     "pa_bm_create": (_vp, [_i64, _i32, _vp]),
     "pa_bm_destroy": (None, [_vp]),
     "pa_bm_add_seq": (ctypes.c_int, [_vp, _i64, _i32]),

@@ -433,4 +433,18 @@ pa_status_t pa_probe_read_bandwidth(const void* buf, int64_t bytes, uint32_t* si
                     "read probe launch");
 }
 
+pa_status_t pa_probe_gather_bandwidth(const void* buf, int64_t buf_bytes, const int32_t* tiles, int64_t num_tiles,
+                                      int32_t tile_bytes, uint32_t* sink, int32_t workgroups, void* stream) {
+  if (buf_bytes < 0 || num_tiles < 0 || workgroups <= 0) return fail(PA_EINVAL, "sizes must be >= 0 and workgroups > 0");
+  if (tile_bytes <= 0 || tile_bytes % 1024 != 0 || tile_bytes > (64 << 10))
+    return fail(PA_EINVAL, "tile_bytes must be a multiple of 1024 up to 64 KiB (got %d)", tile_bytes);
+  if (num_tiles == 0) return PA_OK;
+  if (!buf || !tiles || !sink) return fail(PA_EINVAL, "null pointer argument");
+  if (reinterpret_cast<uintptr_t>(buf) % 16 != 0) return fail(PA_EINVAL, "buf must be 16-byte aligned");
+  if (buf_bytes / tile_bytes > INT32_MAX) return fail(PA_EUNSUPPORTED, "more than 2^31 tiles in buf");
+  return hip_status(launch_gather_probe(buf, buf_bytes / tile_bytes, tiles, num_tiles, tile_bytes, sink, workgroups,
+                                        static_cast<hipStream_t>(stream)),
+                    "gather probe launch");
+}
+
 }  // extern "C"

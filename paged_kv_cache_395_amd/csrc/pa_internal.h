@@ -95,5 +95,7 @@ hipError_t launch_patch_tables(int32_t* tables, int32_t max_blocks, int32_t num_
                                int32_t num_patches, hipStream_t stream);
 
 hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, int32_t workgroups, hipStream_t stream);
+hipError_t launch_gather_probe(const void* buf, int64_t buf_tiles, const int32_t* tiles, int64_t num_tiles,
+                               int32_t tile_bytes, uint32_t* sink, int32_t workgroups, hipStream_t stream);
 
 }  // namespace pa

@@ -283,6 +283,18 @@ def probe_read_bandwidth(buf: torch.Tensor, sink: torch.Tensor, workgroups: int 
                                                    int(workgroups), _stream(stream)))
 
 
+def probe_gather_bandwidth(buf: torch.Tensor, tiles: torch.Tensor, tile_bytes: int, sink: torch.Tensor,
+                           workgroups: int = 1024, stream=None) -> None:
+    """Read tiles ``tiles`` (int32 tile indices) of ``tile_bytes`` bytes of ``buf`` once, in the access
+    pattern of paged decode (the gather ceiling probe)."""
+    _dev(buf, tiles, sink)
+    if tiles.dtype != torch.int32 or not tiles.is_contiguous():
+        raise ValueError("tiles must be a contiguous int32 tensor")
+    _lib.check(_lib.load().pa_probe_gather_bandwidth(_p(buf), buf.numel() * buf.element_size(), _p(tiles),
+                                                     tiles.numel(), int(tile_bytes), _p(sink), int(workgroups),
+                                                     _stream(stream)))
+
+
 class StepPlan:
     """One decode step (cache write, decode partitions, merge) on fixed buffers.
 

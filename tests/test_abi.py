@@ -229,3 +229,18 @@ def test_prefill_rejects_bad_arguments():
 def test_package_exposes_the_binding():
     assert pa.BlockManager is not None
     assert callable(pa.ops.decode)
+
+
+def test_gather_probe_rejects_bad_arguments():
+    def call(**kw):
+        a = dict(buf=16, buf_bytes=1 << 20, tiles=1, n=4, tile_bytes=4096, sink=1, wg=8)
+        a.update(kw)
+        return L.pa_probe_gather_bandwidth(a["buf"], a["buf_bytes"], a["tiles"], a["n"], a["tile_bytes"], a["sink"],
+                                           a["wg"], NULL)
+    assert call(tile_bytes=1000) == _lib.PA_EINVAL
+    assert call(tile_bytes=128 << 10) == _lib.PA_EINVAL
+    assert call(wg=0) == _lib.PA_EINVAL
+    assert call(n=-1) == _lib.PA_EINVAL
+    assert call(buf=8) == _lib.PA_EINVAL  # not 16-byte aligned
+    assert call(tiles=None) == _lib.PA_EINVAL
+    assert call(n=0, tiles=None) == _lib.PA_OK
