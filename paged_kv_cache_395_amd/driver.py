@@ -3,10 +3,10 @@ the device kernels over fixed buffers.
 
 Each step has a host half (``schedule``: the scheduler picks the batch,
 allocates slots, preempts and brings back requests) and a device half
-(``launch``, all on one stream): swap-out copies into the pinned host pool,
-swap-in copies back, copy-on-write, table patches, the cache write that also
-patches the device-resident tables and lengths, then decode over every batch
-row.  Between the two halves the caller fills ``key[:T]``, ``value[:T]``
+(``launch``): swap-out copies into the pinned host pool (on a second stream,
+beside the previous step's decode), then on the main stream swap-in copies
+back, copy-on-write, table patches, the cache write that also patches the
+device-resident tables and lengths, and decode over every batch row.  Between the two halves the caller fills ``key[:T]``, ``value[:T]``
 (the step's new K/V rows, in the order of ``Step.slots``) and ``q`` (one
 query per row).  Every computation runs in libpa's kernels; this module only
 stages metadata and marshals arguments.
@@ -69,6 +69,10 @@ class Driver:
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
         self.stream = torch.cuda.current_stream(dev)
         self._s = ctypes.c_void_p(self.stream.cuda_stream)
+        # swap-outs run on a second stream (default priority) beside the previous step's decode
+        self.swap_stream = torch.cuda.Stream(dev)
+        self._ss = ctypes.c_void_p(self.swap_stream.cuda_stream)
+        self._after_append = None  # recorded on the main stream after the last step's cache write
         # pinned staging, one set per in-flight step
         pair_cap = 2 * max(num_blocks, nh)
         self._ring = []
@@ -119,8 +123,18 @@ class Driver:
         r = self._ring[self._i % len(self._ring)]
         Hkv, D, NB, NH = self.Hkv, self.D, self.NB, max(self.NH, 1)
         if len(st.swap_out):
+            # A preempted request ran in the last step: its blocks are final once that step's cache
+            # write is done, and the last step's decode only reads them, so the copy to host memory
+            # starts there, beside that decode.  This step's work waits for it: the freed blocks may
+            # take this step's writes.  Host blocks it fills were released by swap-ins of earlier
+            # steps, which ran before that cache write.
+            if self._after_append is not None:
+                self.swap_stream.wait_event(self._after_append)
             _lib.check(L.pa_swap_blocks(_p(self.k_host), _p(self.v_host), NH, _p(self.k_pool), _p(self.v_pool), NB,
-                                        _p(r["out_pairs"]), len(st.swap_out), Hkv, D, self.bs, code, s))
+                                        _p(r["out_pairs"]), len(st.swap_out), Hkv, D, self.bs, code, self._ss))
+            swapped = torch.cuda.Event()
+            swapped.record(self.swap_stream)
+            self.stream.wait_event(swapped)
         if len(st.swap_in):
             _lib.check(L.pa_swap_blocks(_p(self.k_pool), _p(self.v_pool), NB, _p(self.k_host), _p(self.v_host), NH,
                                         _p(r["in_pairs"]), len(st.swap_in), Hkv, D, self.bs, code, s))
@@ -132,8 +146,10 @@ class Driver:
         _lib.check(L.pa_append_step(_p(self.key), _p(self.value), _p(self.k_pool), _p(self.v_pool), _p(r["slots"]),
                                     _p(r["rows"]), _p(r["pos"]), len(st.slots), _p(self.table), self.maxB,
                                     _p(self.ctx), _p(r["ctx"]), self.rows, Hkv, D, self.bs, NB, code, s))
-        r["done"].record(self.stream)
+        r["done"].record(self.stream)  # also after the swap-out: the stream waited for it
         r["used"] = True
+        self._after_append = torch.cuda.Event()
+        self._after_append.record(self.stream)
         self._i += 1
         # with every row empty the kernel still runs and writes zero rows
         max_ctx = max(int(st.context_lens.max()), 1)
