@@ -12,7 +12,10 @@ before timing starts.
 
 Prints one JSON line: whole-step KV throughput (GB/s), the roofline of the
 dominant kernel (decode partitions, timed with HIP events on the launch
-stream), and the CPU oracle timed on a bounded sample of the same workload.
+stream), the HBM read ceilings of a plain stream and of a random gather of
+decode tiles on the same GPU, and the CPU oracle timed on a bounded sample of
+the same workload.  The serving workloads (serving_bf16, serving_prefix_bf16)
+instead time whole scheduler + kernel steps (steps/s).
 """
 
 import argparse
