@@ -457,9 +457,14 @@ int32_t pa_bm_host_refcount(const pa_bm_t* bm, int64_t block);  /* -1: out of ra
  * (pa_swap_blocks device -> host), swap in (host -> device), copy-on-write
  * (pa_copy_blocks), table patches (pa_patch_tables), then pa_append_step with
  * slots / token_rows / token_positions / context_lens, then decode over the
- * max_rows rows (an empty row has length 0 and gives a zero row).
+ * max_rows rows (an empty row has length 0 and gives a zero row).  The swap
+ * out may instead run on another stream as soon as the previous step's
+ * pa_append_step is done, provided the rest of the step waits for it.
  * The arrays in pa_sched_out_t belong to the scheduler and stay valid until
  * its next step or destruction.
+ * pa_sched_step returns PA_ENOENT, changing nothing, when a request it runs
+ * or holds swapped out is no longer in the block manager; after any other
+ * error status the scheduler's state is unspecified (destroy it).
  * ---------------------------------------------------------------------- */
 typedef struct pa_sched pa_sched_t;
 

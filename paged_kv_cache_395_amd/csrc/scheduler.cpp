@@ -128,6 +128,13 @@ pa_status_t pa_sched_submit_tokens(pa_sched_t* s, int64_t seq, const int32_t* pr
 pa_status_t pa_sched_step(pa_sched_t* s, pa_sched_out_t* out) {
   if (!s || !out) return fail(PA_EINVAL, "null argument");
   pa_bm* bm = s->bm;
+  // the requests it runs or has swapped out must still be in the block
+  // manager (checked before anything changes)
+  for (const std::vector<Req>* v : {&s->running, &s->swapped})
+    for (const Req& r : *v)
+      if (!bm->seqs.count(r.seq))
+        return fail(PA_ENOENT, "request %lld was removed from the block manager behind the scheduler",
+                    (long long)r.seq);
   s->slots.clear();
   s->rows.clear();
   s->positions.clear();

@@ -211,6 +211,19 @@ def test_scheduler_and_host_pool_reject_bad_arguments():
     L.pa_bm_destroy(bm)
 
 
+def test_scheduler_refuses_a_request_removed_behind_its_back():
+    bm = L.pa_bm_create(8, 16, None)
+    s = L.pa_sched_create(bm, 2, 4, 64)
+    out = _lib.SchedOut()
+    assert L.pa_sched_submit(s, 7, 20, 40) == _lib.PA_OK
+    assert L.pa_sched_step(s, ctypes.byref(out)) == _lib.PA_OK and out.num_running == 1
+    assert L.pa_bm_free_seq(bm, 7) == _lib.PA_OK      # misuse: the scheduler owns request 7
+    assert L.pa_sched_step(s, ctypes.byref(out)) == _lib.PA_ENOENT
+    assert b"removed from the block manager" in L.pa_last_error()
+    L.pa_sched_destroy(s)
+    L.pa_bm_destroy(bm)
+
+
 def test_prefill_rejects_bad_arguments():
     def call(**kw):
         a = dict(dtype=_lib.PA_BF16, C=16, max_ctx=64, maxb=4, Hq=8, Hkv=2, out_dtype=_lib.PA_F32)
