@@ -60,10 +60,18 @@ def _pool_dims(k_cache: torch.Tensor, head_dim: int = None):
     raise ValueError("pools are [num_blocks, num_kv_heads, block_size * head_dim]")
 
 
+def _pools(k_cache: torch.Tensor, v_cache: torch.Tensor, head_dim: int = None):
+    """Dimensions of a K / V pool pair; the two must have one shape and dtype
+    (the kernels address both with the K pool's geometry)."""
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache must have the same shape and dtype")
+    return _pool_dims(k_cache, head_dim)
+
+
 def reshape_and_cache(key, value, k_cache, v_cache, slot_mapping, stream=None) -> None:
     """Write key/value [T, Hkv, D] into their slots (int64 [T]) of the pools."""
     _dev(key, value, k_cache, v_cache, slot_mapping)
-    NB, Hkv, D, bs = _pool_dims(k_cache, key.shape[-1])
+    NB, Hkv, D, bs = _pools(k_cache, v_cache, key.shape[-1])
     if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (Hkv, D):
         raise ValueError("key / value must be [T, num_kv_heads, head_dim]")
     if slot_mapping.dtype != torch.int64 or slot_mapping.shape != (key.shape[0],):
@@ -87,7 +95,7 @@ def _append_args(key, value, k_cache, v_cache, slot_mapping, token_rows, token_p
                  context_lens, new_context_lens, stream):
     _dev(key, value, k_cache, v_cache, block_tables, context_lens)
     _dev_or_pinned(slot_mapping, token_rows, token_positions, new_context_lens)
-    NB, Hkv, D, bs = _pool_dims(k_cache, key.shape[-1])
+    NB, Hkv, D, bs = _pools(k_cache, v_cache, key.shape[-1])
     if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (Hkv, D):
         raise ValueError("key / value must be [T, num_kv_heads, head_dim]")
     T = key.shape[0]
@@ -126,7 +134,7 @@ def append_step(key, value, k_cache, v_cache, slot_mapping, token_rows, token_po
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
     """Copy physical blocks src -> dst for each row (src, dst) of int64 ``pairs`` [n, 2]."""
     _dev(k_cache, v_cache, pairs)
-    NB, Hkv, D, bs = _pool_dims(k_cache)
+    NB, Hkv, D, bs = _pools(k_cache, v_cache)
     if pairs.dtype != torch.int64 or pairs.dim() != 2 or pairs.shape[1] != 2:
         raise ValueError("pairs must be int64 [n, 2]")
     _lib.check(_lib.load().pa_copy_blocks(_p(k_cache), _p(v_cache), _p(pairs), pairs.shape[0], Hkv, D, bs,
@@ -179,7 +187,7 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, h
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size,
                  workspace):
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
-    NB, Hkv, D, bs = _pool_dims(k_cache, q.shape[-1])
+    NB, Hkv, D, bs = _pools(k_cache, v_cache, q.shape[-1])
     if q.dim() != 3 or q.shape[2] != D:
         raise ValueError("q must be [num_seqs, num_q_heads, head_dim]")
     S, Hq = q.shape[0], q.shape[1]
@@ -233,7 +241,7 @@ def decode_multi(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
     """Causal attention of the last q_len positions of each context, q [S, q_len, Hq, D], at decode's bandwidth
     (q_len x group <= 16)."""
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
-    NB, Hkv, D, bs = _pool_dims(k_cache, q.shape[-1])
+    NB, Hkv, D, bs = _pools(k_cache, v_cache, q.shape[-1])
     if q.dim() != 4 or q.shape[3] != D:
         raise ValueError("q must be [num_seqs, q_len, num_q_heads, head_dim]")
     S, C, Hq = q.shape[0], q.shape[1], q.shape[2]
@@ -260,7 +268,7 @@ def decode_multi(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
 def prefill_chunk(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, stream=None) -> None:
     """Causal attention of q [S, C, Hq, D] (the last C positions of each context) over the paged cache."""
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
-    NB, Hkv, D, bs = _pool_dims(k_cache, q.shape[-1])
+    NB, Hkv, D, bs = _pools(k_cache, v_cache, q.shape[-1])
     if q.dim() != 4 or q.shape[3] != D:
         raise ValueError("q must be [num_seqs, chunk_len, num_q_heads, head_dim]")
     S, C, Hq = q.shape[0], q.shape[1], q.shape[2]
@@ -317,7 +325,7 @@ class StepPlan:
                  key=None, value=None, slot_mapping=None, partition_size=0, stream=None, append=None):
         self._lib = _lib.load()
         self._stream = _stream(stream)
-        NB, Hkv, D, bs = _pool_dims(k_cache, q.shape[-1])
+        NB, Hkv, D, bs = _pools(k_cache, v_cache, q.shape[-1])
         self._partition = int(partition_size)
         self._multi = q.dim() == 4
         if self._multi:

@@ -104,3 +104,24 @@ def test_copy_on_write_end_to_end():
     got = out.cpu().numpy().astype(np.float64)
     assert np.abs(got - want).max() <= 2e-3
     assert np.linalg.norm(got - want) / np.linalg.norm(want) <= 1e-3
+
+
+def test_pools_of_different_geometry_are_refused_before_launch():
+    """The kernels address V with the K pool's geometry: the binding refuses a
+    pair that differs in shape or dtype."""
+    k = torch.zeros((8, 2, 16 * 128), dtype=torch.bfloat16, device="cuda")
+    v_small = torch.zeros((4, 2, 16 * 128), dtype=torch.bfloat16, device="cuda")
+    v_f16 = torch.zeros_like(k, dtype=torch.float16)
+    key = torch.zeros((1, 2, 128), dtype=torch.bfloat16, device="cuda")
+    slots = torch.zeros(1, dtype=torch.int64, device="cuda")
+    q = torch.zeros((1, 4, 128), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((1, 4, 128), dtype=torch.float32, device="cuda")
+    table = torch.zeros((1, 2), dtype=torch.int32, device="cuda")
+    ctx = torch.ones(1, dtype=torch.int32, device="cuda")
+    for v in (v_small, v_f16):
+        with pytest.raises(ValueError):
+            ops.reshape_and_cache(key, key, k, v, slots)
+        with pytest.raises(ValueError):
+            ops.decode(out, q, k, v, table, ctx, 0.1, 1)
+        with pytest.raises(ValueError):
+            ops.prefill_chunk(out.view(1, 1, 4, 128), q.view(1, 1, 4, 128), k, v, table, ctx, 0.1, 1)
