@@ -87,6 +87,17 @@ def _host_threads() -> int:
     return min(n, len(os.sched_getaffinity(0))) if n else len(os.sched_getaffinity(0))
 
 
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s: float = 15.0):
     """The oracle, as it stands, on the first sequences of the same step until
     ~budget_s of work, with BLAS on every host core the process may use."""
@@ -119,7 +130,7 @@ def cpu_baseline(w, budget_s: float = 15.0):
         dt = time.perf_counter() - t0
     sub = ctx[done]
     gbs = decode_bytes(sub, w) / dt / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle", "cpu": _cpu_model(),
             "sample": f"one decode step (cache write of {w.num_seqs} tokens + fp64 attention) for the first "
                       f"{len(done)} of {w.num_seqs} sequences, all {w.num_q_heads} q heads; "
                       f"{dt:.1f} s; seqs/s {len(done) / dt:.2f}; numpy, BLAS on {cores} cores"}
@@ -185,7 +196,7 @@ def serving_cpu_baseline(c, trace, steps: int, budget_s: float = 15.0, prefix: b
                 break
         t_att = time.perf_counter() - t1
     per_step = t_sched + t_att * len(rows) / len(done)
-    return {"value": round(1.0 / per_step, 4), "unit": "steps/s", "cores": cores, "kind": "oracle",
+    return {"value": round(1.0 / per_step, 4), "unit": "steps/s", "cores": cores, "kind": "oracle", "cpu": _cpu_model(),
             "sample": f"oracle scheduler over the first {steps} steps of the same trace ({t_sched * 1e3:.2f} ms "
                       f"per step) + fp64 oracle decode of {len(done)} of the {len(rows)} running rows at the "
                       f"last step ({t_att:.1f} s), scaled to all rows; numpy, BLAS on {cores} cores"}
