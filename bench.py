@@ -49,6 +49,19 @@ def decode_bytes(ctx: np.ndarray, w) -> float:
     return kv + qo + tab
 
 
+def physical_kv_bytes(table: np.ndarray, ctx: np.ndarray, w) -> float:
+    """K/V bytes of the distinct physical blocks a batch reads: each block's
+    valid tokens once, however many sequences share it."""
+    bs = w.block_size
+    valid = {}
+    for s in range(len(ctx)):
+        n = int(ctx[s])
+        for lb in range((n + bs - 1) // bs):
+            b = int(table[s, lb])
+            valid[b] = max(valid.get(b, 0), min(bs, n - lb * bs))
+    return float(sum(valid.values())) * w.num_kv_heads * w.head_dim * 2 * ESIZE[w.dtype]
+
+
 def prefill_flops(ctx: np.ndarray, chunk: int, w) -> float:
     """4 * D flops (QK and PV) per (query row, q head, attended key)."""
     total = 0.0
@@ -755,6 +768,7 @@ def main():
                                    "algorithmic_tflop": round(fl / 1e12, 4)}
 
     traffic = load_traffic(args.workload, bytes_per_launch)
+    phys_bytes = physical_kv_bytes(t_host, c_host, w)
     value = total_bytes / elapsed / 1e9
     rec = {
         "metric": METRIC,
@@ -770,10 +784,15 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.description}", "num_seqs": S, "num_q_heads": Hq,
-                   "num_kv_heads": Hkv, "head_dim": D, "block_size": 16,
+                   "num_kv_heads": Hkv, "head_dim": D, "block_size": w.block_size,
                    "mean_context": round(float(ctx_now.mean()), 1),
                    "partition": ops.decode_partition_size(S, Hkv, int(ctx_now.max()), args.partition)},
         "hbm_frac_whole_step": round(value / HBM_PEAK_GBS, 4),
+        # shared prefix blocks are read by many rows but come from HBM about once (the rest hit in cache)
+        "kv_physical": {"bytes_per_launch": round(phys_bytes, 1),
+                        "gbs": round(phys_bytes / (float(k2_ms.mean()) * 1e-3) / 1e9, 2),
+                        "note": "K/V of the distinct blocks read at the last timed step, each block's valid "
+                                "tokens once, over the mean decode-kernel time"},
         "seqs_per_s": round(S * args.steps / elapsed, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
