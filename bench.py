@@ -448,8 +448,10 @@ def summarize(args) -> None:
     alg = rec["roofline"]["algorithmic_bytes_per_launch"]
     prof = os.path.join(ROOT, "profiles")
     base = "python -u bench.py --workload %s" % wl
+    serving = "kernels_ms" not in rec  # the serving rows run their own step count and warm-up
+    run_args = "" if serving else " --steps 20 --warmup 3 --cold-iters 3"
     trace_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {args.trace_dir} -o trace -- "
-                 f"{base} --steps 20 --warmup 3 --cold-iters 3 --no-cpu-baseline")
+                 f"{base}{run_args} --no-cpu-baseline")
     pmc_cmd = (f"timeout -s KILL 120 rocprofv3 --pmc {{counter}} --output-format csv -d {{out_dir}} "
                f"-o {{tag}} -- {base} --steps 3 --warmup 1 --cold-iters 0 --no-cpu-baseline --copy-probe-mib 1024")
     lines = [f"# Kernel trace: {wl}", "", f"{rec['config']['workload']}", "",
@@ -458,10 +460,17 @@ def summarize(args) -> None:
     for r in _csv_rows(args.trace_dir, "kernel_stats.csv"):
         lines.append(f"| `{r['Name'][:90]}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                      f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
-    lines += ["", "Same workload, bench.py without the profiler (HIP events on the launch stream):", "",
-              f"- decode kernel: {rec['kernels_ms']['decode_partitions'] * 1e3:.1f} us per launch, "
-              f"{rec['roofline']['achieved']:.0f} GB/s = {rec['roofline']['frac']:.3f} of 8 TB/s",
-              f"- kernels_ms: {rec['kernels_ms']}", f"- whole step: {rec['value']} GB/s, {rec['ms_per_step']} ms", ""]
+    lines += ["", "Same workload, bench.py without the profiler (HIP events on the launch stream):", ""]
+    if serving:
+        lines += [f"- decode kernel over the timed steps: {rec['roofline']['achieved']:.0f} GB/s = "
+                  f"{rec['roofline']['frac']:.3f} of 8 TB/s ({rec['roofline'].get('bytes_note', 'logical bytes')})",
+                  f"- {rec['value']} steps/s, {rec['ms_per_step']} ms per step, {rec['mean_running_rows']} rows "
+                  f"running on average; swap: {rec['swap']}", ""]
+    else:
+        lines += [f"- decode kernel: {rec['kernels_ms']['decode_partitions'] * 1e3:.1f} us per launch, "
+                  f"{rec['roofline']['achieved']:.0f} GB/s = {rec['roofline']['frac']:.3f} of 8 TB/s",
+                  f"- kernels_ms: {rec['kernels_ms']}", f"- whole step: {rec['value']} GB/s, {rec['ms_per_step']} ms",
+                  ""]
     with open(os.path.join(prof, f"decode_{wl}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines))
     if args.fetch_dir is None:
