@@ -1,4 +1,4 @@
-"""Not yet collected (file name): run it by path once the GPU has confirmed it.
+"""Stream semantics of the device entry points.
 
 Every device entry point runs on the stream it is given (the caller's
 current torch stream by default) and waits for nothing else.
