@@ -38,6 +38,60 @@ ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
 KERNEL_SOURCES = ["paged_kv_cache_395_amd/csrc/decode_kernels.hip", "paged_kv_cache_395_amd/csrc/device_common.h"]
 
 
+class TimingEvent:
+    """A HIP event for timing only, recorded without the system-scope fence.
+
+    torch's events release at system scope when they are recorded: the L2 is
+    written back and invalidated, which costs the next kernel its cached
+    inputs and adds several microseconds per record to a ~0.2 ms step.
+    These events are read only after a device synchronisation, so they need
+    no fence (hipEventDisableSystemFence).  They are made through the HIP
+    runtime torch loaded (the library shares that runtime).  Events the host
+    waits on before it rewrites pinned memory stay torch's.
+    """
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        import torch
+
+        if TimingEvent._hip is None:
+            lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._hip = lib
+        self._ct = ctypes
+        self._h = ctypes.c_void_p()
+        self._check(TimingEvent._hip.hipEventCreateWithFlags(ctypes.byref(self._h), self.DISABLE_SYSTEM_FENCE),
+                    "hipEventCreateWithFlags")
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def record(self, stream=None):
+        import torch
+
+        s = stream if stream is not None else torch.cuda.current_stream()
+        self._check(TimingEvent._hip.hipEventRecord(self._h, self._ct.c_void_p(s.cuda_stream)), "hipEventRecord")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to ``end`` (both recorded, the device synchronised)."""
+        ms = self._ct.c_float()
+        self._check(TimingEvent._hip.hipEventElapsedTime(self._ct.byref(ms), self._h, end._h), "hipEventElapsedTime")
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._hip is not None and self._h:
+            TimingEvent._hip.hipEventDestroy(self._h)
+
+
 def decode_bytes(ctx: np.ndarray, w) -> float:
     """Algorithmic bytes of one decode: K+V rows of every context token, q, out, table entries read."""
     e = ESIZE[w.dtype]
@@ -262,7 +316,7 @@ def bench_serving(args) -> None:
             else:
                 drv.submit(i, p, t)
         st = drv.schedule()
-        e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if timed else None
+        e = (TimingEvent(), TimingEvent()) if timed else None
         drv.launch(st, decode_events=e)
         if timed:
             ev.append(e)
@@ -349,7 +403,7 @@ def bench_serving(args) -> None:
     # the swap copy alone: one launch of 2048 block pairs each way
     n = min(2048, c["host_blocks"], c["num_blocks"])
     pairs_out = torch.from_numpy(np.stack([np.arange(n), np.arange(n)], axis=1).astype(np.int64)).cuda()
-    a, b, d = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    a, b, d = (TimingEvent() for _ in range(3))
     ops.swap_blocks(drv.k_host, drv.v_host, drv.k_pool, drv.v_pool, pairs_out)
     a.record()
     ops.swap_blocks(drv.k_host, drv.v_host, drv.k_pool, drv.v_pool, pairs_out)
@@ -644,7 +698,7 @@ def main():
 
     # decode is bracketed by two events in every timed step (its duration feeds
     # the roofline); the small kernels are timed in a separate pass below
-    ev_dec = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev_dec = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
 
     def step(i, timed_idx=None):
         plan, ctx_np = prepare_step(i, grows)
@@ -683,7 +737,7 @@ def main():
     plan, ctx_side = prepare_step(args.warmup + args.steps - 1, False)
     mx_side = int(ctx_side.max())
     for _ in range(10):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e = [TimingEvent() for _ in range(4)]
         e[0].record(stream)
         if grows:
             plan.cache_write()
@@ -709,7 +763,7 @@ def main():
     mx = int(ctx_now.max())
     for _ in range(args.cold_iters):
         scratch.zero_()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record(stream)
         plan.decode_partitions(mx)
         b.record(stream)
@@ -725,7 +779,7 @@ def main():
     ops.probe_read_bandwidth(big, sink)
     probe = []
     for _ in range(5):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record(stream)
         ops.probe_read_bandwidth(big, sink)
         b.record(stream)
@@ -740,7 +794,7 @@ def main():
     ops.probe_gather_bandwidth(big, order, tile_bytes, sink)
     probe = []
     for _ in range(5):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record(stream)
         ops.probe_gather_bandwidth(big, order, tile_bytes, sink)
         b.record(stream)
@@ -764,7 +818,7 @@ def main():
         ops.prefill_chunk(oc, qc, k_pool, v_pool, d_table, d_ctx, w.scale, int(ctx_now.max()))
         pe = []
         for _ in range(3):
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a, b = TimingEvent(), TimingEvent()
             a.record(stream)
             ops.prefill_chunk(oc, qc, k_pool, v_pool, d_table, d_ctx, w.scale, int(ctx_now.max()))
             b.record(stream)
