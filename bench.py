@@ -578,6 +578,9 @@ def main():
                              "specdec_bf16", "serving_bf16", "serving_prefix_bf16", "mha7b_f16_bs32",
                              "mha7b_f16_bs64", "gqa8b_bf16_bs32"])
     ap.add_argument("--partition", type=int, default=0, help="tokens per context partition (0 = the library's choice)")
+    ap.add_argument("--append-meta", choices=["pinned", "args"], default="pinned",
+                    help="where the step's slots, positions and lengths reach the cache write: pinned host memory "
+                         "read by the kernel, or the kernel arguments (pa_append_step_host)")
     ap.add_argument("--cold-iters", type=int, default=20, help="decode launches timed after a 1 GiB cache flush")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -657,16 +660,21 @@ def main():
     ws = torch.empty(max(1, ws_need), dtype=torch.uint8, device=dev)
     seqs = np.ascontiguousarray(w.step_seqs, dtype=np.int64)
     stream = torch.cuda.current_stream()
-    # a step ships only its tokens' slots and positions and the new lengths; the
-    # write kernel reads them straight from pinned host memory (no copy)
-    rows = torch.from_numpy(np.repeat(np.arange(S, dtype=np.int32), w.append)).to(dev)
+    # a step ships only its tokens' slots and positions and the new lengths:
+    # either the write kernel reads them straight from pinned host memory (a
+    # ring of buffers the host refills once the write that read them has run),
+    # or they travel in the kernel arguments, copied at launch
+    host_args = args.append_meta == "args"
+    rows_np = np.repeat(np.arange(S, dtype=np.int32), w.append)
+    rows = torch.from_numpy(rows_np) if host_args else torch.from_numpy(rows_np).to(dev)
     offs = np.tile(np.arange(w.append, dtype=np.int64), S)
-    ring = [{"slots": torch.empty(n_tok, dtype=torch.int64, pin_memory=True),
-             "pos": torch.empty(n_tok, dtype=torch.int32, pin_memory=True),
-             "nctx": torch.empty(S, dtype=torch.int32, pin_memory=True)} for _ in range(4)]
+    ring = [{"slots": torch.empty(n_tok, dtype=torch.int64, pin_memory=not host_args),
+             "pos": torch.empty(n_tok, dtype=torch.int32, pin_memory=not host_args),
+             "nctx": torch.empty(S, dtype=torch.int32, pin_memory=not host_args)}
+            for _ in range(1 if host_args else 4)]
     plans = [ops.StepPlan(out, q, k_pool, v_pool, d_table, d_ctx, w.scale, ws, key=step_k, value=step_v,
                           slot_mapping=r["slots"], partition_size=args.partition,
-                          append=(rows, r["pos"], r["nctx"])) for r in ring]
+                          append=(rows, r["pos"], r["nctx"]), host_args=host_args) for r in ring]
     ring_done = [torch.cuda.Event() for _ in ring]
     ring_used = [False] * len(ring)
 
@@ -686,9 +694,10 @@ def main():
 
     def issue_write(i, plan):
         plan.cache_write()
-        r = i % len(ring)
-        ring_done[r].record(stream)
-        ring_used[r] = True
+        if not host_args:  # copied into the launch otherwise: the host may refill at once
+            r = i % len(ring)
+            ring_done[r].record(stream)
+            ring_used[r] = True
 
     if not grows:
         # the chunk workload: write the chunk once (untimed); every step then decodes in place
@@ -846,7 +855,8 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {w.description}", "num_seqs": S, "num_q_heads": Hq,
+        "config": {"workload": f"{w.name}: {w.description}", "append_meta": args.append_meta, "num_seqs": S,
+                   "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": w.block_size,
                    "mean_context": round(float(ctx_now.mean()), 1),
                    "partition": ops.decode_partition_size(S, Hkv, int(ctx_now.max()), args.partition)},

@@ -141,6 +141,24 @@ pa_status_t pa_append_step(const void* key, const void* value, void* k_cache, vo
                            int64_t num_blocks, pa_dtype_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * pa_append_step with the step's metadata in host memory: slot_mapping,
+ * token_rows, token_positions and new_context_lens are ordinary (pageable
+ * or pinned) host arrays whose values are copied into the launch's kernel
+ * arguments before the call returns, so the caller may overwrite them at
+ * once and the kernel reads nothing across the host link.  Every other
+ * argument, the result and the error behaviour are those of pa_append_step.
+ * One launch carries up to 128 tokens and 256 lengths (about 3 KB of
+ * arguments); a larger step is split into several launches on the stream.
+ * ---------------------------------------------------------------------- */
+pa_status_t pa_append_step_host(const void* key, const void* value, void* k_cache, void* v_cache,
+                                const int64_t* slot_mapping, const int32_t* token_rows,
+                                const int32_t* token_positions, int32_t num_tokens,
+                                int32_t* block_tables, int32_t max_blocks_per_seq,
+                                int32_t* context_lens, const int32_t* new_context_lens, int32_t num_seqs,
+                                int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int64_t num_blocks, pa_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Copy whole physical blocks (K and V, all kv heads) src -> dst: the copy a
  * shared block gets before a sequence writes into it ([OS] "Copy-on-Write:
  * Sharing KV Cache").

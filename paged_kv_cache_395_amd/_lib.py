@@ -45,6 +45,8 @@ SIGNATURES = {
     "pa_reshape_and_cache": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, ctypes.c_int, _vp]),
     "pa_append_step": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32,
                                       _i32, _i64, ctypes.c_int, _vp]),
+    "pa_append_step_host": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32,
+                                           _i32, _i32, _i64, ctypes.c_int, _vp]),
     "pa_copy_blocks": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i64, ctypes.c_int, _vp]),
     "pa_swap_blocks": (ctypes.c_int, [_vp, _vp, _i64, _vp, _vp, _i64, _vp, _i32, _i32, _i32, _i32, ctypes.c_int,
                                       _vp]),

@@ -6,6 +6,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
+#include <cstring>
 #include <string>
 
 #include "pa_internal.h"
@@ -204,12 +206,16 @@ pa_status_t pa_reshape_and_cache(const void* key, const void* value, void* k_cac
                     "reshape_and_cache launch");
 }
 
-pa_status_t pa_append_step(const void* key, const void* value, void* k_cache, void* v_cache,
+namespace {
+
+// Checks the arguments of a step's appends and fills the launch arguments
+// (shared by the device-metadata and kernel-argument variants).
+pa_status_t prepare_append(const void* key, const void* value, void* k_cache, void* v_cache,
                            const int64_t* slot_mapping, const int32_t* token_rows, const int32_t* token_positions,
                            int32_t num_tokens, int32_t* block_tables, int32_t max_blocks_per_seq,
                            int32_t* context_lens, const int32_t* new_context_lens, int32_t num_seqs,
                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
-                           pa_dtype_t dtype, void* stream) {
+                           pa_dtype_t dtype, void* stream, AppendStepArgs* a) {
   pa_status_t st = check_pool(num_kv_heads, head_dim, block_size, num_blocks, dtype);
   if (st != PA_OK) return st;
   if (num_tokens < 0 || num_seqs < 0) return fail(PA_EINVAL, "num_tokens and num_seqs must be >= 0");
@@ -219,27 +225,78 @@ pa_status_t pa_append_step(const void* key, const void* value, void* k_cache, vo
     return fail(PA_EINVAL, "null pointer argument");
   if (num_seqs > 0 && (!context_lens || !new_context_lens)) return fail(PA_EINVAL, "null pointer argument");
   if (int64_t(num_tokens) + (int64_t(num_seqs) + 255) / 256 > INT32_MAX) return fail(PA_EUNSUPPORTED, "grid too large");
+  a->key = key;
+  a->value = value;
+  a->k_cache = k_cache;
+  a->v_cache = v_cache;
+  a->slots = slot_mapping;
+  a->rows = token_rows;
+  a->positions = token_positions;
+  a->num_tokens = num_tokens;
+  a->tables = block_tables;
+  a->max_blocks = max_blocks_per_seq;
+  a->ctx = context_lens;
+  a->new_ctx = new_context_lens;
+  a->num_rows = num_seqs;
+  a->num_kv_heads = num_kv_heads;
+  a->head_dim = head_dim;
+  a->num_blocks = num_blocks;
+  a->tile_shift = tile_shift_of(block_size);
+  a->elem_bytes = elem_bytes(dtype);
+  a->stream = static_cast<hipStream_t>(stream);
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status_t pa_append_step(const void* key, const void* value, void* k_cache, void* v_cache,
+                           const int64_t* slot_mapping, const int32_t* token_rows, const int32_t* token_positions,
+                           int32_t num_tokens, int32_t* block_tables, int32_t max_blocks_per_seq,
+                           int32_t* context_lens, const int32_t* new_context_lens, int32_t num_seqs,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           pa_dtype_t dtype, void* stream) {
   AppendStepArgs a{};
-  a.key = key;
-  a.value = value;
-  a.k_cache = k_cache;
-  a.v_cache = v_cache;
-  a.slots = slot_mapping;
-  a.rows = token_rows;
-  a.positions = token_positions;
-  a.num_tokens = num_tokens;
-  a.tables = block_tables;
-  a.max_blocks = max_blocks_per_seq;
-  a.ctx = context_lens;
-  a.new_ctx = new_context_lens;
-  a.num_rows = num_seqs;
-  a.num_kv_heads = num_kv_heads;
-  a.head_dim = head_dim;
-  a.num_blocks = num_blocks;
-  a.tile_shift = tile_shift_of(block_size);
-  a.elem_bytes = elem_bytes(dtype);
-  a.stream = static_cast<hipStream_t>(stream);
+  const pa_status_t st = prepare_append(key, value, k_cache, v_cache, slot_mapping, token_rows, token_positions,
+                                        num_tokens, block_tables, max_blocks_per_seq, context_lens, new_context_lens,
+                                        num_seqs, num_kv_heads, head_dim, block_size, num_blocks, dtype, stream, &a);
+  if (st != PA_OK) return st;
   return hip_status(launch_append_step(a), "append_step launch");
+}
+
+pa_status_t pa_append_step_host(const void* key, const void* value, void* k_cache, void* v_cache,
+                                const int64_t* slot_mapping, const int32_t* token_rows,
+                                const int32_t* token_positions, int32_t num_tokens, int32_t* block_tables,
+                                int32_t max_blocks_per_seq, int32_t* context_lens,
+                                const int32_t* new_context_lens, int32_t num_seqs, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t block_size, int64_t num_blocks, pa_dtype_t dtype,
+                                void* stream) {
+  AppendStepArgs a{};
+  const pa_status_t st = prepare_append(key, value, k_cache, v_cache, slot_mapping, token_rows, token_positions,
+                                        num_tokens, block_tables, max_blocks_per_seq, context_lens, new_context_lens,
+                                        num_seqs, num_kv_heads, head_dim, block_size, num_blocks, dtype, stream, &a);
+  if (st != PA_OK) return st;
+  // launch i carries tokens [i * kArgTokens, ...) and lengths [i * kArgRows, ...)
+  const int64_t launches = std::max(ceil_div(num_tokens, kArgTokens), ceil_div(num_seqs, kArgRows));
+  const int64_t token_bytes = int64_t(num_kv_heads) * head_dim * a.elem_bytes;
+  for (int64_t i = 0; i < launches; ++i) {
+    AppendArgsMeta m{};
+    const int64_t t0 = i * kArgTokens, r0 = i * kArgRows;
+    m.num_tokens = int32_t(std::min<int64_t>(std::max<int64_t>(num_tokens - t0, 0), kArgTokens));
+    m.row0 = int32_t(r0);
+    m.num_rows = int32_t(std::min<int64_t>(std::max<int64_t>(num_seqs - r0, 0), kArgRows));
+    if (m.num_tokens > 0) {
+      std::memcpy(m.slots, slot_mapping + t0, sizeof(int64_t) * m.num_tokens);
+      std::memcpy(m.rows, token_rows + t0, sizeof(int32_t) * m.num_tokens);
+      std::memcpy(m.positions, token_positions + t0, sizeof(int32_t) * m.num_tokens);
+    }
+    if (m.num_rows > 0) std::memcpy(m.new_ctx, new_context_lens + r0, sizeof(int32_t) * m.num_rows);
+    AppendStepArgs ai = a;
+    ai.key = static_cast<const char*>(key) + (m.num_tokens > 0 ? t0 * token_bytes : 0);
+    ai.value = static_cast<const char*>(value) + (m.num_tokens > 0 ? t0 * token_bytes : 0);
+    const pa_status_t sl = hip_status(launch_append_step_args(ai, m), "append_step_host launch");
+    if (sl != PA_OK) return sl;
+  }
+  return PA_OK;
 }
 
 pa_status_t pa_copy_blocks(void* k_cache, void* v_cache, const int64_t* pairs, int32_t num_pairs,

@@ -88,6 +88,22 @@ struct AppendStepArgs {
 
 hipError_t launch_append_step(const AppendStepArgs& a);
 
+// One launch's share of a step whose metadata travels in the kernel
+// arguments (pa_append_step_host): at most kArgTokens tokens and kArgRows
+// lengths, about 3 KB of arguments.
+constexpr int kArgTokens = 128;
+constexpr int kArgRows = 256;
+struct AppendArgsMeta {
+  int64_t slots[kArgTokens];
+  int32_t rows[kArgTokens];
+  int32_t positions[kArgTokens];
+  int32_t new_ctx[kArgRows];
+  int32_t num_tokens;  // tokens of this launch (key / value point at the first)
+  int32_t row0;        // first row whose length this launch sets
+  int32_t num_rows;    // lengths this launch sets
+};
+hipError_t launch_append_step_args(const AppendStepArgs& a, const AppendArgsMeta& meta);
+
 hipError_t launch_copy_blocks(void* dst_k, void* dst_v, const void* src_k, const void* src_v, const int64_t* pairs,
                               int32_t num_pairs, int64_t block_bytes, int64_t src_blocks, int64_t dst_blocks,
                               hipStream_t stream);

@@ -91,10 +91,18 @@ def _dev_or_pinned(*ts):
             raise ValueError("all tensors must be contiguous")
 
 
+def _host(*ts):
+    for t in ts:
+        if t.is_cuda:
+            raise ValueError("step metadata of append_step_host must live in host memory")
+        if not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+
+
 def _append_args(key, value, k_cache, v_cache, slot_mapping, token_rows, token_positions, block_tables,
-                 context_lens, new_context_lens, stream):
+                 context_lens, new_context_lens, stream, host_meta=False):
     _dev(key, value, k_cache, v_cache, block_tables, context_lens)
-    _dev_or_pinned(slot_mapping, token_rows, token_positions, new_context_lens)
+    (_host if host_meta else _dev_or_pinned)(slot_mapping, token_rows, token_positions, new_context_lens)
     NB, Hkv, D, bs = _pools(k_cache, v_cache, key.shape[-1])
     if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (Hkv, D):
         raise ValueError("key / value must be [T, num_kv_heads, head_dim]")
@@ -129,6 +137,19 @@ def append_step(key, value, k_cache, v_cache, slot_mapping, token_rows, token_po
     _lib.check(_lib.load().pa_append_step(*_append_args(key, value, k_cache, v_cache, slot_mapping, token_rows,
                                                         token_positions, block_tables, context_lens,
                                                         new_context_lens, stream)))
+
+
+def append_step_host(key, value, k_cache, v_cache, slot_mapping, token_rows, token_positions, block_tables,
+                     context_lens, new_context_lens, stream=None) -> None:
+    """append_step with the four step vectors in host memory (CPU tensors, pinned or not).
+
+    Their values are copied into the launch's kernel arguments before the call
+    returns (the caller may overwrite them at once), so the kernel reads
+    nothing from host memory.
+    """
+    _lib.check(_lib.load().pa_append_step_host(*_append_args(key, value, k_cache, v_cache, slot_mapping, token_rows,
+                                                             token_positions, block_tables, context_lens,
+                                                             new_context_lens, stream, host_meta=True)))
 
 
 def copy_blocks(k_cache, v_cache, pairs, stream=None) -> None:
@@ -318,11 +339,15 @@ class StepPlan:
     write is pa_append_step: ``block_tables`` and ``context_lens`` stay on the
     device and the write patches them from the step's slots, so a step ships
     only its tokens' slots / rows / positions and the new lengths (which may
-    sit in pinned host memory) instead of whole tables.
+    sit in pinned host memory) instead of whole tables.  With ``host_args``
+    those four are CPU tensors whose values each ``cache_write`` copies into
+    the kernel arguments (pa_append_step_host): the host may rewrite them as
+    soon as the call returns.
     """
 
     def __init__(self, out, q, k_cache, v_cache, block_tables, context_lens, scale, workspace,
-                 key=None, value=None, slot_mapping=None, partition_size=0, stream=None, append=None):
+                 key=None, value=None, slot_mapping=None, partition_size=0, stream=None, append=None,
+                 host_args=False):
         self._lib = _lib.load()
         self._stream = _stream(stream)
         NB, Hkv, D, bs = _pools(k_cache, v_cache, q.shape[-1])
@@ -356,7 +381,8 @@ class StepPlan:
         if key is not None and append is not None:
             rows, positions, new_ctx = append
             self._append = _append_args(key, value, k_cache, v_cache, slot_mapping, rows, positions, block_tables,
-                                        context_lens, new_ctx, stream)
+                                        context_lens, new_ctx, stream, host_meta=host_args)
+            self._append_fn = self._lib.pa_append_step_host if host_args else self._lib.pa_append_step
         elif key is not None:
             _dev(key, value, slot_mapping)
             if key.shape != value.shape or key.dim() != 3 or key.shape[1:] != (Hkv, D):
@@ -382,7 +408,7 @@ class StepPlan:
 
     def cache_write(self) -> None:
         if self._append is not None:
-            _lib.check(self._lib.pa_append_step(*self._append))
+            _lib.check(self._append_fn(*self._append))
         else:
             _lib.check(self._lib.pa_reshape_and_cache(*self._write))
 

@@ -162,9 +162,12 @@ def test_cache_write_and_copy_reject_bad_arguments():
     assert L.pa_copy_blocks(None, None, None, 0, 8, 128, 16, 10, _lib.PA_F16, NULL) == _lib.PA_OK
 
 
-def test_append_step_rejects_bad_arguments():
+@pytest.mark.parametrize("entry", ["pa_append_step", "pa_append_step_host"])
+def test_append_step_rejects_bad_arguments(entry):
+    fn = getattr(L, entry)
+
     def call(T=4, maxb=8, S=2, D=128, bs=16, key=1, ctx=1):
-        return L.pa_append_step(key, 1, 1, 1, 1, 1, 1, T, 1, maxb, ctx, 1, S, 8, D, bs, 10, _lib.PA_BF16, NULL)
+        return fn(key, 1, 1, 1, 1, 1, 1, T, 1, maxb, ctx, 1, S, 8, D, bs, 10, _lib.PA_BF16, NULL)
     assert call(D=100) == _lib.PA_EUNSUPPORTED
     assert call(bs=8) == _lib.PA_EUNSUPPORTED
     assert call(bs=48) == _lib.PA_EUNSUPPORTED
@@ -173,8 +176,8 @@ def test_append_step_rejects_bad_arguments():
     assert call(maxb=0) == _lib.PA_EINVAL
     assert call(key=None) == _lib.PA_EINVAL
     assert call(ctx=None) == _lib.PA_EINVAL
-    assert L.pa_append_step(None, None, None, None, None, None, None, 0, None, 8, None, None, 0, 8, 128, 16, 10,
-                            _lib.PA_BF16, NULL) == _lib.PA_OK
+    assert fn(None, None, None, None, None, None, None, 0, None, 8, None, None, 0, 8, 128, 16, 10,
+              _lib.PA_BF16, NULL) == _lib.PA_OK
 
 
 def test_swap_and_patch_reject_bad_arguments():

@@ -1,9 +1,13 @@
-"""Step appends with device-resident block tables (pa_append_step).
+"""Step appends with device-resident block tables (pa_append_step, and
+pa_append_step_host with the step's metadata in the kernel arguments).
 
 After several steps, the device tables and context lengths equal what the
 host block manager reports, bit for bit, and the pools equal the oracle's
 cache writes (and block copies, where a step copies on write); a decode on
-the device-resident tables then matches the oracle.
+the device-resident tables then matches the oracle.  The host-metadata
+variant is also checked across several launches per step (more than 128
+tokens or 256 rows) and with its host arrays overwritten as soon as the
+call returns.
 """
 import numpy as np
 import pytest
@@ -26,7 +30,26 @@ def step_vectors(bm, seqs_in_batch, append):
     return rows, positions.astype(np.int32), (before + append).astype(np.int32)
 
 
-def run_steps(w, steps, pinned, seed):
+def append_with(mode, key, val, dk, dv, slots, rows, positions, d_table, d_ctx, new_ctx):
+    """One step's append with the metadata in device memory, pinned host
+    memory, or ordinary host memory copied into the kernel arguments."""
+    if mode == "host":
+        meta = [np.array(a) for a in (slots, rows, positions, new_ctx)]
+        ops.append_step_host(key, val, dk, dv, *[torch.from_numpy(a) for a in meta[:3]], d_table, d_ctx,
+                             torch.from_numpy(meta[3]))
+        # the values were copied at launch: overwriting them now (with values
+        # that would skip every token) must change nothing
+        meta[0].fill(-1)
+        meta[1].fill(-1)
+        meta[2].fill(-1)
+        meta[3].fill(0)
+        return
+    meta = [torch.from_numpy(a) for a in (slots, rows, positions, new_ctx)]
+    meta = [m.pin_memory() if mode == "pinned" else m.cuda() for m in meta]
+    ops.append_step(key, val, dk, dv, meta[0], meta[1], meta[2], d_table, d_ctx, meta[3])
+
+
+def run_steps(w, steps, mode, seed):
     rng = np.random.default_rng(seed)
     bm = BlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
     ref = RefBlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
@@ -51,10 +74,8 @@ def run_steps(w, steps, pinned, seed):
         if len(cow):
             ops.copy_blocks(dk, dv, torch.from_numpy(np.ascontiguousarray(cow)).cuda())
             OA.copy_blocks(k_ref, v_ref, np.array(r_cow))
-        meta = [torch.from_numpy(a) for a in (slots, rows, positions, new_ctx)]
-        meta = [m.pin_memory() if pinned else m.cuda() for m in meta]
-        ops.append_step(to_dev(key, w.dtype), to_dev(val, w.dtype), dk, dv, meta[0], meta[1], meta[2], d_table,
-                        d_ctx, meta[3])
+        append_with(mode, to_dev(key, w.dtype), to_dev(val, w.dtype), dk, dv, slots, rows, positions, d_table, d_ctx,
+                    new_ctx)
         torch.cuda.synchronize()  # the pinned step vectors are rewritten next step
         OA.reshape_and_cache(k_ref, v_ref, key, val, np.array(r_slots))
     want_table, want_ctx = bm.block_table(w.batch, max_blocks, pad=pad)
@@ -67,16 +88,24 @@ def run_steps(w, steps, pinned, seed):
     return dk, dv, k_ref, v_ref, d_table, d_ctx, want_table, want_ctx
 
 
-@pytest.mark.parametrize("name,kw,steps,pinned", [
-    ("tiny_f32", {}, 20, False),
-    ("mha7b_f16", dict(num_seqs=8), 19, True),
-    ("gqa8b_bf16", dict(num_seqs=32), 17, False),
-    ("shared_prefix_bf16", dict(num_users=40, num_prompts=8), 18, True),
-], ids=["tiny_f32", "f16_pinned", "gqa_bf16", "shared_pinned"])
-def test_resident_tables_follow_the_block_manager(name, kw, steps, pinned):
+@pytest.mark.parametrize("name,kw,steps,mode", [
+    ("tiny_f32", {}, 20, "device"),
+    ("mha7b_f16", dict(num_seqs=8), 19, "pinned"),
+    ("gqa8b_bf16", dict(num_seqs=32), 17, "device"),
+    ("shared_prefix_bf16", dict(num_users=40, num_prompts=8), 18, "pinned"),
+    ("tiny_f32", {}, 20, "host"),
+    ("mha7b_f16", dict(num_seqs=64, hi=600), 5, "host"),
+    ("shared_prefix_bf16", dict(num_users=40, num_prompts=8), 18, "host"),
+    # 300 tokens and rows per step: launches of 128 + 128 + 44 tokens and 256 + 44 rows
+    ("gqa8b_bf16", dict(num_seqs=300, hi=300), 3, "host"),
+    # 4 tokens per row, 280 per step: the rows' lengths all travel in the first launch
+    ("specdec_bf16", dict(num_seqs=70, hi=400), 3, "host"),
+], ids=["tiny_f32", "f16_pinned", "gqa_bf16", "shared_pinned", "tiny_f32_host", "f16_host", "shared_host",
+        "gqa_host_3_launches", "multi_token_host"])
+def test_resident_tables_follow_the_block_manager(name, kw, steps, mode):
     w = make_workload(name, **kw)
-    say(f"[append-step] {name} steps={steps} pinned={pinned}")
-    dk, dv, k_ref, v_ref, d_table, d_ctx, table, ctx = run_steps(w, steps, pinned, seed=41)
+    say(f"[append-step] {name} steps={steps} mode={mode}")
+    dk, dv, k_ref, v_ref, d_table, d_ctx, table, ctx = run_steps(w, steps, mode, seed=41)
     # decode on the tables the kernel maintained
     rng = np.random.default_rng(43)
     q = to_storage(rng.standard_normal((w.num_seqs, w.num_q_heads, w.head_dim), dtype=np.float32), w.dtype)
@@ -124,7 +153,8 @@ def test_resident_tables_through_copy_on_write():
     assert np.array_equal(to_host(dk, "bf16"), k_ref) and np.array_equal(to_host(dv, "bf16"), v_ref)
 
 
-def test_skipped_and_out_of_table_tokens():
+@pytest.mark.parametrize("mode", ["device", "host"])
+def test_skipped_and_out_of_table_tokens(mode):
     """A negative or out-of-pool slot stores nothing and leaves the table; a
     row or position outside the table stores the token but leaves the table."""
     w = make_workload("tiny_f32")
@@ -141,9 +171,8 @@ def test_skipped_and_out_of_table_tokens():
     positions = np.array([0, 16, 34, 0, 64, 20], dtype=np.int32)  # position 64 is past 4 blocks
     new_ctx = np.array([21, 35, 7], dtype=np.int32)
     dk, dv = to_dev(w.k_pool, "f32"), to_dev(w.v_pool, "f32")
-    ops.append_step(to_dev(key, "f32"), to_dev(val, "f32"), dk, dv,
-                    *[torch.from_numpy(a).cuda() for a in (slots, rows, positions)], d_table, d_ctx,
-                    torch.from_numpy(new_ctx).cuda())
+    append_with(mode, to_dev(key, "f32"), to_dev(val, "f32"), dk, dv, slots, rows, positions, d_table, d_ctx,
+                new_ctx)
     k_ref, v_ref = w.k_pool.copy(), w.v_pool.copy()
     OA.reshape_and_cache(k_ref, v_ref, key, val, np.where(slots >= NB * 16, -1, slots))
     table[1, 2] = 3
@@ -154,9 +183,11 @@ def test_skipped_and_out_of_table_tokens():
     assert np.array_equal(to_host(dv, "f32").view(np.uint32), v_ref.view(np.uint32))
 
 
-def test_step_plan_with_resident_tables_matches_the_oracle():
+@pytest.mark.parametrize("host_args", [False, True], ids=["pinned", "kernel_args"])
+def test_step_plan_with_resident_tables_matches_the_oracle(host_args):
     """StepPlan in append mode: the per-step write keeps tables on the device
-    and the decode that follows reads them."""
+    and the decode that follows reads them (step metadata in pinned memory,
+    or in plain host memory copied into the kernel arguments)."""
     w = make_workload("gqa8b_bf16", num_seqs=16)
     bm = BlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
     run_program(bm, w.program)
@@ -172,14 +203,15 @@ def test_step_plan_with_resident_tables_matches_the_oracle():
     val = torch.empty_like(key)
     q = torch.empty((S, Hq, D), dtype=TORCH[w.dtype], device="cuda")
     out = torch.empty((S, Hq, D), dtype=torch.float32, device="cuda")
-    slots = torch.empty(S, dtype=torch.int64).pin_memory()
-    rows = torch.arange(S, dtype=torch.int32).pin_memory()
-    positions = torch.empty(S, dtype=torch.int32).pin_memory()
-    new_ctx = torch.empty(S, dtype=torch.int32).pin_memory()
+    host = (lambda t: t) if host_args else (lambda t: t.pin_memory())
+    slots = host(torch.empty(S, dtype=torch.int64))
+    rows = host(torch.arange(S, dtype=torch.int32))
+    positions = host(torch.empty(S, dtype=torch.int32))
+    new_ctx = host(torch.empty(S, dtype=torch.int32))
     max_ctx = int(ctx.max()) + steps
     ws = torch.empty(ops.StepPlan.workspace_bytes_for(S, 1, Hq, Hkv, D, max_ctx), dtype=torch.uint8, device="cuda")
     plan = ops.StepPlan(out, q, dk, dv, d_table, d_ctx, w.scale, ws, key=key, value=val, slot_mapping=slots,
-                        append=(rows, positions, new_ctx))
+                        append=(rows, positions, new_ctx), host_args=host_args)
     for step in range(steps):
         _, pos, nc = step_vectors(bm, list(w.batch), 1)
         s, cow = bm.append_tokens(w.step_seqs)
@@ -203,8 +235,9 @@ def test_step_plan_with_resident_tables_matches_the_oracle():
     assert np.array_equal(d_ctx.cpu().numpy(), c_now)
 
 
+@pytest.mark.parametrize("mode", ["device", "host"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_wide_tokens_take_several_runs_per_thread(dtype):
+def test_wide_tokens_take_several_runs_per_thread(dtype, mode):
     """64 kv heads x 128 dims is 1,024 eight-element runs per token, twice the
     workgroup: each thread stores the run it read before the slot arrived and
     then reads and stores a second one."""
@@ -224,9 +257,8 @@ def test_wide_tokens_take_several_runs_per_thread(dtype):
     d_table = torch.from_numpy(table.copy()).cuda()
     d_ctx = torch.zeros(2, dtype=torch.int32, device="cuda")
     dk, dv = to_dev(k, dtype), to_dev(v, dtype)
-    ops.append_step(to_dev(key, dtype), to_dev(val, dtype), dk, dv,
-                    *[torch.from_numpy(a).cuda() for a in (slots, rows, positions)], d_table, d_ctx,
-                    torch.from_numpy(new_ctx).cuda())
+    append_with(mode, to_dev(key, dtype), to_dev(val, dtype), dk, dv, slots, rows, positions, d_table, d_ctx,
+                new_ctx)
     k_ref, v_ref = k.copy(), v.copy()
     OA.reshape_and_cache(k_ref, v_ref, key, val, slots)
     table[0, 0], table[1, 1] = 7, 2

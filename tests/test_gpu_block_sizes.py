@@ -77,7 +77,7 @@ def test_append_step_and_block_copies_on_32_token_blocks():
     from tests.test_gpu_append import run_steps
     w = make_workload("gqa8b_bf16", num_seqs=16, block_size=32)
     say("[block-size] append steps bs=32")
-    dk, dv, k_ref, v_ref, d_table, d_ctx, table, ctx = run_steps(w, 40, True, seed=91)
+    dk, dv, k_ref, v_ref, d_table, d_ctx, table, ctx = run_steps(w, 40, "pinned", seed=91)
     q = to_storage(np.random.default_rng(92).standard_normal((16, 32, 128), dtype=np.float32), "bf16")
     out = torch.empty((16, 32, 128), dtype=torch.float32, device="cuda")
     ops.decode(out, to_dev(q, "bf16"), dk, dv, d_table, d_ctx, w.scale, int(ctx.max()))
