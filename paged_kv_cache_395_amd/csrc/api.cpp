@@ -224,7 +224,8 @@ pa_status_t prepare_append(const void* key, const void* value, void* k_cache, vo
                          !block_tables))
     return fail(PA_EINVAL, "null pointer argument");
   if (num_seqs > 0 && (!context_lens || !new_context_lens)) return fail(PA_EINVAL, "null pointer argument");
-  if (int64_t(num_tokens) + (int64_t(num_seqs) + 255) / 256 > INT32_MAX) return fail(PA_EUNSUPPORTED, "grid too large");
+  // grid: one column of workgroups per token, then one workgroup per 128 lengths
+  if (int64_t(num_tokens) + (int64_t(num_seqs) + 127) / 128 > INT32_MAX) return fail(PA_EUNSUPPORTED, "grid too large");
   a->key = key;
   a->value = value;
   a->k_cache = k_cache;

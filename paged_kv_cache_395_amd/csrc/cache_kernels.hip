@@ -61,59 +61,61 @@ reshape_and_cache_kernel(const E* __restrict__ key, const E* __restrict__ value,
 template <typename E>
 using Vec8 = E __attribute__((ext_vector_type(8)));
 
-// Stores token t's K/V rows (every kv head) into `slot` and sets
-// table[row][pos / 16] = slot / 16: the block the slot lies in (a new block
-// when pos % 16 == 0, the fresh copy after a copy-on-write, the same block
-// otherwise).  kv0 / vv0: this thread's first 8-element run, already loaded.
+// A step's token t is spread over gridDim.y workgroups: thread i of
+// workgroup (t, y) moves run c = y * blockDim.x + i (dims 8j..8j+7 of kv
+// head c / (D / 8)), so the scattered single-element V stores of one token
+// run on several CUs.
+__device__ inline int step_run() { return int(blockIdx.y * blockDim.x + threadIdx.x); }
+
+// This thread's K/V run of token t (zeros past the token's runs), loaded
+// before the slot is known.
 template <typename E>
-__device__ inline void store_step_token(const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ kc,
-                                        E* __restrict__ vc, int t, int64_t slot, int row, int pos, int32_t* tables,
-                                        int32_t max_blocks, int32_t num_rows, int32_t kv_heads, int32_t head_dim,
-                                        int64_t num_blocks, int32_t sh, Vec8<E> kv0, Vec8<E> vv0) {
-  if (slot < 0 || slot >= (num_blocks << (4 + sh))) return;  // skipped token, or outside the pool
-  if (threadIdx.x == 0 && row >= 0 && row < num_rows && pos >= 0 && (pos >> (4 + sh)) < max_blocks)
-    tables[int64_t(row) * max_blocks + (pos >> (4 + sh))] = int32_t(slot >> (4 + sh));
+__device__ inline void load_step_run(const E* __restrict__ key, const E* __restrict__ value, int t, int32_t kv_heads,
+                                     int32_t head_dim, Vec8<E>& kv, Vec8<E>& vv) {
   const int runs_per_head = head_dim / 8;
-  const int nruns = kv_heads * runs_per_head;
-  const int o = int(slot & 15);
-  for (int c = threadIdx.x; c < nruns; c += blockDim.x) {
+  const int c = step_run();
+  kv = Vec8<E>{};
+  vv = Vec8<E>{};
+  if (c < kv_heads * runs_per_head) {
     const int h = c / runs_per_head, j = c - h * runs_per_head;
     const int64_t src = (int64_t(t) * kv_heads + h) * head_dim + 8 * j;
-    const int64_t tile = slot_tile(slot, h, kv_heads, head_dim, sh);
-    const bool first = c == int(threadIdx.x);
-    *reinterpret_cast<Vec8<E>*>(kc + tile + (j * kBlockTokens + o) * 8) =
-        first ? kv0 : *reinterpret_cast<const Vec8<E>*>(key + src);
-    const Vec8<E> vv = first ? vv0 : *reinterpret_cast<const Vec8<E>*>(value + src);
-    E* vt = vc + tile;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * j + e;
-      vt[(((d >> 5) * 4 + (o >> 2)) * 16 + (d & 15)) * 8 + ((d >> 4) & 1) * 4 + (o & 3)] = vv[e];
-    }
+    kv = *reinterpret_cast<const Vec8<E>*>(key + src);
+    vv = *reinterpret_cast<const Vec8<E>*>(value + src);
   }
 }
 
-// This thread's first K/V run of token t (zeros past the token's runs).
+// Stores this thread's run of token t into `slot`; the first thread of the
+// token sets table[row][pos / 16] = slot / 16: the block the slot lies in (a
+// new block when pos % 16 == 0, the fresh copy after a copy-on-write, the
+// same block otherwise).
 template <typename E>
-__device__ inline void load_first_run(const E* __restrict__ key, const E* __restrict__ value, int t,
-                                      int32_t kv_heads, int32_t head_dim, Vec8<E>& kv0, Vec8<E>& vv0) {
+__device__ inline void store_step_run(E* __restrict__ kc, E* __restrict__ vc, int64_t slot, int row, int pos,
+                                      int32_t* tables, int32_t max_blocks, int32_t num_rows, int32_t kv_heads,
+                                      int32_t head_dim, int64_t num_blocks, int32_t sh, Vec8<E> kv, Vec8<E> vv) {
+  if (slot < 0 || slot >= (num_blocks << (4 + sh))) return;  // skipped token, or outside the pool
+  const int c = step_run();
+  if (c == 0 && row >= 0 && row < num_rows && pos >= 0 && (pos >> (4 + sh)) < max_blocks)
+    tables[int64_t(row) * max_blocks + (pos >> (4 + sh))] = int32_t(slot >> (4 + sh));
   const int runs_per_head = head_dim / 8;
-  kv0 = Vec8<E>{};
-  vv0 = Vec8<E>{};
-  if (int(threadIdx.x) < kv_heads * runs_per_head) {
-    const int h = threadIdx.x / runs_per_head, j = threadIdx.x - h * runs_per_head;
-    const int64_t src = (int64_t(t) * kv_heads + h) * head_dim + 8 * j;
-    kv0 = *reinterpret_cast<const Vec8<E>*>(key + src);
-    vv0 = *reinterpret_cast<const Vec8<E>*>(value + src);
+  if (c >= kv_heads * runs_per_head) return;
+  const int h = c / runs_per_head, j = c - h * runs_per_head;
+  const int o = int(slot & 15);
+  const int64_t tile = slot_tile(slot, h, kv_heads, head_dim, sh);
+  *reinterpret_cast<Vec8<E>*>(kc + tile + (j * kBlockTokens + o) * 8) = kv;
+  E* vt = vc + tile;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int d = 8 * j + e;
+    vt[(((d >> 5) * 4 + (o >> 2)) * 16 + (d & 15)) * 8 + ((d >> 4) & 1) * 4 + (o & 3)] = vv[e];
   }
 }
 
 // One step's appends with the block tables and context lengths kept on the
-// device: workgroup t < T stores token t (store_step_token); the workgroups
+// device: workgroups (t < T, y) store token t; the workgroups (t >= T, 0)
 // after those copy new_ctx into ctx.  The token's (slot, row, pos) are read
-// once, by thread 0, into LDS: they may live in pinned host memory, where
-// every read crosses the host link.
-constexpr int kAppendThreads = 512;  // one 8-element run per thread for 32 kv heads x 128 dims
+// once per workgroup, by thread 0, into LDS: they may live in pinned host
+// memory, where every read crosses the host link.
+constexpr int kAppendThreads = 128;
 template <typename E>
 __global__ void __launch_bounds__(kAppendThreads)
 append_step_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __restrict__ kc, E* __restrict__ vc,
@@ -123,23 +125,23 @@ append_step_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __
   const int t = blockIdx.x;
   if (t >= num_tokens) {
     const int i = (t - num_tokens) * blockDim.x + threadIdx.x;
-    if (i < num_rows) ctx[i] = new_ctx[i];
+    if (blockIdx.y == 0 && i < num_rows) ctx[i] = new_ctx[i];
     return;
   }
   __shared__ int64_t s_slot;
   __shared__ int32_t s_row, s_pos;
-  // the thread's first K/V run is read before the metadata wait, so the
-  // device reads overlap the (slower) read of the slot from host memory
-  Vec8<E> kv0, vv0;
-  load_first_run(key, value, t, kv_heads, head_dim, kv0, vv0);
+  // the thread's K/V run is read before the metadata wait, so the device
+  // reads overlap the (slower) read of the slot from host memory
+  Vec8<E> kv, vv;
+  load_step_run(key, value, t, kv_heads, head_dim, kv, vv);
   if (threadIdx.x == 0) {
     s_slot = slots[t];
     s_row = rows[t];
     s_pos = positions[t];
   }
   __syncthreads();
-  store_step_token(key, value, kc, vc, t, s_slot, s_row, s_pos, tables, max_blocks, num_rows, kv_heads, head_dim,
-                   num_blocks, sh, kv0, vv0);
+  store_step_run(kc, vc, s_slot, s_row, s_pos, tables, max_blocks, num_rows, kv_heads, head_dim, num_blocks, sh, kv,
+                 vv);
 }
 
 // The same step with its metadata in the kernel arguments (one launch's
@@ -155,13 +157,13 @@ append_args_kernel(const E* __restrict__ key, const E* __restrict__ value, E* __
   const int t = blockIdx.x;
   if (t >= meta.num_tokens) {
     const int i = (t - meta.num_tokens) * blockDim.x + threadIdx.x;
-    if (i < meta.num_rows) ctx[meta.row0 + i] = meta.new_ctx[i];
+    if (blockIdx.y == 0 && i < meta.num_rows) ctx[meta.row0 + i] = meta.new_ctx[i];
     return;
   }
-  Vec8<E> kv0, vv0;
-  load_first_run(key, value, t, kv_heads, head_dim, kv0, vv0);
-  store_step_token(key, value, kc, vc, t, meta.slots[t], meta.rows[t], meta.positions[t], tables, max_blocks,
-                   num_rows, kv_heads, head_dim, num_blocks, sh, kv0, vv0);
+  Vec8<E> kv, vv;
+  load_step_run(key, value, t, kv_heads, head_dim, kv, vv);
+  store_step_run(kc, vc, meta.slots[t], meta.rows[t], meta.positions[t], tables, max_blocks, num_rows, kv_heads,
+                 head_dim, num_blocks, sh, kv, vv);
 }
 
 // Grid (chunks of one block, pairs, 2): z = 0 copies K, z = 1 copies V; each
@@ -217,18 +219,24 @@ hipError_t launch_reshape_and_cache(const void* key, const void* value, void* k_
   return hipGetLastError();
 }
 
+// workgroups per token: one 8-element run per thread
+int64_t step_run_groups(const AppendStepArgs& a) {
+  return (int64_t(a.num_kv_heads) * (a.head_dim / 8) + kAppendThreads - 1) / kAppendThreads;
+}
+
 hipError_t launch_append_step(const AppendStepArgs& a) {
   const int64_t ctx_groups = (int64_t(a.num_rows) + kAppendThreads - 1) / kAppendThreads;
-  const int64_t grid = int64_t(a.num_tokens) + ctx_groups;
-  if (grid == 0) return hipSuccess;
+  const int64_t grid_x = int64_t(a.num_tokens) + ctx_groups;
+  if (grid_x == 0) return hipSuccess;
+  const dim3 grid(unsigned(grid_x), unsigned(step_run_groups(a)));
   if (a.elem_bytes == 2) {
-    hipLaunchKernelGGL(append_step_kernel<uint16_t>, dim3(unsigned(grid)), dim3(kAppendThreads), 0, a.stream,
+    hipLaunchKernelGGL(append_step_kernel<uint16_t>, grid, dim3(kAppendThreads), 0, a.stream,
                        static_cast<const uint16_t*>(a.key), static_cast<const uint16_t*>(a.value),
                        static_cast<uint16_t*>(a.k_cache), static_cast<uint16_t*>(a.v_cache), a.slots, a.rows,
                        a.positions, a.num_tokens, a.tables, a.max_blocks, a.ctx, a.new_ctx, a.num_rows,
                        a.num_kv_heads, a.head_dim, a.num_blocks, a.tile_shift);
   } else {
-    hipLaunchKernelGGL(append_step_kernel<uint32_t>, dim3(unsigned(grid)), dim3(kAppendThreads), 0, a.stream,
+    hipLaunchKernelGGL(append_step_kernel<uint32_t>, grid, dim3(kAppendThreads), 0, a.stream,
                        static_cast<const uint32_t*>(a.key), static_cast<const uint32_t*>(a.value),
                        static_cast<uint32_t*>(a.k_cache), static_cast<uint32_t*>(a.v_cache), a.slots, a.rows,
                        a.positions, a.num_tokens, a.tables, a.max_blocks, a.ctx, a.new_ctx, a.num_rows,
@@ -238,15 +246,16 @@ hipError_t launch_append_step(const AppendStepArgs& a) {
 }
 
 hipError_t launch_append_step_args(const AppendStepArgs& a, const AppendArgsMeta& meta) {
-  const int64_t grid = int64_t(meta.num_tokens) + (int64_t(meta.num_rows) + kAppendThreads - 1) / kAppendThreads;
-  if (grid == 0) return hipSuccess;
+  const int64_t grid_x = int64_t(meta.num_tokens) + (int64_t(meta.num_rows) + kAppendThreads - 1) / kAppendThreads;
+  if (grid_x == 0) return hipSuccess;
+  const dim3 grid(unsigned(grid_x), unsigned(step_run_groups(a)));
   if (a.elem_bytes == 2) {
-    hipLaunchKernelGGL(append_args_kernel<uint16_t>, dim3(unsigned(grid)), dim3(kAppendThreads), 0, a.stream,
+    hipLaunchKernelGGL(append_args_kernel<uint16_t>, grid, dim3(kAppendThreads), 0, a.stream,
                        static_cast<const uint16_t*>(a.key), static_cast<const uint16_t*>(a.value),
                        static_cast<uint16_t*>(a.k_cache), static_cast<uint16_t*>(a.v_cache), meta, a.tables,
                        a.max_blocks, a.ctx, a.num_rows, a.num_kv_heads, a.head_dim, a.num_blocks, a.tile_shift);
   } else {
-    hipLaunchKernelGGL(append_args_kernel<uint32_t>, dim3(unsigned(grid)), dim3(kAppendThreads), 0, a.stream,
+    hipLaunchKernelGGL(append_args_kernel<uint32_t>, grid, dim3(kAppendThreads), 0, a.stream,
                        static_cast<const uint32_t*>(a.key), static_cast<const uint32_t*>(a.value),
                        static_cast<uint32_t*>(a.k_cache), static_cast<uint32_t*>(a.v_cache), meta, a.tables,
                        a.max_blocks, a.ctx, a.num_rows, a.num_kv_heads, a.head_dim, a.num_blocks, a.tile_shift);

@@ -237,10 +237,10 @@ def test_step_plan_with_resident_tables_matches_the_oracle(host_args):
 
 @pytest.mark.parametrize("mode", ["device", "host"])
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_wide_tokens_take_several_runs_per_thread(dtype, mode):
-    """64 kv heads x 128 dims is 1,024 eight-element runs per token, twice the
-    workgroup: each thread stores the run it read before the slot arrived and
-    then reads and stores a second one."""
+def test_wide_tokens_spread_over_several_workgroups(dtype, mode):
+    """64 kv heads x 128 dims is 1,024 eight-element runs per token: eight
+    workgroups of 128 threads per token, each thread storing the run it read
+    before the slot arrived, the token's table entry written once."""
     rng = np.random.default_rng(61 if dtype == "bf16" else 62)
     NB, Hkv, D = 12, 64, 128
     k = to_storage(rng.standard_normal((NB, Hkv, 16 * D), dtype=np.float32), dtype)
