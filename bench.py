@@ -92,6 +92,16 @@ class TimingEvent:
             TimingEvent._hip.hipEventDestroy(self._h)
 
 
+def appends_fit(bm, w, tokens: int) -> bool:
+    """Whether the pool's free blocks hold ``tokens`` more tokens for every sequence of the batch."""
+    bs = w.block_size
+    need = 0
+    for s in w.batch:
+        n = bm.num_tokens(int(s))
+        need += -(-(n + tokens) // bs) - -(-n // bs)
+    return need <= bm.num_free()
+
+
 def decode_bytes(ctx: np.ndarray, w) -> float:
     """Algorithmic bytes of one decode: K+V rows of every context token, q, out, table entries read."""
     e = ESIZE[w.dtype]
@@ -570,7 +580,9 @@ def summarize(args) -> None:
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None, help="timed steps (50; 200 for serving_bf16)")
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (decode: up to 200, fewer when the pool cannot hold that many appends; "
+                         "serving: 200)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (5; 150 for serving_bf16, which fills its batch meanwhile)")
     ap.add_argument("--workload", default="mha7b_f16",
@@ -596,10 +608,9 @@ def main():
     ap.add_argument("--prefill-grbm-dir")
     args = ap.parse_args()
     serving = args.workload in ("serving_bf16", "serving_prefix_bf16")
-    if args.steps is None:
-        args.steps = 200 if serving else 50
-    if args.warmup is None:
-        args.warmup = 150 if serving else 5
+    if serving:
+        args.steps = 200 if args.steps is None else args.steps
+        args.warmup = 150 if args.warmup is None else args.warmup
     if args.summarize:
         summarize(args)
         return
@@ -635,11 +646,19 @@ def main():
     # decode workloads append one token per step (the verification workload w.append); the chunk
     # workload writes its chunk once and then decodes in place
     grows = w.append == 1 or multi
+    bm = BlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
+    run_program(bm, w.program)
+    if args.steps is None or args.warmup is None:
+        # the longest run (about 40-60 ms timed, so a host stall of a few ms
+        # does not decide the figure) whose appends the pool can hold
+        for k in (200, 100, 50, 20):
+            if not grows or appends_fit(bm, w, (k + k // 10 + 2) * w.append):
+                break
+        args.steps = k if args.steps is None else args.steps
+        args.warmup = max(5, k // 10) if args.warmup is None else args.warmup
     extra = (args.warmup + args.steps + 2) * w.append if grows else 0
     maxB = w.max_blocks_per_seq(extra)
     pad = w.num_blocks + 1  # never read
-    bm = BlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
-    run_program(bm, w.program)
 
     k_pool, v_pool = to_dev(w.k_pool), to_dev(w.v_pool)
     step_k, step_v = to_dev(w.step_rows("k")), to_dev(w.step_rows("v"))
@@ -671,7 +690,7 @@ def main():
     ring = [{"slots": torch.empty(n_tok, dtype=torch.int64, pin_memory=not host_args),
              "pos": torch.empty(n_tok, dtype=torch.int32, pin_memory=not host_args),
              "nctx": torch.empty(S, dtype=torch.int32, pin_memory=not host_args)}
-            for _ in range(1 if host_args else 4)]
+            for _ in range(1 if host_args else 16)]
     plans = [ops.StepPlan(out, q, k_pool, v_pool, d_table, d_ctx, w.scale, ws, key=step_k, value=step_v,
                           slot_mapping=r["slots"], partition_size=args.partition,
                           append=(rows, r["pos"], r["nctx"]), host_args=host_args) for r in ring]
