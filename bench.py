@@ -144,16 +144,20 @@ def kernel_source_hash() -> str:
 
 
 def load_traffic(workload: str, bytes_per_launch: float):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source; else None."""
+    """(HBM bytes per launch, HBM / algorithmic bytes) from committed rocprofv3
+    counter runs, if they were taken on the current kernel source; else
+    (None, None).  The counter runs time a few short steps; the measured
+    ratio of HBM to algorithmic bytes carries over to this run's mean launch
+    (longer contexts after more steps), so the bytes are scaled by it."""
     path = os.path.join(ROOT, "profiles", f"decode_partitions_{workload}_traffic.json")
     if not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha") != kernel_source_hash():
-        return None
-    return rec.get("hbm_bytes_per_launch")
+        return None, None
+    ratio = rec["hbm_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"]
+    return ratio * bytes_per_launch, ratio
 
 
 def _host_threads() -> int:
@@ -513,7 +517,8 @@ def summarize(args) -> None:
     prof = os.path.join(ROOT, "profiles")
     base = "python -u bench.py --workload %s" % wl
     serving = "kernels_ms" not in rec  # the serving rows run their own step count and warm-up
-    run_args = "" if serving else " --steps 20 --warmup 3 --cold-iters 3"
+    # the bench's own step count, so the trace's mean decode launch is the launch bench.py times
+    run_args = "" if serving else " --cold-iters 3"
     trace_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {args.trace_dir} -o trace -- "
                  f"{base}{run_args} --no-cpu-baseline")
     pmc_cmd = (f"timeout -s KILL 120 rocprofv3 --pmc {{counter}} --output-format csv -d {{out_dir}} "
@@ -858,7 +863,7 @@ def main():
                                    "frac_of_dense_mfma_peak": round(fl / (p_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                                    "algorithmic_tflop": round(fl / 1e12, 4)}
 
-    traffic = load_traffic(args.workload, bytes_per_launch)
+    traffic, traffic_ratio = load_traffic(args.workload, bytes_per_launch)
     phys_bytes = physical_kv_bytes(t_host, c_host, w)
     value = total_bytes / elapsed / 1e9
     rec = {
@@ -889,6 +894,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic, 1),
+                     "traffic_over_algorithmic": None if traffic_ratio is None else round(traffic_ratio, 4),
                      "kernel": "decode_mfma_kernel" if w.dtype != "f32" else "decode_f32_kernel",
                      "algorithmic_bytes_per_launch": round(bytes_per_launch, 1)},
         "kernels_ms": {"append_step": round(float(k1_ms.mean()), 5),
