@@ -545,6 +545,10 @@ def summarize(args) -> None:
     if args.fetch_dir is None:
         return
 
+    if args.counter_log:
+        # the counter runs' own algorithmic bytes (their JSON line): a few short steps, not the bench's mean
+        with open(args.counter_log) as f:
+            alg = json.loads([l for l in f if l.startswith("{")][-1])["roofline"]["algorithmic_bytes_per_launch"]
     fetch = _csv_rows(args.fetch_dir, "counter_collection.csv")
     write = _csv_rows(args.write_dir, "counter_collection.csv")
     f_dec, n_dec = _per_dispatch(fetch, DECODE_KERNEL)
@@ -573,7 +577,7 @@ def summarize(args) -> None:
           f"WRITE_SIZE {w_cp:.1f} KiB for {probe_kib} KiB moved each way: scale x{fs:.4f} (fetch), x{ws:.4f} (write)",
           f"- HBM bytes per launch (scaled): fetch {hbm_f / 1e9:.4f} GB + write {hbm_w / 1e9:.4f} GB = "
           f"{(hbm_f + hbm_w) / 1e9:.4f} GB",
-          f"- algorithmic bytes per launch (bench formula): {alg / 1e9:.4f} GB -> traffic / algorithmic = "
+          f"- algorithmic bytes per launch of the counter runs (bench formula): {alg / 1e9:.4f} GB -> traffic / algorithmic = "
           f"{(hbm_f + hbm_w) / alg:.3f}",
           f"- kernel source sha256[:16]: {out['kernel_source_sha']} (bench.py reports `traffic` only while this "
           "matches)", ""]
@@ -608,6 +612,8 @@ def main():
     ap.add_argument("--trace-dir")
     ap.add_argument("--fetch-dir")
     ap.add_argument("--write-dir")
+    ap.add_argument("--counter-log", help="output of the FETCH_SIZE counter run (its JSON line gives the "
+                                          "algorithmic bytes per launch of that run)")
     ap.add_argument("--bench-json")
     ap.add_argument("--prefill-pmc-dir")
     ap.add_argument("--prefill-grbm-dir")

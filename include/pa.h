@@ -222,9 +222,9 @@ pa_status_t pa_patch_tables(int32_t* block_tables, int32_t max_blocks_per_seq, i
  * ---------------------------------------------------------------------- */
 /* Effective partition size for these sizes (partition_size 0 = the
  * library's choice: 512 to 4096 tokens, as large as keeps >= 1024
- * workgroups; within a quarter of the longest context once the (sequence,
- * kv head) pairs alone reach 1024, and 4096 once they reach 4096); -1 for
- * invalid arguments. */
+ * workgroups; small enough that the longest context spans >= 4
+ * partitions once the (sequence, kv head) pairs alone reach 1024, and 4096
+ * once they reach 4096); -1 for invalid arguments. */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                  int32_t partition_size);
 

@@ -49,13 +49,13 @@ pa_status_t check_pool(int32_t kv_heads, int32_t head_dim, int32_t block_size, i
 // (HBM writes interleaved with the read stream), so partitions are made as
 // large as the grid allows: starting from 512 tokens they double, up to
 // 4096, while the grid still holds >= kMinWorkgroups workgroups (4 per CU)
-// and, once the (sequence, kv head) pairs alone fill the GPU, while a
-// partition stays within a quarter of the longest context (larger ones
-// only unbalance ragged batches).  With >= kManyPairs pairs (16 per CU) the
+// and, once the (sequence, kv head) pairs alone fill the GPU, while the
+// longest context still spans at least 4 partitions (larger ones only
+// unbalance ragged batches).  With >= kManyPairs pairs (16 per CU) the
 // pairs balance the GPU on their own and partitions go straight to 4096:
 // on 1,024 sequences x 8 kv heads of up to ~1,200 tokens that drops the
 // split and the merge launch (+10% per step), while at 2,048 pairs the
-// quarter rule stays the better choice.
+// 4-partition rule stays the better choice.
 constexpr int32_t kMinPartition = 512;
 constexpr int32_t kMaxDefaultPartition = 4096;
 constexpr int64_t kMinWorkgroups = 1024;
@@ -68,7 +68,7 @@ int32_t choose_partition(int64_t S, int64_t Hkv, int64_t max_ctx, int32_t reques
   while (p < kMaxDefaultPartition) {
     const int64_t next = 2 * int64_t(p);
     if (pairs * ceil_div(max_ctx, next) < kMinWorkgroups) break;
-    if (pairs >= kMinWorkgroups && pairs < kManyPairs && next > max_ctx / 4) break;
+    if (pairs >= kMinWorkgroups && pairs < kManyPairs && ceil_div(max_ctx, next) < 4) break;
     p = int32_t(next);
   }
   return p;

@@ -145,6 +145,8 @@ def test_workspace_size_formula():
     (16, 8, 32768, 4096),     # few long sequences: split to fill the GPU, into large pieces
     (64, 32, 2048, 512),      # many pairs, short contexts: small pieces balance the ragged lengths
     (256, 8, 8192, 2048),     # many pairs, a long tail of lengths
+    (256, 8, 7872, 2048),     # the longest context still spans 4 partitions of 2048
+    (256, 8, 6144, 1024),     # 3 partitions of 2048 would be too few
     (1024, 8, 1100, 4096),    # pairs enough to balance the GPU alone (>= 4096): no split below 4096 tokens
     (512, 8, 20000, 4096),
 ])
