@@ -180,8 +180,9 @@ def _cpu_model() -> str:
 
 
 def cpu_baseline(w, budget_s: float = 15.0):
-    """The oracle, as it stands, on the first sequences of the same step until
-    ~budget_s of work, with BLAS on every host core the process may use."""
+    """The oracle, as it stands, on the sequences of the same step in order,
+    cycling over the batch again when a pass ends, until ~budget_s of work,
+    with BLAS on every host core the process may use."""
     from threadpoolctl import threadpool_limits
 
     from oracle import attention as OA
@@ -200,7 +201,8 @@ def cpu_baseline(w, budget_s: float = 15.0):
         t0 = time.perf_counter()
         OA.reshape_and_cache(k, v, w.step_rows("k"), w.step_rows("v"), np.array(slots))
         multi = w.lengths.get("mode") == "multi"
-        for s in range(w.num_seqs):
+        for i in range(100 * w.num_seqs):
+            s = i % w.num_seqs
             if multi:  # the verification workload: each sequence's last w.append positions, causally
                 OA.prefill_chunk(w.q, k, v, table, ctx, w.scale, w.dtype, seqs=[s])
             else:
@@ -211,10 +213,12 @@ def cpu_baseline(w, budget_s: float = 15.0):
         dt = time.perf_counter() - t0
     sub = ctx[done]
     gbs = decode_bytes(sub, w) / dt / 1e9
+    passes = len(done) / w.num_seqs
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle", "cpu": _cpu_model(),
-            "sample": f"one decode step (cache write of {w.num_seqs} tokens + fp64 attention) for the first "
-                      f"{len(done)} of {w.num_seqs} sequences, all {w.num_q_heads} q heads; "
-                      f"{dt:.1f} s; seqs/s {len(done) / dt:.2f}; numpy, BLAS on {cores} cores"}
+            "sample": f"the step's cache write of {w.num_seqs} tokens, then fp64 attention over its sequences "
+                      f"in order, {len(done)} sequence decodes ({passes:.2f} passes over the {w.num_seqs}), all "
+                      f"{w.num_q_heads} q heads; {dt:.1f} s; seqs/s {len(done) / dt:.2f}; numpy, BLAS on "
+                      f"{cores} cores"}
 
 
 SERVING = dict(num_q_heads=32, num_kv_heads=8, head_dim=128, dtype="bf16", rows=256, num_blocks=10000,
