@@ -288,8 +288,8 @@ pa_status_t pa_append_step_host(const void* key, const void* value, void* k_cach
     AppendArgsMeta m{};
     const int64_t t0 = i * kArgTokens, r0 = i * kArgRows;
     m.num_tokens = int32_t(std::min<int64_t>(std::max<int64_t>(num_tokens - t0, 0), kArgTokens));
-    m.row0 = int32_t(r0);
     m.num_rows = int32_t(std::min<int64_t>(std::max<int64_t>(num_seqs - r0, 0), kArgRows));
+    m.row0 = m.num_rows > 0 ? int32_t(r0) : 0;
     if (m.num_tokens > 0) {
       std::memcpy(m.slots, slot_mapping + t0, sizeof(int64_t) * m.num_tokens);
       std::memcpy(m.rows, token_rows + t0, sizeof(int32_t) * m.num_tokens);
