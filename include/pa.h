@@ -228,6 +228,12 @@ pa_status_t pa_patch_tables(int32_t* block_tables, int32_t max_blocks_per_seq, i
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                  int32_t partition_size);
 
+/* Workgroups the fp16 / bf16 decode launch uses on the current device at
+ * most: as many as are resident at once (occupancy per CU x CUs); each takes
+ * an equal share of the batch's tiles.  -1 for an unsupported dtype /
+ * head_dim / out_dtype. */
+int64_t pa_decode_workgroups(pa_dtype_t dtype, int32_t head_dim, pa_dtype_t out_dtype);
+
 /* Workspace bytes pa_decode needs for these sizes (0: none). */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_context_len, int32_t partition_size);

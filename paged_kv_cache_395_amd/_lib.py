@@ -52,6 +52,7 @@ SIGNATURES = {
                                       _vp]),
     "pa_patch_tables": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp]),
     "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32]),
+    "pa_decode_workgroups": (_i64, [ctypes.c_int, _i32, ctypes.c_int]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _i64, _f32, _i32, _i32, _vp, _sz, ctypes.c_int, _vp]),

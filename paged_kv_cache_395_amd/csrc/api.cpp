@@ -111,21 +111,31 @@ pa_status_t check_decode(const void* out, pa_dtype_t out_dtype, const void* q, i
   return PA_OK;
 }
 
-size_t ws_size(int64_t S, int64_t Hq, int64_t D, int64_t nparts) {
+// Workspace of a split decode (none without a split): a 256-byte header (the
+// call's geometry, checked by the merge), the partial-slot count of every
+// (sequence, kv head), then the partials acc [rows][D], m [rows], l [rows]
+// with rows = S * q_len * Hq * nparts; 256-byte aligned pieces.
+int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+
+size_t ws_size(int64_t S, int64_t q_len, int64_t Hq, int64_t Hkv, int64_t D, int64_t nparts) {
   if (nparts <= 1) return 0;
-  const int64_t rows = S * Hq * nparts;
-  // acc [rows][D], then m [rows], then l [rows]; 256-byte aligned pieces
-  auto align = [](int64_t b) { return (b + 255) / 256 * 256; };
-  return size_t(align(rows * D * 4) + 2 * align(rows * 4));
+  const int64_t rows = S * q_len * Hq * nparts;
+  return size_t(256 + align256(S * Hkv * 4) + align256(rows * D * 4) + 2 * align256(rows * 4));
 }
 
-void split_workspace(void* ws, int64_t S, int64_t Hq, int64_t D, int64_t nparts, float** acc, float** m, float** l) {
-  auto align = [](int64_t b) { return (b + 255) / 256 * 256; };
-  const int64_t rows = S * Hq * nparts;
-  char* base = static_cast<char*>(ws);
-  *acc = reinterpret_cast<float*>(base);
-  *m = reinterpret_cast<float*>(base + align(rows * D * 4));
-  *l = reinterpret_cast<float*>(base + align(rows * D * 4) + align(rows * 4));
+void split_workspace(void* ws, int64_t S, int64_t q_len, int64_t Hq, int64_t Hkv, int64_t D, int64_t nparts,
+                     DecodeArgs* a) {
+  const int64_t rows = S * q_len * Hq * nparts;
+  char* p = static_cast<char*>(ws);
+  a->ws_hdr = reinterpret_cast<int32_t*>(p);
+  p += 256;
+  a->ws_nseg = reinterpret_cast<int32_t*>(p);
+  p += align256(S * Hkv * 4);
+  a->ws_acc = reinterpret_cast<float*>(p);
+  p += align256(rows * D * 4);
+  a->ws_m = reinterpret_cast<float*>(p);
+  p += align256(rows * 4);
+  a->ws_l = reinterpret_cast<float*>(p);
 }
 
 enum class DecodePhase { kBoth, kPartitions, kReduce };
@@ -139,7 +149,7 @@ pa_status_t run_decode(DecodePhase phase, void* out, pa_dtype_t out_dtype, const
   pa_status_t st = check_decode(out, out_dtype, q, q_len, k_cache, v_cache, block_tables, max_blocks, context_lens,
                                 S, Hq, Hkv, D, bs, NB, scale, max_ctx, partition, dtype, &dc);
   if (st != PA_OK) return st;
-  const size_t need = ws_size(int64_t(S) * q_len, Hq, D, dc.nparts);
+  const size_t need = ws_size(S, q_len, Hq, Hkv, D, dc.nparts);
   if (need > 0 && (workspace == nullptr || workspace_bytes_given < need))
     return fail(PA_EWORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes_given);
   if (S == 0) return PA_OK;
@@ -163,7 +173,7 @@ pa_status_t run_decode(DecodePhase phase, void* out, pa_dtype_t out_dtype, const
   a.num_partitions = dc.nparts;
   a.q_len = q_len;
   a.tile_shift = tile_shift_of(bs);
-  if (need > 0) split_workspace(workspace, int64_t(S) * q_len, Hq, D, dc.nparts, &a.ws_acc, &a.ws_m, &a.ws_l);
+  if (need > 0) split_workspace(workspace, S, q_len, Hq, Hkv, D, dc.nparts, &a);
   a.dtype = dtype;
   a.stream = static_cast<hipStream_t>(stream);
   if (phase != DecodePhase::kReduce) {
@@ -345,6 +355,12 @@ pa_status_t pa_patch_tables(int32_t* block_tables, int32_t max_blocks_per_seq, i
                     "patch_tables launch");
 }
 
+int64_t pa_decode_workgroups(pa_dtype_t dtype, int32_t head_dim, pa_dtype_t out_dtype) {
+  if (!(dtype == PA_F16 || dtype == PA_BF16) || (head_dim != 64 && head_dim != 128)) return -1;
+  if (!(out_dtype == PA_F32 || out_dtype == dtype)) return -1;
+  return decode_resident_workgroups(dtype, head_dim, out_dtype == PA_F32);
+}
+
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                  int32_t partition_size) {
   if (num_seqs < 0 || num_kv_heads <= 0 || max_context_len < 0 || partition_size < 0 || partition_size % 16 != 0)
@@ -357,7 +373,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t 
   if (num_seqs <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_context_len <= 0) return 0;
   if (partition_size < 0 || partition_size % 16 != 0) return 0;
   const int32_t p = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
-  return ws_size(num_seqs, num_q_heads, head_dim, ceil_div(max_context_len, p));
+  return ws_size(num_seqs, 1, num_q_heads, num_kv_heads, head_dim, ceil_div(max_context_len, p));
 }
 
 size_t pa_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
@@ -366,7 +382,7 @@ size_t pa_decode_multi_workspace_bytes(int32_t num_seqs, int32_t q_len, int32_t 
     return 0;
   if (partition_size < 0 || partition_size % 16 != 0) return 0;
   const int32_t p = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
-  return ws_size(int64_t(num_seqs) * q_len, num_q_heads, head_dim, ceil_div(max_context_len, p));
+  return ws_size(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, ceil_div(max_context_len, p));
 }
 
 pa_status_t pa_decode_multi(void* out, pa_dtype_t out_dtype, const void* q, int32_t q_len, const void* k_cache,
@@ -416,7 +432,7 @@ pa_status_t pa_decode_reduce(void* out, pa_dtype_t out_dtype, const int32_t* con
     return fail(PA_EINVAL, "partition_size must be 0 or a positive multiple of 16");
   const int32_t p = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
   const int64_t nparts = max_context_len == 0 ? 1 : ceil_div(max_context_len, p);
-  const size_t need = ws_size(num_seqs, num_q_heads, head_dim, nparts);
+  const size_t need = ws_size(num_seqs, 1, num_q_heads, num_kv_heads, head_dim, nparts);
   if (need == 0 || num_seqs == 0) return PA_OK;
   if (workspace == nullptr || workspace_bytes < need)
     return fail(PA_EWORKSPACE, "workspace of %zu bytes required (got %zu)", need, workspace_bytes);
@@ -434,7 +450,7 @@ pa_status_t pa_decode_reduce(void* out, pa_dtype_t out_dtype, const int32_t* con
   a.partition = p;
   a.num_partitions = int32_t(nparts);
   a.q_len = 1;
-  split_workspace(const_cast<void*>(workspace), num_seqs, num_q_heads, head_dim, nparts, &a.ws_acc, &a.ws_m, &a.ws_l);
+  split_workspace(const_cast<void*>(workspace), num_seqs, 1, num_q_heads, num_kv_heads, head_dim, nparts, &a);
   a.dtype = out_dtype == PA_F32 ? PA_F16 : out_dtype;
   a.stream = static_cast<hipStream_t>(stream);
   return hip_status(launch_decode_reduce(a), "decode reduce launch");

@@ -35,6 +35,9 @@
 
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "device_common.h"
 #include "pa_internal.h"
 
@@ -45,6 +48,8 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * kWave;
 // "no max yet": finite so that 2^(s - m) of a masked score is 0, not NaN
 constexpr float kNoMax = -1e30f;
+// first word of the workspace header the partition kernels write
+constexpr int32_t kWorkspaceMagic = 0x50413031;
 
 struct KParams {
   void* out;
@@ -64,6 +69,11 @@ struct KParams {
   int32_t max_blocks;
   int32_t hq, hkv, max_ctx, partition, nparts_max;
   int32_t qlen;  // queries per sequence (1: plain decode)
+  int32_t num_seqs, head_dim;
+  // the merge's bookkeeping in the workspace (null without one): the call's
+  // geometry, and per (sequence, kv head) the number of partial slots
+  int32_t* ws_hdr;
+  int32_t* ws_nseg;
   // log2 of 16-token tiles per block: a (block, kv head) run of the pool is
   // 2^tile_shift consecutive tiles; the table has one entry per block
   int32_t tile_shift;
@@ -85,21 +95,32 @@ __device__ inline bool context_out_of_contract(int ctx, const KParams& P) {
 }
 
 // ------------------------------------------------------------------------
-// Matrix-core partition kernel (fp16 / bf16).  Grid (Hkv, S, partitions):
-// the hardware deals workgroups to the 8 XCDs round-robin by linear id, so
-// the kv head runs fastest and every XCD gets an even share of the
-// partitions that hold work (with the partition index fastest, the XCDs
-// serving late partitions, which are empty for short contexts, sat idle).
+// Matrix-core decode (fp16 / bf16) on a persistent grid.
 //
-// Wave w of the workgroup takes blocks w, w + 4, ... of the partition.  Its
-// physical block ids are read once per window of 64 tiles into one VGPR
-// (lane i = tile i) and picked with readlane.  K and V tiles are fetched
-// with buffer loads through a per-tile resource whose range is the tile:
-// an index past the window gets an empty range, which returns zeros
-// without touching memory, so every loop iteration issues the same loads
-// in the same order and the compiler's wait counts stay exact (a load
-// under a branch makes it wait for all outstanding loads).  The loads are
-// non-temporal: each tile is read exactly once.
+// The batch's work is one stream of 16-token tiles in (sequence, kv head,
+// tile) order; each (sequence, kv head) pair's tiles are cut into
+// partitions of P.partition tokens.  The grid holds as many workgroups as
+// fit on the GPU at once, and workgroup b takes the partitions that start
+// in the b-th equal share of the stream, so every workgroup reads the same
+// number of tiles to within one partition whatever the mix of context
+// lengths.  The partitions of one pair that fall to one workgroup form a
+// segment, folded by the online softmax in registers.  A pair split over
+// several workgroups leaves one fp32 partial (accumulator, max, sum) per
+// segment for the log-sum-exp merge, i.e. about one per workgroup instead
+// of one per partition: partials written to HBM in the middle of the read
+// stream cost far more than their bytes (with one partial per 512-token
+// partition, 16 x 32,768 tokens took 380 us; with the same stores kept in
+// one cache-resident region, 321 us).
+//
+// Inside a segment wave w takes tiles w, w + 4, ...  Its physical block ids
+// are read once per window of 64 tiles into one VGPR (lane i = tile i) and
+// picked with readlane.  K and V tiles are fetched with buffer loads
+// through a per-tile resource whose range is the tile: an index past the
+// window gets an empty range, which returns zeros without touching memory,
+// so every loop iteration issues the same loads in the same order and the
+// compiler's wait counts stay exact (a load under a branch makes it wait
+// for all outstanding loads).  The loads are non-temporal: each tile is
+// read exactly once.
 // ------------------------------------------------------------------------
 __device__ inline __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0, bytes, kBufferRsrcWord3);
@@ -109,19 +130,64 @@ __device__ inline u32x4_t load16_nt(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicyNT));
 }
 
+__device__ inline int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ inline int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+// 16-token tiles of one (sequence, kv head) pair that decode reads; 0 for a
+// sequence whose rows are written without reading (an empty context, or a
+// length outside the contract).
+__device__ inline int pair_tiles(int ctx, const KParams& P) {
+  if (ctx <= 0 || ctx < P.qlen || context_out_of_contract(ctx, P)) return 0;
+  return (ctx + kBlockTokens - 1) / kBlockTokens;
+}
+
+// What a segment costs beyond its tiles, in tiles: its start (query and
+// table loads, then the first tiles) and its merge are latency nothing else
+// in the workgroup hides.  The persistent split weighs every pair by its
+// tiles plus this, so a share of many short contexts holds fewer tiles
+// (measured on 256 lognormal GQA contexts: 267 us with 0, 254 us with 8, 255
+// with 16; 64 x U[128, 2048] MHA contexts: 196, 182, 182).
+constexpr int kSegmentCost = 8;
+
+// The call's geometry, recorded by the partition kernel for the merge.
+__device__ inline void write_header(const KParams& P) {
+  int32_t* h = P.ws_hdr;
+  h[0] = kWorkspaceMagic;
+  h[1] = P.partition;
+  h[2] = P.nparts_max;
+  h[3] = P.num_seqs * P.qlen;
+  h[4] = P.hq;
+  h[5] = P.hkv;
+  h[6] = P.head_dim;
+  h[7] = P.max_ctx;
+}
+
+template <int D>
+struct DecodeShared {
+  float m[kWaves][16];
+  float l[kWaves][16];
+  float o[kWaves][16][D + 1];
+  int64_t scan[kThreads];
+  int64_t total, base0;
+  int s0;
+  int bad;
+};
+
+// One segment: tokens [tok0, tok0 + ntok) of kv head g of sequence s, the
+// partitions of that pair that fall to this workgroup.  With nseg == 1 the
+// segment is the whole context and the rows are final; otherwise they go to
+// partial slot `seg` of the pair's nseg.
 template <typename T, int D, bool OUT_F32>
-__global__ void __launch_bounds__(kThreads)
-decode_mfma_kernel(KParams P) {
+__device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>& sh, int s, int g, int ctx,
+                                               int tok0, int ntok, int nseg, int seg) {
   constexpr int DC = D / 32;  // 16-byte chunks per lane per tile
   constexpr int NT = D / 16;  // 16-dim output tiles
   constexpr int kTileElems = kBlockTokens * D;
 
-  __shared__ float s_m[kWaves][16];
-  __shared__ float s_l[kWaves][16];
-  __shared__ float s_o[kWaves][16][D + 1];
-  __shared__ int s_bad;
-
-  const int g = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;     // head column of this lane
@@ -129,27 +195,14 @@ decode_mfma_kernel(KParams P) {
   const int G = P.hq / P.hkv;
   const int C = P.qlen;
   const int ncol = G * C;  // accumulator columns in use: (query i, head n) = column i * G + n
-  const int ctx = P.ctxs[s];
   // output / partial row of column c: query i = c / G, head g * G + c % G
   auto col_row = [&](int c) {
     return (int64_t(s) * C + c / G) * P.hq + int64_t(g) * G + c % G;
   };
 
-  if (context_out_of_contract(ctx, P) || ctx < C || ctx == 0) {
-    if (part == 0) {
-      const float v = ctx == 0 ? 0.f : __builtin_nanf("");
-      for (int idx = threadIdx.x; idx < ncol * D; idx += kThreads)
-        store_out<T, OUT_F32>(P.out, col_row(idx / D) * D + idx % D, v);
-    }
-    return;
-  }
-  const int tok0 = part * P.partition;
-  if (tok0 >= ctx) return;
-  const int ntok = min(P.partition, ctx - tok0);
   const int nblk = (ntok + kBlockTokens - 1) / kBlockTokens;
-  const int nparts = (ctx + P.partition - 1) / P.partition;
-  const int sh = P.tile_shift;
-  const int tile0 = tok0 / kBlockTokens;  // the partition's first tile in the sequence
+  const int tsh = P.tile_shift;
+  const int tile0 = tok0 / kBlockTokens;  // the segment's first tile in the sequence
   const int32_t* trow = P.tables + int64_t(s) * P.max_blocks;
 
   // Q^T as the B operand: lane supplies column n, dims 8 * (4 i + quad) + 0..7.
@@ -165,9 +218,9 @@ decode_mfma_kernel(KParams P) {
   // last key column n may attend (its query's position)
   const int last_n = ctx - C + (n < ncol ? n / G : 0);
 
-  const uint16_t* kg = P.k16 + (int64_t(g) << sh) * kTileElems;
-  const uint16_t* vg = P.v16 + (int64_t(g) << sh) * kTileElems;
-  const int64_t blk_stride = (int64_t(P.hkv) << sh) * kTileElems;
+  const uint16_t* kg = P.k16 + (int64_t(g) << tsh) * kTileElems;
+  const uint16_t* vg = P.v16 + (int64_t(g) << tsh) * kTileElems;
+  const int64_t blk_stride = (int64_t(P.hkv) << tsh) * kTileElems;
   const int voff = lane * 16;
 
   // Online softmax in the exp2 domain.  The reference max m of head n is
@@ -187,11 +240,11 @@ decode_mfma_kernel(KParams P) {
   const int ntw_all = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;  // tiles of this wave
   for (int wb = 0; wb < ntw_all; wb += kWave) {
     const int ntw = min(kWave, ntw_all - wb);
-    const int tbl = lane < ntw ? trow[(tile0 + kWaves * (wb + lane) + w) >> sh] : 0;
+    const int tbl = lane < ntw ? trow[(tile0 + kWaves * (wb + lane) + w) >> tsh] : 0;
 
     auto rsrc = [&](int i, const uint16_t* base) {
       const int phys = __builtin_amdgcn_readlane(tbl, i < ntw ? i : 0);
-      const int sub = (tile0 + kWaves * (wb + i) + w) & ((1 << sh) - 1);  // tile inside the block
+      const int sub = (tile0 + kWaves * (wb + i) + w) & ((1 << tsh) - 1);  // tile inside the block
       const bool ok = i < ntw && phys >= 0 && int64_t(phys) < P.num_blocks;
       bad |= i < ntw && !ok;  // an entry outside the pool: NaN result, nothing read
       return tile_rsrc(base + int64_t(ok ? phys : 0) * blk_stride + (ok ? sub : 0) * kTileElems,
@@ -286,44 +339,198 @@ decode_mfma_kernel(KParams P) {
   lsum += shfl_xor(lsum, 32);
 
   // ---- merge the 4 waves
-  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();  // every reader of the previous segment's merge is done
+  if (threadIdx.x == 0) sh.bad = 0;
   __syncthreads();
-  if (bad) s_bad = 1;
+  if (bad) sh.bad = 1;
   if (quad == 0) {
-    s_m[w][n] = m;
-    s_l[w][n] = lsum;
+    sh.m[w][n] = m;
+    sh.l[w][n] = lsum;
   }
   if (n < ncol) {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) s_o[w][n][16 * t + 4 * quad + r] = o[t][r];
+      for (int r = 0; r < 4; ++r) sh.o[w][n][16 * t + 4 * quad + r] = o[t][r];
   }
   __syncthreads();
-  const bool any_bad = s_bad != 0;
+  const bool any_bad = sh.bad != 0;
   for (int idx = threadIdx.x; idx < ncol * D; idx += kThreads) {
     const int h = idx / D, d = idx - (idx / D) * D;
-    float M = s_m[0][h];
+    float M = sh.m[0][h];
 #pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, s_m[ww][h]);
+    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sh.m[ww][h]);
     float L = 0.f, O = 0.f;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = fast_exp2(s_m[ww][h] - M);
-      L += f * s_l[ww][h];
-      O += f * s_o[ww][h][d];
+      const float f = fast_exp2(sh.m[ww][h] - M);
+      L += f * sh.l[ww][h];
+      O += f * sh.o[ww][h][d];
     }
     if (any_bad) O = __builtin_nanf("");
-    if (nparts == 1) {
+    if (nseg == 1) {
       store_out<T, OUT_F32>(P.out, col_row(h) * D + d, O / L);
     } else {
-      const int64_t prow = col_row(h) * P.nparts_max + part;
+      const int64_t prow = col_row(h) * P.nparts_max + seg;
       P.ws_acc[prow * D + d] = O;
       if (d == 0) {
         P.ws_m[prow] = M;
         P.ws_l[prow] = L;
       }
     }
+  }
+}
+
+// Rows of sequence s's kv head g that are written without reading: zeros
+// for an empty context, NaN for a length outside the contract.
+template <typename T, int D, bool OUT_F32>
+__device__ void write_unread_rows(const KParams& P, int s, int g, int ctx) {
+  const int G = P.hq / P.hkv, C = P.qlen, ncol = G * C;
+  const float v = ctx == 0 ? 0.f : __builtin_nanf("");
+  for (int idx = threadIdx.x; idx < ncol * D; idx += kThreads) {
+    const int c = idx / D, d = idx % D;
+    const int64_t row = (int64_t(s) * C + c / G) * P.hq + int64_t(g) * G + c % G;
+    store_out<T, OUT_F32>(P.out, row * D + d, v);
+  }
+}
+
+// One workgroup per (kv head, sequence, partition), grid (Hkv, S,
+// partitions): for batches whose longest context spans few partitions.  The
+// hardware deals workgroups to the 8 XCDs round-robin by linear id, so the
+// kv head runs fastest and every XCD gets an even share of the partitions
+// that hold work (with the partition index fastest, the XCDs serving late
+// partitions, which are empty for short contexts, sat idle).
+template <typename T, int D, bool OUT_F32>
+__global__ void __launch_bounds__(kThreads)
+decode_partition_kernel(KParams P) {
+  __shared__ DecodeShared<D> sh;
+  const int g = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+  if (g == 0 && s == 0 && part == 0 && threadIdx.x == 0 && P.ws_hdr != nullptr) write_header(P);
+  const int ctx = P.ctxs[s];
+  const bool read = pair_tiles(ctx, P) > 0;
+  const int nparts = read ? (ctx + P.partition - 1) / P.partition : 0;
+  if (part == 0 && threadIdx.x == 0 && P.ws_nseg != nullptr) P.ws_nseg[int64_t(s) * P.hkv + g] = nparts;
+  if (!read) {
+    if (part == 0) write_unread_rows<T, D, OUT_F32>(P, s, g, ctx);
+    return;
+  }
+  const int tok0 = part * P.partition;
+  if (tok0 >= ctx) return;
+  decode_segment<T, D, OUT_F32>(P, sh, s, g, ctx, tok0, min(P.partition, ctx - tok0), nparts, part);
+}
+
+// The persistent grid.  Three waves per SIMD: two tiles in flight per wave
+// then keep enough reads outstanding per CU for the HBM stream (two waves per
+// SIMD do not).
+template <typename T, int D, bool OUT_F32>
+__global__ void __launch_bounds__(kThreads, 3)
+decode_mfma_kernel(KParams P) {
+  __shared__ DecodeShared<D> sh;
+  const int S = P.num_seqs;
+  const int tid = threadIdx.x;
+
+  if (blockIdx.x == 0 && tid == 0 && P.ws_hdr != nullptr) write_header(P);
+
+  // ---- the batch's tiles (kv heads included) and this workgroup's share.
+  // Thread i sums the tiles of sequences [i * chunk, (i + 1) * chunk); wave 0
+  // turns the 256 sums into an exclusive prefix.
+  const int chunk = (S + kThreads - 1) / kThreads;
+  const int sa = min(S, tid * chunk), sb = min(S, sa + chunk);
+  auto weight = [&](int ctx) {
+    const int t = pair_tiles(ctx, P);
+    return t > 0 ? t + kSegmentCost : 0;
+  };
+  int64_t mine = 0;
+  for (int s = sa; s < sb; ++s) mine += weight(P.ctxs[s]);
+  mine *= P.hkv;
+  sh.scan[tid] = mine;
+  __syncthreads();
+  if (tid < kWave) {
+    int64_t a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = sh.scan[4 * tid + i];
+    const int64_t tot = (a[0] + a[1]) + (a[2] + a[3]);
+    int64_t inc = tot;
+#pragma unroll
+    for (int k = 1; k < kWave; k <<= 1) {
+      const int64_t y = __shfl_up(inc, k, kWave);
+      if (tid >= k) inc += y;
+    }
+    int64_t e = inc - tot;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sh.scan[4 * tid + i] = e;
+      e += a[i];
+    }
+    if (tid == kWave - 1) sh.total = inc;
+  }
+  __syncthreads();
+  const int64_t T_all = uniform64(sh.total);
+  const int ut = P.partition / kBlockTokens;  // tiles per partition
+  // Every share holds at least one partition's worth of tiles, so each
+  // workgroup between the first and the last owner of a pair's partitions
+  // owns at least one of them: a pair's segments are numbered without gaps.
+  const int64_t nw = max<int64_t>(1, min<int64_t>(gridDim.x, T_all / ut));
+  const int64_t b = blockIdx.x;
+  const int64_t lo = T_all * b / nw;
+  const int64_t hi = b < nw ? T_all * (b + 1) / nw : lo;
+  if (lo < hi) {
+    // the thread whose sequences hold tile `lo` finds the first of them
+    const int64_t e = sh.scan[tid];
+    if (e <= lo && lo < e + mine) {
+      int64_t base = e;
+      int s = sa;
+      for (; s < sb; ++s) {
+        const int64_t ts = int64_t(weight(P.ctxs[s])) * P.hkv;
+        if (base + ts > lo) break;
+        base += ts;
+      }
+      sh.s0 = s;
+      sh.base0 = base;
+    }
+  }
+  __syncthreads();
+  if (lo < hi) {
+    // pair (s, g) spans t = its tiles + kSegmentCost of the weighted stream;
+    // its partition k starts at pb + k * ut and belongs to the workgroup
+    // whose share holds that position
+    auto owner = [&](int64_t x) { return ((x + 1) * nw - 1) / T_all; };
+    int s = uniform(sh.s0);
+    int64_t base = uniform64(sh.base0);
+    while (s < S && base < hi) {
+      const int ctx = uniform(P.ctxs[s]);
+      const int t = weight(ctx);
+      if (t > 0) {
+        const int nu = (ctx + P.partition - 1) / P.partition;
+        for (int g = 0; g < P.hkv; ++g) {
+          const int64_t pb = base + int64_t(g) * t + kSegmentCost;
+          if (pb >= hi) break;
+          const int64_t last = pb + int64_t(nu - 1) * ut;  // the pair's last partition
+          if (last < lo) continue;
+          const int k0 = lo <= pb ? 0 : int((lo - pb + ut - 1) / ut);
+          const int k1 = min(nu - 1, int((hi - pb + ut - 1) / ut) - 1);
+          if (k0 > k1) continue;
+          const int64_t first_owner = owner(pb);
+          const int nseg = int(owner(last) - first_owner + 1);
+          const int tok0 = k0 * P.partition;
+          const int ntok = min((k1 + 1) * P.partition, ctx) - tok0;
+          decode_segment<T, D, OUT_F32>(P, sh, s, g, ctx, tok0, ntok, nseg, int(b - first_owner));
+          if (k0 == 0 && P.ws_nseg != nullptr && tid == 0) P.ws_nseg[int64_t(s) * P.hkv + g] = nseg;
+        }
+      }
+      base += int64_t(t) * P.hkv;
+      ++s;
+    }
+  }
+
+  // rows outside the stream: an empty context gives zeros, a length outside
+  // the contract NaN (reported, nothing read)
+  for (int s = blockIdx.x; s < S; s += gridDim.x) {
+    const int ctx = P.ctxs[s];
+    if (pair_tiles(ctx, P) > 0) continue;
+    for (int gg = 0; gg < P.hkv; ++gg) write_unread_rows<T, D, OUT_F32>(P, s, gg, ctx);
+    if (P.ws_nseg != nullptr)
+      for (int gg = tid; gg < P.hkv; gg += kThreads) P.ws_nseg[int64_t(s) * P.hkv + gg] = 0;
   }
 }
 
@@ -351,8 +558,13 @@ decode_f32_kernel(KParams P) {
   const int g = h / G;
   const int ctx = P.ctxs[s];
   const int64_t row = int64_t(s) * P.hq + h;
+  const bool no_read = context_out_of_contract(ctx, P) || ctx == 0;
+  // every partition is its own partial slot; the merge reads how many
+  if (part == 0 && h % G == 0 && threadIdx.x == 0 && P.ws_nseg != nullptr)
+    P.ws_nseg[int64_t(s) * P.hkv + g] = no_read ? 0 : (ctx + P.partition - 1) / P.partition;
+  if (part == 0 && h == 0 && s == 0 && threadIdx.x == 0 && P.ws_hdr != nullptr) write_header(P);
 
-  if (context_out_of_contract(ctx, P) || ctx == 0) {
+  if (no_read) {
     if (part == 0) {
       const float v = ctx == 0 ? 0.f : __builtin_nanf("");
       for (int d = threadIdx.x; d < D; d += kThreads) static_cast<float*>(P.out)[row * D + d] = v;
@@ -483,16 +695,20 @@ decode_f32_kernel(KParams P) {
 }
 
 // ------------------------------------------------------------------------
-// Log-sum-exp merge of the partition partials.  Grid (Hq, S), D threads:
+// Log-sum-exp merge of the partials.  Grid (Hq, S * qlen), D threads:
 //   M = max_j m_j,  w_j = 2^(m_j - M),  out = sum_j w_j acc_j / sum_j w_j l_j
-// Thread d owns output dim d.  A row of up to kReduceFew partitions loads
-// all its partials at once; longer rows compute the weights of up to
-// kReduceChunk partitions at a time once into LDS and read every
-// partition's row with one coalesced load.  Sums run in partition order, so
-// the result is deterministic.
+// over the partial slots j of the row's (sequence, kv head) pair, whose
+// count the partition kernel recorded (1: the row is already final).
+// Thread d owns output dim d.  A row of up to kReduceFew slots loads all
+// its partials at once; longer rows compute the weights of up to
+// kReduceChunk slots at a time once into LDS and read every slot's row
+// with one coalesced load.  Sums run in slot order, so the result is
+// deterministic.  A workspace whose header does not match this call's
+// geometry (not filled by the partition launch of the same sizes) gives
+// NaN rows instead of a merge at the wrong stride.
 // ------------------------------------------------------------------------
 constexpr int kReduceChunk = 256;
-constexpr int kReduceFew = 8;  // rows with at most this many partitions take the one-pass path
+constexpr int kReduceFew = 8;  // rows with at most this many slots take the one-pass path
 
 template <typename T, int D, bool OUT_F32>
 __global__ void __launch_bounds__(D)
@@ -503,15 +719,22 @@ decode_reduce_kernel(KParams P) {
   const int h = blockIdx.x, sq = blockIdx.y;  // sq = s * qlen + query
   const int s = sq / P.qlen;
   const int d = threadIdx.x;
-  const int ctx = P.ctxs[s];
-  if (context_out_of_contract(ctx, P) || ctx < P.qlen || ctx <= P.partition) return;  // written by the partition kernel
-  const int nparts = (ctx + P.partition - 1) / P.partition;
-  const int64_t prow0 = (int64_t(sq) * P.hq + h) * P.nparts_max;
+  const int64_t orow = int64_t(sq) * P.hq + h;
+  const int32_t* hd = P.ws_hdr;
+  if (hd[0] != kWorkspaceMagic || hd[1] != P.partition || hd[2] != P.nparts_max || hd[3] != P.num_seqs * P.qlen ||
+      hd[4] != P.hq || hd[5] != P.hkv || hd[6] != D || hd[7] != P.max_ctx) {
+    store_out<T, OUT_F32>(P.out, orow * D + d, __builtin_nanf(""));
+    return;
+  }
+  // partial slots of the row's pair, at most the partitions the workspace holds
+  const int nparts = min(P.ws_nseg[int64_t(s) * P.hkv + h / (P.hq / P.hkv)], P.nparts_max);
+  if (nparts <= 1) return;  // written by the partition kernel
+  const int64_t prow0 = orow * P.nparts_max;
 
   if (nparts <= kReduceFew) {
-    // few partitions (the common case): every partial of the row is loaded
-    // at once, with no barrier, so the merge costs one round trip to memory
-    // (slots past the row's last partition reload that one and weigh 0)
+    // few slots (the common case): every partial of the row is loaded at
+    // once, with no barrier, so the merge costs one round trip to memory
+    // (entries past the row's last slot reload that one and weigh 0)
     float mj[kReduceFew], lj[kReduceFew], aj[kReduceFew];
 #pragma unroll
     for (int j = 0; j < kReduceFew; ++j) {
@@ -530,7 +753,7 @@ decode_reduce_kernel(KParams P) {
       L += wj * lj[j];
       O += wj * aj[j];
     }
-    store_out<T, OUT_F32>(P.out, (int64_t(sq) * P.hq + h) * D + d, O / L);
+    store_out<T, OUT_F32>(P.out, orow * D + d, O / L);
     return;
   }
 
@@ -557,7 +780,7 @@ decode_reduce_kernel(KParams P) {
       O += wj * acc[int64_t(j0 + j) * D];
     }
   }
-  store_out<T, OUT_F32>(P.out, (int64_t(sq) * P.hq + h) * D + d, O / L);
+  store_out<T, OUT_F32>(P.out, orow * D + d, O / L);
 }
 
 KParams make_params(const DecodeArgs& a) {
@@ -584,18 +807,58 @@ KParams make_params(const DecodeArgs& a) {
   p.nparts_max = a.num_partitions;
   p.qlen = a.q_len;
   p.tile_shift = a.tile_shift;
+  p.num_seqs = a.num_seqs;
+  p.head_dim = a.head_dim;
+  p.ws_hdr = a.ws_hdr;
+  p.ws_nseg = a.ws_nseg;
   return p;
+}
+
+// Workgroups of `kernel` (kThreads threads) that fit on the current device
+// at once: its occupancy per CU times the CU count, looked up once per device.
+template <typename K>
+int64_t resident_workgroups(K kernel) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int64_t> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = -1;
+  if (dev >= 0) {
+    const int64_t c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev < 0 ? 0 : dev) != hipSuccess || cus <= 0)
+    cus = 1;
+  const int64_t n = int64_t(per_cu) * cus;
+  if (dev >= 0) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// One resident grid: as many workgroups as fit at once, never more than
+// there are partitions in the batch's upper bound.
+template <typename T, int D, bool OUT_F32>
+hipError_t launch_mfma_grid(const DecodeArgs& a, const KParams& p) {
+  const auto kernel = decode_mfma_kernel<T, D, OUT_F32>;
+  const int64_t units = int64_t(a.num_seqs) * a.num_kv_heads * std::max(1, a.num_partitions);
+  const int64_t n = std::max<int64_t>(1, std::min(resident_workgroups(kernel), units));
+  hipLaunchKernelGGL(kernel, dim3(unsigned(n)), dim3(kThreads), 0, a.stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D, bool OUT_F32>
+hipError_t launch_partition_grid(const DecodeArgs& a, const KParams& p) {
+  const dim3 grid(unsigned(a.num_kv_heads), unsigned(a.num_seqs), unsigned(a.num_partitions));
+  hipLaunchKernelGGL((decode_partition_kernel<T, D, OUT_F32>), grid, dim3(kThreads), 0, a.stream, p);
+  return hipGetLastError();
 }
 
 template <typename T, int D>
 hipError_t launch_mfma(const DecodeArgs& a, const KParams& p) {
-  const dim3 grid(unsigned(a.num_kv_heads), unsigned(a.num_seqs), unsigned(a.num_partitions));
-  if (a.out_f32) {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, true>), grid, dim3(kThreads), 0, a.stream, p);
-  } else {
-    hipLaunchKernelGGL((decode_mfma_kernel<T, D, false>), grid, dim3(kThreads), 0, a.stream, p);
-  }
-  return hipGetLastError();
+  if (decode_uses_persistent_grid(a.num_partitions))
+    return a.out_f32 ? launch_mfma_grid<T, D, true>(a, p) : launch_mfma_grid<T, D, false>(a, p);
+  return a.out_f32 ? launch_partition_grid<T, D, true>(a, p) : launch_partition_grid<T, D, false>(a, p);
 }
 
 template <typename T, int D>
@@ -624,6 +887,21 @@ hipError_t launch_decode_partitions(const DecodeArgs& a) {
   }
   if (a.dtype == PA_BF16) return a.head_dim == 64 ? launch_mfma<Bf16, 64>(a, p) : launch_mfma<Bf16, 128>(a, p);
   return a.head_dim == 64 ? launch_mfma<F16, 64>(a, p) : launch_mfma<F16, 128>(a, p);
+}
+
+int64_t decode_resident_workgroups(pa_dtype_t dtype, int32_t head_dim, bool out_f32) {
+  if (dtype == PA_BF16) {
+    if (head_dim == 64)
+      return out_f32 ? resident_workgroups(decode_mfma_kernel<Bf16, 64, true>)
+                     : resident_workgroups(decode_mfma_kernel<Bf16, 64, false>);
+    return out_f32 ? resident_workgroups(decode_mfma_kernel<Bf16, 128, true>)
+                   : resident_workgroups(decode_mfma_kernel<Bf16, 128, false>);
+  }
+  if (head_dim == 64)
+    return out_f32 ? resident_workgroups(decode_mfma_kernel<F16, 64, true>)
+                   : resident_workgroups(decode_mfma_kernel<F16, 64, false>);
+  return out_f32 ? resident_workgroups(decode_mfma_kernel<F16, 128, true>)
+                 : resident_workgroups(decode_mfma_kernel<F16, 128, false>);
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a) {

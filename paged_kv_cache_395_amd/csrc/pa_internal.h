@@ -29,6 +29,11 @@ struct DecodeArgs {
   int32_t num_partitions;  // ceil(max_context_len / partition)
   int32_t q_len;           // queries per sequence (1: plain decode)
   int32_t tile_shift;      // log2(block_size / 16)
+  // workspace (all null when num_partitions <= 1): the call's geometry for
+  // the merge's check, the partial-slot count of every (sequence, kv head),
+  // and the partial slots
+  int32_t* ws_hdr;         // [8]
+  int32_t* ws_nseg;        // [S][Hkv]
   float* ws_acc;           // [S][q_len][Hq][num_partitions][D]
   float* ws_m;             // [S][q_len][Hq][num_partitions]
   float* ws_l;             // [S][q_len][Hq][num_partitions]
@@ -36,8 +41,20 @@ struct DecodeArgs {
   hipStream_t stream;
 };
 
+// fp16 / bf16 decode runs one workgroup per partition while the longest
+// context spans at most kPartitionGridMax partitions, and on the persistent
+// grid beyond: there, one partial per partition would cost more than the
+// per-partition grid's better balance gains (measured on 16 x 32,768 tokens
+// at 512-token partitions: 380 us per partition, 333 us persistent; on 64
+// MHA contexts U[128, 2048] at 4 partitions: 176 us per partition, 182 us
+// persistent).
+constexpr int32_t kPartitionGridMax = 4;
+inline bool decode_uses_persistent_grid(int32_t num_partitions) { return num_partitions > kPartitionGridMax; }
+
 hipError_t launch_decode_partitions(const DecodeArgs& a);
 hipError_t launch_decode_reduce(const DecodeArgs& a);
+// Workgroups of the fp16 / bf16 decode kernel resident at once on the current device.
+int64_t decode_resident_workgroups(pa_dtype_t dtype, int32_t head_dim, bool out_f32);
 
 struct PrefillArgs {
   void* out;

@@ -115,7 +115,8 @@ def test_multi_query_workspace_scales_with_queries():
     assert L.pa_decode_multi_workspace_bytes(8, 1, 32, 8, 128, 5000, 512) == one
     align = lambda b: (b + 255) // 256 * 256  # noqa: E731
     rows = 8 * 4 * 32 * 10
-    assert L.pa_decode_multi_workspace_bytes(8, 4, 32, 8, 128, 5000, 512) == align(rows * 128 * 4) + 2 * align(rows * 4)
+    assert L.pa_decode_multi_workspace_bytes(8, 4, 32, 8, 128, 5000, 512) == (
+        256 + align(8 * 8 * 4) + align(rows * 128 * 4) + 2 * align(rows * 4))
     assert L.pa_decode_multi(None, 0, None, 4, None, None, None, 4, None, 0, 8, 2, 128, 16, 10, 0.1, 64, 0, None, 0,
                              _lib.PA_BF16, NULL) == _lib.PA_OK
 
@@ -125,16 +126,18 @@ def test_decode_with_no_sequences_is_a_no_op():
 
 
 def test_workspace_size_formula():
-    # single partition: no workspace; otherwise acc + m + l, 256-byte aligned
+    # single partition: no workspace; otherwise a 256-byte header, one slot
+    # count per (sequence, kv head), then acc + m + l, 256-byte aligned
     assert L.pa_decode_workspace_bytes(8, 32, 8, 128, 512, 512) == 0
     S, Hq, Hkv, D, n = 8, 32, 8, 128, 3
     rows = S * Hq * n
     align = lambda b: (b + 255) // 256 * 256  # noqa: E731
-    assert L.pa_decode_workspace_bytes(S, Hq, Hkv, D, 1100, 512) == align(rows * D * 4) + 2 * align(rows * 4)
+    head = 256 + align(S * Hkv * 4)
+    assert L.pa_decode_workspace_bytes(S, Hq, Hkv, D, 1100, 512) == head + align(rows * D * 4) + 2 * align(rows * 4)
     # the default partition is reported and sizes the workspace
     p = L.pa_decode_partition_size(S, Hkv, 1100, 0)
     n0 = -(-1100 // p)
-    want = 0 if n0 == 1 else align(S * Hq * n0 * D * 4) + 2 * align(S * Hq * n0 * 4)
+    want = 0 if n0 == 1 else head + align(S * Hq * n0 * D * 4) + 2 * align(S * Hq * n0 * 4)
     assert L.pa_decode_workspace_bytes(S, Hq, Hkv, D, 1100, 0) == want
     assert L.pa_decode_partition_size(S, Hkv, 1100, 48) == 48
     assert L.pa_decode_partition_size(S, Hkv, 1100, 24) == -1

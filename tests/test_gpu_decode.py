@@ -49,6 +49,61 @@ def test_decode_full_size_matches_oracle(name):
     say(f"[decode] {name} {stats}")
 
 
+def test_long_context_at_its_stated_partitions_matches_oracle():
+    """16 x 32,768 tokens, 64/8 heads, at the 512-token partitions the
+    workload states (64 partitions per context, merged by log-sum-exp): the
+    launch the benchmark times."""
+    p = prepared("longctx_bf16")
+    assert p.w.partition_size == 512
+    say(f"[decode] longctx_bf16 P=512 max_ctx={p.max_ctx}")
+    d = p.device()
+    p.write_step(d)
+    out = p.gpu_decode(d, partition=p.w.partition_size)
+    torch.cuda.synchronize()
+    stats = assert_close(out_f64(out), p.oracle_decode(), "bf16", "longctx P=512")
+    say(f"[decode] longctx_bf16 P=512 {stats}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_merge_of_more_than_256_slots_per_row(dtype):
+    """One sequence of 8,192 tokens and one kv head at 16-token partitions:
+    more partial slots per row than the merge weighs in one round (256)."""
+    name = "longctx_bf16"
+    p = Prepared(make_workload(name, num_seqs=1, ctx=8192, chunk=1, Hq=8, Hkv=1,
+                               dtype=dtype, head_dim=128 if dtype == "bf16" else 64))
+    d = p.device()
+    p.write_step(d)
+    out = p.gpu_decode(d, partition=16)
+    assert_close(out_f64(out), p.oracle_decode(), dtype, f"{dtype} P=16")
+
+
+def test_reduce_with_other_sizes_than_the_partition_launch_gives_nan_rows():
+    """pa_decode_reduce reads the partials at the stride the partition launch
+    used; a call with another partition size or length bound is detected
+    from the workspace header and reported as NaN rows."""
+    from paged_kv_cache_395_amd import ops
+    p = prepared("gqa8b_bf16", num_seqs=12, hi=1500)
+    d = p.device()
+    p.write_step(d)
+    S, Hq, Hkv, D = 12, 32, 8, 128
+    ws = torch.empty(ops.decode_workspace_bytes(S, Hq, Hkv, D, p.max_ctx, 64), dtype=torch.uint8, device="cuda")
+    out = torch.empty(S, Hq, D, dtype=torch.float32, device="cuda")
+    ops.decode_partitions(out, d["q"], d["k"], d["v"], d["table"], d["ctx"], p.w.scale, p.max_ctx, 64, ws)
+    ops.decode_reduce(out, d["ctx"], Hkv, p.max_ctx, 64, ws)
+    assert_close(out_f64(out), p.oracle_decode(), "bf16", "matched")
+    # same workspace, another partition size (a smaller stride): every row NaN
+    ops.decode_reduce(out, d["ctx"], Hkv, p.max_ctx, 128, ws)
+    assert torch.isnan(out).all()
+    # another length bound
+    ops.decode_partitions(out, d["q"], d["k"], d["v"], d["table"], d["ctx"], p.w.scale, p.max_ctx, 64, ws)
+    ops.decode_reduce(out, d["ctx"], Hkv, p.max_ctx - 16, 64, ws)
+    assert torch.isnan(out).all()
+    # a workspace no partition launch wrote
+    ws.zero_()
+    ops.decode_reduce(out, d["ctx"], Hkv, p.max_ctx, 64, ws)
+    assert torch.isnan(out).all()
+
+
 @pytest.mark.parametrize("name,kw", REDUCED, ids=[r[0] for r in REDUCED])
 def test_decode_reduced_matches_oracle(name, kw):
     p = prepared(name, **kw)
@@ -89,8 +144,10 @@ def ordered_bits(bits: np.ndarray, dt: str) -> np.ndarray:
     return np.where(x & 0x8000, -(x & 0x7FFF), x)
 
 
-@pytest.mark.parametrize("partition", [16, 64, 512, 2048, 0])
+@pytest.mark.parametrize("partition", [16, 64, 256, 512, 2048, 0])
 def test_partition_sizes_agree(partition):
+    # up to 4 partitions of the longest context (1,500 tokens): one workgroup
+    # per partition; more: the persistent grid
     p = prepared("gqa8b_bf16", num_seqs=12, hi=1500)
     d = p.device()
     p.write_step(d)
