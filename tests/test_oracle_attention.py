@@ -409,3 +409,44 @@ def test_tolerance_readings_hold_on_a_realistic_case():
     e1 = np.linalg.norm(one - exact) / np.linalg.norm(exact)
     e2 = np.linalg.norm(two - exact) / np.linalg.norm(exact)
     assert e1 > 1e-3 > 1e-5 > e2
+
+
+# ------------------------------------------------- whole-block copies (CoW, swap)
+
+def _labelled_pool(labels, codes, heads, run):
+    """K and V pools whose block i holds label labels[i] (fixture rule)."""
+    e = np.arange(run, dtype=np.float64)
+    k = np.empty((len(labels), heads, run), dtype=np.float32)
+    v = np.empty_like(k)
+    for i, lab in enumerate(labels):
+        for h in range(heads):
+            k[i, h] = 1000 * (10 * codes[lab] + h) + e
+            v[i, h] = 1000 * (10 * codes[lab] + h) + e + 500
+    return k, v
+
+
+def _assert_holds(k, v, labels, codes):
+    want_k, want_v = _labelled_pool(labels, codes, k.shape[1], k.shape[2])
+    assert np.array_equal(k, want_k)
+    assert np.array_equal(v, want_v)
+
+
+def test_copy_blocks_by_hand():
+    g = load("block_copies_by_hand.txt")
+    codes, H, run = g["label_codes"], g["num_kv_heads"], g["block_size"] * g["head_dim"]
+    k, v = _labelled_pool(g["cow_pool"], codes, H, run)
+    A.copy_blocks(k, v, np.array(g["cow_pairs"], dtype=np.int64))
+    _assert_holds(k, v, g["cow_after"], codes)
+
+
+def test_swap_blocks_by_hand():
+    g = load("block_copies_by_hand.txt")
+    codes, H, run = g["label_codes"], g["num_kv_heads"], g["block_size"] * g["head_dim"]
+    dk, dv = _labelled_pool(g["swap_out_device"], codes, H, run)
+    hk, hv = _labelled_pool(g["swap_out_host"], codes, H, run)
+    A.swap_blocks(hk, hv, dk, dv, np.array(g["swap_out_pairs"], dtype=np.int64))
+    _assert_holds(hk, hv, g["swap_out_host_after"], codes)
+    _assert_holds(dk, dv, g["swap_out_device_after"], codes)
+    A.swap_blocks(dk, dv, hk, hv, np.array(g["swap_in_pairs"], dtype=np.int64))
+    _assert_holds(dk, dv, g["swap_in_device_after"], codes)
+    _assert_holds(hk, hv, g["swap_in_host_after"], codes)

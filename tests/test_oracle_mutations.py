@@ -99,6 +99,23 @@ MUTATIONS = [
      ("oracle",)),
     (oracle.block_manager, "RefBlockManager.add_seq_tokens", "if i < full:", "if i <= full:",
      PC.test_only_full_blocks_are_cached_and_a_miss_ends_the_run, ("oracle",)),
+    (oracle.attention, "copy_blocks", "k_cache[dst] = k_cache[src]", "k_cache[src] = k_cache[dst]",
+     PA.test_copy_blocks_by_hand, ()),
+    (oracle.attention, "copy_blocks", "v_cache[dst] = v_cache[src]", "pass",
+     PA.test_copy_blocks_by_hand, ()),
+    (oracle.attention, "copy_blocks", "k_cache[dst] = k_cache[src]", "pass",
+     PA.test_copy_blocks_by_hand, ()),
+    (oracle.attention, "copy_blocks", "k_cache[dst] = k_cache[src]", "k_cache[dst, 0] = k_cache[src, 0]",
+     PA.test_copy_blocks_by_hand, ()),
+    (oracle.attention, "swap_blocks", "dst_k[dst] = src_k[src]", "dst_k[src] = src_k[dst]",
+     PA.test_swap_blocks_by_hand, ()),
+    (oracle.attention, "swap_blocks", "dst_v[dst] = src_v[src]", "pass",
+     PA.test_swap_blocks_by_hand, ()),
+    (oracle.attention, "swap_blocks", "dst_k[dst] = src_k[src]", "pass",
+     PA.test_swap_blocks_by_hand, ()),
+    (oracle.attention, "swap_blocks", "for src, dst in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):",
+     "for dst, src in np.asarray(pairs, dtype=np.int64).reshape(-1, 2):",
+     PA.test_swap_blocks_by_hand, ()),
     (oracle.block_manager, "RefBlockManager._take", "b, _ = self.lru.popitem(last=False)",
      "b, _ = self.lru.popitem(last=True)", PC.test_released_prefixes_wait_in_lru_and_are_evicted_from_their_end,
      ("oracle",)),
