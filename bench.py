@@ -32,6 +32,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "paged decode KV GB/s and % of HBM peak (seqs/s) at 1 MI355X"
+# The headline: the largest single-GPU decode configuration, 16 sequences at
+# 32,768 tokens, 64/8 heads, bf16, at its stated 512-token partitions.  The
+# other gated decode configurations, and the headline's at the library's
+# default partition, are reported in the same line (kernel figures only).
+HEADLINE = "longctx_bf16"
+EXTRA_CONFIGS = ["mha7b_f16", "gqa8b_bf16", "longctx_bf16"]
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix, published
 ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
@@ -410,7 +416,7 @@ def bench_serving(args) -> None:
                  "preempted_recompute": stats["recompute"]},
         "admitted": stats["admitted"], "finished": stats["finished"],
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "decode_mfma_kernel",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None, "kernel": "decode_partition_kernel",
                      "algorithmic_bytes_per_launch": round(read_bytes / K, 1)},
     }
     if unique is not None:
@@ -437,7 +443,6 @@ def bench_serving(args) -> None:
     print(json.dumps(rec), flush=True)
 
 
-DECODE_KERNEL = "decode_mfma_kernel"
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
@@ -484,7 +489,8 @@ def summarize_prefill(args, rec) -> None:
     wcyc, _ = avg(rows, "SQ_WAVE_CYCLES")
     gui, _ = avg(grbm, "GRBM_GUI_ACTIVE")
     pf = rec["prefill"]
-    base = "python -u bench.py --workload %s --steps 2 --warmup 1 --cold-iters 0 --no-cpu-baseline" % wl
+    base = ("python -u bench.py --workload %s --steps 2 --warmup 1 --cold-iters 0 --no-cpu-baseline "
+            "--no-extra-configs" % wl)
     md = [f"# Matrix-core utilisation of `prefill_mfma_kernel`: {wl}", "",
           "Two counter passes of the same command (one per counter block):", "", "```",
           f"timeout -s KILL 180 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
@@ -518,15 +524,17 @@ def summarize(args) -> None:
     if args.trace_dir is None:
         return
     alg = rec["roofline"]["algorithmic_bytes_per_launch"]
+    kname = rec["roofline"]["kernel"]
     prof = os.path.join(ROOT, "profiles")
     base = "python -u bench.py --workload %s" % wl
     serving = "kernels_ms" not in rec  # the serving rows run their own step count and warm-up
     # the bench's own step count, so the trace's mean decode launch is the launch bench.py times
-    run_args = "" if serving else " --cold-iters 3"
+    run_args = "" if serving else " --cold-iters 3 --no-extra-configs"
     trace_cmd = (f"rocprofv3 --kernel-trace --stats --output-format csv -d {args.trace_dir} -o trace -- "
                  f"{base}{run_args} --no-cpu-baseline")
     pmc_cmd = (f"timeout -s KILL 120 rocprofv3 --pmc {{counter}} --output-format csv -d {{out_dir}} "
-               f"-o {{tag}} -- {base} --steps 3 --warmup 1 --cold-iters 0 --no-cpu-baseline --copy-probe-mib 1024")
+               f"-o {{tag}} -- {base} --steps 3 --warmup 1 --cold-iters 0 --no-cpu-baseline --no-extra-configs "
+               f"--copy-probe-mib 1024")
     lines = [f"# Kernel trace: {wl}", "", f"{rec['config']['workload']}", "",
              "Command (from the repository root, one MI355X):", "", "```", trace_cmd, "```", "",
              "| kernel | calls | avg us | min us | max us | % time |", "|---|---|---|---|---|---|"]
@@ -555,14 +563,14 @@ def summarize(args) -> None:
             alg = json.loads([l for l in f if l.startswith("{")][-1])["roofline"]["algorithmic_bytes_per_launch"]
     fetch = _csv_rows(args.fetch_dir, "counter_collection.csv")
     write = _csv_rows(args.write_dir, "counter_collection.csv")
-    f_dec, n_dec = _per_dispatch(fetch, DECODE_KERNEL)
-    w_dec, _ = _per_dispatch(write, DECODE_KERNEL)
+    f_dec, n_dec = _per_dispatch(fetch, kname)
+    w_dec, _ = _per_dispatch(write, kname)
     f_cp = _largest_dispatch(fetch, COPY_KERNEL)
     w_cp = _largest_dispatch(write, COPY_KERNEL)
     probe_kib = 1024 * 1024
     fs, ws = probe_kib / f_cp, probe_kib / w_cp  # each counter against a copy of known size
     hbm_f, hbm_w = f_dec * 1024 * fs, w_dec * 1024 * ws
-    out = {"workload": wl, "kernel": DECODE_KERNEL, "kernel_source_sha": kernel_source_hash(),
+    out = {"workload": wl, "kernel": kname, "kernel_source_sha": kernel_source_hash(),
            "fetch_kib_per_dispatch_raw": f_dec, "write_kib_per_dispatch_raw": w_dec, "dispatches": n_dec,
            "copy_probe_kib": probe_kib, "copy_fetch_kib_raw": f_cp, "copy_write_kib_raw": w_cp,
            "fetch_scale": fs, "write_scale": ws, "hbm_fetch_bytes_per_launch": hbm_f,
@@ -572,7 +580,7 @@ def summarize(args) -> None:
                         pmc_cmd.format(counter="WRITE_SIZE", out_dir=args.write_dir, tag="write")]}
     with open(os.path.join(prof, f"decode_partitions_{wl}_traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
-    md = [f"# HBM traffic of `{DECODE_KERNEL}`: {wl}", "",
+    md = [f"# HBM traffic of `{kname}`: {wl}", "",
           "Two counter passes (one counter each), same command otherwise:", "", "```"] + out["commands"] + [
           "```", "",
           f"- FETCH_SIZE per dispatch (raw): {f_dec:.1f} KiB over {n_dec} dispatches",
@@ -598,11 +606,15 @@ def main():
                          "serving: 200)")
     ap.add_argument("--warmup", type=int, default=None,
                     help="untimed steps first (5; 150 for serving_bf16, which fills its batch meanwhile)")
-    ap.add_argument("--workload", default="mha7b_f16",
+    ap.add_argument("--workload", default=HEADLINE,
                     choices=["tiny_f32", "mha7b_f16", "gqa8b_bf16", "shared_prefix_bf16", "longctx_bf16",
                              "specdec_bf16", "serving_bf16", "serving_prefix_bf16", "mha7b_f16_bs32",
                              "mha7b_f16_bs64", "gqa8b_bf16_bs32"])
-    ap.add_argument("--partition", type=int, default=0, help="tokens per context partition (0 = the library's choice)")
+    ap.add_argument("--partition", type=int, default=None,
+                    help="tokens per context partition (0 = the library's choice; default: the workload's stated "
+                         "partition, 512 for longctx_bf16, else the library's choice)")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the other decode configurations the headline line reports")
     ap.add_argument("--append-meta", choices=["pinned", "args"], default="pinned",
                     help="where the step's slots, positions and lengths reach the cache write: pinned host memory "
                          "read by the kernel, or the kernel arguments (pa_append_step_host)")
@@ -642,12 +654,42 @@ def main():
 
     import torch
 
-    from paged_kv_cache_395_amd import BlockManager, ops
-    from workloads import make_workload, run_program
+    from workloads import make_workload
 
     torch.cuda.set_device(0)
-    dev = torch.device("cuda", 0)
     w = make_workload(args.workload)
+    partition = w.partition_size if args.partition is None else args.partition
+    rec = bench_decode(w, partition, args, full=True)
+    if args.workload == HEADLINE and not args.no_extra_configs:
+        # the other gated decode configurations (and the headline's at the
+        # library's default partition), kernel figures only, same step
+        del w
+        torch.cuda.empty_cache()
+        extra = {}
+        for name in EXTRA_CONFIGS:
+            wx = make_workload(name)
+            px = wx.partition_size if name != HEADLINE else 0
+            r = bench_decode(wx, px, argparse.Namespace(**dict(vars(args), steps=None, warmup=None)), full=False)
+            extra[name if name != HEADLINE else f"{name}_default_partition"] = r
+            del wx
+            torch.cuda.empty_cache()
+        rec["other_configs"] = extra
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(make_workload(args.workload))
+    print(json.dumps(rec), flush=True)
+
+
+def bench_decode(w, partition: int, args, full: bool = True) -> dict:
+    """Time the decode step of workload ``w`` at ``partition`` tokens per
+    context partition (0: the library's choice).  With ``full`` the record
+    is the benchmark line (ceilings, cold-cache decode, prefill); otherwise
+    the kernel figures only."""
+    import torch
+
+    from paged_kv_cache_395_amd import BlockManager, ops
+    from workloads import run_program
+
+    dev = torch.device("cuda", 0)
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
 
     def to_dev(a):
@@ -658,56 +700,71 @@ def main():
 
     S, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
     multi = w.lengths.get("mode") == "multi"  # each step appends and verifies w.append drafted tokens per sequence
-    # decode workloads append one token per step (the verification workload w.append); the chunk
-    # workload writes its chunk once and then decodes in place
-    grows = w.append == 1 or multi
+    # tokens every sequence appends in a timed step: the verification workload
+    # its w.append drafted tokens, the others one.  The long-context workload
+    # first writes its w.append-token chunk (untimed); its steps then decode
+    # one new token per sequence like the rest.
+    per_step = w.append if multi else 1
+    chunk = w.append > 1 and not multi
     bm = BlockManager(w.num_blocks, block_size=w.block_size, free_order=w.free_order)
     run_program(bm, w.program)
-    if args.steps is None or args.warmup is None:
-        # the longest run (about 40-60 ms timed, so a host stall of a few ms
+    k_pool, v_pool = to_dev(w.k_pool), to_dev(w.v_pool)
+    if chunk:
+        slots0, cow0 = bm.append_tokens(np.ascontiguousarray(w.step_seqs, dtype=np.int64))
+        if len(cow0):
+            raise RuntimeError("copy-on-write is not expected in this workload")
+        ops.reshape_and_cache(to_dev(w.step_rows("k")), to_dev(w.step_rows("v")), k_pool, v_pool,
+                              torch.from_numpy(slots0).to(dev))
+        torch.cuda.synchronize()
+    steps, warmup = args.steps, args.warmup
+    if steps is None or warmup is None:
+        # the longest run (about 40-80 ms timed, so a host stall of a few ms
         # does not decide the figure) whose appends the pool can hold
         for k in (200, 100, 50, 20):
-            if not grows or appends_fit(bm, w, (k + k // 10 + 2) * w.append):
+            if appends_fit(bm, w, (k + k // 10 + 2) * per_step):
                 break
-        args.steps = k if args.steps is None else args.steps
-        args.warmup = max(5, k // 10) if args.warmup is None else args.warmup
-    extra = (args.warmup + args.steps + 2) * w.append if grows else 0
+        steps = k if steps is None else steps
+        warmup = max(5, k // 10) if warmup is None else warmup
+    extra = (warmup + steps + 2) * per_step
     maxB = w.max_blocks_per_seq(extra)
     pad = w.num_blocks + 1  # never read
 
-    k_pool, v_pool = to_dev(w.k_pool), to_dev(w.v_pool)
-    step_k, step_v = to_dev(w.step_rows("k")), to_dev(w.step_rows("v"))
+    if multi:
+        step_k, step_v = to_dev(w.step_rows("k")), to_dev(w.step_rows("v"))
+    else:  # one row per sequence: each sequence's last drawn row
+        step_k = to_dev(np.ascontiguousarray(w.step_k[:, -1]))
+        step_v = to_dev(np.ascontiguousarray(w.step_v[:, -1]))
     q = to_dev(w.q) if multi else to_dev(w.decode_q)
     out = torch.empty(tuple(q.shape), dtype=tdt, device=dev)
 
     # block tables and context lengths live on the device: copied once here,
     # then patched in place by each step's cache write from the step's slots
-    n_tok = S * w.append
+    n_tok = S * per_step
     table0, ctx0 = bm.block_table(np.ascontiguousarray(w.batch, dtype=np.int64), maxB, pad=pad)
     d_table = torch.from_numpy(table0).to(dev)
     d_ctx = torch.from_numpy(ctx0).to(dev)
     host_ctx = ctx0.astype(np.int64)  # the host's copy of the lengths (the block manager's counts)
-    final_ctx = int(w.lengths["final_ctx"].max()) + extra
-    first_ctx = int(w.lengths["final_ctx"].max())
-    ws_need = max(ops.StepPlan.workspace_bytes_for(S, w.append if multi else 1, Hq, Hkv, D, c, args.partition)
+    first_ctx = int(host_ctx.max())
+    final_ctx = first_ctx + extra
+    ws_need = max(ops.StepPlan.workspace_bytes_for(S, per_step, Hq, Hkv, D, c, partition)
                   for c in range(first_ctx, final_ctx + 1))
     ws = torch.empty(max(1, ws_need), dtype=torch.uint8, device=dev)
-    seqs = np.ascontiguousarray(w.step_seqs, dtype=np.int64)
+    seqs = np.repeat(np.ascontiguousarray(w.batch, dtype=np.int64), per_step)
     stream = torch.cuda.current_stream()
     # a step ships only its tokens' slots and positions and the new lengths:
     # either the write kernel reads them straight from pinned host memory (a
     # ring of buffers the host refills once the write that read them has run),
     # or they travel in the kernel arguments, copied at launch
     host_args = args.append_meta == "args"
-    rows_np = np.repeat(np.arange(S, dtype=np.int32), w.append)
+    rows_np = np.repeat(np.arange(S, dtype=np.int32), per_step)
     rows = torch.from_numpy(rows_np) if host_args else torch.from_numpy(rows_np).to(dev)
-    offs = np.tile(np.arange(w.append, dtype=np.int64), S)
+    offs = np.tile(np.arange(per_step, dtype=np.int64), S)
     ring = [{"slots": torch.empty(n_tok, dtype=torch.int64, pin_memory=not host_args),
              "pos": torch.empty(n_tok, dtype=torch.int32, pin_memory=not host_args),
              "nctx": torch.empty(S, dtype=torch.int32, pin_memory=not host_args)}
             for _ in range(1 if host_args else 16)]
     plans = [ops.StepPlan(out, q, k_pool, v_pool, d_table, d_ctx, w.scale, ws, key=step_k, value=step_v,
-                          slot_mapping=r["slots"], partition_size=args.partition,
+                          slot_mapping=r["slots"], partition_size=partition,
                           append=(rows, r["pos"], r["nctx"]), host_args=host_args) for r in ring]
     ring_done = [torch.cuda.Event() for _ in ring]
     ring_used = [False] * len(ring)
@@ -721,8 +778,8 @@ def main():
             _, cow = bm.append_tokens(seqs, slots_out=ring[r]["slots"].numpy())
             if len(cow):
                 raise RuntimeError("copy-on-write is not expected in this workload")
-            np.add(np.repeat(host_ctx, w.append), offs, out=ring[r]["pos"].numpy(), casting="unsafe")
-            host_ctx[:] += w.append
+            np.add(np.repeat(host_ctx, per_step), offs, out=ring[r]["pos"].numpy(), casting="unsafe")
+            host_ctx[:] += per_step
             ring[r]["nctx"].numpy()[:] = host_ctx
         return plans[r], host_ctx.copy()
 
@@ -733,38 +790,33 @@ def main():
             ring_done[r].record(stream)
             ring_used[r] = True
 
-    if not grows:
-        # the chunk workload: write the chunk once (untimed); every step then decodes in place
-        plan, _ = prepare_step(0, True)
-        issue_write(0, plan)
-        torch.cuda.synchronize()
-
-    # decode is bracketed by two events in every timed step (its duration feeds
-    # the roofline); the small kernels are timed in a separate pass below
-    ev_dec = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
+    # decode is bracketed by events in every timed step: the partition kernel
+    # alone (the roofline's kernel) and with the merge
+    ev_dec = [(TimingEvent(), TimingEvent(), TimingEvent()) for _ in range(steps)]
 
     def step(i, timed_idx=None):
-        plan, ctx_np = prepare_step(i, grows)
+        plan, ctx_np = prepare_step(i, True)
         mx = int(ctx_np.max())
-        if grows:
-            issue_write(i, plan)
+        issue_write(i, plan)
         if timed_idx is not None:
             ev_dec[timed_idx][0].record(stream)
         plan.decode_partitions(mx)
         if timed_idx is not None:
             ev_dec[timed_idx][1].record(stream)
         plan.decode_reduce(mx)
+        if timed_idx is not None:
+            ev_dec[timed_idx][2].record(stream)
         return decode_bytes(ctx_np, w)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     total_bytes = 0.0
     host_s = 0.0  # time the host spends issuing a step (the GPU runs behind it)
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         h0 = time.perf_counter()
-        total_bytes += step(args.warmup + i, i)
+        total_bytes += step(warmup + i, i)
         host_s += time.perf_counter() - h0
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -777,13 +829,12 @@ def main():
     if not (np.array_equal(d_table.cpu().numpy(), t_host) and np.array_equal(d_ctx.cpu().numpy(), c_host)):
         raise RuntimeError("device block tables diverged from the block manager")
     # re-issuing the last step's write is idempotent (same slots, rows and lengths)
-    plan, ctx_side = prepare_step(args.warmup + args.steps - 1, False)
+    plan, ctx_side = prepare_step(warmup + steps - 1, False)
     mx_side = int(ctx_side.max())
     for _ in range(10):
         e = [TimingEvent() for _ in range(4)]
         e[0].record(stream)
-        if grows:
-            plan.cache_write()
+        plan.cache_write()
         e[1].record(stream)
         plan.decode_partitions(mx_side)
         e[2].record(stream)
@@ -792,13 +843,30 @@ def main():
         side.append(e)
     torch.cuda.synchronize()
 
-    k2_ms = np.array([a.elapsed_time(b) for a, b in ev_dec])
+    k2_ms = np.array([a.elapsed_time(b) for a, b, _ in ev_dec])
+    k23_ms = np.array([a.elapsed_time(c) for a, _, c in ev_dec])
     k1_ms = np.array([a[0].elapsed_time(a[1]) for a in side])
     k3_ms = np.array([a[2].elapsed_time(a[3]) for a in side])
     kd_side = np.array([a[1].elapsed_time(a[2]) for a in side])  # decode on the last timed step's tables
     span_ms = np.array([a[0].elapsed_time(a[3]) for a in side])  # first kernel start to last kernel end
-    bytes_per_launch = total_bytes / args.steps
+    bytes_per_launch = total_bytes / steps
     achieved = bytes_per_launch / (k2_ms.mean() * 1e-3) / 1e9
+    achieved23 = bytes_per_launch / (k23_ms.mean() * 1e-3) / 1e9
+    value = total_bytes / elapsed / 1e9
+    used_partition = ops.decode_partition_size(S, Hkv, int(host_ctx.max()), partition)
+    kernel, nwg = ops.decode_launch_shape(q.dtype, D, out.dtype, S * per_step, Hq, Hkv, int(host_ctx.max()),
+                                          partition)
+    grid = {"kernel": kernel, "workgroups": nwg}
+    if not full:
+        return {"workload": f"{w.name}: {w.description}", "partition": used_partition, "decode_grid": grid,
+                "mean_context": round(float(host_ctx.mean()), 1), "steps": steps,
+                "decode_partitions_us": round(float(k2_ms.mean()) * 1e3, 2),
+                "decode_reduce_us": round(float(k3_ms.mean()) * 1e3, 2),
+                "frac_decode_kernel": round(achieved / HBM_PEAK_GBS, 4),
+                "frac_decode_with_merge": round(achieved23 / HBM_PEAK_GBS, 4),
+                "whole_step_gbs": round(value, 2), "hbm_frac_whole_step": round(value / HBM_PEAK_GBS, 4),
+                "ms_per_step": round(elapsed / steps * 1e3, 4),
+                "algorithmic_bytes_per_launch": round(bytes_per_launch, 1)}
 
     # cold-cache decode: each launch after a 1 GiB write evicts L2 and the 256 MiB MALL
     scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -815,7 +883,6 @@ def main():
     torch.cuda.synchronize()
     cold_ms = np.array([a.elapsed_time(b) for a, b in cold])
     cold_gbs = decode_bytes(ctx_now, w) / (np.median(cold_ms) * 1e-3) / 1e9 if len(cold_ms) else None
-
     # HBM read ceiling: one streaming read of a 4 GiB buffer with decode's load style
     big = torch.empty(1 << 32, dtype=torch.uint8, device=dev)
     big.fill_(1)
@@ -855,8 +922,10 @@ def main():
         torch.cuda.synchronize()
         extra_fields["copy_probe_bytes"] = {"read": src.numel(), "write": dst.numel()}
         del src, dst
-    if w.append > 1 and not multi:
-        # the chunk workload also times its chunked prefill (matrix-core bound)
+    if chunk:
+        # the chunk workload also times its chunked prefill (matrix-core
+        # bound): the w.append-token chunk at the end of each context as it
+        # stands after the timed steps
         qc = to_dev(w.q)
         oc = torch.empty(qc.shape, dtype=tdt, device=dev)
         ops.prefill_chunk(oc, qc, k_pool, v_pool, d_table, d_ctx, w.scale, int(ctx_now.max()))
@@ -874,7 +943,7 @@ def main():
                                    "frac_of_dense_mfma_peak": round(fl / (p_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                                    "algorithmic_tflop": round(fl / 1e12, 4)}
 
-    traffic, traffic_ratio = load_traffic(args.workload, bytes_per_launch)
+    traffic, traffic_ratio = load_traffic(w.name, bytes_per_launch)
     phys_bytes = physical_kv_bytes(t_host, c_host, w)
     value = total_bytes / elapsed / 1e9
     rec = {
@@ -882,9 +951,9 @@ def main():
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(elapsed / steps * 1e3, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -894,25 +963,28 @@ def main():
                    "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": D, "block_size": w.block_size,
                    "mean_context": round(float(ctx_now.mean()), 1),
-                   "partition": ops.decode_partition_size(S, Hkv, int(ctx_now.max()), args.partition)},
+                   "partition": used_partition, "decode_grid": grid},
         "hbm_frac_whole_step": round(value / HBM_PEAK_GBS, 4),
         # shared prefix blocks are read by many rows but come from HBM about once (the rest hit in cache)
         "kv_physical": {"bytes_per_launch": round(phys_bytes, 1),
                         "gbs": round(phys_bytes / (float(kd_side.mean()) * 1e-3) / 1e9, 2),
                         "note": "K/V of the distinct blocks the last timed step reads, each block's valid "
                                 "tokens once, over the time of decode launches on that same state"},
-        "seqs_per_s": round(S * args.steps / elapsed, 1),
+        "seqs_per_s": round(S * steps / elapsed, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if traffic is None else round(traffic, 1),
                      "traffic_over_algorithmic": None if traffic_ratio is None else round(traffic_ratio, 4),
-                     "kernel": "decode_mfma_kernel" if w.dtype != "f32" else "decode_f32_kernel",
-                     "algorithmic_bytes_per_launch": round(bytes_per_launch, 1)},
+                     "kernel": kernel,
+                     "algorithmic_bytes_per_launch": round(bytes_per_launch, 1),
+                     # the same bytes over the partition kernel plus the log-sum-exp merge launch
+                     "achieved_with_merge": round(achieved23, 2),
+                     "frac_with_merge": round(achieved23 / HBM_PEAK_GBS, 4)},
         "kernels_ms": {"append_step": round(float(k1_ms.mean()), 5),
                        "decode_partitions": round(float(k2_ms.mean()), 5),
                        "decode_reduce": round(float(k3_ms.mean()), 5),
                        "step_kernels_span": round(float(span_ms.mean()), 5)},
-        "host_ms_per_step": round(host_s / args.steps * 1e3, 4),
+        "host_ms_per_step": round(host_s / steps * 1e3, 4),
         "decode_partitions_cold": None if cold_gbs is None else {
             "median_ms": round(float(np.median(cold_ms)), 5), "p10_ms": round(float(np.percentile(cold_ms, 10)), 5),
             "p90_ms": round(float(np.percentile(cold_ms, 90)), 5), "gbs": round(cold_gbs, 2)},
@@ -920,9 +992,9 @@ def main():
         "hbm_gather_ceiling_gbs": round(gather_gbs, 1),
         **extra_fields,
     }
-    if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(w)
-    print(json.dumps(rec), flush=True)
+    return rec
+
+
 
 
 if __name__ == "__main__":

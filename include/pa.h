@@ -228,11 +228,28 @@ pa_status_t pa_patch_tables(int32_t* block_tables, int32_t max_blocks_per_seq, i
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                  int32_t partition_size);
 
-/* Workgroups the fp16 / bf16 decode launch uses on the current device at
- * most: as many as are resident at once (occupancy per CU x CUs); each takes
- * an equal share of the batch's tiles.  -1 for an unsupported dtype /
- * head_dim / out_dtype. */
-int64_t pa_decode_workgroups(pa_dtype_t dtype, int32_t head_dim, pa_dtype_t out_dtype);
+/* How decode's partition launch is shaped for these sizes on the current
+ * device, and its workgroup count (*workgroups, may be NULL):
+ *   PA_DECODE_GRID_VECTOR      fp32: one workgroup per (query head,
+ *                              partition), vector ALUs
+ *   PA_DECODE_GRID_PARTITIONS  fp16 / bf16 whose longest context spans at
+ *                              most 8 partitions: one workgroup per (kv head,
+ *                              sequence, partition)
+ *   PA_DECODE_GRID_PERSISTENT  fp16 / bf16 beyond: as many workgroups as are
+ *                              resident at once (occupancy x CUs, at most one
+ *                              per partition); each takes an equal share of
+ *                              the batch's tiles (each pair weighed by its
+ *                              tiles plus a fixed start-up cost), whole
+ *                              partitions only, and folds the partitions of
+ *                              one (sequence, kv head) it holds in registers,
+ *                              so the merge reads about one partial per
+ *                              workgroup instead of one per partition.
+ * -1 for invalid arguments.  Results are the same whichever shape runs
+ * (within the stated tolerances; each shape is deterministic). */
+enum { PA_DECODE_GRID_VECTOR = 0, PA_DECODE_GRID_PARTITIONS = 1, PA_DECODE_GRID_PERSISTENT = 2 };
+int32_t pa_decode_launch_shape(pa_dtype_t dtype, int32_t head_dim, pa_dtype_t out_dtype, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len,
+                               int32_t partition_size, int64_t* workgroups);
 
 /* Workspace bytes pa_decode needs for these sizes (0: none). */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,

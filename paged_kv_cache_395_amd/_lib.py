@@ -12,6 +12,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libp
 
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, PA_ENOSPC, PA_ENOENT = range(7)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+PA_DECODE_GRID_VECTOR, PA_DECODE_GRID_PARTITIONS, PA_DECODE_GRID_PERSISTENT = 0, 1, 2
 STATUS_NAMES = {0: "PA_OK", 1: "PA_EINVAL", 2: "PA_EUNSUPPORTED", 3: "PA_EWORKSPACE", 4: "PA_EHIP",
                 5: "PA_ENOSPC", 6: "PA_ENOENT"}
 
@@ -52,7 +53,7 @@ SIGNATURES = {
                                       _vp]),
     "pa_patch_tables": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _vp]),
     "pa_decode_partition_size": (_i32, [_i32, _i32, _i32, _i32]),
-    "pa_decode_workgroups": (_i64, [ctypes.c_int, _i32, ctypes.c_int]),
+    "pa_decode_launch_shape": (_i32, [ctypes.c_int, _i32, ctypes.c_int, _i32, _i32, _i32, _i32, _i32, _pi64]),
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _i64, _f32, _i32, _i32, _vp, _sz, ctypes.c_int, _vp]),

@@ -355,10 +355,30 @@ pa_status_t pa_patch_tables(int32_t* block_tables, int32_t max_blocks_per_seq, i
                     "patch_tables launch");
 }
 
-int64_t pa_decode_workgroups(pa_dtype_t dtype, int32_t head_dim, pa_dtype_t out_dtype) {
-  if (!(dtype == PA_F16 || dtype == PA_BF16) || (head_dim != 64 && head_dim != 128)) return -1;
+int32_t pa_decode_launch_shape(pa_dtype_t dtype, int32_t head_dim, pa_dtype_t out_dtype, int32_t num_seqs,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t max_context_len,
+                               int32_t partition_size, int64_t* workgroups) {
+  if (!known_dtype(dtype) || (head_dim != 64 && head_dim != 128) || num_seqs < 0 || num_kv_heads <= 0 ||
+      num_q_heads <= 0 || num_q_heads % num_kv_heads != 0 || max_context_len < 0 || partition_size < 0 ||
+      partition_size % 16 != 0)
+    return -1;
   if (!(out_dtype == PA_F32 || out_dtype == dtype)) return -1;
-  return decode_resident_workgroups(dtype, head_dim, out_dtype == PA_F32);
+  const int32_t p = choose_partition(num_seqs, num_kv_heads, max_context_len, partition_size);
+  const int64_t nparts = max_context_len == 0 ? 1 : ceil_div(max_context_len, p);
+  int64_t n = 0;
+  int32_t shape = PA_DECODE_GRID_PARTITIONS;
+  if (dtype == PA_F32) {
+    shape = PA_DECODE_GRID_VECTOR;
+    n = int64_t(num_seqs) * num_q_heads * nparts;  // one workgroup per (query head, partition)
+  } else if (decode_uses_persistent_grid(int32_t(nparts))) {
+    shape = PA_DECODE_GRID_PERSISTENT;
+    n = std::max<int64_t>(1, std::min(decode_resident_workgroups(dtype, head_dim, out_dtype == PA_F32),
+                                      int64_t(num_seqs) * num_kv_heads * nparts));
+  } else {
+    n = int64_t(num_seqs) * num_kv_heads * nparts;
+  }
+  if (workgroups) *workgroups = n;
+  return shape;
 }
 
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,

@@ -424,7 +424,7 @@ decode_partition_kernel(KParams P) {
 // SIMD do not).
 template <typename T, int D, bool OUT_F32>
 __global__ void __launch_bounds__(kThreads, 3)
-decode_mfma_kernel(KParams P) {
+decode_persistent_kernel(KParams P) {
   __shared__ DecodeShared<D> sh;
   const int S = P.num_seqs;
   const int tid = threadIdx.x;
@@ -840,7 +840,7 @@ int64_t resident_workgroups(K kernel) {
 // there are partitions in the batch's upper bound.
 template <typename T, int D, bool OUT_F32>
 hipError_t launch_mfma_grid(const DecodeArgs& a, const KParams& p) {
-  const auto kernel = decode_mfma_kernel<T, D, OUT_F32>;
+  const auto kernel = decode_persistent_kernel<T, D, OUT_F32>;
   const int64_t units = int64_t(a.num_seqs) * a.num_kv_heads * std::max(1, a.num_partitions);
   const int64_t n = std::max<int64_t>(1, std::min(resident_workgroups(kernel), units));
   hipLaunchKernelGGL(kernel, dim3(unsigned(n)), dim3(kThreads), 0, a.stream, p);
@@ -892,16 +892,16 @@ hipError_t launch_decode_partitions(const DecodeArgs& a) {
 int64_t decode_resident_workgroups(pa_dtype_t dtype, int32_t head_dim, bool out_f32) {
   if (dtype == PA_BF16) {
     if (head_dim == 64)
-      return out_f32 ? resident_workgroups(decode_mfma_kernel<Bf16, 64, true>)
-                     : resident_workgroups(decode_mfma_kernel<Bf16, 64, false>);
-    return out_f32 ? resident_workgroups(decode_mfma_kernel<Bf16, 128, true>)
-                   : resident_workgroups(decode_mfma_kernel<Bf16, 128, false>);
+      return out_f32 ? resident_workgroups(decode_persistent_kernel<Bf16, 64, true>)
+                     : resident_workgroups(decode_persistent_kernel<Bf16, 64, false>);
+    return out_f32 ? resident_workgroups(decode_persistent_kernel<Bf16, 128, true>)
+                   : resident_workgroups(decode_persistent_kernel<Bf16, 128, false>);
   }
   if (head_dim == 64)
-    return out_f32 ? resident_workgroups(decode_mfma_kernel<F16, 64, true>)
-                   : resident_workgroups(decode_mfma_kernel<F16, 64, false>);
-  return out_f32 ? resident_workgroups(decode_mfma_kernel<F16, 128, true>)
-                 : resident_workgroups(decode_mfma_kernel<F16, 128, false>);
+    return out_f32 ? resident_workgroups(decode_persistent_kernel<F16, 64, true>)
+                   : resident_workgroups(decode_persistent_kernel<F16, 64, false>);
+  return out_f32 ? resident_workgroups(decode_persistent_kernel<F16, 128, true>)
+                 : resident_workgroups(decode_persistent_kernel<F16, 128, false>);
 }
 
 hipError_t launch_decode_reduce(const DecodeArgs& a) {

@@ -44,11 +44,12 @@ struct DecodeArgs {
 // fp16 / bf16 decode runs one workgroup per partition while the longest
 // context spans at most kPartitionGridMax partitions, and on the persistent
 // grid beyond: there, one partial per partition would cost more than the
-// per-partition grid's better balance gains (measured on 16 x 32,768 tokens
-// at 512-token partitions: 380 us per partition, 333 us persistent; on 64
-// MHA contexts U[128, 2048] at 4 partitions: 176 us per partition, 182 us
-// persistent).
-constexpr int32_t kPartitionGridMax = 4;
+// per-partition grid's better balance gains.  Measured on one MI355X:
+// 16 x 32,768 tokens at 512-token partitions (64 per context): 380 us per
+// partition, 333 us persistent; the same at 4096 (8): 329 vs 334; 256
+// lognormal GQA contexts at 512 (16): 271 vs 254; 64 MHA contexts
+// U[128, 2048] at 512 (4 to 5): 176 vs 182.
+constexpr int32_t kPartitionGridMax = 8;
 inline bool decode_uses_persistent_grid(int32_t num_partitions) { return num_partitions > kPartitionGridMax; }
 
 hipError_t launch_decode_partitions(const DecodeArgs& a);

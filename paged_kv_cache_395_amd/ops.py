@@ -199,6 +199,22 @@ def decode_partition_size(num_seqs: int, num_kv_heads: int, max_context_len: int
     return int(_lib.load().pa_decode_partition_size(num_seqs, num_kv_heads, max_context_len, partition_size))
 
 
+DECODE_KERNELS = {_lib.PA_DECODE_GRID_VECTOR: "decode_f32_kernel",
+                  _lib.PA_DECODE_GRID_PARTITIONS: "decode_partition_kernel",
+                  _lib.PA_DECODE_GRID_PERSISTENT: "decode_persistent_kernel"}
+
+
+def decode_launch_shape(dtype: torch.dtype, head_dim: int, out_dtype: torch.dtype, num_seqs: int, num_q_heads: int,
+                        num_kv_heads: int, max_context_len: int, partition_size: int = 0):
+    """(kernel name, workgroups) of decode's partition launch for these sizes on the current device."""
+    n = ctypes.c_int64(0)
+    shape = _lib.load().pa_decode_launch_shape(_DTYPE[dtype], head_dim, _DTYPE[out_dtype], num_seqs, num_q_heads,
+                                               num_kv_heads, max_context_len, partition_size, ctypes.byref(n))
+    if shape < 0:
+        raise ValueError("invalid decode sizes")
+    return DECODE_KERNELS[shape], int(n.value)
+
+
 def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, max_context_len: int,
                            partition_size: int = 0) -> int:
     return int(_lib.load().pa_decode_workspace_bytes(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len,

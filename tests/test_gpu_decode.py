@@ -146,7 +146,7 @@ def ordered_bits(bits: np.ndarray, dt: str) -> np.ndarray:
 
 @pytest.mark.parametrize("partition", [16, 64, 256, 512, 2048, 0])
 def test_partition_sizes_agree(partition):
-    # up to 4 partitions of the longest context (1,500 tokens): one workgroup
+    # up to 8 partitions of the longest context (1,500 tokens): one workgroup
     # per partition; more: the persistent grid
     p = prepared("gqa8b_bf16", num_seqs=12, hi=1500)
     d = p.device()

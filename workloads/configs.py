@@ -118,7 +118,7 @@ class Workload:
     head_dim: int
     num_blocks: int
     scale: float
-    partition_size: int
+    partition_size: int              # tokens per context partition the workload states (0: the library's choice)
     append: int                      # tokens each batch sequence appends in the step
     free_order: np.ndarray           # int32 [num_blocks], the initial free-list order
     program: List[Tuple]             # block-manager operations that build the cached state
@@ -210,7 +210,7 @@ def _decode_from_lengths(rng, name, dtype, ctx, Hq, Hkv, D, P, NB=None, descript
 
 def _tiny_f32(rng, ctx=(20, 37, 16, 1), block_size=BLOCK_SIZE):
     return _decode_from_lengths(
-        rng, "tiny_f32", "f32", ctx, 4, 4, 64, 512, NB=20,
+        rng, "tiny_f32", "f32", ctx, 4, 4, 64, 0, NB=20,
         description="4 sequences, fp32, 4/4 heads, head_dim 64, 20-block pool, 1 new token each",
         block_size=block_size)
 
@@ -218,7 +218,7 @@ def _tiny_f32(rng, ctx=(20, 37, 16, 1), block_size=BLOCK_SIZE):
 def _mha7b_f16(rng, num_seqs=64, lo=128, hi=2048, block_size=BLOCK_SIZE, name="mha7b_f16"):
     ctx = rng.integers(lo, hi + 1, size=num_seqs)
     return _decode_from_lengths(
-        rng, name, "f16", ctx, 32, 32, 128, 512,
+        rng, name, "f16", ctx, 32, 32, 128, 0,
         description=f"7B-shaped decode, fp16, batch {num_seqs}, 32/32 heads, head_dim 128, "
                     f"ctx U[{lo},{hi}], pool 1.25x need", block_size=block_size)
 
@@ -226,7 +226,7 @@ def _mha7b_f16(rng, num_seqs=64, lo=128, hi=2048, block_size=BLOCK_SIZE, name="m
 def _gqa8b_bf16(rng, num_seqs=256, median=1024, lo=16, hi=8192, block_size=BLOCK_SIZE, name="gqa8b_bf16"):
     ctx = np.clip(np.rint(np.exp(math.log(median) + rng.standard_normal(num_seqs))), lo, hi).astype(np.int64)
     return _decode_from_lengths(
-        rng, name, "bf16", ctx, 32, 8, 128, 512, block_size=block_size,
+        rng, name, "bf16", ctx, 32, 8, 128, 0, block_size=block_size,
         description=f"Llama-3-8B-shaped GQA decode, bf16, batch {num_seqs}, 32/8 heads, head_dim 128, "
                     f"ctx lognormal(median {median}, sigma 1) clipped to [{lo},{hi}]")
 
@@ -258,7 +258,7 @@ def _shared_prefix_bf16(rng, num_users=512, num_prompts=128, n_samples=4,
     need = (_blocks(sys_tokens) + int(sum(_blocks(t) for t in user_tails))
             + num_prompts * _blocks(prompt_tokens) + int(sum(_blocks(t) for t in sample_tails)))
     NB = int(math.ceil(1.25 * need))
-    return _finish(rng, "shared_prefix_bf16", "bf16", S, 32, 8, 128, NB, 1.0 / math.sqrt(128), 512, 1,
+    return _finish(rng, "shared_prefix_bf16", "bf16", S, 32, 8, 128, NB, 1.0 / math.sqrt(128), 0, 1,
                    program, np.arange(S),
                    f"{num_users} sequences on a {sys_tokens}-token shared prompt plus {num_prompts} prompts "
                    f"of {prompt_tokens} tokens sampled n={n_samples}; bf16, 32/8 heads, head_dim 128",
@@ -289,7 +289,7 @@ def _specdec_bf16(rng, num_seqs=256, median=1024, lo=16, hi=8192, q_len=4, block
     need = int(sum(_blocks(c, block_size) for c in ctx))
     NB = int(math.ceil(1.25 * need))
     program = [("add", s, int(ctx[s]) - q_len) for s in range(num_seqs)]
-    return _finish(rng, "specdec_bf16", "bf16", num_seqs, 32, 8, 128, NB, 1.0 / math.sqrt(128), 512, q_len,
+    return _finish(rng, "specdec_bf16", "bf16", num_seqs, 32, 8, 128, NB, 1.0 / math.sqrt(128), 0, q_len,
                    program, np.arange(num_seqs),
                    f"Llama-3-8B-shaped GQA verification of {q_len} drafted tokens per sequence, bf16, batch "
                    f"{num_seqs}, 32/8 heads, head_dim 128, ctx lognormal(median {median}, sigma 1) clipped to "
