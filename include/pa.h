@@ -266,6 +266,31 @@ pa_status_t pa_decode(void* out, pa_dtype_t out_dtype, const void* q,
                       pa_dtype_t dtype, void* stream);
 
 /* ------------------------------------------------------------------------
+ * pa_decode for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, contract and results as pa_decode, without the workspace: the
+ * split-context partials go to a device array of
+ * pa_decode_noalloc_scratch_bytes() (64 MiB) that the library holds on every
+ * GPU it runs on until the process ends.  The call allocates nothing (no
+ * hipMalloc, no hipFree, no allocating library routine); sizes whose
+ * workspace (pa_decode_workspace_bytes) exceeds the array give
+ * PA_EWORKSPACE.  All calls on one GPU share that GPU's array: calls that
+ * overlap on one GPU (on different streams) race and must not be issued.
+ * The first call on a device also looks the array's address up
+ * (hipGetSymbolAddress); a failure there gives PA_EHIP.
+ * ---------------------------------------------------------------------- */
+size_t pa_decode_noalloc_scratch_bytes(void);
+
+pa_status_t pa_decode_noalloc(void* out, pa_dtype_t out_dtype, const void* q,
+                              const void* k_cache, const void* v_cache,
+                              const int32_t* block_tables, int32_t max_blocks_per_seq,
+                              const int32_t* context_lens,
+                              int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                              float scale, int32_t max_context_len, int32_t partition_size,
+                              pa_dtype_t dtype, void* stream);
+
+/* ------------------------------------------------------------------------
  * Several queries per sequence: the last q_len positions of each context
  * (ctx - q_len .. ctx - 1, their K/V already written), each attending
  * causally to keys 0 .. its own position -- e.g. verifying q_len drafted

@@ -57,6 +57,9 @@ SIGNATURES = {
     "pa_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                  _i64, _f32, _i32, _i32, _vp, _sz, ctypes.c_int, _vp]),
+    "pa_decode_noalloc_scratch_bytes": (_sz, []),
+    "pa_decode_noalloc": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                         _i32, _i64, _f32, _i32, _i32, ctypes.c_int, _vp]),
     "pa_decode_multi_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "pa_decode_multi": (ctypes.c_int, [_vp, ctypes.c_int, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                        _i32, _i64, _f32, _i32, _i32, _vp, _sz, ctypes.c_int, _vp]),

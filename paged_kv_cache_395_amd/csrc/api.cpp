@@ -186,6 +186,26 @@ pa_status_t run_decode(DecodePhase phase, void* out, pa_dtype_t out_dtype, const
 
 }  // namespace
 
+pa_status_t decode_in_scratch(void* scratch, size_t scratch_bytes, void* out, pa_dtype_t out_dtype, const void* q,
+                              const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                              int32_t max_blocks, const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t bs, int64_t NB, float scale, int32_t max_ctx, int32_t partition,
+                              pa_dtype_t dtype, void* stream) {
+  DecodeCheck dc{};
+  pa_status_t st = check_decode(out, out_dtype, q, 1, k_cache, v_cache, block_tables, max_blocks, context_lens, S, Hq,
+                                Hkv, D, bs, NB, scale, max_ctx, partition, dtype, &dc);
+  if (st != PA_OK) return st;
+  const size_t need = ws_size(S, 1, Hq, Hkv, D, dc.nparts);
+  if (need > scratch_bytes)
+    return fail(PA_EWORKSPACE,
+                "these sizes need %zu bytes of split-context scratch; the allocation-free decode holds %zu "
+                "(use pa_decode with a workspace, or a larger partition_size)",
+                need, scratch_bytes);
+  return run_decode(DecodePhase::kBoth, out, out_dtype, q, 1, k_cache, v_cache, block_tables, max_blocks,
+                    context_lens, S, Hq, Hkv, D, bs, NB, scale, max_ctx, partition, scratch, scratch_bytes, dtype,
+                    stream);
+}
+
 pa_status_t fail(pa_status_t st, const char* fmt, ...) {
   char buf[512];
   va_list ap;

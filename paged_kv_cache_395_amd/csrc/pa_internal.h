@@ -52,6 +52,14 @@ struct DecodeArgs {
 constexpr int32_t kPartitionGridMax = 8;
 inline bool decode_uses_persistent_grid(int32_t num_partitions) { return num_partitions > kPartitionGridMax; }
 
+// pa_decode with `scratch` (scratch_bytes) as its workspace; PA_EWORKSPACE
+// when the sizes need more.
+pa_status_t decode_in_scratch(void* scratch, size_t scratch_bytes, void* out, pa_dtype_t out_dtype, const void* q,
+                              const void* k_cache, const void* v_cache, const int32_t* block_tables,
+                              int32_t max_blocks, const int32_t* context_lens, int32_t S, int32_t Hq, int32_t Hkv,
+                              int32_t D, int32_t bs, int64_t NB, float scale, int32_t max_ctx, int32_t partition,
+                              pa_dtype_t dtype, void* stream);
+
 hipError_t launch_decode_partitions(const DecodeArgs& a);
 hipError_t launch_decode_reduce(const DecodeArgs& a);
 // Workgroups of the fp16 / bf16 decode kernel resident at once on the current device.

@@ -222,7 +222,7 @@ def decode_workspace_bytes(num_seqs: int, num_q_heads: int, num_kv_heads: int, h
 
 
 def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size,
-                 workspace):
+                 workspace, allocate=True):
     _dev(out, q, k_cache, v_cache, block_tables, context_lens)
     NB, Hkv, D, bs = _pools(k_cache, v_cache, q.shape[-1])
     if q.dim() != 3 or q.shape[2] != D:
@@ -237,7 +237,7 @@ def _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, ma
     if not (q.dtype == k_cache.dtype == v_cache.dtype):
         raise TypeError("q and the pools must share one dtype")
     need = decode_workspace_bytes(S, Hq, Hkv, D, max_context_len, partition_size)
-    if workspace is None and need > 0:
+    if workspace is None and need > 0 and allocate:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _p(workspace) if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -252,6 +252,15 @@ def decode(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_cont
     args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
                            partition_size, workspace)
     _lib.check(_lib.load().pa_decode(*args, _stream(stream)))
+
+
+def decode_noalloc(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size=0,
+                   stream=None) -> None:
+    """decode without a workspace: the split partials go to the library's fixed device array
+    (pa_decode_noalloc); nothing is allocated.  Calls that overlap on one GPU race."""
+    args, _ = _decode_args(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len,
+                           partition_size, None, allocate=False)
+    _lib.check(_lib.load().pa_decode_noalloc(*args[:17], args[19], _stream(stream)))
 
 
 def decode_partitions(out, q, k_cache, v_cache, block_tables, context_lens, scale, max_context_len, partition_size,
