@@ -85,7 +85,16 @@ typedef enum {
   PA_ENOENT = 6        /* block manager: unknown sequence                */
 } pa_status_t;
 
-typedef enum { PA_F32 = 0, PA_F16 = 1, PA_BF16 = 2 } pa_dtype_t;
+/* Element types.  The two sentinels give the type the range of int32_t, so
+ * any 32-bit value a caller passes is a value of the type and is refused
+ * with PA_EUNSUPPORTED rather than being undefined in the C++ library. */
+typedef enum {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2,
+  PA_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  PA_DTYPE_RANGE_MAX_ = 2147483647
+} pa_dtype_t;
 
 /* Version string of the library build. */
 const char* pa_version(void);
@@ -341,7 +350,11 @@ pa_status_t pa_decode_reduce(void* out, pa_dtype_t out_dtype, const int32_t* con
 
 /* ------------------------------------------------------------------------
  * Chunked prefill: causal attention of a chunk of chunk_len new queries per
- * sequence over the paged cache.  The chunk occupies the last chunk_len
+ * sequence over the paged cache ([OS] "PagedAttention: Virtual Memory for
+ * KV Cache": a request's tokens live in fixed-size blocks that its block
+ * table maps from logical to physical position; a chunk of new tokens is
+ * stored into such blocks and attends through the same table).  The chunk
+ * occupies the last chunk_len
  * positions of the context (its K/V already written by
  * pa_reshape_and_cache); query i of sequence s sits at position
  * context_lens[s] - chunk_len + i and attends keys 0 .. that position.

@@ -8,7 +8,9 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa.so")
+# PA_LIBRARY may name another build of the same library (the host-sanitized
+# build of build.py --sanitize); it must exist like the default one.
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libpa.so")
 
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP, PA_ENOSPC, PA_ENOENT = range(7)
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2

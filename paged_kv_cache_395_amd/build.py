@@ -7,6 +7,15 @@ compiles every source under ``csrc/`` (in parallel) and links
 by path), never imported through the package, whose import loads the
 library.  hipcc cross-compiles for gfx950
 without a GPU present.
+
+    python paged_kv_cache_395_amd/build.py --sanitize
+
+builds the same library with the host code (block manager, scheduler,
+argument checks, launchers) instrumented by AddressSanitizer and
+UndefinedBehaviorSanitizer, errors fatal, into
+``paged_kv_cache_395_amd/lib/sanitize/libpa.so``; device code is built as
+usual.  The CPU test suite runs against it with the sanitizer runtime
+preloaded and ``PA_LIBRARY`` naming that file (the command is printed).
 """
 
 import os
@@ -20,6 +29,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "lib", "_build")
 LIB = os.path.join(PKG, "lib", "libpa.so")
+SAN_BUILD = os.path.join(PKG, "lib", "sanitize", "_build")
+SAN_LIB = os.path.join(PKG, "lib", "sanitize", "libpa.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -38,9 +49,15 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-c", src, "-o", obj] + COMMON
+# host-side sanitizers only (each flag after -Xarch_host): device code is not instrumented
+SANITIZERS = ("address", "undefined")
+SAN_FLAGS = [f for k in SANITIZERS for f in ("-Xarch_host", "-fsanitize=" + k)] + [
+    "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+
+
+def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, "-c", src, "-o", obj] + COMMON + list(extra)
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"  # host pass does not know the device feature
     err = "\n".join(l for l in (r.stderr or "").splitlines() if noise not in l)
@@ -51,21 +68,40 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    build_dir, lib = (SAN_BUILD, SAN_LIB) if sanitize else (BUILD, LIB)
+    extra = SAN_FLAGS if sanitize else []
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+        objs = list(ex.map(lambda src: _compile(src, build_dir, extra), srcs))
+    tmp = lib + ".tmp"
+    link_extra = [f for k in SANITIZERS for f in ("-fsanitize=" + k,)] + ["-shared-libsan"] if sanitize else []
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs + link_extra
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
+
+
+def sanitizer_runtime() -> str:
+    """The clang AddressSanitizer runtime the sanitized library links against."""
+    r = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True, text=True)
+    path = r.stdout.strip()
+    if not os.path.isabs(path):  # older layouts: ask for the runtime directory
+        rd = subprocess.run([HIPCC, "-print-runtime-dir"], capture_output=True, text=True).stdout.strip()
+        path = os.path.join(rd, "libclang_rt.asan-x86_64.so")
+    return path
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv[1:]:
+        lib = build(verbose=True, sanitize=True)
+        print("run the CPU tests against it with:\n"
+              f"  LD_PRELOAD={sanitizer_runtime()} ASAN_OPTIONS=detect_leaks=0 PA_LIBRARY={lib} "
+              "python -m pytest tests/ -q -m \"not gpu\"")
+    else:
+        build(verbose=True)

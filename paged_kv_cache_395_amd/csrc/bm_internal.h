@@ -36,7 +36,7 @@ struct pa_bm {
   std::unordered_map<uint64_t, int32_t> cached;  // prefix hash -> block
   std::vector<uint64_t> key;                     // per block: its prefix hash (valid when keyed)
   std::vector<uint64_t> parent_key;              // per block: the hash of the prefix before it
-  std::vector<int32_t> key_tokens;               // per block: its 16 token ids
+  std::vector<int32_t> key_tokens;               // per block: its block_size token ids
   std::vector<char> keyed, in_lru;
   std::list<int32_t> lru;
   std::vector<std::list<int32_t>::iterator> lru_pos;
