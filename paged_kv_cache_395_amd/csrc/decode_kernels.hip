@@ -88,6 +88,18 @@ __device__ inline void store_out(void* out, int64_t idx, float v) {
   }
 }
 
+// Four consecutive output elements (idx a multiple of 4).
+template <typename T, bool OUT_F32>
+__device__ inline void store_out4(void* out, int64_t idx, f32x4_t v) {
+  if constexpr (OUT_F32) {
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + idx) = v;
+  } else {
+    typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+    const u32x2_t p = {pack2(T::from_float(v[0]), T::from_float(v[1])), pack2(T::from_float(v[2]), T::from_float(v[3]))};
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + idx) = p;
+  }
+}
+
 // A context length the grid / table cannot cover is a caller error: report it
 // as NaN rows instead of reading out of bounds.
 __device__ inline bool context_out_of_contract(int ctx, const KParams& P) {
@@ -170,7 +182,7 @@ template <int D>
 struct DecodeShared {
   float m[kWaves][16];
   float l[kWaves][16];
-  float o[kWaves][16][D + 1];
+  float o[kWaves][16][D + 4];  // rows stay 16-byte aligned
   int64_t scan[kThreads];
   int64_t total, base0;
   int s0;
@@ -338,7 +350,11 @@ __device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>
   lsum += shfl_xor(lsum, 16);
   lsum += shfl_xor(lsum, 32);
 
-  // ---- merge the 4 waves
+  // ---- merge the 4 waves.  Each wave leaves its (max, sum) per column and
+  // its accumulator in LDS; wave w then combines output tiles
+  // w * NT/4 .. (w + 1) * NT/4 - 1 of every column, each lane the four dims
+  // its own accumulator lanes held (16-byte LDS reads), with the column's
+  // four weights computed once.
   __syncthreads();  // every reader of the previous segment's merge is done
   if (threadIdx.x == 0) sh.bad = 0;
   __syncthreads();
@@ -347,36 +363,43 @@ __device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>
     sh.m[w][n] = m;
     sh.l[w][n] = lsum;
   }
-  if (n < ncol) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sh.o[w][n][16 * t + 4 * quad + r] = o[t][r];
-  }
+  for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(&sh.o[w][n][16 * t + 4 * quad]) = o[t];
   __syncthreads();
-  const bool any_bad = sh.bad != 0;
-  for (int idx = threadIdx.x; idx < ncol * D; idx += kThreads) {
-    const int h = idx / D, d = idx - (idx / D) * D;
-    float M = sh.m[0][h];
-#pragma unroll
-    for (int ww = 1; ww < kWaves; ++ww) M = fmaxf(M, sh.m[ww][h]);
-    float L = 0.f, O = 0.f;
+  if (n < ncol) {
+    const bool any_bad = sh.bad != 0;
+    float mw[kWaves], fw[kWaves];
+    float M = kNoMax;
 #pragma unroll
     for (int ww = 0; ww < kWaves; ++ww) {
-      const float f = fast_exp2(sh.m[ww][h] - M);
-      L += f * sh.l[ww][h];
-      O += f * sh.o[ww][h][d];
+      mw[ww] = sh.m[ww][n];
+      M = fmaxf(M, mw[ww]);
     }
-    if (any_bad) O = __builtin_nanf("");
-    if (nseg == 1) {
-      store_out<T, OUT_F32>(P.out, col_row(h) * D + d, O / L);
-    } else {
-      const int64_t prow = col_row(h) * P.nparts_max + seg;
-      P.ws_acc[prow * D + d] = O;
-      if (d == 0) {
-        P.ws_m[prow] = M;
-        P.ws_l[prow] = L;
+    float L = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kWaves; ++ww) {
+      fw[ww] = fast_exp2(mw[ww] - M);
+      L += fw[ww] * sh.l[ww][n];
+    }
+    const int64_t row = col_row(n);
+    const int64_t prow = row * P.nparts_max + seg;
+    constexpr int kTilesPerWave = NT / kWaves;
+#pragma unroll
+    for (int j = 0; j < kTilesPerWave; ++j) {
+      const int d0 = 16 * (w * kTilesPerWave + j) + 4 * quad;
+      f32x4_t O = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) O += fw[ww] * *reinterpret_cast<const f32x4_t*>(&sh.o[ww][n][d0]);
+      if (any_bad) O = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      if (nseg == 1) {
+        store_out4<T, OUT_F32>(P.out, row * D + d0, O * (1.f / L));
+      } else {
+        *reinterpret_cast<f32x4_t*>(P.ws_acc + prow * D + d0) = O;
       }
+    }
+    if (nseg > 1 && w == 0 && quad == 0) {
+      P.ws_m[prow] = M;
+      P.ws_l[prow] = L;
     }
   }
 }
