@@ -44,7 +44,7 @@
 namespace pa {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;  // the merges below name the 4 waves' slots explicitly
 constexpr int kThreads = kWaves * kWave;
 // "no max yet": finite so that 2^(s - m) of a masked score is 0, not NaN
 constexpr float kNoMax = -1e30f;
@@ -178,15 +178,21 @@ __device__ inline void write_header(const KParams& P) {
   h[7] = P.max_ctx;
 }
 
+// LDS of one segment's 4-wave merge.
 template <int D>
 struct DecodeShared {
   float m[kWaves][16];
   float l[kWaves][16];
   float o[kWaves][16][D + 4];  // rows stay 16-byte aligned
+  int bad[kWaves];             // per wave: a table entry outside the pool was seen
+};
+
+// LDS of the persistent grid's split: per-thread tile sums, then their
+// exclusive prefix; the batch's total; the first sequence of the share.
+struct SplitShared {
   int64_t scan[kThreads];
   int64_t total, base0;
   int s0;
-  int bad;
 };
 
 // One segment: tokens [tok0, tok0 + ntok) of kv head g of sequence s, the
@@ -195,7 +201,7 @@ struct DecodeShared {
 // partial slot `seg` of the pair's nseg.
 template <typename T, int D, bool OUT_F32>
 __device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>& sh, int s, int g, int ctx,
-                                               int tok0, int ntok, int nseg, int seg) {
+                                               int tok0, int ntok, int nseg, int seg, bool first) {
   constexpr int DC = D / 32;  // 16-byte chunks per lane per tile
   constexpr int NT = D / 16;  // 16-dim output tiles
   constexpr int kTileElems = kBlockTokens * D;
@@ -351,55 +357,56 @@ __device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>
   lsum += shfl_xor(lsum, 32);
 
   // ---- merge the 4 waves.  Each wave leaves its (max, sum) per column and
-  // its accumulator in LDS; wave w then combines output tiles
-  // w * NT/4 .. (w + 1) * NT/4 - 1 of every column, each lane the four dims
-  // its own accumulator lanes held (16-byte LDS reads), with the column's
-  // four weights computed once.
-  __syncthreads();  // every reader of the previous segment's merge is done
-  if (threadIdx.x == 0) sh.bad = 0;
-  __syncthreads();
-  if (bad) sh.bad = 1;
+  // its accumulator in LDS; then each half-wave combines one whole column
+  // (32 lanes x 4 dims): wave w takes columns w, w + 4, ..., its lower half
+  // the even ones of those.  Each lane reads the four waves' values of its
+  // four dims with 16-byte LDS reads and the column's four weights once, and
+  // a column's output row leaves as one contiguous run.
+  if (!first) __syncthreads();  // every reader of the previous segment's merge is done
+  if (lane == 0) sh.bad[w] = __builtin_amdgcn_ballot_w64(bad) != 0;
   if (quad == 0) {
     sh.m[w][n] = m;
     sh.l[w][n] = lsum;
   }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(&sh.o[w][n][16 * t + 4 * quad]) = o[t];
-  __syncthreads();
   if (n < ncol) {
-    const bool any_bad = sh.bad != 0;
-    float mw[kWaves], fw[kWaves];
-    float M = kNoMax;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      mw[ww] = sh.m[ww][n];
-      M = fmaxf(M, mw[ww]);
-    }
-    float L = 0.f;
+    for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(&sh.o[w][n][16 * t + 4 * quad]) = o[t];
+  }
+  __syncthreads();
+  static_assert(kWaves == 4, "one flag per wave");
+  static_assert(D == 4 * 32 || D == 2 * 32, "a half-wave covers a row in whole 4-dim pieces");
+  const bool any_bad = (sh.bad[0] | sh.bad[1] | sh.bad[2] | sh.bad[3]) != 0;
+  constexpr int kLanesPerRow = D / 4;  // lanes of one column's row
+  const int half = lane / 32;
+  for (int c = w + kWaves * half; c < ncol; c += 2 * kWaves) {
+    for (int part = lane % 32; part < kLanesPerRow; part += 32) {
+      const int d0 = 4 * part;
+      float mw[kWaves], M = kNoMax;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      fw[ww] = fast_exp2(mw[ww] - M);
-      L += fw[ww] * sh.l[ww][n];
-    }
-    const int64_t row = col_row(n);
-    const int64_t prow = row * P.nparts_max + seg;
-    constexpr int kTilesPerWave = NT / kWaves;
-#pragma unroll
-    for (int j = 0; j < kTilesPerWave; ++j) {
-      const int d0 = 16 * (w * kTilesPerWave + j) + 4 * quad;
+      for (int ww = 0; ww < kWaves; ++ww) {
+        mw[ww] = sh.m[ww][c];
+        M = fmaxf(M, mw[ww]);
+      }
+      float L = 0.f;
       f32x4_t O = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ww = 0; ww < kWaves; ++ww) O += fw[ww] * *reinterpret_cast<const f32x4_t*>(&sh.o[ww][n][d0]);
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const float f = fast_exp2(mw[ww] - M);
+        L += f * sh.l[ww][c];
+        O += f * *reinterpret_cast<const f32x4_t*>(&sh.o[ww][c][d0]);
+      }
       if (any_bad) O = f32x4_t{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+      const int64_t row = col_row(c);
       if (nseg == 1) {
         store_out4<T, OUT_F32>(P.out, row * D + d0, O * (1.f / L));
       } else {
+        const int64_t prow = row * P.nparts_max + seg;
         *reinterpret_cast<f32x4_t*>(P.ws_acc + prow * D + d0) = O;
+        if (d0 == 0) {
+          P.ws_m[prow] = M;
+          P.ws_l[prow] = L;
+        }
       }
-    }
-    if (nseg > 1 && w == 0 && quad == 0) {
-      P.ws_m[prow] = M;
-      P.ws_l[prow] = L;
     }
   }
 }
@@ -439,7 +446,7 @@ decode_partition_kernel(KParams P) {
   }
   const int tok0 = part * P.partition;
   if (tok0 >= ctx) return;
-  decode_segment<T, D, OUT_F32>(P, sh, s, g, ctx, tok0, min(P.partition, ctx - tok0), nparts, part);
+  decode_segment<T, D, OUT_F32>(P, sh, s, g, ctx, tok0, min(P.partition, ctx - tok0), nparts, part, true);
 }
 
 // The persistent grid.  Three waves per SIMD: two tiles in flight per wave
@@ -449,6 +456,7 @@ template <typename T, int D, bool OUT_F32>
 __global__ void __launch_bounds__(kThreads, 3)
 decode_persistent_kernel(KParams P) {
   __shared__ DecodeShared<D> sh;
+  __shared__ SplitShared sp;
   const int S = P.num_seqs;
   const int tid = threadIdx.x;
 
@@ -466,12 +474,12 @@ decode_persistent_kernel(KParams P) {
   int64_t mine = 0;
   for (int s = sa; s < sb; ++s) mine += weight(P.ctxs[s]);
   mine *= P.hkv;
-  sh.scan[tid] = mine;
+  sp.scan[tid] = mine;
   __syncthreads();
   if (tid < kWave) {
     int64_t a[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = sh.scan[4 * tid + i];
+    for (int i = 0; i < 4; ++i) a[i] = sp.scan[4 * tid + i];
     const int64_t tot = (a[0] + a[1]) + (a[2] + a[3]);
     int64_t inc = tot;
 #pragma unroll
@@ -482,13 +490,13 @@ decode_persistent_kernel(KParams P) {
     int64_t e = inc - tot;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sh.scan[4 * tid + i] = e;
+      sp.scan[4 * tid + i] = e;
       e += a[i];
     }
-    if (tid == kWave - 1) sh.total = inc;
+    if (tid == kWave - 1) sp.total = inc;
   }
   __syncthreads();
-  const int64_t T_all = uniform64(sh.total);
+  const int64_t T_all = uniform64(sp.total);
   const int ut = P.partition / kBlockTokens;  // tiles per partition
   // Every share holds at least one partition's worth of tiles, so each
   // workgroup between the first and the last owner of a pair's partitions
@@ -499,7 +507,7 @@ decode_persistent_kernel(KParams P) {
   const int64_t hi = b < nw ? T_all * (b + 1) / nw : lo;
   if (lo < hi) {
     // the thread whose sequences hold tile `lo` finds the first of them
-    const int64_t e = sh.scan[tid];
+    const int64_t e = sp.scan[tid];
     if (e <= lo && lo < e + mine) {
       int64_t base = e;
       int s = sa;
@@ -508,8 +516,8 @@ decode_persistent_kernel(KParams P) {
         if (base + ts > lo) break;
         base += ts;
       }
-      sh.s0 = s;
-      sh.base0 = base;
+      sp.s0 = s;
+      sp.base0 = base;
     }
   }
   __syncthreads();
@@ -518,8 +526,9 @@ decode_persistent_kernel(KParams P) {
     // its partition k starts at pb + k * ut and belongs to the workgroup
     // whose share holds that position
     auto owner = [&](int64_t x) { return ((x + 1) * nw - 1) / T_all; };
-    int s = uniform(sh.s0);
-    int64_t base = uniform64(sh.base0);
+    int s = uniform(sp.s0);
+    int64_t base = uniform64(sp.base0);
+    bool first = true;  // no earlier segment's merge to wait for
     while (s < S && base < hi) {
       const int ctx = uniform(P.ctxs[s]);
       const int t = weight(ctx);
@@ -537,7 +546,8 @@ decode_persistent_kernel(KParams P) {
           const int nseg = int(owner(last) - first_owner + 1);
           const int tok0 = k0 * P.partition;
           const int ntok = min((k1 + 1) * P.partition, ctx) - tok0;
-          decode_segment<T, D, OUT_F32>(P, sh, s, g, ctx, tok0, ntok, nseg, int(b - first_owner));
+          decode_segment<T, D, OUT_F32>(P, sh, s, g, ctx, tok0, ntok, nseg, int(b - first_owner), first);
+          first = false;
           if (k0 == 0 && P.ws_nseg != nullptr && tid == 0) P.ws_nseg[int64_t(s) * P.hkv + g] = nseg;
         }
       }
