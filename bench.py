@@ -483,6 +483,7 @@ def summarize_prefill(args, rec) -> None:
 
     busy, n = avg(rows, "SQ_VALU_MFMA_BUSY_CYCLES")
     cu, _ = avg(rows, "SQ_BUSY_CU_CYCLES")
+    vact, _ = avg(rows, "SQ_ACTIVE_INST_VALU")
     mfma, _ = avg(rows, "SQ_INSTS_MFMA")
     valu, _ = avg(rows, "SQ_INSTS_VALU")
     lds, _ = avg(rows, "SQ_INSTS_LDS")
@@ -495,20 +496,26 @@ def summarize_prefill(args, rec) -> None:
     md = [f"# Matrix-core utilisation of `prefill_mfma_kernel`: {wl}", "",
           "Two counter passes of the same command (one per counter block):", "", "```",
           f"timeout -s KILL 180 rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CU_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU "
-          f"SQ_INSTS_LDS SQ_WAVES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY --output-format csv -d {args.prefill_pmc_dir} -o pf "
-          f"-- {base}",
+          f"SQ_INSTS_LDS SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES SQ_WAIT_INST_ANY --output-format csv "
+          f"-d {args.prefill_pmc_dir} -o pf -- {base}",
           f"timeout -s KILL 180 rocprofv3 --pmc GRBM_GUI_ACTIVE --output-format csv -d {args.prefill_grbm_dir} "
           f"-o pfg -- {base}", "```", "",
           f"Per dispatch (mean of {n}):", "",
           f"- GRBM_GUI_ACTIVE {gui:.4g} (summed over the 8 XCDs: {gui / 8:.4g} cycles of the GPU clock)",
           f"- SQ_BUSY_CU_CYCLES {cu:.4g} (summed over CUs); SQ_VALU_MFMA_BUSY_CYCLES {busy:.4g} (summed over SIMDs)",
           f"- matrix pipe busy = MFMA_BUSY / (4 x BUSY_CU) = {busy / (4 * cu):.3f} of the time each SIMD is active",
-          f"- instructions: MFMA {mfma:.4g}, VALU {valu:.4g} ({valu / mfma:.2f} per MFMA), LDS {lds:.4g}",
+          f"- instructions: MFMA {mfma:.4g}, VALU {valu:.4g} (MFMAs included; {(valu - mfma) / mfma:.2f} others "
+          f"per MFMA), LDS {lds:.4g}",
+          f"- per SIMD (1024 of them): VALU {vact * 4 / 1024:.4g} cycles (SQ_ACTIVE_INST_VALU counts 4-cycle units: "
+          f"x4 matches the VALU count at 4 cycles each, 16 for an exponential), matrix {busy / 1024:.4g} cycles, "
+          f"busy {cu / 256:.4g} cycles; VALU hidden under matrix work = "
+          f"{max(0.0, (vact * 4 + busy) / 1024 - cu / 256):.4g} cycles",
           f"- SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES = {waits / wcyc:.3f} (waves stalled on a dependency)", "",
           "Same workload, bench.py without the profiler:", "",
           f"- {pf['ms']} ms for {pf['algorithmic_tflop']} TFLOP (4 D flops per attended (query, head, key)) = "
           f"{pf['tflops']} TFLOP/s = {pf['frac_of_dense_mfma_peak']:.3f} of the 2.5 PFLOP/s dense bf16 peak",
-          "- the PV product runs twice (P split hi + lo), so the matrix pipe executes 1.5x the algorithmic flops", ""]
+          "- per 64-key stage a wave issues 68 products for 64 algorithmic ones (32 QK, 32 PV, 4 row sums): "
+          "the matrix pipe executes 1.06x the algorithmic flops", ""]
     with open(os.path.join(ROOT, "profiles", f"prefill_{wl}_mfma.md"), "w") as f:
         f.write("\n".join(md))
     print("\n".join(md))

@@ -102,3 +102,35 @@ def test_prefill_follows_scores_that_keep_growing_along_the_context():
     k, v = p.oracle_pools()
     ref = OA.prefill_chunk(w.q, k, v, p.table, p.ctx, w.scale, "bf16")
     assert_close(out_f64(out), ref, "bf16", "growing scores")
+
+
+def test_prefill_with_values_beyond_half_precision_range():
+    """One V element of every third key block is 2^20, which half precision
+    cannot hold: such blocks keep their bf16 bits and every pair of blocks
+    that holds one (alone or beside a converted block) takes the bf16 path
+    with P split hi + lo, while the other pairs run on half precision.  Dim 0
+    carries the large values, so it is compared after scaling by 2^-20
+    (exact); the other dims at the usual tolerance."""
+    p = Prepared(make_workload("longctx_bf16", num_seqs=2, ctx=700, chunk=90, Hq=16, Hkv=2))
+    w = p.w
+    bits = w.v_pool.astype(np.uint32) << np.uint32(16)
+    v32 = bits.view(np.float32).reshape(w.v_pool.shape)
+    big = np.float32(2.0 ** 20)
+    flat = v32.reshape(v32.shape[0], -1)
+    for s in range(w.num_seqs):
+        for lb in range(0, -(-int(p.ctx[s]) // 16), 3):
+            # the pool's element order within a block is the library's; the
+            # oracle reads the same array, so any element of the block works
+            flat[p.table[s, lb], 5] = big
+    w.v_pool[...] = to_storage(v32, "bf16")
+    say("[prefill] values beyond half precision")
+    _, out = run_prefill(p)
+    got = out_f64(out)
+    k, v = p.oracle_pools()
+    ref = OA.prefill_chunk(w.q, k, v, p.table, p.ctx, w.scale, "bf16")
+    assert np.abs(ref).max() > 1e3, "the large values must reach the output"
+    scale = 2.0 ** -20
+    assert_close(got * scale, ref * scale, "bf16", "scaled by 2^-20")
+    small = np.abs(ref).max(axis=(0, 1, 2)) < 100  # dims the large values never reach
+    assert small.sum() > 100
+    assert_close(got[..., small], ref[..., small], "bf16", "dims without large values")
