@@ -7,15 +7,15 @@
 // Memory for KV Cache").
 //
 // Work split: rows are (query i, head n of the kv group), row = i * G + n.
-// One workgroup of 4 waves owns 128 consecutive rows (2 tiles of 16 per
-// wave) of one (kv head, sequence) and walks the keys in stages of 64 (4
-// blocks); wave w fetches block w of each stage for the whole workgroup.
-// K tiles go from HBM straight into LDS (16-byte direct-to-LDS loads).  V
-// tiles go through registers: the loading wave converts its tile to fp16
-// and stores it in LDS already in the A-operand layout of the PV product
-// (the two blocks of a pair side by side in each lane's 16 bytes), so each
-// operand is one 16-byte LDS read.  Both are double-buffered so the next
-// stage loads while this one computes.
+// One workgroup of 8 waves per CU owns 256 consecutive rows (2 tiles of 16
+// per wave) of one (kv head, sequence) and walks the keys in stages of 64
+// (4 blocks).  Waves 0-3 fetch the stage: K straight into LDS, V raw into
+// LDS (16-byte direct-to-LDS loads), one block per wave, double-buffered so
+// the next stage loads while this one computes.  The V tiles are then
+// converted to fp16 and stored in LDS in the A-operand layout of the PV
+// product (the two blocks of a pair side by side in each lane's 16 bytes),
+// so each operand is one 16-byte LDS read and each value is converted once
+// per 256 rows.
 // Products are written transposed as in decode, all on the 16x16x32
 // matrix instructions (the 16x16x16 forms run at half their rate):
 //   S^T[token][row] = K . Q^T                      (per 16-token block)
@@ -24,12 +24,12 @@
 // P is carried in fp16 (11 significant bits); the row sums are taken from
 // the same rounded P, so a weight's rounding changes numerator and
 // denominator together.  bf16 V is exact in fp16 below 2^16 in magnitude
-// (values under 2^-17 lose low bits, an absolute error below 2^-24); a
-// block holding anything larger, or a NaN, keeps its bf16 bits, and the
-// pair it belongs to runs with P split hi + lo in bf16 instead.  The grid
-// is one-dimensional and XCD-aware: all row tiles of one (sequence, kv
-// head) run on one XCD, so their shared K / V stream is fetched from HBM
-// once into that XCD's L2.
+// (values under 2^-17 lose low bits, an absolute error below 2^-24); a run
+// of V holding anything larger, or a NaN, keeps its bf16 bits, and the pair
+// of blocks it belongs to runs in bf16 with each weight split exactly into
+// hi + lo bf16 halves instead.  The grid is one-dimensional and XCD-aware:
+// all row tiles of one (sequence, kv head) run on one XCD, so their shared
+// K / V stream is fetched from HBM once into that XCD's L2.
 
 #include <math.h>
 
@@ -67,13 +67,8 @@ __device__ inline void store_row4(void* out, int64_t idx, f32x4_t v) {
   }
 }
 
-constexpr int kPfWaves = 4;
-constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kStageBlocks = 4;                        // 16-token blocks per stage
-constexpr int kTabWindow = 2048;                       // block-table entries held in LDS
 constexpr int kXcds = 8;
-constexpr int kPrefillRowTiles = 2;      // 16-row tiles per wave
-constexpr int kPrefillWavesPerSimd = 2;  // register budget: two waves per SIMD
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -121,35 +116,54 @@ constexpr float kPOffset = 7.f;
 // NaN) keeps its bf16 bits
 constexpr float kF16Limit = 65536.f;
 
-// RT 16-row tiles per wave; WPE waves per SIMD the register budget is cut for
-template <typename T, int D, bool OUT_F32, int RT, int WPE>
-__global__ void __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+// ---------------------------------------------------------------------------
+// Ping-pong form: one workgroup of 8 waves per CU owns 256 rows; waves 0-3
+// (group 0) and 4-7 (group 1) own 128 of them each.  Every wave runs the same
+// sequence per stage k, a matrix phase M(k) = PV(k-1) + QK(k) and a VALU
+// phase S(k) (row max, reference check and rescale, P in fp16, and the
+// conversion of a share of V), separated by workgroup barriers; group 1 runs
+// one phase behind group 0 (it passes one barrier first, group 0 one last),
+// so each SIMD always has one wave in its products and one in its vector
+// work (the hardware overlaps the two across waves, not within one wave's
+// instruction stream).  Group 0 fetches stage k+1 (K straight into LDS, V raw
+// into LDS) at the start of M(k) and waits for it at the end of S(k); S(j) of
+// group h converts its half of V(j + h) into the operand buffer.  K, raw V
+// and V operands are double-buffered.  The masked tail runs afterwards, both
+// groups in step.
+// ---------------------------------------------------------------------------
+constexpr int kPpWaves = 8;
+constexpr int kPpThreads = kPpWaves * kWave;
+constexpr int kPpRowTiles = 2;  // 16-row tiles per wave
+
+template <typename T, int D, bool OUT_F32>
+__global__ void __launch_bounds__(kPpThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   constexpr bool kBf16 = std::is_same<T, Bf16>::value;
-  constexpr int kPfRT = RT;
-  constexpr int kPfRows = kPfWaves * kPfRT * 16;  // rows per workgroup
-  constexpr int DC = D / 32;                         // 16-byte chunks per lane per tile
-  constexpr int NT = D / 16;                         // 16-dim output tiles
+  constexpr int RT = kPpRowTiles;
+  constexpr int kRows = kPpWaves * RT * 16;  // rows per workgroup
+  constexpr int DC = D / 32;                  // 16-byte chunks per lane per tile
+  constexpr int NT = D / 16;                  // 16-dim output tiles
   constexpr int kTileElems = kBlockTokens * D;
   constexpr int kTileBytes = kTileElems * 2;
-  constexpr int kRunsPerTile = kTileBytes / 1024;    // 1 KiB wave loads per tile
-  static_assert(kRunsPerTile == DC, "one 16-byte chunk per lane per 1 KiB run");
-  static_assert(kStageBlocks == kPfWaves, "each wave loads one block of a stage");
-  constexpr int kStageU4 = kStageBlocks * kTileElems / 8;  // u32x4 per stage buffer (K or V)
+  constexpr int kRuns = kTileBytes / 1024;    // 1 KiB wave loads per tile
+  constexpr int kRunsPerWave = kRuns / 2;     // each group converts half of a block's runs
+  static_assert(kRuns == DC && kRunsPerWave >= 1, "one 16-byte chunk per lane per run, two waves per block");
+  static_assert(2 * kStageBlocks == kPpWaves, "a block per wave of a group");
+  constexpr int kStageU4 = kStageBlocks * kTileElems / 8;  // u32x4 per stage buffer
 
   __shared__ u32x4_t s_k0[kStageU4];
   __shared__ u32x4_t s_k1[kStageU4];
-  // V operands of a stage: [pair][output tile t][lane] 16 bytes = the lane's
-  // 4 tokens of dim 16 t + (lane % 16) in the pair's first block, then the
-  // same in its second block
-  __shared__ u32x4_t s_v0[kStageU4];
-  __shared__ u32x4_t s_v1[kStageU4];
-  __shared__ int32_t s_tab[kTabWindow];
-  __shared__ int s_vkeep[2][kStageBlocks];  // per V buffer: block kept in bf16
+  __shared__ u32x4_t s_r0[kStageU4];  // raw V tiles
+  __shared__ u32x4_t s_r1[kStageU4];
+  // V operands: [pair][output tile t][lane] 16 bytes = the lane's 4 tokens
+  // of dim 16 t + (lane % 16) in the pair's first block, then in its second
+  __shared__ u32x4_t s_o0[kStageU4];
+  __shared__ u32x4_t s_o1[kStageU4];
+  // per operand buffer, byte 2 b + h set = the runs of block b converted by
+  // group h kept their bf16 bits (word pr covers the blocks of pair pr)
+  __shared__ uint32_t s_keep[2][2];
   __shared__ int s_bad;
 
-  // XCD-aware work order: workgroup id % 8 picks the XCD; groups of 8
-  // (sequence, kv head) pairs are dealt one per XCD, each with all its tiles
   const int id = blockIdx.x;
   const int full = (num_pairs / kXcds) * kXcds;
   int pair, tile;
@@ -166,18 +180,18 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
 
   const int lane = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int grp = w >> 2;
   const int n = lane & 15, quad = lane >> 4;
   const int G = P.hq / P.hkv;
   const int C = P.chunk;
   const int R = C * G;
   const int ctx = P.ctxs[s];
-  const int row_wg0 = tile * kPfRows;
+  const int row_wg0 = tile * kRows;
   if (row_wg0 >= R) return;
 
   if (ctx < C || ctx > P.max_ctx || int64_t(ctx) > (int64_t(P.max_blocks) * kBlockTokens << P.tile_shift)) {
-    // contract violation: NaN rows for this workgroup's share
     const float nan = __builtin_nanf("");
-    for (int idx = threadIdx.x; idx < kPfRows * D; idx += kPfThreads) {
+    for (int idx = threadIdx.x; idx < kRows * D; idx += kPpThreads) {
       const int row = row_wg0 + idx / D, d = idx % D;
       if (row >= R) break;
       const int i = row / G, hh = row - i * G;
@@ -188,13 +202,12 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
     return;
   }
 
-  // rows of this lane (one per row tile), their last attended key, Q^T operands
-  int last[kPfRT];
-  bool live[kPfRT];
-  u32x4_t qb[kPfRT][DC];
+  int last[RT];
+  bool live[RT];
+  u32x4_t qb[RT][DC];
 #pragma unroll
-  for (int rt = 0; rt < kPfRT; ++rt) {
-    const int row = row_wg0 + (w * kPfRT + rt) * 16 + n;
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = row_wg0 + (w * RT + rt) * 16 + n;
     live[rt] = row < R;
     const int i = live[rt] ? row / G : 0;
     const int hh = live[rt] ? row - i * G : 0;
@@ -206,14 +219,13 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
     }
   }
   // Wait for the Q operands here, on every path.  Left to the compiler, the
-  // wait lands at their first use inside the key loop, where a path that
-  // skips the first stage's load makes it count the next stage's tile
-  // loads too: every other stage then waited for its successor's tiles
-  // before its first product (a third of the kernel's time).
+  // wait lands at their first use inside the key loop, where it counts the
+  // next stage's tile loads too and every stage then waits for its
+  // successor's tiles before its first product.
   wait_loads();
-  const int row_wg_last = min(R, row_wg0 + kPfRows) - 1;
-  const int first_masked = ctx - C + row_wg0 / G;          // smallest last-key of the workgroup's rows
-  const int nkb = (ctx - C + row_wg_last / G) / kBlockTokens + 1;  // key blocks any row needs
+  const int row_wg_last = min(R, row_wg0 + kRows) - 1;
+  const int first_masked = ctx - C + row_wg0 / G;
+  const int nkb = (ctx - C + row_wg_last / G) / kBlockTokens + 1;
   const int nst = (nkb + kStageBlocks - 1) / kStageBlocks;
   const int32_t* trow = P.tables + int64_t(s) * P.max_blocks;
   const int sh = P.tile_shift;
@@ -221,11 +233,11 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   const char* kg = reinterpret_cast<const char*>(P.k + (int64_t(g) << sh) * kTileElems);
   const char* vg = reinterpret_cast<const char*>(P.v + (int64_t(g) << sh) * kTileElems);
 
-  float m[kPfRT];
-  f32x4_t lacc[kPfRT];  // row sums, every element of a lane holds its row's
-  f32x4_t o[kPfRT][NT];
+  float m[RT];
+  f32x4_t lacc[RT];
+  f32x4_t o[RT][NT];
 #pragma unroll
-  for (int rt = 0; rt < kPfRT; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     m[rt] = -INFINITY;
     lacc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -233,24 +245,25 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   }
   int bad = 0;
 
-  int tab_base = 0;
-  auto fill_table = [&](int base) {  // all threads; caller synchronises
-    // one entry per 16-token tile (a block of 2^sh tiles repeats its entry)
-    for (int j = threadIdx.x; j < kTabWindow && base + j < nkb; j += kPfThreads) s_tab[j] = trow[(base + j) >> sh];
+  // Table entry (physical block) of this wave's block of stage st (a block
+  // of 2^sh tiles repeats its entry); -1 past the key window.  It is a
+  // vector load: the main loop loads it a stage ahead and reads it into a
+  // scalar only when it issues that stage, so its wait never covers the
+  // tile loads issued just before it.
+  const int my_blk = w & 3;
+  auto load_entry = [&](int st) __attribute__((always_inline)) {
+    const int blk = st * kStageBlocks + my_blk;
+    return blk < nkb ? trow[blk >> sh] : -1;
   };
-
-  // Loads of the stage's tiles: each lane moves 16 bytes per 1 KiB run.
-  // Wave w fetches block w of the stage: its K tile into LDS directly, its
-  // V tile into vreg.
-  // One lookup and one buffer resource per tile (base in scalar registers,
-  // range = the tile), so each load needs only the lane's 16-byte offset
-  // and the run's scalar offset; a block past the key window or outside the
-  // pool gets an empty range and reads as zeros without touching memory.
+  auto lookup = [&](int st) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(load_entry(st)); };
+  // Fetch runs [r0, r0 + nr) of block my_blk of stage st, K and raw V,
+  // straight into LDS (one buffer resource per tile; a block past the key
+  // window or outside the pool gets an empty range and reads as zeros).
   const int lane_off = lane * 16;
-  u32x4_t vreg[DC];
-  auto issue_stage = [&](int st, u32x4_t* kbuf) {
-    const int blk = st * kStageBlocks + w;
-    const int phys = blk < nkb ? __builtin_amdgcn_readfirstlane(s_tab[blk - tab_base]) : 0;
+  auto issue_runs = [&](int st, int phys, u32x4_t* kbuf, u32x4_t* rbuf, int r0, auto nr_tag)
+      __attribute__((always_inline)) {
+    constexpr int NR = decltype(nr_tag)::value;
+    const int blk = st * kStageBlocks + my_blk;
     const bool in_pool = phys >= 0 && int64_t(phys) < P.num_blocks;
     bad |= blk < nkb && !in_pool;
     const bool ok = blk < nkb && in_pool;
@@ -260,110 +273,96 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vg + off), 0,
                                                                         ok ? kTileBytes : 0, kBufferRsrcWord3);
 #pragma unroll
-    for (int part = 0; part < kRunsPerTile; ++part) {
-      lds_void* dst = (lds_void*)(kbuf + w * (kTileElems / 8) + part * 64);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, lane_off, part * 1024, 0, 0);
+    for (int i = 0; i < NR; ++i) {
+      const int part = r0 + i;
+      lds_void* dk = (lds_void*)(kbuf + my_blk * (kTileElems / 8) + part * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dk, 16, lane_off, part * 1024, 0, 0);
+      lds_void* dv = (lds_void*)(rbuf + my_blk * (kTileElems / 8) + part * 64);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dv, 16, lane_off, part * 1024, 0, 0);
     }
-#pragma unroll
-    for (int part = 0; part < kRunsPerTile; ++part)
-      vreg[part] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, lane_off, part * 1024, 0));
   };
 
-  // The wave's V tile (block w of the stage) to LDS in the operand layout,
-  // as fp16 when every value converts exactly.  Chunk cc of a V tile holds,
-  // for lane (quad, n), tokens 4 quad + 0..3 of dim 32 cc + n (first 8
-  // bytes) and of dim 32 cc + 16 + n (last 8 bytes): the lane's part of
-  // output tiles 2 cc and 2 cc + 1.
+  // Group grp's runs of block my_blk, raw V to the operand buffer, as fp16
+  // when every value converts exactly.  Run cc of a V tile holds, for lane
+  // (quad, n), tokens 4 quad + 0..3 of dim 32 cc + n (first 8 bytes) and of
+  // dim 32 cc + 16 + n (last 8 bytes): the lane's part of output tiles 2 cc
+  // and 2 cc + 1, stored beside the paired block's part.
   typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
-  auto commit_v = [&](u32x4_t* vbuf, int slot) {
-    u32x2_t* dst = reinterpret_cast<u32x2_t*>(vbuf) + ((w >> 1) * NT * 64 + lane) * 2 + (w & 1);
+  const int run0 = grp * kRunsPerWave;
+  auto convert_own = [&](const u32x4_t* rbuf, u32x4_t* obuf, int slot) __attribute__((always_inline)) {
+    u32x2_t* dst = reinterpret_cast<u32x2_t*>(obuf) + ((my_blk >> 1) * NT * 64 + lane) * 2 + (my_blk & 1);
+    u32x4_t x[kRunsPerWave], y[kRunsPerWave];
+#pragma unroll
+    for (int i = 0; i < kRunsPerWave; ++i) x[i] = rbuf[my_blk * (kTileElems / 8) + (run0 + i) * 64 + lane];
     bool keep = false;
-    u32x4_t y[DC];
     if constexpr (kBf16) {
       float big = 0.f;
 #pragma unroll
-      for (int cc = 0; cc < DC; ++cc)
+      for (int i = 0; i < kRunsPerWave; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) y[cc][j] = bf16x2_to_f16x2(vreg[cc][j], big);
+        for (int j = 0; j < 4; ++j) y[i][j] = bf16x2_to_f16x2(x[i][j], big);
       keep = __builtin_amdgcn_ballot_w64(!(big < kF16Limit)) != 0;
     }
     if (!kBf16 || keep) {
 #pragma unroll
-      for (int cc = 0; cc < DC; ++cc) y[cc] = vreg[cc];
+      for (int i = 0; i < kRunsPerWave; ++i) y[i] = x[i];
     }
 #pragma unroll
-    for (int cc = 0; cc < DC; ++cc) {
-      dst[(2 * cc) * 64 * 2] = u32x2_t{y[cc][0], y[cc][1]};
-      dst[(2 * cc + 1) * 64 * 2] = u32x2_t{y[cc][2], y[cc][3]};
+    for (int i = 0; i < kRunsPerWave; ++i) {
+      const int cc = run0 + i;
+      dst[(2 * cc) * 64 * 2] = u32x2_t{y[i][0], y[i][1]};
+      dst[(2 * cc + 1) * 64 * 2] = u32x2_t{y[i][2], y[i][3]};
     }
-    if (lane == 0) s_vkeep[slot][w] = keep;
+    if (lane == 0) reinterpret_cast<uint8_t*>(s_keep[slot])[my_blk * 2 + grp] = keep;
   };
 
-  // Scores are kept raw (q . k) and the scale is folded into the exponent:
-  // p = 2^(c s - m) with c = scale * log2(e) > 0 (a negative scale flips the
-  // sign bits of q, which is exact; a zero scale becomes a tiny positive one
-  // so masked keys stay at -inf), so the row max is taken over raw scores.
   float c = P.scale_log2;
   if (c < 0.f) {
     c = -c;
 #pragma unroll
-    for (int rt = 0; rt < kPfRT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int cc = 0; cc < DC; ++cc) qb[rt][cc] ^= u32x4_t{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
   }
   c = fmaxf(c, 1e-30f);
-
   const u32x4_t ones_f16 = u32x4_t{0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
-  const u32x4_t ones_bf16 = u32x4_t{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
-  // MASKED: the stage holds keys past some row's causal limit, past the
-  // context or past the key window; every other stage skips all mask work
-  auto compute_stage = [&](auto masked_tag, int st, const u32x4_t* kbuf, const u32x4_t* vbuf, int slot) {
+
+  // ---- QK of stage st: raw scores, -inf outside the causal / context window
+  auto qk = [&](auto masked_tag, int st, const u32x4_t* kbuf, f32x4_t (&sc)[RT][kStageBlocks])
+      __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
     const int k0 = st * kStageBlocks * kBlockTokens;
-    const int nvalid = min(kStageBlocks, nkb - st * kStageBlocks);  // blocks of this stage in the key window
-    // ---- raw scores of the stage's 4 blocks for both row tiles
-    f32x4_t sc[kPfRT][kStageBlocks];
-    auto scores = [&]() {
+    const int nvalid = min(kStageBlocks, nkb - st * kStageBlocks);
 #pragma unroll
-      for (int b = 0; b < kStageBlocks; ++b) {
-        u32x4_t kf[DC];
+    for (int b = 0; b < kStageBlocks; ++b) {
+      u32x4_t kf[DC];
 #pragma unroll
-        for (int cc = 0; cc < DC; ++cc) kf[cc] = kbuf[b * (kTileElems / 8) + cc * 64 + lane];
+      for (int cc = 0; cc < DC; ++cc) kf[cc] = kbuf[b * (kTileElems / 8) + cc * 64 + lane];
 #pragma unroll
-        for (int rt = 0; rt < kPfRT; ++rt) {
-          f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int rt = 0; rt < RT; ++rt) {
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int cc = 0; cc < DC; ++cc) acc = Mfma<T>::k32(kf[cc], qb[rt][cc], acc);
-          if constexpr (MASKED) {
+        for (int cc = 0; cc < DC; ++cc) acc = Mfma<T>::k32(kf[cc], qb[rt][cc], acc);
+        if constexpr (MASKED) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = k0 + b * kBlockTokens + 4 * quad + r;
-              acc[r] = (key <= last[rt] && b < nvalid) ? acc[r] : -INFINITY;
-            }
+          for (int r = 0; r < 4; ++r) {
+            const int key = k0 + b * kBlockTokens + 4 * quad + r;
+            acc[r] = (key <= last[rt] && b < nvalid) ? acc[r] : -INFINITY;
           }
-          sc[rt][b] = acc;
         }
+        sc[rt][b] = acc;
       }
-    };
-    // ---- P of pair pr: 8 values per lane and row tile = tokens 4 quad +
-    // 0..3 of the pair's first block, then of its second (the k order of
-    // the V operands)
-    auto probabilities = [&](int pr, float (&pv)[kPfRT][8]) {
-#pragma unroll
-      for (int rt = 0; rt < kPfRT; ++rt) {
-        const float neg_m = kPOffset - m[rt];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pv[rt][e] = fast_exp2(fmaf(sc[rt][2 * pr + e / 4][e % 4], c, neg_m));
-      }
-    };
-    scores();
-    // ---- one reference-max check per stage: the max moves only past a 2^8
-    // margin (rare after the first stage), so the accumulator rescale is
-    // mostly skipped and the rest of the stage is straight-line code
-    float bm[kPfRT];
+    }
+  };
+  // ---- S: row max, reference check and rescale, P in fp16 (8 values per
+  // lane, row tile and pair: tokens 4 quad + 0..3 of the pair's first block,
+  // then of its second)
+  auto softmax = [&](const f32x4_t (&sc)[RT][kStageBlocks], u32x4_t (&ph)[RT][kStageBlocks / 2])
+      __attribute__((always_inline)) {
+    float bm[RT];
     bool grow_any = false;
 #pragma unroll
-    for (int rt = 0; rt < kPfRT; ++rt) {
+    for (int rt = 0; rt < RT; ++rt) {
       float v = -INFINITY;
 #pragma unroll
       for (int b = 0; b < kStageBlocks; ++b)
@@ -373,7 +372,7 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
     }
     if (__builtin_amdgcn_ballot_w64(grow_any)) {
 #pragma unroll
-      for (int rt = 0; rt < kPfRT; ++rt) {
+      for (int rt = 0; rt < RT; ++rt) {
         const float mn = bm[rt] > m[rt] + 8.f ? bm[rt] : m[rt];
         const float alpha = fast_exp2(m[rt] - mn);
         lacc[rt] *= alpha;
@@ -382,153 +381,162 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
         m[rt] = mn;
       }
     }
-    // ---- O^T += V^T P^T and l += 1 P^T over each pair of blocks (K = 32)
-    auto pair_masks = [&](int pr, uint32_t (&mk)[4]) {
-      mk[0] = mk[1] = mk[2] = mk[3] = ~0u;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float neg_m = kPOffset - m[rt];
+#pragma unroll
+      for (int pr = 0; pr < kStageBlocks / 2; ++pr) {
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(sc[rt][2 * pr + j / 4][j % 4], c, neg_m));
+        ph[rt][pr] = u32x4_t{f16x2_rne(e[0], e[1]), f16x2_rne(e[2], e[3]), f16x2_rne(e[4], e[5]), f16x2_rne(e[6], e[7])};
+      }
+    }
+  };
+  // ---- PV of stage st: O^T += V^T P^T and l += 1 P^T per pair (K = 32)
+  auto pv = [&](auto masked_tag, int st, const u32x4_t* obuf, int slot, const u32x4_t (&ph)[RT][kStageBlocks / 2])
+      __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+#pragma unroll
+    for (int pr = 0; pr < kStageBlocks / 2; ++pr) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) lacc[rt] = Mfma<F16>::k32(ones_f16, ph[rt][pr], lacc[rt]);
+      uint32_t mk[4] = {~0u, ~0u, ~0u, ~0u};
       if constexpr (MASKED) {
-        // blocks outside the window and slots past the context may hold
-        // anything (NaN included): zero them so 0 * garbage never reaches o
+        const int k0 = st * kStageBlocks * kBlockTokens;
+        const int nvalid = min(kStageBlocks, nkb - st * kStageBlocks);
         const int t0 = k0 + 4 * quad;
         const int b0 = 2 * pr, b1 = 2 * pr + 1;
-        const int e0 = b0 < nvalid ? ctx - (t0 + b0 * kBlockTokens) : 0;  // valid tokens of the quad
+        const int e0 = b0 < nvalid ? ctx - (t0 + b0 * kBlockTokens) : 0;
         const int e1 = b1 < nvalid ? ctx - (t0 + b1 * kBlockTokens) : 0;
         mk[0] = (e0 > 0 ? 0x0000FFFFu : 0u) | (e0 > 1 ? 0xFFFF0000u : 0u);
         mk[1] = (e0 > 2 ? 0x0000FFFFu : 0u) | (e0 > 3 ? 0xFFFF0000u : 0u);
         mk[2] = (e1 > 0 ? 0x0000FFFFu : 0u) | (e1 > 1 ? 0xFFFF0000u : 0u);
         mk[3] = (e1 > 2 ? 0x0000FFFFu : 0u) | (e1 > 3 ? 0xFFFF0000u : 0u);
       }
-    };
-#pragma unroll
-    for (int pr = 0; pr < kStageBlocks / 2; ++pr) {
-      float pv[kPfRT][8];
-      probabilities(pr, pv);
-      uint32_t mk[4];
-      pair_masks(pr, mk);
-      const u32x4_t* vop = vbuf + pr * NT * 64 + lane;
-      bool keep0 = false, keep1 = false;
-      if constexpr (kBf16) {
-        keep0 = __builtin_amdgcn_readfirstlane(s_vkeep[slot][2 * pr]) != 0;
-        keep1 = __builtin_amdgcn_readfirstlane(s_vkeep[slot][2 * pr + 1]) != 0;
-      }
-      if (!keep0 && !keep1) {
-        // P in fp16, one product per operand
-        u32x4_t ph[kPfRT];
-#pragma unroll
-        for (int rt = 0; rt < kPfRT; ++rt) {
-          ph[rt] = u32x4_t{f16x2_rne(pv[rt][0], pv[rt][1]), f16x2_rne(pv[rt][2], pv[rt][3]),
-                           f16x2_rne(pv[rt][4], pv[rt][5]), f16x2_rne(pv[rt][6], pv[rt][7])};
-          lacc[rt] = Mfma<F16>::k32(ones_f16, ph[rt], lacc[rt]);
-        }
+      const u32x4_t* vop = obuf + pr * NT * 64 + lane;
+      uint32_t keep = 0;
+      if constexpr (kBf16) keep = __builtin_amdgcn_readfirstlane(s_keep[slot][pr]);
+      if (keep == 0) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           u32x4_t av = vop[t * 64];
           if constexpr (MASKED) av = av & u32x4_t{mk[0], mk[1], mk[2], mk[3]};
 #pragma unroll
-          for (int rt = 0; rt < kPfRT; ++rt) o[rt][t] = Mfma<F16>::k32(av, ph[rt], o[rt][t]);
+          for (int rt = 0; rt < RT; ++rt) o[rt][t] = Mfma<F16>::k32(av, ph[rt][pr], o[rt][t]);
         }
       } else if constexpr (kBf16) {
-        // a block of the pair holds V beyond fp16: the pair runs in bf16
-        // with P split hi + lo (fp16 halves go back to bf16, exactly)
-        u32x4_t ph[kPfRT], pl[kPfRT];
+        // V of the pair partly kept in bf16: the pair runs in bf16 with each
+        // fp16 weight split exactly into hi + lo bf16 halves (one row tile at
+        // a time: this rare path must not hold more registers than the
+        // common one)
 #pragma unroll
-        for (int rt = 0; rt < kPfRT; ++rt) {
-          uint16_t hi[8], lo[8];
+        for (int rt = 0; rt < RT; ++rt) {
+          u32x4_t phi, plo;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            hi[e] = Bf16::from_float(pv[rt][e]);
-            lo[e] = Bf16::from_float(pv[rt][e] - Bf16::to_float(hi[e]));
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t x = ph[rt][pr][j];
+            const float a = F16::to_float(uint16_t(x)), b = F16::to_float(uint16_t(x >> 16));
+            const uint16_t ha = Bf16::from_float(a), hb = Bf16::from_float(b);
+            phi[j] = pack2(ha, hb);
+            plo[j] = pack2(Bf16::from_float(a - Bf16::to_float(ha)), Bf16::from_float(b - Bf16::to_float(hb)));
           }
-          ph[rt] = u32x4_t{pack2(hi[0], hi[1]), pack2(hi[2], hi[3]), pack2(hi[4], hi[5]), pack2(hi[6], hi[7])};
-          pl[rt] = u32x4_t{pack2(lo[0], lo[1]), pack2(lo[2], lo[3]), pack2(lo[4], lo[5]), pack2(lo[6], lo[7])};
-          lacc[rt] = Mfma<Bf16>::k32(ones_bf16, ph[rt], lacc[rt]);
-          lacc[rt] = Mfma<Bf16>::k32(ones_bf16, pl[rt], lacc[rt]);
-        }
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          u32x4_t av = vop[t * 64];
-          if (!keep0) {
-            av[0] = f16x2_to_bf16x2(av[0]);
-            av[1] = f16x2_to_bf16x2(av[1]);
-          }
-          if (!keep1) {
-            av[2] = f16x2_to_bf16x2(av[2]);
-            av[3] = f16x2_to_bf16x2(av[3]);
-          }
-          if constexpr (MASKED) av = av & u32x4_t{mk[0], mk[1], mk[2], mk[3]};
-#pragma unroll
-          for (int rt = 0; rt < kPfRT; ++rt) {
-            o[rt][t] = Mfma<Bf16>::k32(av, ph[rt], o[rt][t]);
-            o[rt][t] = Mfma<Bf16>::k32(av, pl[rt], o[rt][t]);
+          for (int t = 0; t < NT; ++t) {
+            u32x4_t av = vop[t * 64];
+            const int h = (t / 2) / kRunsPerWave;  // group that converted run t / 2
+            if (!((keep >> (8 * h)) & 0xFFu)) {
+              av[0] = f16x2_to_bf16x2(av[0]);
+              av[1] = f16x2_to_bf16x2(av[1]);
+            }
+            if (!((keep >> (8 * (2 + h))) & 0xFFu)) {
+              av[2] = f16x2_to_bf16x2(av[2]);
+              av[3] = f16x2_to_bf16x2(av[3]);
+            }
+            if constexpr (MASKED) av = av & u32x4_t{mk[0], mk[1], mk[2], mk[3]};
+            o[rt][t] = Mfma<Bf16>::k32(av, phi, o[rt][t]);
+            o[rt][t] = Mfma<Bf16>::k32(av, plo, o[rt][t]);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
     }
   };
-  // Stages wholly below every row's causal limit and inside the key window
-  // (all but the last few) need no masks: they run double-buffered, the next
-  // stage loading while this one computes.  The masked tail runs one stage at
-  // a time.
-  const int nst_plain = min(nst, (first_masked + 1) / (kStageBlocks * kBlockTokens));
-  auto refill_table_for = [&](int st) {
-    // keep the table window over the blocks of stage st (it only moves
-    // forward; the check both ways keeps a stale window from being read)
-    if (st * kStageBlocks < tab_base || (st + 1) * kStageBlocks - tab_base > kTabWindow) {
-      __syncthreads();
-      tab_base = st * kStageBlocks;
-      fill_table(tab_base);
-      __syncthreads();
-    }
-  };
+
+  const int K = min(nst, (first_masked + 1) / (kStageBlocks * kBlockTokens));  // plain stages
+  f32x4_t sc[RT][kStageBlocks];
+  u32x4_t ph[RT][kStageBlocks / 2];
   if (threadIdx.x == 0) s_bad = 0;
-  fill_table(0);
-  __syncthreads();
-  if (nst_plain > 0) {
-    issue_stage(0, s_k0);
-    wait_loads();
-    commit_v(s_v0, 0);
+  int entry_next = 0;  // group 0: table entry of the stage it fetches next
+  if (K > 0) {
+    if (grp == 0) {
+      issue_runs(0, lookup(0), s_k0, s_r0, 0, std::integral_constant<int, kRuns>{});
+      if (K > 1) entry_next = load_entry(1);
+      wait_loads();
+    }
+    __syncthreads();
+    if (grp == 1) {
+      convert_own(s_r0, s_o0, 0);  // group 1's share of V(0), in the phase group 0 spends on M(0)
+      __syncthreads();
+    }
+  }
+  // One stage: M(k), barrier, S(k), barrier.  Stage k uses buffers k % 2
+  // (fixed names per half of the loop body, so the compiler sees the loads
+  // into one never alias reads of the other).
+  auto stage = [&](int k, const u32x4_t* kb, const u32x4_t* ob_prev, int slot_prev, u32x4_t* kb_next,
+                   u32x4_t* rb_next, const u32x4_t* rb, u32x4_t* ob, int slot, u32x4_t* ob_next, int slot_next)
+      __attribute__((always_inline)) {
+    if (grp == 0 && k + 1 < K) {
+      issue_runs(k + 1, __builtin_amdgcn_readfirstlane(entry_next), kb_next, rb_next, 0,
+                 std::integral_constant<int, kRuns>{});
+      if (k + 2 < K) entry_next = load_entry(k + 2);
+    }
+    if (k > 0) pv(std::false_type{}, k - 1, ob_prev, slot_prev, ph);
+    qk(std::false_type{}, k, kb, sc);
+    __syncthreads();
+    softmax(sc, ph);
+    if (grp == 0) {
+      convert_own(rb, ob, slot);  // V(k)
+      wait_loads();               // stage k + 1
+    } else if (k + 1 < K) {
+      convert_own(rb_next, ob_next, slot_next);  // V(k + 1)
+    }
+    __syncthreads();
+  };
+  for (int k = 0; k < K; k += 2) {
+    stage(k, s_k0, s_o1, 1, s_k1, s_r1, s_r0, s_o0, 0, s_o1, 1);
+    if (k + 1 >= K) break;
+    stage(k + 1, s_k1, s_o0, 0, s_k0, s_r0, s_r1, s_o1, 1, s_o0, 0);
+  }
+  if (K > 0) {
+    // M(K): PV of the last plain stage; then the two groups meet again
+    if ((K - 1) % 2 == 0) pv(std::false_type{}, K - 1, s_o0, 0, ph);
+    else pv(std::false_type{}, K - 1, s_o1, 1, ph);
+    if (grp == 0) __syncthreads();
     __syncthreads();
   }
-  // two stages per iteration so each buffer has a fixed name (the compiler
-  // then knows the loads into one never alias reads of the other)
-  for (int st = 0; st < nst_plain; st += 2) {
-    const bool next1 = st + 1 < nst_plain;
-    if (next1) {
-      refill_table_for(st + 1);
-      issue_stage(st + 1, s_k1);
-    }
-    compute_stage(std::false_type{}, st, s_k0, s_v0, 0);
+  // masked tail: both groups in step, each wave fetching half a block
+  for (int st = K; st < nst; ++st) {
+    issue_runs(st, lookup(st), s_k0, s_r0, run0, std::integral_constant<int, kRunsPerWave>{});
     wait_loads();
-    if (next1) commit_v(s_v1, 1);
     __syncthreads();
-    if (!next1) break;
-    const bool next2 = st + 2 < nst_plain;
-    if (next2) {
-      refill_table_for(st + 2);
-      issue_stage(st + 2, s_k0);
-    }
-    compute_stage(std::false_type{}, st + 1, s_k1, s_v1, 1);
-    wait_loads();
-    if (next2) commit_v(s_v0, 0);
+    convert_own(s_r0, s_o0, 0);
     __syncthreads();
-  }
-  for (int st = nst_plain; st < nst; ++st) {
-    refill_table_for(st);
-    issue_stage(st, s_k0);
-    wait_loads();
-    commit_v(s_v0, 0);
-    __syncthreads();
-    compute_stage(std::true_type{}, st, s_k0, s_v0, 0);
+    f32x4_t scm[RT][kStageBlocks];
+    u32x4_t phm[RT][kStageBlocks / 2];
+    qk(std::true_type{}, st, s_k0, scm);
+    softmax(scm, phm);
+    pv(std::true_type{}, st, s_o0, 0, phm);
     __syncthreads();
   }
 
-  // an out-of-pool table entry seen by any wave poisons every row
   if (bad) s_bad = 1;
   __syncthreads();
   const bool any_bad = s_bad != 0;
 #pragma unroll
-  for (int rt = 0; rt < kPfRT; ++rt) {
+  for (int rt = 0; rt < RT; ++rt) {
     if (!live[rt]) continue;
-    const int row = row_wg0 + (w * kPfRT + rt) * 16 + n;
+    const int row = row_wg0 + (w * RT + rt) * 16 + n;
     const int i = row / G, hh = row - i * G;
     const int64_t obase = ((int64_t(s) * C + i) * P.hq + int64_t(g) * G + hh) * D;
     const float inv = any_bad ? __builtin_nanf("") : 1.f / lacc[rt][0];
@@ -539,18 +547,16 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
 
 template <typename T, int D>
 hipError_t launch_prefill_t(const PrefillArgs& a, const PParams& p) {
-  constexpr int RT = kPrefillRowTiles, WPE = kPrefillWavesPerSimd;
-  constexpr int rows = kPfWaves * RT * 16;
+  constexpr int rows = kPpWaves * kPpRowTiles * 16;
   const int G = a.num_q_heads / a.num_kv_heads;
   const int64_t R = int64_t(a.chunk) * G;
   const int tiles = int((R + rows - 1) / rows);
   const int pairs = a.num_seqs * a.num_kv_heads;  // the caller bounds tiles x pairs by INT32_MAX
   const dim3 grid(unsigned(int64_t(tiles) * pairs));
   if (a.out_f32) {
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, D, true, RT, WPE>), grid, dim3(kPfThreads), 0, a.stream, p, tiles, pairs);
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, D, true>), grid, dim3(kPpThreads), 0, a.stream, p, tiles, pairs);
   } else {
-    hipLaunchKernelGGL((prefill_mfma_kernel<T, D, false, RT, WPE>), grid, dim3(kPfThreads), 0, a.stream, p, tiles,
-                       pairs);
+    hipLaunchKernelGGL((prefill_mfma_kernel<T, D, false>), grid, dim3(kPpThreads), 0, a.stream, p, tiles, pairs);
   }
   return hipGetLastError();
 }
