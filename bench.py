@@ -38,6 +38,7 @@ METRIC = "paged decode KV GB/s and % of HBM peak (seqs/s) at 1 MI355X"
 # default partition, are reported in the same line (kernel figures only).
 HEADLINE = "longctx_bf16"
 EVENT_EVERY = 4  # timed steps per step whose decode launches are bracketed by timing events
+RING_GROUP = 8  # pinned metadata slots covered by one completion event
 EXTRA_CONFIGS = ["mha7b_f16", "gqa8b_bf16", "longctx_bf16"]
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix, published
@@ -774,15 +775,24 @@ def bench_decode(w, partition: int, args, full: bool = True) -> dict:
     plans = [ops.StepPlan(out, q, k_pool, v_pool, d_table, d_ctx, w.scale, ws, key=step_k, value=step_v,
                           slot_mapping=r["slots"], partition_size=partition,
                           append=(rows, r["pos"], r["nctx"]), host_args=host_args) for r in ring]
-    ring_done = [torch.cuda.Event() for _ in ring]
-    ring_used = [False] * len(ring)
+    # one event per group of RING_GROUP slots, recorded after the group's last
+    # write: an event record carries a system-scope fence that costs the step
+    # queue time, so one per step would be the step's largest overhead
+    n_groups = max(1, len(ring) // RING_GROUP)
+    ring_done = [torch.cuda.Event() for _ in range(n_groups)]
+    ring_used = [False] * n_groups
+
+    def ring_group(r):
+        return r * n_groups // len(ring)
 
     def prepare_step(i, append):
         """Host part of a step: block manager -> this step's pinned metadata."""
         r = i % len(ring)
         if append:
-            if ring_used[r]:
-                ring_done[r].synchronize()  # the write that last read this metadata slot has run
+            grp = ring_group(r)
+            if ring_used[grp] and r * n_groups % len(ring) == 0:
+                # first slot of a group: every write that last read the group has run
+                ring_done[grp].synchronize()
             _, cow = bm.append_tokens(seqs, slots_out=ring[r]["slots"].numpy())
             if len(cow):
                 raise RuntimeError("copy-on-write is not expected in this workload")
@@ -795,8 +805,10 @@ def bench_decode(w, partition: int, args, full: bool = True) -> dict:
         plan.cache_write()
         if not host_args:  # copied into the launch otherwise: the host may refill at once
             r = i % len(ring)
-            ring_done[r].record(stream)
-            ring_used[r] = True
+            if ring_group(r + 1) != ring_group(r) or r + 1 == len(ring):  # the group's last slot
+                grp = ring_group(r)
+                ring_done[grp].record(stream)
+                ring_used[grp] = True
 
     # decode is bracketed by events in every EVENT_EVERY-th timed step: the
     # partition kernel alone (the roofline's kernel) and with the merge.  An
