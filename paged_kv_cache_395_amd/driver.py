@@ -29,9 +29,50 @@ from .scheduler import Scheduler
 _TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
 
+class _DeviceEvent:
+    """A HIP event that only other streams wait on, created through the HIP
+    runtime torch loaded with hipEventDisableSystemFence | hipEventDisableTiming.
+    torch's events release to system scope at every record (an L2 write-back
+    and invalidate) so the host may read them; a stream-to-stream dependency
+    does not need that."""
+
+    _hip = None
+    _FLAGS = 0x20000000 | 0x2  # hipEventDisableSystemFence | hipEventDisableTiming
+
+    def __init__(self):
+        if _DeviceEvent._hip is None:
+            import os
+
+            lib = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+            lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            lib.hipStreamWaitEvent.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint]
+            lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            _DeviceEvent._hip = lib
+        self._h = ctypes.c_void_p()
+        self._check(_DeviceEvent._hip.hipEventCreateWithFlags(ctypes.byref(self._h), self._FLAGS),
+                    "hipEventCreateWithFlags")
+
+    @staticmethod
+    def _check(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def record(self, stream: ctypes.c_void_p) -> None:
+        self._check(_DeviceEvent._hip.hipEventRecord(self._h, stream), "hipEventRecord")
+
+    def make_wait(self, stream: ctypes.c_void_p) -> None:
+        """Work enqueued on ``stream`` from now on waits for the last record."""
+        self._check(_DeviceEvent._hip.hipStreamWaitEvent(stream, self._h, 0), "hipStreamWaitEvent")
+
+    def __del__(self):
+        if self._h and _DeviceEvent._hip is not None:
+            _DeviceEvent._hip.hipEventDestroy(self._h)
+
+
 class Driver:
     def __init__(self, num_blocks, num_host_blocks, num_q_heads, num_kv_heads, head_dim, dtype, max_rows,
-                 max_blocks_per_seq, max_batched_tokens, scale, free_order=None, device="cuda", ring=4,
+                 max_blocks_per_seq, max_batched_tokens, scale, free_order=None, device="cuda", ring=8,
                  partition_size=0, prefix_cache=False, block_size=16):
         self._l = _lib.load()
         self.dtype = dtype
@@ -72,9 +113,17 @@ class Driver:
         # swap-outs run on a second stream (default priority) beside the previous step's decode
         self.swap_stream = torch.cuda.Stream(dev)
         self._ss = ctypes.c_void_p(self.swap_stream.cuda_stream)
-        self._after_append = None  # recorded on the main stream after the last step's cache write
-        # pinned staging, one set per in-flight step
+        # recorded on the main stream after every step's cache write; a swap-out waits for it
+        self._after_append = _DeviceEvent()
+        self._appended = False
+        # pinned staging, one set per in-flight step, in two groups: one
+        # host-visible completion event per group, recorded after its last
+        # set's launch and waited for before its first set is refilled (each
+        # record of such an event costs the step a system-scope fence)
         pair_cap = 2 * max(num_blocks, nh)
+        self._groups = 2 if ring >= 4 else ring
+        self._group_done = [torch.cuda.Event() for _ in range(self._groups)]
+        self._group_used = [False] * self._groups
         self._ring = []
         for _ in range(ring):
             self._ring.append({
@@ -86,11 +135,13 @@ class Driver:
                 "in_pairs": torch.empty((pair_cap, 2), dtype=torch.int64).pin_memory(),
                 "cow": torch.empty((max_rows, 2), dtype=torch.int64).pin_memory(),
                 "patches": torch.empty((max_rows * max_blocks_per_seq, 3), dtype=torch.int32).pin_memory(),
-                "done": torch.cuda.Event(), "used": False,
             })
         self._i = 0
         self._code = _code(self.k_pool)
         self.steps = 0
+
+    def _group_of(self, i: int) -> int:
+        return i * self._groups // len(self._ring)
 
     # -- host half -------------------------------------------------------------
     def submit(self, seq: int, prompt_tokens: int, total_tokens: int, prompt_ids=None) -> None:
@@ -102,9 +153,11 @@ class Driver:
         T = len(st.slots)
         if T > self.cap:
             raise RuntimeError(f"step writes {T} tokens, more than the staging capacity {self.cap}")
-        r = self._ring[self._i % len(self._ring)]
-        if r["used"]:
-            r["done"].synchronize()  # the launch that last read this staging set has run
+        i = self._i % len(self._ring)
+        r = self._ring[i]
+        g = self._group_of(i)
+        if self._group_used[g] and i * self._groups % len(self._ring) == 0:
+            self._group_done[g].synchronize()  # the launches that last read this group's sets have run
         r["slots"].numpy()[:T] = st.slots
         r["rows"].numpy()[:T] = st.token_rows
         r["pos"].numpy()[:T] = st.token_positions
@@ -128,8 +181,8 @@ class Driver:
             # starts there, beside that decode.  This step's work waits for it: the freed blocks may
             # take this step's writes.  Host blocks it fills were released by swap-ins of earlier
             # steps, which ran before that cache write.
-            if self._after_append is not None:
-                self.swap_stream.wait_event(self._after_append)
+            if self._appended:
+                self._after_append.make_wait(self._ss)
             _lib.check(L.pa_swap_blocks(_p(self.k_host), _p(self.v_host), NH, _p(self.k_pool), _p(self.v_pool), NB,
                                         _p(r["out_pairs"]), len(st.swap_out), Hkv, D, self.bs, code, self._ss))
             swapped = torch.cuda.Event()
@@ -146,10 +199,13 @@ class Driver:
         _lib.check(L.pa_append_step(_p(self.key), _p(self.value), _p(self.k_pool), _p(self.v_pool), _p(r["slots"]),
                                     _p(r["rows"]), _p(r["pos"]), len(st.slots), _p(self.table), self.maxB,
                                     _p(self.ctx), _p(r["ctx"]), self.rows, Hkv, D, self.bs, NB, code, s))
-        r["done"].record(self.stream)  # also after the swap-out: the stream waited for it
-        r["used"] = True
-        self._after_append = torch.cuda.Event()
-        self._after_append.record(self.stream)
+        i = self._i % len(self._ring)
+        if i + 1 == len(self._ring) or self._group_of(i + 1) != self._group_of(i):  # the group's last set
+            g = self._group_of(i)
+            self._group_done[g].record(self.stream)  # also after the swap-out: the stream waited for it
+            self._group_used[g] = True
+        self._after_append.record(self._s)
+        self._appended = True
         self._i += 1
         # with every row empty the kernel still runs and writes zero rows
         max_ctx = max(int(st.context_lens.max()), 1)
