@@ -230,10 +230,13 @@ pa_status_t pa_patch_tables(int32_t* block_tables, int32_t max_blocks_per_seq, i
  * accumulation and an fp32 softmax.
  * ---------------------------------------------------------------------- */
 /* Effective partition size for these sizes (partition_size 0 = the
- * library's choice: 512 to 4096 tokens, as large as keeps >= 1024
- * workgroups; small enough that the longest context spans >= 4
- * partitions once the (sequence, kv head) pairs alone reach 1024, and 4096
- * once they reach 4096); -1 for invalid arguments. */
+ * library's choice: 512 tokens where the longest context spans more than 8
+ * partitions of 512 and the (sequence, kv head) pairs are fewer than 4096,
+ * which runs the persistent grid; otherwise 512 to 4096 tokens, as large as
+ * keeps >= 1024 workgroups, small enough that the longest context spans >= 4
+ * partitions once the pairs alone reach 1024, and 4096 once they reach
+ * 4096); -1 for invalid arguments.  pa_decode_noalloc takes the second rule
+ * where the first one's partials would not fit its array. */
 int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                                  int32_t partition_size);
 

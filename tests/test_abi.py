@@ -145,18 +145,19 @@ def test_workspace_size_formula():
 
 @pytest.mark.parametrize("S,Hkv,max_ctx,want", [
     (4, 4, 57, 512),          # tiny batch: nothing to split
-    (16, 8, 32768, 4096),     # few long sequences: split to fill the GPU, into large pieces
+    (16, 8, 32768, 512),      # few long sequences: the persistent grid, at its finest partitions
     (64, 32, 2048, 512),      # many pairs, short contexts: small pieces balance the ragged lengths
-    (256, 8, 8192, 2048),     # many pairs, a long tail of lengths
-    (256, 8, 7872, 2048),     # the longest context still spans 4 partitions of 2048
-    (256, 8, 6144, 1024),     # 3 partitions of 2048 would be too few
+    (256, 8, 8192, 512),      # many pairs, a long tail of lengths: > 8 partitions of 512, persistent
+    (256, 8, 4096, 1024),     # 8 partitions of 512 at most: the per-partition grid's rule, 4 of 1024
+    (256, 8, 3000, 512),      # 6 partitions of 512, 3 of 1024 would be too few
     (1024, 8, 1100, 4096),    # pairs enough to balance the GPU alone (>= 4096): no split below 4096 tokens
-    (512, 8, 20000, 4096),
+    (512, 8, 20000, 4096),    # the same for long contexts (the persistent rule is for fewer pairs)
+    (1, 1, 40 * 10 ** 6, 624),  # the finest partitions that keep the count within 65535
 ])
 def test_default_partition_choice(S, Hkv, max_ctx, want):
     p = L.pa_decode_partition_size(S, Hkv, max_ctx, 0)
     assert p == want
-    assert 512 <= p <= 4096 and p % 16 == 0
+    assert 512 <= p and p % 16 == 0 and -(-max_ctx // p) <= 65535
 
 
 def test_cache_write_and_copy_reject_bad_arguments():
