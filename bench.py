@@ -881,8 +881,8 @@ def bench_decode(w, partition: int, args, full: bool = True) -> dict:
     achieved23 = ev_bytes_mean / (k23_ms.mean() * 1e-3) / 1e9
     value = total_bytes / elapsed / 1e9
     used_partition = ops.decode_partition_size(S, Hkv, int(host_ctx.max()), partition)
-    kernel, nwg = ops.decode_launch_shape(q.dtype, D, out.dtype, S * per_step, Hq, Hkv, int(host_ctx.max()),
-                                          partition)
+    # the launch is over sequences; a sequence's queries share its workgroups
+    kernel, nwg = ops.decode_launch_shape(q.dtype, D, out.dtype, S, Hq, Hkv, int(host_ctx.max()), partition)
     grid = {"kernel": kernel, "workgroups": nwg}
     if not full:
         return {"workload": f"{w.name}: {w.description}", "partition": used_partition, "decode_grid": grid,

@@ -88,15 +88,16 @@ __device__ inline void store_out(void* out, int64_t idx, float v) {
   }
 }
 
-// Four consecutive output elements (idx a multiple of 4).
+// Four consecutive output elements (idx a multiple of 4), stored
+// non-temporally: nothing in the kernel reads them back.
 template <typename T, bool OUT_F32>
 __device__ inline void store_out4(void* out, int64_t idx, f32x4_t v) {
   if constexpr (OUT_F32) {
-    *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + idx) = v;
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + idx));
   } else {
     typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
     const u32x2_t p = {pack2(T::from_float(v[0]), T::from_float(v[1])), pack2(T::from_float(v[2]), T::from_float(v[3]))};
-    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + idx) = p;
+    __builtin_nontemporal_store(p, reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + idx));
   }
 }
 
@@ -196,12 +197,15 @@ struct SplitShared {
 };
 
 // One segment: tokens [tok0, tok0 + ntok) of kv head g of sequence s, the
-// partitions of that pair that fall to this workgroup.  With nseg == 1 the
-// segment is the whole context and the rows are final; otherwise they go to
-// partial slot `seg` of the pair's nseg.
-template <typename T, int D, bool OUT_F32>
-__device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>& sh, int s, int g, int ctx,
-                                               int tok0, int ntok, int nseg, int seg, bool first) {
+// partitions of that pair that fall to this workgroup.  segment_run folds
+// the tiles and leaves each wave's (max, sum, accumulator) in LDS;
+// segment_combine (below) merges the four waves into the pair's rows.
+// `mid` runs once per wave as soon as the segment's first tiles are in
+// flight: the persistent grid combines the previous segment there, so that
+// work and the new segment's first round trip to memory overlap.
+template <typename T, int D, typename Mid>
+__device__ __forceinline__ void segment_run(const KParams& P, DecodeShared<D>& sh, int s, int g, int ctx,
+                                            int tok0, int ntok, bool first, Mid&& mid) {
   constexpr int DC = D / 32;  // 16-byte chunks per lane per tile
   constexpr int NT = D / 16;  // 16-dim output tiles
   constexpr int kTileElems = kBlockTokens * D;
@@ -256,6 +260,7 @@ __device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>
   bool bad = false;
 
   const int ntw_all = nblk > w ? (nblk - w + kWaves - 1) / kWaves : 0;  // tiles of this wave
+  if (ntw_all == 0) mid();
   for (int wb = 0; wb < ntw_all; wb += kWave) {
     const int ntw = min(kWave, ntw_all - wb);
     const int tbl = lane < ntw ? trow[(tile0 + kWaves * (wb + lane) + w) >> tsh] : 0;
@@ -345,6 +350,7 @@ __device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>
     // two tiles in flight: while one is computed the other is loading
     u32x4_t ka[DC], va[DC], kb[DC], vb[DC];
     load(0, ka, va);
+    if (wb == 0) mid();
     load(1, kb, vb);
     for (int i = 0; i < ntw; i += 2) {
       step(ka, va, i);
@@ -356,12 +362,8 @@ __device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>
   lsum += shfl_xor(lsum, 16);
   lsum += shfl_xor(lsum, 32);
 
-  // ---- merge the 4 waves.  Each wave leaves its (max, sum) per column and
-  // its accumulator in LDS; then each half-wave combines one whole column
-  // (32 lanes x 4 dims): wave w takes columns w, w + 4, ..., its lower half
-  // the even ones of those.  Each lane reads the four waves' values of its
-  // four dims with 16-byte LDS reads and the column's four weights once, and
-  // a column's output row leaves as one contiguous run.
+  // ---- each wave leaves its (max, sum) per column and its accumulator in
+  // LDS for segment_combine.
   if (!first) __syncthreads();  // every reader of the previous segment's merge is done
   if (lane == 0) sh.bad[w] = __builtin_amdgcn_ballot_w64(bad) != 0;
   if (quad == 0) {
@@ -373,6 +375,26 @@ __device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>
     for (int t = 0; t < NT; ++t) *reinterpret_cast<f32x4_t*>(&sh.o[w][n][16 * t + 4 * quad]) = o[t];
   }
   __syncthreads();
+}
+
+// Merge of the four waves' results in LDS into the rows of (s, g): each
+// half-wave combines one whole column (32 lanes x 4 dims): wave w takes
+// columns w, w + 4, ..., its lower half the even ones of those.  Each lane
+// reads the four waves' values of its four dims with 16-byte LDS reads and
+// the column's four weights once, and a column's output row leaves as one
+// contiguous run.  With nseg == 1 the segment was the whole context and the
+// rows are final; otherwise they go to partial slot `seg` of the pair's nseg.
+template <typename T, int D, bool OUT_F32>
+__device__ __forceinline__ void segment_combine(const KParams& P, DecodeShared<D>& sh, int s, int g, int nseg,
+                                                int seg) {
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int G = P.hq / P.hkv;
+  const int C = P.qlen;
+  const int ncol = G * C;
+  auto col_row = [&](int c) {
+    return (int64_t(s) * C + c / G) * P.hq + int64_t(g) * G + c % G;
+  };
   static_assert(kWaves == 4, "one flag per wave");
   static_assert(D == 4 * 32 || D == 2 * 32, "a half-wave covers a row in whole 4-dim pieces");
   const bool any_bad = (sh.bad[0] | sh.bad[1] | sh.bad[2] | sh.bad[3]) != 0;
@@ -401,7 +423,7 @@ __device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>
         store_out4<T, OUT_F32>(P.out, row * D + d0, O * (1.f / L));
       } else {
         const int64_t prow = row * P.nparts_max + seg;
-        *reinterpret_cast<f32x4_t*>(P.ws_acc + prow * D + d0) = O;
+        __builtin_nontemporal_store(O, reinterpret_cast<f32x4_t*>(P.ws_acc + prow * D + d0));
         if (d0 == 0) {
           P.ws_m[prow] = M;
           P.ws_l[prow] = L;
@@ -409,6 +431,14 @@ __device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>
       }
     }
   }
+}
+
+// A whole segment, run and merged.
+template <typename T, int D, bool OUT_F32>
+__device__ __forceinline__ void decode_segment(const KParams& P, DecodeShared<D>& sh, int s, int g, int ctx,
+                                               int tok0, int ntok, int nseg, int seg) {
+  segment_run<T, D>(P, sh, s, g, ctx, tok0, ntok, true, [] {});
+  segment_combine<T, D, OUT_F32>(P, sh, s, g, nseg, seg);
 }
 
 // Rows of sequence s's kv head g that are written without reading: zeros
@@ -446,7 +476,7 @@ decode_partition_kernel(KParams P) {
   }
   const int tok0 = part * P.partition;
   if (tok0 >= ctx) return;
-  decode_segment<T, D, OUT_F32>(P, sh, s, g, ctx, tok0, min(P.partition, ctx - tok0), nparts, part, true);
+  decode_segment<T, D, OUT_F32>(P, sh, s, g, ctx, tok0, min(P.partition, ctx - tok0), nparts, part);
 }
 
 // The persistent grid.  Three waves per SIMD: two tiles in flight per wave
@@ -529,6 +559,12 @@ decode_persistent_kernel(KParams P) {
     int s = uniform(sp.s0);
     int64_t base = uniform64(sp.base0);
     bool first = true;  // no earlier segment's merge to wait for
+    // the previous segment, merged while the next one's first tiles load
+    bool pending = false;
+    int ps = 0, pg = 0, pnseg = 0, pseg = 0;
+    auto combine_previous = [&] {
+      if (pending) segment_combine<T, D, OUT_F32>(P, sh, ps, pg, pnseg, pseg);
+    };
     while (s < S && base < hi) {
       const int ctx = uniform(P.ctxs[s]);
       const int t = weight(ctx);
@@ -546,14 +582,20 @@ decode_persistent_kernel(KParams P) {
           const int nseg = int(owner(last) - first_owner + 1);
           const int tok0 = k0 * P.partition;
           const int ntok = min((k1 + 1) * P.partition, ctx) - tok0;
-          decode_segment<T, D, OUT_F32>(P, sh, s, g, ctx, tok0, ntok, nseg, int(b - first_owner), first);
+          segment_run<T, D>(P, sh, s, g, ctx, tok0, ntok, first, combine_previous);
           first = false;
+          pending = true;
+          ps = s;
+          pg = g;
+          pnseg = nseg;
+          pseg = int(b - first_owner);
           if (k0 == 0 && P.ws_nseg != nullptr && tid == 0) P.ws_nseg[int64_t(s) * P.hkv + g] = nseg;
         }
       }
       base += int64_t(t) * P.hkv;
       ++s;
     }
+    combine_previous();  // the last segment
   }
 
   // rows outside the stream: an empty context gives zeros, a length outside
