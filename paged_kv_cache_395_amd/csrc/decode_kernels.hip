@@ -770,92 +770,100 @@ decode_f32_kernel(KParams P) {
 }
 
 // ------------------------------------------------------------------------
-// Log-sum-exp merge of the partials.  Grid (Hq, S * qlen), D threads:
+// Log-sum-exp merge of the partials.  Workgroups per (sequence, kv head)
+// pair, grid (Hkv, S, row groups):
 //   M = max_j m_j,  w_j = 2^(m_j - M),  out = sum_j w_j acc_j / sum_j w_j l_j
-// over the partial slots j of the row's (sequence, kv head) pair, whose
-// count the partition kernel recorded (1: the row is already final).
-// Thread d owns output dim d.  A row of up to kReduceFew slots loads all
-// its partials at once; longer rows compute the weights of up to
-// kReduceChunk slots at a time once into LDS and read every slot's row
-// with one coalesced load.  Sums run in slot order, so the result is
-// deterministic.  A workspace whose header does not match this call's
-// geometry (not filled by the partition launch of the same sizes) gives
-// NaN rows instead of a merge at the wrong stride.
+// over the pair's partial slots j, whose count the partition kernel
+// recorded (at most 1: the pair's rows are already final, and the
+// workgroup leaves after that one read -- most pairs of a batch of short
+// contexts, where a workgroup per row spent the merge's time on dispatch).
+// A workgroup has one wave per row up to 4; with few pairs (a few long
+// contexts) a pair's rows are spread over several workgroups, one row per
+// wave, so no wave merges rows one after another.  Wave w of row group z
+// merges rows 4 z + w, then every (4 x groups)-th; lane i owns dims i,
+// i + 64, ...  A row of up to kReduceFew slots loads all its partials at
+// once; longer rows take the slots' weights 64 at a time, one per lane, and
+// read every slot's row with one coalesced load.  Sums run in slot order,
+// so the result is deterministic.  A workspace whose header does not match
+// this call's geometry (not filled by the partition launch of the same
+// sizes) gives NaN rows instead of a merge at the wrong stride.
 // ------------------------------------------------------------------------
-constexpr int kReduceChunk = 256;
 constexpr int kReduceFew = 8;  // rows with at most this many slots take the one-pass path
+constexpr int64_t kMergeManyPairs = 1024;  // from here on one workgroup per pair
 
 template <typename T, int D, bool OUT_F32>
-__global__ void __launch_bounds__(D)
+__global__ void __launch_bounds__(kThreads)
 decode_reduce_kernel(KParams P) {
-  constexpr int kW = D / kWave;
-  __shared__ float s_w[kReduceChunk];
-  __shared__ float s_red[kW];
-  const int h = blockIdx.x, sq = blockIdx.y;  // sq = s * qlen + query
-  const int s = sq / P.qlen;
-  const int d = threadIdx.x;
-  const int64_t orow = int64_t(sq) * P.hq + h;
+  constexpr int DL = D / kWave;  // dims per lane
+  const int g = blockIdx.x, s = blockIdx.y;
+  const int G = P.hq / P.hkv, C = P.qlen, ncol = G * C;
+  const int lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x / kWave;
+  const int c0 = blockIdx.z * nw + w, cstep = nw * gridDim.z;  // this wave's rows
+  // output row of column c: query c / G of head g * G + c % G
+  auto col_row = [&](int c) { return (int64_t(s) * C + c / G) * P.hq + int64_t(g) * G + c % G; };
   const int32_t* hd = P.ws_hdr;
   if (hd[0] != kWorkspaceMagic || hd[1] != P.partition || hd[2] != P.nparts_max || hd[3] != P.num_seqs * P.qlen ||
       hd[4] != P.hq || hd[5] != P.hkv || hd[6] != D || hd[7] != P.max_ctx) {
-    store_out<T, OUT_F32>(P.out, orow * D + d, __builtin_nanf(""));
+    for (int c = c0; c < ncol; c += cstep)
+      for (int d = lane; d < D; d += kWave) store_out<T, OUT_F32>(P.out, col_row(c) * D + d, __builtin_nanf(""));
     return;
   }
-  // partial slots of the row's pair, at most the partitions the workspace holds
-  const int nparts = min(P.ws_nseg[int64_t(s) * P.hkv + h / (P.hq / P.hkv)], P.nparts_max);
+  // partial slots of the pair, at most the partitions the workspace holds
+  const int nparts = min(P.ws_nseg[int64_t(s) * P.hkv + g], P.nparts_max);
   if (nparts <= 1) return;  // written by the partition kernel
-  const int64_t prow0 = orow * P.nparts_max;
 
-  if (nparts <= kReduceFew) {
-    // few slots (the common case): every partial of the row is loaded at
-    // once, with no barrier, so the merge costs one round trip to memory
-    // (entries past the row's last slot reload that one and weigh 0)
-    float mj[kReduceFew], lj[kReduceFew], aj[kReduceFew];
+  for (int c = c0; c < ncol; c += cstep) {
+    const int64_t orow = col_row(c);
+    const int64_t prow0 = orow * P.nparts_max;
+    float O[DL], L = 0.f;
 #pragma unroll
-    for (int j = 0; j < kReduceFew; ++j) {
-      const int jj = min(j, nparts - 1);
-      mj[j] = P.ws_m[prow0 + jj];
-      lj[j] = P.ws_l[prow0 + jj];
-      aj[j] = P.ws_acc[(prow0 + jj) * D + d];
+    for (int i = 0; i < DL; ++i) O[i] = 0.f;
+    if (nparts <= kReduceFew) {
+      // few slots (the common case): every partial of the row is loaded at
+      // once, so the merge costs one round trip to memory (entries past the
+      // row's last slot reload that one and weigh 0)
+      float mj[kReduceFew], lj[kReduceFew], aj[kReduceFew][DL];
+#pragma unroll
+      for (int j = 0; j < kReduceFew; ++j) {
+        const int jj = min(j, nparts - 1);
+        mj[j] = P.ws_m[prow0 + jj];
+        lj[j] = P.ws_l[prow0 + jj];
+#pragma unroll
+        for (int i = 0; i < DL; ++i) aj[j][i] = P.ws_acc[(prow0 + jj) * D + lane + kWave * i];
+      }
+      float M = mj[0];
+#pragma unroll
+      for (int j = 1; j < kReduceFew; ++j) M = fmaxf(M, mj[j]);
+#pragma unroll
+      for (int j = 0; j < kReduceFew; ++j) {
+        const float wj = j < nparts ? fast_exp2(mj[j] - M) : 0.f;
+        L += wj * lj[j];
+#pragma unroll
+        for (int i = 0; i < DL; ++i) O[i] += wj * aj[j][i];
+      }
+    } else {
+      float M = -INFINITY;
+      for (int j = lane; j < nparts; j += kWave) M = fmaxf(M, P.ws_m[prow0 + j]);
+#pragma unroll
+      for (int k = 1; k < kWave; k <<= 1) M = fmaxf(M, shfl_xor(M, k));
+      for (int j0 = 0; j0 < nparts; j0 += kWave) {
+        const int nj = min(kWave, nparts - j0);
+        // lane k holds slot j0 + k's weight and sum
+        const float wl = lane < nj ? fast_exp2(P.ws_m[prow0 + j0 + lane] - M) : 0.f;
+        const float ll = lane < nj ? P.ws_l[prow0 + j0 + lane] : 0.f;
+        for (int j = 0; j < nj; ++j) {
+          const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), j));
+          L += wj * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ll), j));
+#pragma unroll
+          for (int i = 0; i < DL; ++i) O[i] += wj * P.ws_acc[(prow0 + j0 + j) * D + lane + kWave * i];
+        }
+      }
     }
-    float M = mj[0];
 #pragma unroll
-    for (int j = 1; j < kReduceFew; ++j) M = fmaxf(M, mj[j]);
-    float L = 0.f, O = 0.f;
-#pragma unroll
-    for (int j = 0; j < kReduceFew; ++j) {
-      const float wj = j < nparts ? fast_exp2(mj[j] - M) : 0.f;
-      L += wj * lj[j];
-      O += wj * aj[j];
-    }
-    store_out<T, OUT_F32>(P.out, orow * D + d, O / L);
-    return;
+    for (int i = 0; i < DL; ++i) store_out<T, OUT_F32>(P.out, orow * D + lane + kWave * i, O[i] / L);
   }
-
-  float M = -INFINITY;
-  for (int j = d; j < nparts; j += D) M = fmaxf(M, P.ws_m[prow0 + j]);
-#pragma unroll
-  for (int k = 1; k < kWave; k <<= 1) M = fmaxf(M, shfl_xor(M, k));
-  if ((d & (kWave - 1)) == 0) s_red[d / kWave] = M;
-  __syncthreads();
-  M = s_red[0];
-#pragma unroll
-  for (int i = 1; i < kW; ++i) M = fmaxf(M, s_red[i]);
-
-  float L = 0.f, O = 0.f;
-  const float* acc = P.ws_acc + prow0 * D + d;
-  for (int j0 = 0; j0 < nparts; j0 += kReduceChunk) {
-    const int nj = min(kReduceChunk, nparts - j0);
-    __syncthreads();  // s_w and s_red of the previous round are consumed
-    for (int j = d; j < nj; j += D) s_w[j] = fast_exp2(P.ws_m[prow0 + j0 + j] - M);
-    __syncthreads();
-    for (int j = 0; j < nj; ++j) {
-      const float wj = s_w[j];
-      L += wj * P.ws_l[prow0 + j0 + j];
-      O += wj * acc[int64_t(j0 + j) * D];
-    }
-  }
-  store_out<T, OUT_F32>(P.out, orow * D + d, O / L);
 }
 
 KParams make_params(const DecodeArgs& a) {
@@ -938,11 +946,18 @@ hipError_t launch_mfma(const DecodeArgs& a, const KParams& p) {
 
 template <typename T, int D>
 hipError_t launch_reduce(const DecodeArgs& a, const KParams& p) {
-  const dim3 grid(unsigned(a.num_q_heads), unsigned(a.num_seqs) * unsigned(a.q_len));
+  // one wave per row of a pair up to kWaves; below kMergeManyPairs pairs the
+  // rows of a pair are spread over enough workgroups for a row per wave
+  const int rows = a.num_q_heads / a.num_kv_heads * a.q_len;
+  const int waves = std::min(kWaves, rows);
+  const int64_t pairs = int64_t(a.num_seqs) * a.num_kv_heads;
+  const int groups = pairs < kMergeManyPairs ? (rows + waves - 1) / waves : 1;
+  const dim3 grid(unsigned(a.num_kv_heads), unsigned(a.num_seqs), unsigned(groups));
+  const dim3 block(unsigned(waves * kWave));
   if (a.out_f32) {
-    hipLaunchKernelGGL((decode_reduce_kernel<T, D, true>), grid, dim3(D), 0, a.stream, p);
+    hipLaunchKernelGGL((decode_reduce_kernel<T, D, true>), grid, block, 0, a.stream, p);
   } else {
-    hipLaunchKernelGGL((decode_reduce_kernel<T, D, false>), grid, dim3(D), 0, a.stream, p);
+    hipLaunchKernelGGL((decode_reduce_kernel<T, D, false>), grid, block, 0, a.stream, p);
   }
   return hipGetLastError();
 }
