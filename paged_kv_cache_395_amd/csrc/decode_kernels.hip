@@ -163,8 +163,10 @@ __device__ inline int pair_tiles(int ctx, const KParams& P) {
 // in the workgroup hides.  The persistent split weighs every pair by its
 // tiles plus this, so a share of many short contexts holds fewer tiles
 // (measured on 256 lognormal GQA contexts: 267 us with 0, 254 us with 8, 255
-// with 16; 64 x U[128, 2048] MHA contexts: 196, 182, 182).
-constexpr int kSegmentCost = 8;
+// with 16; 64 x U[128, 2048] MHA contexts: 196, 182, 182; since a segment's
+// merge overlaps the next one's start, GQA 254 / 250.5 / 249.3 / 250.6 us
+// with 8 / 10 / 12 / 14, four queries per sequence and 16 x 32,768 equal).
+constexpr int kSegmentCost = 12;
 
 // The call's geometry, recorded by the partition kernel for the merge.
 __device__ inline void write_header(const KParams& P) {
