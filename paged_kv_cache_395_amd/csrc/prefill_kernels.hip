@@ -24,10 +24,12 @@
 // P is carried in fp16 (11 significant bits); the row sums are taken from
 // the same rounded P, so a weight's rounding changes numerator and
 // denominator together.  bf16 V is exact in fp16 below 2^16 in magnitude
-// (values under 2^-17 lose low bits, an absolute error below 2^-24); a run
-// of V holding anything larger, or a NaN, keeps its bf16 bits, and the pair
-// of blocks it belongs to runs in bf16 with each weight split exactly into
-// hi + lo bf16 halves instead.  The grid is one-dimensional and XCD-aware:
+// (values under 2^-17 lose low bits, an absolute error below 2^-24).  A
+// workgroup's key loop first runs with every V run in fp16; if a run held
+// anything larger, or a NaN, inside the context, the loop runs again on the
+// exact path, where such a run keeps its bf16 bits and the pair of blocks it
+// belongs to runs in bf16 with each weight split exactly into hi + lo bf16
+// halves instead.  The grid is one-dimensional and XCD-aware:
 // all row tiles of one (sequence, kv head) run on one XCD, so their shared
 // K / V stream is fetched from HBM once into that XCD's L2.
 
@@ -91,9 +93,12 @@ __device__ inline float quad_vmax(float v) {
 // bf16 pair -> fp16 pair (exact below 2^16 in magnitude); big collects the
 // largest magnitude seen (NaN once any value is NaN) so a wave can tell
 // whether its tile converted exactly
-__device__ inline uint32_t bf16x2_to_f16x2(uint32_t x, float& big) {
+// (only the halves `valid` keeps count toward big: slots past the context
+// are never read, whatever they hold)
+__device__ inline uint32_t bf16x2_to_f16x2(uint32_t x, uint32_t valid, float& big) {
   const float lo = __uint_as_float(x << 16), hi = __uint_as_float(x & 0xFFFF0000u);
-  big = vmax(big, vmax(__builtin_fabsf(lo), __builtin_fabsf(hi)));
+  const uint32_t xv = x & valid;
+  big = vmax(big, vmax(__builtin_fabsf(__uint_as_float(xv << 16)), __builtin_fabsf(__uint_as_float(xv & 0xFFFF0000u))));
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
 }
 // fp16 pair holding bf16-representable values -> the same values in bf16 (exact)
@@ -163,6 +168,7 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   // group h kept their bf16 bits (word pr covers the blocks of pair pr)
   __shared__ uint32_t s_keep[2][2];
   __shared__ int s_bad;
+  __shared__ int s_fallback;  // some V value of the workgroup's keys needs its bf16 bits
 
   const int id = blockIdx.x;
   const int full = (num_pairs / kXcds) * kXcds;
@@ -289,7 +295,24 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   // and 2 cc + 1, stored beside the paired block's part.
   typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
   const int run0 = grp * kRunsPerWave;
-  auto convert_own = [&](const u32x4_t* rbuf, u32x4_t* obuf, int slot) __attribute__((always_inline)) {
+  // On the fast pass the conversion is stored as it is and only reported
+  // (the pass is redone if any run needed its bf16 bits); the exact pass
+  // keeps such runs raw and records them per operand buffer for PV.
+  // In the masked tail `ntok` is the number of block my_blk's tokens inside
+  // the context: lane (quad, n)'s word j holds tokens 4 quad + 2 (j % 2) and
+  // the next one.
+  auto convert_own = [&](const u32x4_t* rbuf, u32x4_t* obuf, int slot, auto slow_tag, auto masked_tag, int ntok)
+      __attribute__((always_inline)) {
+    constexpr bool SLOW = decltype(slow_tag)::value;
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    uint32_t valid[2] = {~0u, ~0u};
+    if constexpr (MASKED) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = 4 * quad + 2 * h;
+        valid[h] = (t < ntok ? 0x0000FFFFu : 0u) | (t + 1 < ntok ? 0xFFFF0000u : 0u);
+      }
+    }
     u32x2_t* dst = reinterpret_cast<u32x2_t*>(obuf) + ((my_blk >> 1) * NT * 64 + lane) * 2 + (my_blk & 1);
     u32x4_t x[kRunsPerWave], y[kRunsPerWave];
 #pragma unroll
@@ -300,10 +323,15 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
 #pragma unroll
       for (int i = 0; i < kRunsPerWave; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) y[i][j] = bf16x2_to_f16x2(x[i][j], big);
+        for (int j = 0; j < 4; ++j) y[i][j] = bf16x2_to_f16x2(x[i][j], valid[j % 2], big);
       keep = __builtin_amdgcn_ballot_w64(!(big < kF16Limit)) != 0;
-    }
-    if (!kBf16 || keep) {
+      if constexpr (SLOW) {
+        if (keep) {
+#pragma unroll
+          for (int i = 0; i < kRunsPerWave; ++i) y[i] = x[i];
+        }
+      }
+    } else {
 #pragma unroll
       for (int i = 0; i < kRunsPerWave; ++i) y[i] = x[i];
     }
@@ -313,7 +341,10 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
       dst[(2 * cc) * 64 * 2] = u32x2_t{y[i][0], y[i][1]};
       dst[(2 * cc + 1) * 64 * 2] = u32x2_t{y[i][2], y[i][3]};
     }
-    if (lane == 0) reinterpret_cast<uint8_t*>(s_keep[slot])[my_blk * 2 + grp] = keep;
+    if constexpr (SLOW) {
+      if (lane == 0) reinterpret_cast<uint8_t*>(s_keep[slot])[my_blk * 2 + grp] = keep;
+    }
+    return keep;
   };
 
   float c = P.scale_log2;
@@ -394,9 +425,10 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
     }
   };
   // ---- PV of stage st: O^T += V^T P^T and l += 1 P^T per pair (K = 32)
-  auto pv = [&](auto masked_tag, int st, const u32x4_t* obuf, int slot, const u32x4_t (&ph)[RT][kStageBlocks / 2])
-      __attribute__((always_inline)) {
+  auto pv = [&](auto masked_tag, int st, const u32x4_t* obuf, int slot, const u32x4_t (&ph)[RT][kStageBlocks / 2],
+                auto slow_tag) __attribute__((always_inline)) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr bool SLOW = decltype(slow_tag)::value;  // the pass that honours kept bf16 runs
 #pragma unroll
     for (int pr = 0; pr < kStageBlocks / 2; ++pr) {
 #pragma unroll
@@ -416,7 +448,7 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
       }
       const u32x4_t* vop = obuf + pr * NT * 64 + lane;
       uint32_t keep = 0;
-      if constexpr (kBf16) keep = __builtin_amdgcn_readfirstlane(s_keep[slot][pr]);
+      if constexpr (kBf16 && SLOW) keep = __builtin_amdgcn_readfirstlane(s_keep[slot][pr]);
       if (keep == 0) {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
@@ -425,7 +457,7 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) o[rt][t] = Mfma<F16>::k32(av, ph[rt][pr], o[rt][t]);
         }
-      } else if constexpr (kBf16) {
+      } else if constexpr (kBf16 && SLOW) {
         // V of the pair partly kept in bf16: the pair runs in bf16 with each
         // fp16 weight split exactly into hi + lo bf16 halves (one row tile at
         // a time: this rare path must not hold more registers than the
@@ -463,71 +495,96 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
     }
   };
 
-  const int K = min(nst, (first_masked + 1) / (kStageBlocks * kBlockTokens));  // plain stages
-  f32x4_t sc[RT][kStageBlocks];
-  u32x4_t ph[RT][kStageBlocks / 2];
-  if (threadIdx.x == 0) s_bad = 0;
-  int entry_next = 0;  // group 0: table entry of the stage it fetches next
-  if (K > 0) {
-    if (grp == 0) {
-      issue_runs(0, lookup(0), s_k0, s_r0, 0, std::integral_constant<int, kRuns>{});
-      if (K > 1) entry_next = load_entry(1);
-      wait_loads();
+  if (threadIdx.x == 0) {
+    s_bad = 0;
+    s_fallback = 0;
+  }
+  // The key loop.  The fast pass takes every V run as fp16 (no per-pair
+  // branch in the matrix phase, so both pairs' products share one block);
+  // a run whose values need their bf16 bits (beyond fp16's range, or a NaN)
+  // flags the workgroup, which then runs the loop again on the exact path.
+  auto run = [&](auto slow_tag) __attribute__((always_inline)) {
+    bool fb = false;  // this wave converted a run that needs its bf16 bits
+    const int K = min(nst, (first_masked + 1) / (kStageBlocks * kBlockTokens));  // plain stages
+    f32x4_t sc[RT][kStageBlocks];
+    u32x4_t ph[RT][kStageBlocks / 2];
+    int entry_next = 0;  // group 0: table entry of the stage it fetches next
+    if (K > 0) {
+      if (grp == 0) {
+        issue_runs(0, lookup(0), s_k0, s_r0, 0, std::integral_constant<int, kRuns>{});
+        if (K > 1) entry_next = load_entry(1);
+        wait_loads();
+      }
+      __syncthreads();
+      if (grp == 1) {
+        fb |= convert_own(s_r0, s_o0, 0, slow_tag, std::false_type{}, 0);  // group 1's share of V(0), in the phase group 0 spends on M(0)
+        __syncthreads();
+      }
     }
-    __syncthreads();
-    if (grp == 1) {
-      convert_own(s_r0, s_o0, 0);  // group 1's share of V(0), in the phase group 0 spends on M(0)
+    // One stage: M(k), barrier, S(k), barrier.  Stage k uses buffers k % 2
+    // (fixed names per half of the loop body, so the compiler sees the loads
+    // into one never alias reads of the other).
+    auto stage = [&](int k, const u32x4_t* kb, const u32x4_t* ob_prev, int slot_prev, u32x4_t* kb_next,
+                     u32x4_t* rb_next, const u32x4_t* rb, u32x4_t* ob, int slot, u32x4_t* ob_next, int slot_next)
+        __attribute__((always_inline)) {
+      if (grp == 0 && k + 1 < K) {
+        issue_runs(k + 1, __builtin_amdgcn_readfirstlane(entry_next), kb_next, rb_next, 0,
+                   std::integral_constant<int, kRuns>{});
+        if (k + 2 < K) entry_next = load_entry(k + 2);
+      }
+      if (k > 0) pv(std::false_type{}, k - 1, ob_prev, slot_prev, ph, slow_tag);
+      qk(std::false_type{}, k, kb, sc);
+      __syncthreads();
+      softmax(sc, ph);
+      if (grp == 0) {
+        fb |= convert_own(rb, ob, slot, slow_tag, std::false_type{}, 0);  // V(k)
+        wait_loads();               // stage k + 1
+      } else if (k + 1 < K) {
+        fb |= convert_own(rb_next, ob_next, slot_next, slow_tag, std::false_type{}, 0);  // V(k + 1)
+      }
+      __syncthreads();
+    };
+    for (int k = 0; k < K; k += 2) {
+      stage(k, s_k0, s_o1, 1, s_k1, s_r1, s_r0, s_o0, 0, s_o1, 1);
+      if (k + 1 >= K) break;
+      stage(k + 1, s_k1, s_o0, 0, s_k0, s_r0, s_r1, s_o1, 1, s_o0, 0);
+    }
+    if (K > 0) {
+      // M(K): PV of the last plain stage; then the two groups meet again
+      if ((K - 1) % 2 == 0) pv(std::false_type{}, K - 1, s_o0, 0, ph, slow_tag);
+      else pv(std::false_type{}, K - 1, s_o1, 1, ph, slow_tag);
+      if (grp == 0) __syncthreads();
       __syncthreads();
     }
-  }
-  // One stage: M(k), barrier, S(k), barrier.  Stage k uses buffers k % 2
-  // (fixed names per half of the loop body, so the compiler sees the loads
-  // into one never alias reads of the other).
-  auto stage = [&](int k, const u32x4_t* kb, const u32x4_t* ob_prev, int slot_prev, u32x4_t* kb_next,
-                   u32x4_t* rb_next, const u32x4_t* rb, u32x4_t* ob, int slot, u32x4_t* ob_next, int slot_next)
-      __attribute__((always_inline)) {
-    if (grp == 0 && k + 1 < K) {
-      issue_runs(k + 1, __builtin_amdgcn_readfirstlane(entry_next), kb_next, rb_next, 0,
-                 std::integral_constant<int, kRuns>{});
-      if (k + 2 < K) entry_next = load_entry(k + 2);
+    // masked tail: both groups in step, each wave fetching half a block
+    for (int st = K; st < nst; ++st) {
+      issue_runs(st, lookup(st), s_k0, s_r0, run0, std::integral_constant<int, kRunsPerWave>{});
+      wait_loads();
+      __syncthreads();
+      fb |= convert_own(s_r0, s_o0, 0, slow_tag, std::true_type{}, ctx - (st * kStageBlocks + my_blk) * kBlockTokens);
+      __syncthreads();
+      f32x4_t scm[RT][kStageBlocks];
+      u32x4_t phm[RT][kStageBlocks / 2];
+      qk(std::true_type{}, st, s_k0, scm);
+      softmax(scm, phm);
+      pv(std::true_type{}, st, s_o0, 0, phm, slow_tag);
+      __syncthreads();
     }
-    if (k > 0) pv(std::false_type{}, k - 1, ob_prev, slot_prev, ph);
-    qk(std::false_type{}, k, kb, sc);
-    __syncthreads();
-    softmax(sc, ph);
-    if (grp == 0) {
-      convert_own(rb, ob, slot);  // V(k)
-      wait_loads();               // stage k + 1
-    } else if (k + 1 < K) {
-      convert_own(rb_next, ob_next, slot_next);  // V(k + 1)
-    }
-    __syncthreads();
+    if (fb && lane == 0) s_fallback = 1;
   };
-  for (int k = 0; k < K; k += 2) {
-    stage(k, s_k0, s_o1, 1, s_k1, s_r1, s_r0, s_o0, 0, s_o1, 1);
-    if (k + 1 >= K) break;
-    stage(k + 1, s_k1, s_o0, 0, s_k0, s_r0, s_r1, s_o1, 1, s_o0, 0);
-  }
-  if (K > 0) {
-    // M(K): PV of the last plain stage; then the two groups meet again
-    if ((K - 1) % 2 == 0) pv(std::false_type{}, K - 1, s_o0, 0, ph);
-    else pv(std::false_type{}, K - 1, s_o1, 1, ph);
-    if (grp == 0) __syncthreads();
-    __syncthreads();
-  }
-  // masked tail: both groups in step, each wave fetching half a block
-  for (int st = K; st < nst; ++st) {
-    issue_runs(st, lookup(st), s_k0, s_r0, run0, std::integral_constant<int, kRunsPerWave>{});
-    wait_loads();
-    __syncthreads();
-    convert_own(s_r0, s_o0, 0);
-    __syncthreads();
-    f32x4_t scm[RT][kStageBlocks];
-    u32x4_t phm[RT][kStageBlocks / 2];
-    qk(std::true_type{}, st, s_k0, scm);
-    softmax(scm, phm);
-    pv(std::true_type{}, st, s_o0, 0, phm);
-    __syncthreads();
+  run(std::false_type{});
+  if constexpr (kBf16) {
+    __syncthreads();  // every wave has reported: the flag is final
+    if (s_fallback) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        m[rt] = -INFINITY;
+        lacc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < NT; ++t) o[rt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      run(std::true_type{});
+    }
   }
 
   if (bad) s_bad = 1;

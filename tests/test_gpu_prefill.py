@@ -134,3 +134,32 @@ def test_prefill_with_values_beyond_half_precision_range():
     small = np.abs(ref).max(axis=(0, 1, 2)) < 100  # dims the large values never reach
     assert small.sum() > 100
     assert_close(got[..., small], ref[..., small], "bf16", "dims without large values")
+
+
+def test_prefill_ignores_nan_past_the_context():
+    """K and V slots past each context in its last block hold NaN: they are
+    outside every row's causal window, so the output is the clean result (the
+    half-precision pass checks only the tokens inside the context, and the
+    masked products never see the rest)."""
+    p = Prepared(make_workload("longctx_bf16", num_seqs=3, ctx=700, chunk=100, Hq=16, Hkv=2))
+    w = p.w
+    k, v = (a.copy() for a in p.oracle_pools())
+    poisoned = 0
+    for s, c in enumerate(p.ctx):
+        nb = -(-int(c) // 16)
+        tail = [int(p.table[s, nb - 1]) * 16 + o for o in range(int(c) - (nb - 1) * 16, 16)]
+        if tail:
+            nan = np.full((len(tail), w.num_kv_heads, w.head_dim), 0x7FC0, np.uint16)
+            OA.reshape_and_cache(k, v, nan, nan, np.array(tail))
+            poisoned += len(tail)
+    assert poisoned > 0
+    d = p.device()
+    d["k"] = to_dev(k, "bf16")
+    d["v"] = to_dev(v, "bf16")
+    q = to_dev(w.q, w.dtype)
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    say("[prefill] NaN past the context")
+    ops.prefill_chunk(out, q, d["k"], d["v"], d["table"], d["ctx"], w.scale, p.max_ctx)
+    kc, vc = p.oracle_pools()
+    ref = OA.prefill_chunk(w.q, kc, vc, p.table, p.ctx, w.scale, "bf16")
+    assert_close(out_f64(out), ref, "bf16", "NaN past the context")
