@@ -168,6 +168,22 @@ __device__ inline int pair_tiles(int ctx, const KParams& P) {
 // with 8 / 10 / 12 / 14, four queries per sequence and 16 x 32,768 equal).
 constexpr int kSegmentCost = 12;
 
+
+// Boundary x of the weighted stream, inside the pair whose weighted range
+// starts at a (tiles, nu partitions of ut tiles, the first starting at
+// pb = a + kSegmentCost): unchanged, or moved to pb (all of the pair after
+// it) or to just past the last partition's start (all of it before).
+__device__ inline int64_t snap_boundary(int64_t x, int64_t a, int tiles, int nu, int ut, int snap) {
+  const int64_t pb = a + kSegmentCost;
+  if (x <= pb) return x;
+  const int64_t k = (x - pb + ut - 1) / ut;  // partitions starting before x
+  if (k >= nu) return x;
+  const int64_t left = k * ut, right = tiles - left;
+  if (right <= snap && right <= left) return pb + int64_t(nu - 1) * ut + 1;
+  if (left <= snap) return pb;
+  return x;
+}
+
 // The call's geometry, recorded by the partition kernel for the merge.
 __device__ inline void write_header(const KParams& P) {
   int32_t* h = P.ws_hdr;
@@ -195,6 +211,7 @@ struct DecodeShared {
 struct SplitShared {
   int64_t scan[kThreads];
   int64_t total, base0;
+  int64_t lo, hi;  // the share's boundaries after snapping
   int s0;
 };
 
@@ -535,28 +552,59 @@ decode_persistent_kernel(KParams P) {
   // owns at least one of them: a pair's segments are numbered without gaps.
   const int64_t nw = max<int64_t>(1, min<int64_t>(gridDim.x, T_all / ut));
   const int64_t b = blockIdx.x;
-  const int64_t lo = T_all * b / nw;
-  const int64_t hi = b < nw ? T_all * (b + 1) / nw : lo;
-  if (lo < hi) {
-    // the thread whose sequences hold tile `lo` finds the first of them
+  const int64_t lo0 = T_all * b / nw;
+  const int64_t hi0 = b < nw ? T_all * (b + 1) / nw : lo0;
+  // A share boundary that would leave at most `snap` tiles of a pair on one
+  // side moves to that side's edge, so the pair is not split: the partials
+  // of a split pair cost decode time in proportion to its rows, the move's
+  // imbalance does not (on 256 lognormal contexts with 4 queries per
+  // sequence, 16 rows per pair: 293.6 us unmoved, 287 us with up to 16 or
+  // 32 tiles moved; with a fixed 16 tiles, 1-row pairs slowed by 1.3% and
+  // with 32 by 6%).  Boundaries move only inside the pair they fall in, at
+  // most one each way per pair, and never past another boundary while every
+  // share is longer than the move plus a partition.
+  const int rows = P.hq / P.hkv * P.qlen;
+  const int snap = T_all / nw > min(rows, ut) + ut ? min(rows, ut) : 0;
+  auto snap_at = [&](int64_t x, int s, int64_t base) {
+    const int ctx = P.ctxs[s];
+    const int t = weight(ctx);
+    const int64_t a = base + (x - base) / t * t;
+    return snap_boundary(x, a, pair_tiles(ctx, P), (ctx + P.partition - 1) / P.partition, ut, snap);
+  };
+  if (lo0 < hi0) {
+    // the threads whose sequences hold tiles lo0 and hi0 find them (the
+    // first also the sequence the share starts in)
     const int64_t e = sp.scan[tid];
-    if (e <= lo && lo < e + mine) {
+    if (e <= lo0 && lo0 < e + mine) {
       int64_t base = e;
       int s = sa;
       for (; s < sb; ++s) {
         const int64_t ts = int64_t(weight(P.ctxs[s])) * P.hkv;
-        if (base + ts > lo) break;
+        if (base + ts > lo0) break;
         base += ts;
       }
       sp.s0 = s;
       sp.base0 = base;
+      sp.lo = snap_at(lo0, s, base);
+    }
+    if (e <= hi0 && hi0 < e + mine) {
+      int64_t base = e;
+      int s = sa;
+      for (; s < sb; ++s) {
+        const int64_t ts = int64_t(weight(P.ctxs[s])) * P.hkv;
+        if (base + ts > hi0) break;
+        base += ts;
+      }
+      sp.hi = snap_at(hi0, s, base);
     }
   }
   __syncthreads();
-  if (lo < hi) {
+  if (lo0 < hi0) {
+    const int64_t lo = uniform64(sp.lo);
+    const int64_t hi = hi0 < T_all ? uniform64(sp.hi) : hi0;
     // pair (s, g) spans t = its tiles + kSegmentCost of the weighted stream;
     // its partition k starts at pb + k * ut and belongs to the workgroup
-    // whose share holds that position
+    // whose share holds that position once the boundaries have moved
     auto owner = [&](int64_t x) { return ((x + 1) * nw - 1) / T_all; };
     int s = uniform(sp.s0);
     int64_t base = uniform64(sp.base0);
@@ -572,16 +620,26 @@ decode_persistent_kernel(KParams P) {
       const int t = weight(ctx);
       if (t > 0) {
         const int nu = (ctx + P.partition - 1) / P.partition;
+        const int tiles = t - kSegmentCost;
         for (int g = 0; g < P.hkv; ++g) {
-          const int64_t pb = base + int64_t(g) * t + kSegmentCost;
+          const int64_t a = base + int64_t(g) * t;
+          const int64_t pb = a + kSegmentCost;
           if (pb >= hi) break;
           const int64_t last = pb + int64_t(nu - 1) * ut;  // the pair's last partition
           if (last < lo) continue;
           const int k0 = lo <= pb ? 0 : int((lo - pb + ut - 1) / ut);
           const int k1 = min(nu - 1, int((hi - pb + ut - 1) / ut) - 1);
           if (k0 > k1) continue;
-          const int64_t first_owner = owner(pb);
-          const int nseg = int(owner(last) - first_owner + 1);
+          // the first boundary past pb may have moved to pb, the last one
+          // before `last` past it
+          int64_t first_owner = owner(pb);
+          int64_t last_owner = owner(last);
+          if (first_owner < last_owner) {
+            const int64_t jf = first_owner + 1, jl = last_owner;
+            if (snap_boundary(T_all * jf / nw, a, tiles, nu, ut, snap) == pb) ++first_owner;
+            if (snap_boundary(T_all * jl / nw, a, tiles, nu, ut, snap) == last + 1) --last_owner;
+          }
+          const int nseg = int(last_owner - first_owner + 1);
           const int tok0 = k0 * P.partition;
           const int ntok = min((k1 + 1) * P.partition, ctx) - tok0;
           segment_run<T, D>(P, sh, s, g, ctx, tok0, ntok, first, combine_previous);

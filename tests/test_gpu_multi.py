@@ -7,7 +7,7 @@ import torch
 
 from oracle import attention as OA
 from paged_kv_cache_395_amd import PAError, ops
-from tests._gpu import Prepared, assert_close, out_f64, say, to_dev
+from tests._gpu import TORCH, Prepared, assert_close, out_f64, say, to_dev
 from workloads import make_workload
 
 pytestmark = pytest.mark.gpu
@@ -32,6 +32,26 @@ def test_multi_query_matches_oracle_on_ragged_contexts(partition):
     k, v = p.oracle_pools()
     ref = OA.prefill_chunk(p.w.q, k, v, p.table, p.ctx, p.w.scale, "bf16")
     assert_close(out_f64(out), ref, "bf16", f"P={partition}")
+
+
+def test_multi_query_with_moved_share_boundaries():
+    # The longest context spans 9 partitions of 512 (the persistent grid) and
+    # the shares are longer than 16 + 32 tiles, so a boundary that would
+    # leave at most 16 tiles (16 rows per pair) of a pair on one side moves
+    # to the pair's edge.  Every row is checked.
+    p = Prepared(make_workload("specdec_bf16", num_seqs=64, hi=4600))
+    w = p.w
+    kernel, grid = ops.decode_launch_shape(TORCH[w.dtype], w.head_dim, torch.float32, w.num_seqs, w.num_q_heads,
+                                           w.num_kv_heads, p.max_ctx)
+    weight = sum(((int(c) + 15) // 16 + 12) * w.num_kv_heads for c in p.ctx if c > 0)
+    assert kernel == "decode_persistent_kernel" and weight // min(grid, weight // 32) > 16 + 32, (kernel, grid, weight)
+    say(f"[multi] specdec 64 sequences, moved share boundaries, grid {grid}")
+    d = p.device()
+    p.write_step(d)
+    out = run_multi(p, d)
+    k, v = p.oracle_pools()
+    ref = OA.prefill_chunk(w.q, k, v, p.table, p.ctx, w.scale, "bf16")
+    assert_close(out_f64(out), ref, "bf16", "64 sequences")
 
 
 def test_multi_query_full_size_on_sampled_sequences():
