@@ -830,100 +830,97 @@ decode_f32_kernel(KParams P) {
 }
 
 // ------------------------------------------------------------------------
-// Log-sum-exp merge of the partials.  Workgroups per (sequence, kv head)
-// pair, grid (Hkv, S, row groups):
+// Log-sum-exp merge of the partials.  One workgroup per (sequence, kv head)
+// pair, grid (Hkv, S):
 //   M = max_j m_j,  w_j = 2^(m_j - M),  out = sum_j w_j acc_j / sum_j w_j l_j
 // over the pair's partial slots j, whose count the partition kernel
 // recorded (at most 1: the pair's rows are already final, and the
 // workgroup leaves after that one read -- most pairs of a batch of short
-// contexts, where a workgroup per row spent the merge's time on dispatch).
-// A workgroup has one wave per row up to 4; with few pairs (a few long
-// contexts) a pair's rows are spread over several workgroups, one row per
-// wave, so no wave merges rows one after another.  Wave w of row group z
-// merges rows 4 z + w, then every (4 x groups)-th; lane i owns dims i,
-// i + 64, ...  A row of up to kReduceFew slots loads all its partials at
-// once; longer rows take the slots' weights 64 at a time, one per lane, and
-// read every slot's row with one coalesced load.  Sums run in slot order,
+// contexts).  Thread t merges dims 8 (t % (D / 8)) .. + 7 of the pair's row
+// t / (D / 8), so all rows of a pair merge at once (with one wave per row,
+// the 16 rows of four queries per sequence took four round trips to memory
+// in series).  A row of up to kReduceFew slots loads all its partials at
+// once; longer rows run over their slots in order.  Sums run in slot order,
 // so the result is deterministic.  A workspace whose header does not match
 // this call's geometry (not filled by the partition launch of the same
 // sizes) gives NaN rows instead of a merge at the wrong stride.
 // ------------------------------------------------------------------------
-constexpr int kReduceFew = 8;  // rows with at most this many slots take the one-pass path
-constexpr int64_t kMergeManyPairs = 1024;  // from here on one workgroup per pair
+constexpr int kReduceFew = 8;  // rows with at most this many slots load them all at once
+constexpr int kMergeDims = 8;  // dims per thread
 
 template <typename T, int D, bool OUT_F32>
 __global__ void __launch_bounds__(kThreads)
 decode_reduce_kernel(KParams P) {
-  constexpr int DL = D / kWave;  // dims per lane
+  constexpr int kRowThreads = D / kMergeDims;
   const int g = blockIdx.x, s = blockIdx.y;
-  const int G = P.hq / P.hkv, C = P.qlen, ncol = G * C;
-  const int lane = lane_id();
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int nw = blockDim.x / kWave;
-  const int c0 = blockIdx.z * nw + w, cstep = nw * gridDim.z;  // this wave's rows
+  const int G = P.hq / P.hkv, C = P.qlen;
+  const int c = threadIdx.x / kRowThreads, d0 = threadIdx.x % kRowThreads * kMergeDims;
+  if (c >= G * C) return;
   // output row of column c: query c / G of head g * G + c % G
-  auto col_row = [&](int c) { return (int64_t(s) * C + c / G) * P.hq + int64_t(g) * G + c % G; };
+  const int64_t orow = (int64_t(s) * C + c / G) * P.hq + int64_t(g) * G + c % G;
+  auto store8 = [&](f32x4_t lo, f32x4_t hi) {
+    store_out4<T, OUT_F32>(P.out, orow * D + d0, lo);
+    store_out4<T, OUT_F32>(P.out, orow * D + d0 + 4, hi);
+  };
   const int32_t* hd = P.ws_hdr;
   if (hd[0] != kWorkspaceMagic || hd[1] != P.partition || hd[2] != P.nparts_max || hd[3] != P.num_seqs * P.qlen ||
       hd[4] != P.hq || hd[5] != P.hkv || hd[6] != D || hd[7] != P.max_ctx) {
-    for (int c = c0; c < ncol; c += cstep)
-      for (int d = lane; d < D; d += kWave) store_out<T, OUT_F32>(P.out, col_row(c) * D + d, __builtin_nanf(""));
+    const float nan = __builtin_nanf("");
+    store8(f32x4_t{nan, nan, nan, nan}, f32x4_t{nan, nan, nan, nan});
     return;
   }
   // partial slots of the pair, at most the partitions the workspace holds
   const int nparts = min(P.ws_nseg[int64_t(s) * P.hkv + g], P.nparts_max);
   if (nparts <= 1) return;  // written by the partition kernel
 
-  for (int c = c0; c < ncol; c += cstep) {
-    const int64_t orow = col_row(c);
-    const int64_t prow0 = orow * P.nparts_max;
-    float O[DL], L = 0.f;
+  const int64_t prow0 = orow * P.nparts_max;
+  const float* acc = P.ws_acc + prow0 * D + d0;
+  f32x4_t O0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, O1 = O0;
+  float L = 0.f;
+  // every partial of the row at once: one round trip to memory (entries
+  // past the row's last slot reload that one and weigh 0)
+  auto few = [&](auto nj_tag) __attribute__((always_inline)) {
+    constexpr int NJ = decltype(nj_tag)::value;
+    float mj[NJ], lj[NJ];
+    f32x4_t a0[NJ], a1[NJ];
 #pragma unroll
-    for (int i = 0; i < DL; ++i) O[i] = 0.f;
-    if (nparts <= kReduceFew) {
-      // few slots (the common case): every partial of the row is loaded at
-      // once, so the merge costs one round trip to memory (entries past the
-      // row's last slot reload that one and weigh 0)
-      float mj[kReduceFew], lj[kReduceFew], aj[kReduceFew][DL];
-#pragma unroll
-      for (int j = 0; j < kReduceFew; ++j) {
-        const int jj = min(j, nparts - 1);
-        mj[j] = P.ws_m[prow0 + jj];
-        lj[j] = P.ws_l[prow0 + jj];
-#pragma unroll
-        for (int i = 0; i < DL; ++i) aj[j][i] = P.ws_acc[(prow0 + jj) * D + lane + kWave * i];
-      }
-      float M = mj[0];
-#pragma unroll
-      for (int j = 1; j < kReduceFew; ++j) M = fmaxf(M, mj[j]);
-#pragma unroll
-      for (int j = 0; j < kReduceFew; ++j) {
-        const float wj = j < nparts ? fast_exp2(mj[j] - M) : 0.f;
-        L += wj * lj[j];
-#pragma unroll
-        for (int i = 0; i < DL; ++i) O[i] += wj * aj[j][i];
-      }
-    } else {
-      float M = -INFINITY;
-      for (int j = lane; j < nparts; j += kWave) M = fmaxf(M, P.ws_m[prow0 + j]);
-#pragma unroll
-      for (int k = 1; k < kWave; k <<= 1) M = fmaxf(M, shfl_xor(M, k));
-      for (int j0 = 0; j0 < nparts; j0 += kWave) {
-        const int nj = min(kWave, nparts - j0);
-        // lane k holds slot j0 + k's weight and sum
-        const float wl = lane < nj ? fast_exp2(P.ws_m[prow0 + j0 + lane] - M) : 0.f;
-        const float ll = lane < nj ? P.ws_l[prow0 + j0 + lane] : 0.f;
-        for (int j = 0; j < nj; ++j) {
-          const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wl), j));
-          L += wj * __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ll), j));
-#pragma unroll
-          for (int i = 0; i < DL; ++i) O[i] += wj * P.ws_acc[(prow0 + j0 + j) * D + lane + kWave * i];
-        }
-      }
+    for (int j = 0; j < NJ; ++j) {
+      const int jj = min(j, nparts - 1);
+      mj[j] = P.ws_m[prow0 + jj];
+      lj[j] = P.ws_l[prow0 + jj];
+      a0[j] = *reinterpret_cast<const f32x4_t*>(acc + int64_t(jj) * D);
+      a1[j] = *reinterpret_cast<const f32x4_t*>(acc + int64_t(jj) * D + 4);
     }
+    float M = mj[0];
 #pragma unroll
-    for (int i = 0; i < DL; ++i) store_out<T, OUT_F32>(P.out, orow * D + lane + kWave * i, O[i] / L);
+    for (int j = 1; j < NJ; ++j) M = fmaxf(M, mj[j]);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const float wj = j < nparts ? fast_exp2(mj[j] - M) : 0.f;
+      L += wj * lj[j];
+      O0 += wj * a0[j];
+      O1 += wj * a1[j];
+    }
+  };
+  if (nparts <= 2) {
+    few(std::integral_constant<int, 2>{});
+  } else if (nparts <= 4) {
+    few(std::integral_constant<int, 4>{});
+  } else if (nparts <= kReduceFew) {
+    few(std::integral_constant<int, kReduceFew>{});
+  } else {
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int j = 0; j < nparts; ++j) M = fmaxf(M, P.ws_m[prow0 + j]);
+#pragma unroll 4
+    for (int j = 0; j < nparts; ++j) {
+      const float wj = fast_exp2(P.ws_m[prow0 + j] - M);
+      L += wj * P.ws_l[prow0 + j];
+      O0 += wj * *reinterpret_cast<const f32x4_t*>(acc + int64_t(j) * D);
+      O1 += wj * *reinterpret_cast<const f32x4_t*>(acc + int64_t(j) * D + 4);
+    }
   }
+  store8(O0 / L, O1 / L);
 }
 
 KParams make_params(const DecodeArgs& a) {
@@ -1006,14 +1003,10 @@ hipError_t launch_mfma(const DecodeArgs& a, const KParams& p) {
 
 template <typename T, int D>
 hipError_t launch_reduce(const DecodeArgs& a, const KParams& p) {
-  // one wave per row of a pair up to kWaves; below kMergeManyPairs pairs the
-  // rows of a pair are spread over enough workgroups for a row per wave
-  const int rows = a.num_q_heads / a.num_kv_heads * a.q_len;
-  const int waves = std::min(kWaves, rows);
-  const int64_t pairs = int64_t(a.num_seqs) * a.num_kv_heads;
-  const int groups = pairs < kMergeManyPairs ? (rows + waves - 1) / waves : 1;
-  const dim3 grid(unsigned(a.num_kv_heads), unsigned(a.num_seqs), unsigned(groups));
-  const dim3 block(unsigned(waves * kWave));
+  // one workgroup per (sequence, kv head) pair, 8 dims of one row per thread
+  const int threads = a.num_q_heads / a.num_kv_heads * a.q_len * (D / kMergeDims);
+  const dim3 grid(unsigned(a.num_kv_heads), unsigned(a.num_seqs));
+  const dim3 block(unsigned((threads + kWave - 1) / kWave * kWave));
   if (a.out_f32) {
     hipLaunchKernelGGL((decode_reduce_kernel<T, D, true>), grid, block, 0, a.stream, p);
   } else {
