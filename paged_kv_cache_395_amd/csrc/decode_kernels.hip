@@ -168,6 +168,10 @@ __device__ inline int pair_tiles(int ctx, const KParams& P) {
 // with 8 / 10 / 12 / 14, four queries per sequence and 16 x 32,768 equal).
 constexpr int kSegmentCost = 12;
 
+// Share weights of the persistent split's even and odd workgroups (XCDs).
+constexpr int64_t kEvenShareWeight = 25;
+constexpr int64_t kOddShareWeight = 23;
+
 
 // Boundary x of the weighted stream, inside the pair whose weighted range
 // starts at a (tiles, nu partitions of ut tiles, the first starting at
@@ -552,8 +556,21 @@ decode_persistent_kernel(KParams P) {
   // owns at least one of them: a pair's segments are numbered without gaps.
   const int64_t nw = max<int64_t>(1, min<int64_t>(gridDim.x, T_all / ut));
   const int64_t b = blockIdx.x;
-  const int64_t lo0 = T_all * b / nw;
-  const int64_t hi0 = b < nw ? T_all * (b + 1) / nw : lo0;
+  // Workgroup b runs on XCD b % 8, and the odd XCDs finish equal shares
+  // about 8% later than the even ones; with one query per sequence the odd
+  // workgroups get 23/25 of an even one's share (measured on two MI355X:
+  // GQA lognormal -1.1 / -1.6%, 16 x 32,768 -1.0 / -1.1%, the reverse
+  // weighting +2 to 3.5% on every shape; four queries per sequence +0.5 /
+  // +0.7%, so those stay unweighted).  Only while every share stays at
+  // least two partitions long.  Boundary j sits at T_all C(j) / C(nw) with
+  // C(j) = ceil(j / 2) we + floor(j / 2) wo.
+  const bool weigh = P.qlen == 1 && T_all / nw >= 2 * ut;
+  const int64_t we = weigh ? kEvenShareWeight : 1, wo = weigh ? kOddShareWeight : 1;
+  auto cum = [&](int64_t j) { return (j + 1) / 2 * we + j / 2 * wo; };
+  const int64_t ctot = cum(nw);
+  auto boundary = [&](int64_t j) { return T_all * cum(j) / ctot; };
+  const int64_t lo0 = boundary(b);
+  const int64_t hi0 = b < nw ? boundary(b + 1) : lo0;
   // A share boundary that would leave at most `snap` tiles of a pair on one
   // side moves to that side's edge, so the pair is not split: the partials
   // of a split pair cost decode time in proportion to its rows, the move's
@@ -564,7 +581,7 @@ decode_persistent_kernel(KParams P) {
   // most one each way per pair, and never past another boundary while every
   // share is longer than the move plus a partition.
   const int rows = P.hq / P.hkv * P.qlen;
-  const int snap = T_all / nw > min(rows, ut) + ut ? min(rows, ut) : 0;
+  const int snap = T_all * min(we, wo) / ctot > min(rows, ut) + ut ? min(rows, ut) : 0;
   auto snap_at = [&](int64_t x, int s, int64_t base) {
     const int ctx = P.ctxs[s];
     const int t = weight(ctx);
@@ -605,7 +622,12 @@ decode_persistent_kernel(KParams P) {
     // pair (s, g) spans t = its tiles + kSegmentCost of the weighted stream;
     // its partition k starts at pb + k * ut and belongs to the workgroup
     // whose share holds that position once the boundaries have moved
-    auto owner = [&](int64_t x) { return ((x + 1) * nw - 1) / T_all; };
+    // the last boundary at or before x: the largest j with C(j) <= y
+    auto owner = [&](int64_t x) {
+      const int64_t y = ((x + 1) * ctot - 1) / T_all;
+      const int64_t k = y / (we + wo);
+      return 2 * k + (y - k * (we + wo) >= we ? 1 : 0);
+    };
     int s = uniform(sp.s0);
     int64_t base = uniform64(sp.base0);
     bool first = true;  // no earlier segment's merge to wait for
@@ -636,8 +658,8 @@ decode_persistent_kernel(KParams P) {
           int64_t last_owner = owner(last);
           if (first_owner < last_owner) {
             const int64_t jf = first_owner + 1, jl = last_owner;
-            if (snap_boundary(T_all * jf / nw, a, tiles, nu, ut, snap) == pb) ++first_owner;
-            if (snap_boundary(T_all * jl / nw, a, tiles, nu, ut, snap) == last + 1) --last_owner;
+            if (snap_boundary(boundary(jf), a, tiles, nu, ut, snap) == pb) ++first_owner;
+            if (snap_boundary(boundary(jl), a, tiles, nu, ut, snap) == last + 1) --last_owner;
           }
           const int nseg = int(last_owner - first_owner + 1);
           const int tok0 = k0 * P.partition;
