@@ -246,7 +246,9 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t
  *                              partition), vector ALUs
  *   PA_DECODE_GRID_PARTITIONS  fp16 / bf16 whose longest context spans at
  *                              most 8 partitions: one workgroup per (kv head,
- *                              sequence, partition)
+ *                              sequence, partition); with 16 or more kv heads
+ *                              and enough of them, dealt unevenly over the
+ *                              XCDs, plus up to ~5% that exit at once
  *   PA_DECODE_GRID_PERSISTENT  fp16 / bf16 beyond: as many workgroups as are
  *                              resident at once (occupancy x CUs, at most one
  *                              per partition); each takes an equal share of

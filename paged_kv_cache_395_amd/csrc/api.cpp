@@ -422,7 +422,7 @@ int32_t pa_decode_launch_shape(pa_dtype_t dtype, int32_t head_dim, pa_dtype_t ou
     n = std::max<int64_t>(1, std::min(decode_resident_workgroups(dtype, head_dim, out_dtype == PA_F32),
                                       int64_t(num_seqs) * num_kv_heads * nparts));
   } else {
-    n = int64_t(num_seqs) * num_kv_heads * nparts;
+    n = partition_grid_workgroups(int64_t(num_seqs) * num_kv_heads * nparts, num_kv_heads);
   }
   if (workgroups) *workgroups = n;
   return shape;

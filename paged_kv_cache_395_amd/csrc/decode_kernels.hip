@@ -487,7 +487,25 @@ template <typename T, int D, bool OUT_F32>
 __global__ void __launch_bounds__(kThreads)
 decode_partition_kernel(KParams P) {
   __shared__ DecodeShared<D> sh;
-  const int g = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+  // this workgroup's item (see partition_grid_workgroups): grid (Hkv, S,
+  // partitions), or one dimension dealt over the XCDs
+  int g = blockIdx.x, s = blockIdx.y, part = blockIdx.z;
+  const int64_t items = int64_t(P.hkv) * P.num_seqs * P.nparts_max;
+  if (partition_grid_weighted(items, P.hkv)) {  // items < 2^31 (checked at launch)
+    const uint32_t x = blockIdx.x % 8, r = blockIdx.x / 8;
+    uint32_t j;
+    if (x % 2 == 0) {
+      const uint32_t R = r / 25, rr = r % 25;
+      j = rr < 23 ? 192 * R + 8 * rr + x : 192 * R + 184 + 4 * (rr - 23) + x / 2;
+    } else {
+      j = 192 * (r / 23) + 8 * (r % 23) + x;
+    }
+    if (j >= uint32_t(items)) return;
+    const uint32_t hkv = uint32_t(P.hkv), js = j / hkv;
+    g = int(j - js * hkv);
+    s = int(js % uint32_t(P.num_seqs));
+    part = int(js / uint32_t(P.num_seqs));
+  }
   if (g == 0 && s == 0 && part == 0 && threadIdx.x == 0 && P.ws_hdr != nullptr) write_header(P);
   const int ctx = P.ctxs[s];
   const bool read = pair_tiles(ctx, P) > 0;
@@ -1011,7 +1029,10 @@ hipError_t launch_mfma_grid(const DecodeArgs& a, const KParams& p) {
 
 template <typename T, int D, bool OUT_F32>
 hipError_t launch_partition_grid(const DecodeArgs& a, const KParams& p) {
-  const dim3 grid(unsigned(a.num_kv_heads), unsigned(a.num_seqs), unsigned(a.num_partitions));
+  const int64_t items = int64_t(a.num_kv_heads) * a.num_seqs * a.num_partitions;
+  const dim3 grid = partition_grid_weighted(items, a.num_kv_heads)
+                        ? dim3(unsigned(partition_grid_workgroups(items, a.num_kv_heads)))
+                        : dim3(unsigned(a.num_kv_heads), unsigned(a.num_seqs), unsigned(a.num_partitions));
   hipLaunchKernelGGL((decode_partition_kernel<T, D, OUT_F32>), grid, dim3(kThreads), 0, a.stream, p);
   return hipGetLastError();
 }

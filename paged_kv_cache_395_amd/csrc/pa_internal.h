@@ -52,6 +52,25 @@ struct DecodeArgs {
 constexpr int32_t kPartitionGridMax = 8;
 inline bool decode_uses_persistent_grid(int32_t num_partitions) { return num_partitions > kPartitionGridMax; }
 
+// The per-partition grid's items ((kv head, sequence, partition), kv head
+// fastest) go to workgroup i = item i, which runs on XCD i % 8: kv head g on
+// XCD g % 8, so K/V blocks that several sequences share stay in one XCD's
+// L2.  With 16 or more kv heads (from 8 rounds of 192 items on) they are
+// dealt in rounds of 192 instead, each XCD 23 of them and the even XCDs 2
+// more, since the odd XCDs finish equal work about 8% later (7B MHA decode
+// -2.7%); with 8 kv heads that cost the shared-prefix batch 1.6% and the
+// serving loops' decode 2.5-5% through the blocks it moved off their XCD,
+// so there workgroup i stays item i.  Workgroups whose item is past the
+// last exit.
+constexpr int64_t kWeightedItemsMin = 8 * 192;
+constexpr int32_t kWeightedKvHeadsMin = 16;
+constexpr bool partition_grid_weighted(int64_t items, int32_t kv_heads) {
+  return items >= kWeightedItemsMin && items < (int64_t(1) << 31) && kv_heads >= kWeightedKvHeadsMin;
+}
+constexpr int64_t partition_grid_workgroups(int64_t items, int32_t kv_heads) {
+  return partition_grid_weighted(items, kv_heads) ? 8 * (25 * ((items - 1) / 192) + 25) : items;
+}
+
 // pa_decode with `scratch` (scratch_bytes) as its workspace; PA_EWORKSPACE
 // when the sizes need more.
 pa_status_t decode_in_scratch(void* scratch, size_t scratch_bytes, void* out, pa_dtype_t out_dtype, const void* q,
