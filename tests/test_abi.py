@@ -267,3 +267,18 @@ def test_gather_probe_rejects_bad_arguments():
     assert call(buf=8) == _lib.PA_EINVAL  # not 16-byte aligned
     assert call(tiles=None) == _lib.PA_EINVAL
     assert call(n=0, tiles=None) == _lib.PA_OK
+
+
+@pytest.mark.parametrize("S, Hq, Hkv, max_ctx, want", [
+    # 64 x 32 kv heads x 4 partitions of 512 = 8,192 items, dealt 25:23 to
+    # even and odd XCDs in rounds of 192: 8 x (25 x 42 + 25) workgroups
+    (64, 32, 32, 2048, 8 * (25 * (8191 // 192) + 25)),
+    # 8 kv heads: one workgroup per (kv head, sequence, partition)
+    (256, 32, 8, 2048, 256 * 8 * 4),
+    # 16 kv heads but fewer than 8 rounds of items: one per item
+    (4, 16, 16, 2048, 4 * 16 * 4),
+])
+def test_partition_grid_workgroups(S, Hq, Hkv, max_ctx, want):
+    n = ctypes.c_int64(0)
+    shape = L.pa_decode_launch_shape(_lib.PA_F16, 128, _lib.PA_F16, S, Hq, Hkv, max_ctx, 0, ctypes.byref(n))
+    assert shape == _lib.PA_DECODE_GRID_PARTITIONS and n.value == want
