@@ -576,10 +576,10 @@ decode_persistent_kernel(KParams P) {
   const int64_t b = blockIdx.x;
   // Workgroup b runs on XCD b % 8, and the odd XCDs finish equal shares
   // about 8% later than the even ones; with one query per sequence the odd
-  // workgroups get 23/25 of an even one's share (measured on two MI355X:
-  // GQA lognormal -1.1 / -1.6%, 16 x 32,768 -1.0 / -1.1%, the reverse
-  // weighting +2 to 3.5% on every shape; four queries per sequence +0.5 /
-  // +0.7%, so those stay unweighted).  Only while every share stays at
+  // workgroups get 23/25 of an even one's share (measured on three MI355X:
+  // GQA lognormal -1.6 / -1.1 / -2.2%, 16 x 32,768 -1.0 / -1.1 / -0.9%, the
+  // reverse weighting +2 to 3.5% on every shape; four queries per sequence
+  // +0.7 / +0.5%, so those stay unweighted).  Only while every share stays at
   // least two partitions long.  Boundary j sits at T_all C(j) / C(nw) with
   // C(j) = ceil(j / 2) we + floor(j / 2) wo.
   const bool weigh = P.qlen == 1 && T_all / nw >= 2 * ut;
