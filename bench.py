@@ -43,7 +43,8 @@ EXTRA_CONFIGS = ["mha7b_f16", "gqa8b_bf16", "longctx_bf16"]
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 matrix, published
 ESIZE = {"f32": 4, "f16": 2, "bf16": 2}
-KERNEL_SOURCES = ["paged_kv_cache_395_amd/csrc/decode_kernels.hip", "paged_kv_cache_395_amd/csrc/device_common.h"]
+KERNEL_SOURCES = ["paged_kv_cache_395_amd/csrc/decode_kernels.hip", "paged_kv_cache_395_amd/csrc/device_common.h",
+                  "paged_kv_cache_395_amd/csrc/pa_internal.h"]
 
 
 class TimingEvent:
