@@ -251,13 +251,17 @@ int32_t pa_decode_partition_size(int32_t num_seqs, int32_t num_kv_heads, int32_t
  *                              XCDs, plus up to ~5% that exit at once
  *   PA_DECODE_GRID_PERSISTENT  fp16 / bf16 beyond: as many workgroups as are
  *                              resident at once (occupancy x CUs, at most one
- *                              per partition); each takes an equal share of
- *                              the batch's tiles (each pair weighed by its
- *                              tiles plus a fixed start-up cost), whole
- *                              partitions only, and folds the partitions of
- *                              one (sequence, kv head) it holds in registers,
- *                              so the merge reads about one partial per
- *                              workgroup instead of one per partition.
+ *                              per partition); each takes a share of the
+ *                              batch's tiles (each pair weighed by its tiles
+ *                              plus a fixed start-up cost; with one query per
+ *                              sequence the odd XCDs' workgroups take 23/25
+ *                              of an even one's), whole partitions only, a
+ *                              boundary that would split off only a few tiles
+ *                              of a pair moved to the pair's edge, and folds
+ *                              the partitions of one (sequence, kv head) it
+ *                              holds in registers, so the merge reads about
+ *                              one partial per workgroup instead of one per
+ *                              partition.
  * -1 for invalid arguments.  Results are the same whichever shape runs
  * (within the stated tolerances; each shape is deterministic). */
 enum { PA_DECODE_GRID_VECTOR = 0, PA_DECODE_GRID_PARTITIONS = 1, PA_DECODE_GRID_PERSISTENT = 2 };
