@@ -277,6 +277,10 @@ def test_gather_probe_rejects_bad_arguments():
     (256, 32, 8, 2048, 256 * 8 * 4),
     # 16 kv heads but fewer than 8 rounds of items: one per item
     (4, 16, 16, 2048, 4 * 16 * 4),
+    # exactly 8 rounds (1,536 items) at 16 kv heads: dealt over the XCDs
+    (24, 16, 16, 2048, 8 * (25 * (1535 // 192) + 25)),
+    # 1,520 items, under 8 rounds: one per item
+    (95, 16, 16, 512, 95 * 16),
 ])
 def test_partition_grid_workgroups(S, Hq, Hkv, max_ctx, want):
     n = ctypes.c_int64(0)
