@@ -117,6 +117,25 @@ __device__ inline uint32_t f16x2_rne(float a, float b) {
 // margin of the reference max, inside fp16's range, with the smallest
 // weights 2^7 further above fp16's subnormals.  The offset cancels in O / l.
 constexpr float kPOffset = 7.f;
+// a weight from here up means the reference fell more than 8 below a score
+constexpr float kPOverflow = 32768.f;
+// The reference before any key: below every finite score, yet finite, so a
+// masked key's weight 2^(-inf - m) is exactly 0 (with m = -inf it would be
+// NaN and hide the first stage's overflow) and every other weight is +inf.
+constexpr float kMStart = -3.40282347e38f;
+
+// Whether any of the 2 x 8 fp16 values reaches `limit` (a NaN among them
+// hides the others: the max propagates it)
+__device__ inline bool f16_words_reach(const u32x4_t (&w)[2], float limit) {
+  typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+  typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
+  typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+  const h8_t a = __builtin_elementwise_maximum(__builtin_bit_cast(h8_t, w[0]), __builtin_bit_cast(h8_t, w[1]));
+  const h4_t b = __builtin_elementwise_maximum(__builtin_shufflevector(a, a, 0, 1, 2, 3),
+                                               __builtin_shufflevector(a, a, 4, 5, 6, 7));
+  const h2_t d = __builtin_elementwise_maximum(__builtin_shufflevector(b, b, 0, 1), __builtin_shufflevector(b, b, 2, 3));
+  return float(__builtin_elementwise_maximum(d.x, d.y)) >= limit;
+}
 // bf16 magnitudes from here up do not fit fp16; a tile holding one (or a
 // NaN) keeps its bf16 bits
 constexpr float kF16Limit = 65536.f;
@@ -244,7 +263,7 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   f32x4_t o[RT][NT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    m[rt] = -INFINITY;
+    m[rt] = kMStart;
     lacc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < NT; ++t) o[rt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -388,20 +407,43 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
   // ---- S: row max, reference check and rescale, P in fp16 (8 values per
   // lane, row tile and pair: tokens 4 quad + 0..3 of the pair's first block,
   // then of its second)
+  // The weights are formed first at the current reference; only when one of
+  // them reaches 2^15 (a score more than ~8 above the reference, or any key
+  // at the starting reference) is the row max taken, the reference moved and
+  // P formed again.  Without such a weight every P < 2^15 fits fp16, and
+  // with one the same rule as an up-front max check applies, so the result
+  // is that of checking the max first.  Only a NaN score (from NaN or
+  // infinite inputs) makes a NaN weight, and it hides only its own row's
+  // weights from the check (that row's output is NaN either way).
   auto softmax = [&](const f32x4_t (&sc)[RT][kStageBlocks], u32x4_t (&ph)[RT][kStageBlocks / 2])
       __attribute__((always_inline)) {
-    float bm[RT];
-    bool grow_any = false;
+    auto weights = [&]() __attribute__((always_inline)) {
 #pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      float v = -INFINITY;
+      for (int rt = 0; rt < RT; ++rt) {
+        const float neg_m = kPOffset - m[rt];
 #pragma unroll
-      for (int b = 0; b < kStageBlocks; ++b)
-        v = vmax(v, vmax(vmax(sc[rt][b][0], sc[rt][b][1]), vmax(sc[rt][b][2], sc[rt][b][3])));
-      bm[rt] = quad_vmax(v) * c;
-      grow_any |= bm[rt] > m[rt] + 8.f;
-    }
-    if (__builtin_amdgcn_ballot_w64(grow_any)) {
+        for (int pr = 0; pr < kStageBlocks / 2; ++pr) {
+          float e[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(sc[rt][2 * pr + j / 4][j % 4], c, neg_m));
+          ph[rt][pr] = u32x4_t{f16x2_rne(e[0], e[1]), f16x2_rne(e[2], e[3]), f16x2_rne(e[4], e[5]), f16x2_rne(e[6], e[7])};
+        }
+      }
+    };
+    weights();
+    bool over = false;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) over |= f16_words_reach(ph[rt], kPOverflow);
+    if (__builtin_amdgcn_ballot_w64(over)) {
+      float bm[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float v = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < kStageBlocks; ++b)
+          v = vmax(v, vmax(vmax(sc[rt][b][0], sc[rt][b][1]), vmax(sc[rt][b][2], sc[rt][b][3])));
+        bm[rt] = quad_vmax(v) * c;
+      }
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
         const float mn = bm[rt] > m[rt] + 8.f ? bm[rt] : m[rt];
@@ -411,17 +453,7 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
         for (int t = 0; t < NT; ++t) o[rt][t] *= alpha;
         m[rt] = mn;
       }
-    }
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const float neg_m = kPOffset - m[rt];
-#pragma unroll
-      for (int pr = 0; pr < kStageBlocks / 2; ++pr) {
-        float e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = fast_exp2(fmaf(sc[rt][2 * pr + j / 4][j % 4], c, neg_m));
-        ph[rt][pr] = u32x4_t{f16x2_rne(e[0], e[1]), f16x2_rne(e[2], e[3]), f16x2_rne(e[4], e[5]), f16x2_rne(e[6], e[7])};
-      }
+      weights();
     }
   };
   // ---- PV of stage st: O^T += V^T P^T and l += 1 P^T per pair (K = 32)
@@ -578,7 +610,7 @@ prefill_mfma_kernel(PParams P, int tiles_per_pair, int num_pairs) {
     if (s_fallback) {
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        m[rt] = -INFINITY;
+        m[rt] = kMStart;
         lacc[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int t = 0; t < NT; ++t) o[rt][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
