@@ -104,6 +104,30 @@ def test_prefill_follows_scores_that_keep_growing_along_the_context():
     assert_close(out_f64(out), ref, "bf16", "growing scores")
 
 
+def test_prefill_nan_query_spoils_only_its_own_row():
+    """One (sequence, query, head) row has a NaN query on top of the growing
+    scores above, so the reference moves again and again while that row's
+    weights are NaN in every stage.  Its output row is NaN; every other row,
+    the rows sharing its lanes, tiles and waves included, is the oracle's."""
+    p = Prepared(make_workload("longctx_bf16", num_seqs=2, ctx=1000, chunk=48, Hq=16, Hkv=2))
+    w = p.w
+    bits = w.k_pool.astype(np.uint32) << np.uint32(16)
+    k32 = bits.view(np.float32)
+    for s in range(w.num_seqs):
+        for lb in range(-(-int(p.ctx[s]) // 16)):
+            k32[p.table[s, lb]] *= np.float32(2.0 ** (lb // 8))
+    w.k_pool[...] = to_storage(k32, "bf16")
+    w.q[1, 20, 5, :] = 0x7FC0
+    say("[prefill] NaN query row with growing scores")
+    _, out = run_prefill(p)
+    got = out_f64(out)
+    assert np.all(np.isnan(got[1, 20, 5]))
+    k, v = p.oracle_pools()
+    ref = OA.prefill_chunk(w.q, k, v, p.table, p.ctx, w.scale, "bf16")
+    got[1, 20, 5] = ref[1, 20, 5] = 0.0
+    assert_close(got, ref, "bf16", "rows beside a NaN query row")
+
+
 def test_prefill_with_values_beyond_half_precision_range():
     """One V element of every third key block is 2^20, which half precision
     cannot hold: such blocks keep their bf16 bits and every pair of blocks
