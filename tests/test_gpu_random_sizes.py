@@ -69,7 +69,7 @@ def _prefill_cases(n, seed=20261204):
     return out
 
 
-@pytest.mark.parametrize("wseed, kw", _prefill_cases(16))
+@pytest.mark.parametrize("wseed, kw", _prefill_cases(24))
 def test_prefill_on_random_shapes_matches_oracle(wseed, kw):
     # chunks of 1 to 128 queries, head groups 1 to 8, both 16-bit types,
     # head_dim 64 / 128, blocks of 16 / 32 / 64 tokens
